@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of the dropless MoE layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+One step is one pass of the whole layer over one batch already resident in HBM:
+router GEMM + top-k, counts/offsets/permutation, permute, grouped gate/up GEMM with
+SiLU*mul, grouped down GEMM, the shared expert, and combine.  The step is issued as
+the sequence of C-ABI calls that moe_layer_fwd makes, with HIP events recorded on the
+launch stream between them, so every kernel's average duration is measured inside
+the timed region.  Prints one JSON line.
+
+The default workload is the single-GPU fusedmoe shape: T=8192 tokens, d=7168, E=8
+routed experts, top-4, d_e=2048 SwiGLU plus one shared expert (d_e=2048), bf16 with
+fp32 accumulation, segments padded to 128 rows.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s; grouped-GEMM TFLOP/s & permute GB/s vs roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="fusedmoe-8x2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter scale reference)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the GEMM kernel")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(2)
+
+    from dropless_grouped_gemm_amd import binding as B
+    from dropless_grouped_gemm_amd import ledger as LG
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(cfg, device=dev)
+    s = B.shape_of_config(cfg)
+    dt = inp.x.dtype
+    eb = 2 if cfg.dtype == "bf16" else 4
+    T, d, E, k, de = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_e
+    M = T * k
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+
+    # Buffers for the staged calls (the same intermediates moe_layer_fwd keeps in its
+    # workspace).
+    i32 = lambda *sh: torch.empty(sh, dtype=torch.int32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    routed = inp.topk_idx is not None
+    topk_idx = inp.topk_idx if routed else i32(T, k)
+    topk_w = inp.topk_w if routed else torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts, offs, pad = i32(E), i32(E + 1), i32(E + 1)
+    meta, nblk, pos, row_src, err = i32(mb, 3), i32(1), i32(M), i32(rows), i32(1)
+    x_perm = torch.empty((rows, d), dtype=dt, device=dev)
+    act = torch.empty((rows, de), dtype=dt, device=dev)
+    y = torch.empty((rows, d), dtype=dt, device=dev)
+    out = torch.empty((T, d), dtype=dt, device=dev)
+    ws = B.alloc_workspace(s, dev)
+    shared = cfg.d_e_shared > 0
+    if shared:
+        ds = cfg.d_e_shared
+        # the shared expert is one dense segment: a static single-expert block table
+        s_sh = B.make_shape(T=T, d=d, E=1, k=1, d_e=ds, block_m=cfg.block_m, dtype=cfg.dtype)
+        nb_sh = B.moe_max_blocks(s_sh)
+        meta_sh = torch.tensor([[0, b * cfg.block_m, min(cfg.block_m, T - b * cfg.block_m)]
+                                for b in range(nb_sh)], dtype=torch.int32, device=dev)
+        nblk_sh = torch.tensor([nb_sh], dtype=torch.int32, device=dev)
+        sh_act = torch.empty((T, ds), dtype=dt, device=dev)
+        sh_out = torch.empty((T, d), dtype=dt, device=dev)
+
+    stages = (["route"] if not routed else []) + ["offsets", "permute", "gateup", "down"]
+    if shared:
+        stages += ["shared_gateup", "shared_down"]
+    stages += ["combine"]
+
+    def step(ev=None):
+        i = 0
+        if ev is not None:
+            ev[i].record()
+        if not routed:
+            B.moe_route(s, inp.x, inp.w_gate, inp.bias, logits, topk_idx, topk_w, ws)
+            i += 1
+            if ev is not None:
+                ev[i].record()
+        B.moe_build_offsets(s, topk_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+        i += 1
+        if ev is not None:
+            ev[i].record()
+        B.moe_permute(s, inp.x, pos, x_perm)
+        i += 1
+        if ev is not None:
+            ev[i].record()
+        B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk, mb, act)
+        i += 1
+        if ev is not None:
+            ev[i].record()
+        B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y)
+        i += 1
+        if ev is not None:
+            ev[i].record()
+        if shared:
+            B.moe_grouped_gemm(s_sh, B.MOE_OP_GATEUP_SWIGLU, inp.x, inp.ws1, inp.ws3, meta_sh,
+                               nblk_sh, nb_sh, sh_act)
+            i += 1
+            if ev is not None:
+                ev[i].record()
+            B.moe_grouped_gemm(s_sh, B.MOE_OP_DOWN, sh_act, inp.ws2, None, meta_sh, nblk_sh,
+                               nb_sh, sh_out)
+            i += 1
+            if ev is not None:
+                ev[i].record()
+        B.moe_combine(s, y, pos, topk_w, sh_out if shared else None, out)
+        i += 1
+        if ev is not None:
+            ev[i].record()
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    nst = len(stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for kk in range(args.steps):
+        step(evs[kk])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {st: 0.0 for st in stages}
+    total_ms = 0.0
+    for kk in range(args.steps):
+        for j, st in enumerate(stages):
+            stage_ms[st] += evs[kk][j].elapsed_time(evs[kk][j + 1])
+        total_ms += evs[kk][0].elapsed_time(evs[kk][nst])
+    ms_per_step = total_ms / args.steps
+    for st in stages:
+        stage_ms[st] /= args.steps
+    if int(err.item()) != 0:
+        raise RuntimeError("device reported out-of-range expert ids")
+
+    # cross-check: the single moe_layer_fwd call runs the same kernels
+    out2 = torch.empty_like(out)
+    ws2 = B.alloc_workspace(s, dev)
+    B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1, inp.ws3,
+                    inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nrep = max(3, args.steps // 2)
+    e0.record()
+    for _ in range(nrep):
+        B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1, inp.ws3,
+                        inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
+    e1.record()
+    torch.cuda.synchronize()
+    layer_fwd_ms = e0.elapsed_time(e1) / nrep
+    same = bool(torch.equal(out.view(torch.int16) if eb == 2 else out.view(torch.int32),
+                            out2.view(torch.int16) if eb == 2 else out2.view(torch.int32)))
+    del ws2, out2
+
+    # ---- algorithmic work per launch --------------------------------------------
+    cnt = counts.cpu().tolist()
+    active = sum(1 for c in cnt if c > 0)
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    gu_flops = LG.gateup_flops(M, d, de)
+    dn_flops = LG.down_flops(M, d, de)
+    gemm = {
+        "gateup": {"tflops": gu_flops / (stage_ms["gateup"] * 1e9),
+                   "flops": gu_flops, "us": stage_ms["gateup"] * 1e3},
+        "down": {"tflops": dn_flops / (stage_ms["down"] * 1e9),
+                 "flops": dn_flops, "us": stage_ms["down"] * 1e3},
+    }
+    if shared:
+        sg, sd = LG.gateup_flops(T, d, cfg.d_e_shared), LG.down_flops(T, d, cfg.d_e_shared)
+        gemm["shared_gateup"] = {"tflops": sg / (stage_ms["shared_gateup"] * 1e9), "flops": sg,
+                                 "us": stage_ms["shared_gateup"] * 1e3}
+        gemm["shared_down"] = {"tflops": sd / (stage_ms["shared_down"] * 1e9), "flops": sd,
+                               "us": stage_ms["shared_down"] * 1e3}
+    for v in gemm.values():
+        v["frac"] = v["tflops"] / peak
+    pb = LG.permute_bytes(T, k, d, eb)
+    cb = LG.combine_bytes(T, k, d, eb, shared)
+    moves = {
+        "permute": {"gbps": pb / (stage_ms["permute"] * 1e6), "bytes": pb,
+                    "us": stage_ms["permute"] * 1e3},
+        "combine": {"gbps": cb / (stage_ms["combine"] * 1e6), "bytes": cb,
+                    "us": stage_ms["combine"] * 1e3},
+    }
+    if not routed:
+        rb = LG.router_bytes(T, d, E, eb)
+        moves["route"] = {"gbps": rb / (stage_ms["route"] * 1e6), "bytes": rb,
+                          "us": stage_ms["route"] * 1e3}
+    for v in moves.values():
+        v["frac"] = v["gbps"] / PEAK_HBM_GBPS
+
+    # the dominant kernel: the one with the largest share of the step
+    dom = max(("gateup", "down", "shared_gateup", "shared_down"),
+              key=lambda n: stage_ms.get(n, -1.0))
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        if tr.get("config") == cfg.name and tr.get("kernel") == dom:
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": gemm[dom]["tflops"], "peak": peak,
+                "unit": "TFLOP/s", "frac": gemm[dom]["frac"], "traffic": traffic}
+
+    # ---- CPU oracle on a bounded sample -----------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": T / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; N(0,1) tokens, N(0,1/fan_in) weights, random-init)",
+        "config": {"workload": cfg.description, "name": cfg.name, "T": T, "d": d, "E": E, "k": k,
+                   "d_e": de, "d_e_shared": cfg.d_e_shared, "block_m": cfg.block_m,
+                   "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "seed": cfg.seed},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_us": {st: round(v * 1e3, 2) for st, v in stage_ms.items()},
+        "gemm": gemm,
+        "moves": moves,
+        "layer_fwd_ms_per_call": layer_fwd_ms,
+        "layer_fwd_matches_staged": same,
+        "active_experts": active,
+        "wall_s": wall,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """The oracle (fp64, numpy; matrix products through the BLAS it links) on the
+    first S tokens of the same inputs, S chosen to take about target_s seconds."""
+    import numpy as np
+    import torch
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    h = lambda t: None if t is None else t.detach().to(torch.float64).cpu().numpy()
+    w1, w3, w2 = h(inp.w1), h(inp.w3), h(inp.w2)
+    wg, bias = h(inp.w_gate), h(inp.bias)
+    ws1, ws3, ws2 = h(inp.ws1), h(inp.ws3), h(inp.ws2)
+    x_all = inp.x
+
+    def run(S):
+        x = h(x_all[:S])
+        kw = dict(k=cfg.k, block_m=cfg.block_m, ws1=ws1, ws3=ws3, ws2=ws2)
+        if inp.topk_idx is not None:
+            kw.update(topk_idx=inp.topk_idx[:S].cpu().numpy(), topk_w=h(inp.topk_w[:S]))
+        else:
+            kw.update(w_gate=wg, bias=bias, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                      renormalize=cfg.renormalize)
+        t0 = time.perf_counter()
+        O.moe_layer(x, w1, w3, w2, **kw)
+        return time.perf_counter() - t0
+
+    S0 = min(cfg.T, 64)
+    t0 = run(S0)
+    S = int(min(cfg.T, max(S0, S0 * target_s / max(t0, 1e-3))))
+    t = run(S) if S != S0 else t0
+    return {"value": S / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens of the same workload, whole layer in fp64 "
+                      f"({t:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+"""Thin Python binding of libmoe's C ABI (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does nothing
+but turn torch tensors into device pointers, pick the current HIP stream and
+raise on a non-zero status; every step of the layer runs in the HIP kernels of
+libmoe.so.  PyTorch provides device memory and streams.  There is no fallback:
+if the library is missing, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime libmoe.so links against (same soname)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
+MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
+MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
+
+ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
+                "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
+                "moe_grouped_gemm", "moe_combine", "moe_layer_fwd")
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "E", "k", "d_e", "n_groups", "topk_groups", "renormalize",
+                 "block_m", "d_e_shared", "dtype")]
+
+
+_LAYOUT_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "padded_offsets",
+                  "block_meta", "num_blocks", "pos", "row_src", "err_flag", "x_perm", "act", "y",
+                  "shared_act", "shared_out", "scratch", "total")
+
+
+class moe_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m dropless_grouped_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        S = ctypes.POINTER(moe_shape)
+        L.moe_status_str.argtypes = [ctypes.c_int32]
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_max_blocks.argtypes = [S]
+        L.moe_max_blocks.restype = ctypes.c_int32
+        L.moe_max_rows.argtypes = [S]
+        L.moe_max_rows.restype = ctypes.c_int64
+        L.moe_workspace_bytes.argtypes = [S]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_layout.argtypes = [S, ctypes.POINTER(moe_ws_layout)]
+        L.moe_workspace_layout.restype = ctypes.c_int32
+        L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_route.restype = ctypes.c_int32
+        L.moe_build_offsets.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_build_offsets.restype = ctypes.c_int32
+        L.moe_permute.argtypes = [S, P, P, P, P]
+        L.moe_permute.restype = ctypes.c_int32
+        L.moe_grouped_gemm.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
+        L.moe_grouped_gemm.restype = ctypes.c_int32
+        L.moe_combine.argtypes = [S, P, P, P, P, P, P]
+        L.moe_combine.restype = ctypes.c_int32
+        L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.moe_layer_fwd.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(status).decode()
+
+
+def make_shape(T, d, E, k, d_e, block_m, dtype="bf16", n_groups=0, topk_groups=0,
+               renormalize=False, d_e_shared=0) -> moe_shape:
+    dt = {"bf16": MOE_DTYPE_BF16, "fp32": MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16,
+          torch.float32: MOE_DTYPE_F32}[dtype]
+    return moe_shape(T, d, E, k, d_e, n_groups, topk_groups, int(bool(renormalize)), block_m,
+                     d_e_shared, dt)
+
+
+def shape_of_config(cfg) -> moe_shape:
+    """moe_shape of a workloads.MoEConfig."""
+    return make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_e, cfg.block_m, cfg.dtype, cfg.n_groups,
+                      cfg.topk_groups, cfg.renormalize, cfg.d_e_shared)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# Host-only helpers
+# ---------------------------------------------------------------------------
+def moe_max_blocks(shape: moe_shape) -> int:
+    return lib().moe_max_blocks(ctypes.byref(shape))
+
+
+def moe_max_rows(shape: moe_shape) -> int:
+    return lib().moe_max_rows(ctypes.byref(shape))
+
+
+def moe_workspace_bytes(shape: moe_shape) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_workspace_layout(shape: moe_shape) -> dict:
+    L = moe_ws_layout()
+    _check("moe_workspace_layout", lib().moe_workspace_layout(ctypes.byref(shape), ctypes.byref(L)))
+    return {n: getattr(L, n) for n in _LAYOUT_FIELDS}
+
+
+def alloc_workspace(shape: moe_shape, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(shape)
+    if n == 0:
+        raise MoEError("moe_workspace_bytes", MOE_EINVAL)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def ws_view(ws: torch.Tensor, shape: moe_shape, name: str, dtype: torch.dtype, shape_out):
+    """A typed view of one intermediate inside a moe_layer_fwd workspace."""
+    off = moe_workspace_layout(shape)[name]
+    n = 1
+    for s in shape_out:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype).view(*shape_out)
+
+
+# ---------------------------------------------------------------------------
+# Entry points
+# ---------------------------------------------------------------------------
+def moe_route(shape, x, w_gate, bias, logits, topk_idx, topk_w, ws, stream=None):
+    _check("moe_route", lib().moe_route(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias),
+                                        _p(logits), _p(topk_idx), _p(topk_w), _p(ws),
+                                        ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_build_offsets(shape, topk_idx, counts, offsets, padded_offsets, block_meta, num_blocks,
+                      pos, row_src, err_flag, ws, stream=None):
+    _check("moe_build_offsets", lib().moe_build_offsets(
+        ctypes.byref(shape), _p(topk_idx), _p(counts), _p(offsets), _p(padded_offsets),
+        _p(block_meta), _p(num_blocks), _p(pos), _p(row_src), _p(err_flag), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_permute(shape, x, pos, x_perm, stream=None):
+    _check("moe_permute", lib().moe_permute(ctypes.byref(shape), _p(x), _p(pos), _p(x_perm),
+                                            _stream(stream)))
+
+
+def moe_grouped_gemm(shape, op, A, B0, B1, block_meta, num_blocks, max_blocks, C, stream=None):
+    _check("moe_grouped_gemm", lib().moe_grouped_gemm(
+        ctypes.byref(shape), op, _p(A), _p(B0), _p(B1), _p(block_meta), _p(num_blocks),
+        int(max_blocks), _p(C), _stream(stream)))
+
+
+def moe_combine(shape, y, pos, topk_w, shared_out, out, stream=None):
+    _check("moe_combine", lib().moe_combine(ctypes.byref(shape), _p(y), _p(pos), _p(topk_w),
+                                            _p(shared_out), _p(out), _stream(stream)))
+
+
+def moe_layer_fwd(shape, x, w_gate, bias, w1, w3, w2, ws1, ws3, ws2, topk_idx_in, topk_w_in,
+                  out, ws, stream=None):
+    _check("moe_layer_fwd", lib().moe_layer_fwd(
+        ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), _p(ws1),
+        _p(ws3), _p(ws2), _p(topk_idx_in), _p(topk_w_in), _p(out), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))

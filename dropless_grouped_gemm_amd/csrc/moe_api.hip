@@ -1,0 +1,287 @@
+// C ABI of libmoe: argument validation, workspace layout and the layer pipeline.
+//
+// Every entry point validates its arguments on the host and returns a status before
+// anything is enqueued; kernels then run on the caller's stream.  Nothing here
+// allocates, frees or synchronises, and no value travels from device to host: the
+// grouped GEMM is launched with a grid derived from the static upper bound
+// moe_max_blocks, and reads the real block count from device memory (dropless notes
+// section 7: the host only needs to know how much work to launch, not the shapes).
+#include "moe_internal.h"
+
+#include <atomic>
+
+namespace moe {
+
+static constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+static int elem_bytes(const moe_shape& s) { return s.dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+// Shape checks common to every call.  Returns MOE_OK, MOE_EINVAL or MOE_ENOTSUP.
+static moe_status check_shape(const moe_shape* sp) {
+  if (!sp) return MOE_EINVAL;
+  const moe_shape& s = *sp;
+  if (s.dtype != MOE_DTYPE_F32 && s.dtype != MOE_DTYPE_BF16) return MOE_EINVAL;
+  const int mult = s.dtype == MOE_DTYPE_BF16 ? 8 : 4;  // 16-byte rows
+  if (s.T < 0 || s.d < 1 || s.E < 1 || s.k < 1 || s.d_e < 1) return MOE_EINVAL;
+  if (s.d % mult || s.d_e % mult) return MOE_EINVAL;
+  if (s.k > s.E) return MOE_EINVAL;
+  if (s.E > 1024) return MOE_ENOTSUP;
+  if ((int64_t)s.T * s.k >= (int64_t)1 << 31) return MOE_EINVAL;
+  if (s.n_groups < 0 || s.topk_groups < 0) return MOE_EINVAL;
+  if (s.n_groups == 0) {
+    if (s.topk_groups != 0) return MOE_EINVAL;
+  } else {
+    if (s.E % s.n_groups) return MOE_EINVAL;
+    if (s.topk_groups < 1 || s.topk_groups > s.n_groups) return MOE_EINVAL;
+    if ((int64_t)s.k > (int64_t)s.topk_groups * (s.E / s.n_groups)) return MOE_EINVAL;
+    if (s.n_groups > 64) return MOE_ENOTSUP;
+  }
+  if (s.renormalize != 0 && s.renormalize != 1) return MOE_EINVAL;
+  if (s.block_m < 1) return MOE_EINVAL;
+  if (s.d_e_shared < 0 || (s.d_e_shared % mult)) return MOE_EINVAL;
+  if (s.dtype == MOE_DTYPE_BF16 && s.block_m % 128) return MOE_ENOTSUP;
+  // the padded row space must stay addressable with int32 row indices
+  const int64_t M = (int64_t)s.T * s.k;
+  const int64_t mb = (M + (int64_t)(M < s.E ? M : s.E) * (s.block_m - 1)) / s.block_m;
+  if (mb * s.block_m >= (int64_t)1 << 31) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static int64_t max_blocks_of(const moe_shape& s) {
+  const int64_t M = (int64_t)s.T * s.k;
+  const int64_t ne = M < s.E ? M : s.E;
+  return (M + ne * (s.block_m - 1)) / s.block_m;
+}
+
+static size_t take(size_t& cur, size_t bytes) {
+  const size_t off = cur;
+  cur = align_up(cur + bytes, 256);
+  return off;
+}
+
+static void layout_of(const moe_shape& s, moe_ws_layout& L) {
+  const size_t b = elem_bytes(s);
+  const size_t T = s.T, E = s.E, M = (size_t)s.T * s.k;
+  const size_t mb = (size_t)max_blocks_of(s);
+  const size_t rows = mb * s.block_m;
+  size_t cur = 0;
+  L.logits = take(cur, T * E * 4);
+  L.topk_idx = take(cur, M * 4);
+  L.topk_w = take(cur, M * 4);
+  L.counts = take(cur, E * 4);
+  L.offsets = take(cur, (E + 1) * 4);
+  L.padded_offsets = take(cur, (E + 1) * 4);
+  L.block_meta = take(cur, mb * 3 * 4);
+  L.num_blocks = take(cur, 4);
+  L.pos = take(cur, M * 4);
+  L.row_src = take(cur, rows * 4);
+  L.err_flag = take(cur, 4);
+  L.x_perm = take(cur, rows * s.d * b);
+  L.act = take(cur, rows * s.d_e * b);
+  L.y = take(cur, rows * s.d * b);
+  L.shared_act = take(cur, s.d_e_shared ? T * s.d_e_shared * b : 0);
+  L.shared_out = take(cur, s.d_e_shared ? T * s.d * b : 0);
+  const size_t rp = router_partial_bytes(s), os = offsets_scratch_bytes(s);
+  L.scratch = take(cur, rp > os ? rp : os);
+  L.total = cur;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ENOTSUP: return "not supported";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t moe_max_blocks(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return -1;
+  return (int32_t)max_blocks_of(*s);
+}
+
+int64_t moe_max_rows(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return -1;
+  return max_blocks_of(*s) * s->block_m;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  moe_ws_layout L;
+  layout_of(*s, L);
+  return L.total;
+}
+
+moe_status moe_workspace_layout(const moe_shape* s, moe_ws_layout* layout) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!layout) return MOE_EINVAL;
+  layout_of(*s, *layout);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                     float* logits, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!x || !w_gate || !topk_idx || !topk_w) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned4(w_gate) || !aligned4(topk_idx) || !aligned4(topk_w) ||
+      (bias && !aligned4(bias)) || (logits && !aligned4(logits)))
+    return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  if (!ws || !aligned16(ws) || ws_bytes < router_partial_bytes(*s)) return MOE_EWORKSPACE;
+  return launch_route(*s, x, w_gate, bias, logits, topk_idx, topk_w, static_cast<float*>(ws),
+                      static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_build_offsets(const moe_shape* s, const int32_t* topk_idx, int32_t* counts,
+                             int32_t* offsets, int32_t* padded_offsets, int32_t* block_meta,
+                             int32_t* num_blocks, int32_t* pos, int32_t* row_src,
+                             int32_t* err_flag, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const void* ptrs[] = {topk_idx, counts, offsets, padded_offsets, block_meta,
+                        num_blocks, pos, row_src, err_flag};
+  for (const void* p : ptrs)
+    if (!p || !aligned4(p)) return MOE_EINVAL;
+  if (!ws || !aligned16(ws) || ws_bytes < offsets_scratch_bytes(*s)) return MOE_EWORKSPACE;
+  return launch_build_offsets(*s, topk_idx, counts, offsets, padded_offsets, block_meta, num_blocks,
+                              pos, row_src, err_flag, ws, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* pos, void* x_perm,
+                       void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!x || !pos || !x_perm || !aligned16(x) || !aligned16(x_perm) || !aligned4(pos))
+    return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  return launch_permute(*s, x, pos, x_perm, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_gemm(const moe_shape* s, int32_t op, const void* A, const void* B0,
+                            const void* B1, const int32_t* block_meta, const int32_t* num_blocks,
+                            int32_t max_blocks, void* C, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
+  if (!A || !B0 || !C || !block_meta || !num_blocks) return MOE_EINVAL;
+  if (op == MOE_OP_GATEUP_SWIGLU && !B1) return MOE_EINVAL;
+  if (op == MOE_OP_DOWN && B1) return MOE_EINVAL;
+  if (!aligned16(A) || !aligned16(B0) || (B1 && !aligned16(B1)) || !aligned16(C) ||
+      !aligned4(block_meta) || !aligned4(num_blocks))
+    return MOE_EINVAL;
+  if (max_blocks < 1 || max_blocks > max_blocks_of(*s)) return MOE_EINVAL;
+  const int K = op == MOE_OP_GATEUP_SWIGLU ? s->d : s->d_e;
+  const int N = op == MOE_OP_GATEUP_SWIGLU ? s->d_e : s->d;
+  return launch_grouped_gemm(*s, op, A, B0, B1, K, N, block_meta, num_blocks, max_blocks, 0, C,
+                             static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos, const float* topk_w,
+                       const void* shared_out, void* out, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!y || !pos || !topk_w || !out) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out) || !aligned4(pos) || !aligned4(topk_w) ||
+      (shared_out && !aligned16(shared_out)))
+    return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  return launch_combine(*s, y, pos, topk_w, shared_out, out, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, const float* bias,
+                         const void* w1, const void* w3, const void* w2, const void* ws1,
+                         const void* ws3, const void* ws2, const int32_t* topk_idx_in,
+                         const float* topk_w_in, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const bool routed = topk_idx_in && topk_w_in;
+  if ((topk_idx_in != nullptr) != (topk_w_in != nullptr)) return MOE_EINVAL;
+  if (!x || !w1 || !w3 || !w2 || !out) return MOE_EINVAL;
+  if (!routed && !w_gate) return MOE_EINVAL;
+  const bool shared = s->d_e_shared > 0;
+  if (shared && (!ws1 || !ws3 || !ws2)) return MOE_EINVAL;
+  if (!shared && (ws1 || ws3 || ws2)) return MOE_EINVAL;
+  const void* p16[] = {x, w1, w3, w2, out};
+  for (const void* p : p16)
+    if (!aligned16(p)) return MOE_EINVAL;
+  if (shared && (!aligned16(ws1) || !aligned16(ws3) || !aligned16(ws2))) return MOE_EINVAL;
+  if ((w_gate && !aligned4(w_gate)) || (bias && !aligned4(bias)) ||
+      (topk_idx_in && !aligned4(topk_idx_in)) || (topk_w_in && !aligned4(topk_w_in)))
+    return MOE_EINVAL;
+  moe_ws_layout L;
+  layout_of(*s, L);
+  if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  int32_t* idx = routed ? const_cast<int32_t*>(topk_idx_in) : static_cast<int32_t*>(at(L.topk_idx));
+  float* wts = routed ? const_cast<float*>(topk_w_in) : static_cast<float*>(at(L.topk_w));
+  if (!routed) {
+    st = launch_route(*s, x, w_gate, bias, static_cast<float*>(at(L.logits)), idx, wts,
+                      static_cast<float*>(at(L.scratch)), hs);
+    if (st != MOE_OK) return st;
+  }
+  int32_t* meta = static_cast<int32_t*>(at(L.block_meta));
+  int32_t* nblk = static_cast<int32_t*>(at(L.num_blocks));
+  int32_t* pos = static_cast<int32_t*>(at(L.pos));
+  st = launch_build_offsets(*s, idx, static_cast<int32_t*>(at(L.counts)),
+                            static_cast<int32_t*>(at(L.offsets)),
+                            static_cast<int32_t*>(at(L.padded_offsets)), meta, nblk, pos,
+                            static_cast<int32_t*>(at(L.row_src)),
+                            static_cast<int32_t*>(at(L.err_flag)), at(L.scratch), hs);
+  if (st != MOE_OK) return st;
+  st = launch_permute(*s, x, pos, at(L.x_perm), hs);
+  if (st != MOE_OK) return st;
+  const int32_t mb = (int32_t)max_blocks_of(*s);
+  st = launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, at(L.x_perm), w1, w3, s->d, s->d_e, meta, nblk,
+                           mb, 0, at(L.act), hs);
+  if (st != MOE_OK) return st;
+  st = launch_grouped_gemm(*s, MOE_OP_DOWN, at(L.act), w2, nullptr, s->d_e, s->d, meta, nblk, mb, 0,
+                           at(L.y), hs);
+  if (st != MOE_OK) return st;
+  const void* sh = nullptr;
+  if (shared) {
+    moe_shape ss = *s;
+    ss.d_e = s->d_e_shared;
+    st = launch_grouped_gemm(ss, MOE_OP_GATEUP_SWIGLU, x, ws1, ws3, s->d, s->d_e_shared, nullptr,
+                             nullptr, 0, s->T, at(L.shared_act), hs);
+    if (st != MOE_OK) return st;
+    st = launch_grouped_gemm(ss, MOE_OP_DOWN, at(L.shared_act), ws2, nullptr, s->d_e_shared, s->d,
+                             nullptr, nullptr, 0, s->T, at(L.shared_out), hs);
+    if (st != MOE_OK) return st;
+    sh = at(L.shared_out);
+  }
+  return launch_combine(*s, at(L.y), pos, wts, sh, out, hs);
+}
+
+}  // extern "C"

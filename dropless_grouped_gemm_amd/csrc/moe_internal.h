@@ -1,0 +1,82 @@
+// Internal declarations shared by the HIP sources of libmoe (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+
+// bf16 <-> fp32.  The widening is exact; the narrowing rounds to nearest even
+// (gfx950 converts in hardware).
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(bf16_t, b);
+}
+// Two floats -> two packed bf16 in one dword (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Load/store helpers for the two element types, going through fp32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// SiLU in fp32: z * sigmoid(z) = z / (1 + exp(-z)).
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of compute units of the current device (queried once per device).
+int device_cu_count();
+
+// ---- launchers (each returns MOE_OK or MOE_EHIP) -------------------------------
+// Router: partial logits over nsplit slices of d, then selection.
+int router_nsplit(const moe_shape& s);
+size_t router_partial_bytes(const moe_shape& s);
+moe_status launch_route(const moe_shape& s, const void* x, const void* w_gate,
+                        const float* bias, float* logits, int32_t* topk_idx,
+                        float* topk_w, float* partial, hipStream_t st);
+
+// Offsets: per-chunk histograms + ranks, one-block scan + metadata, scatter.
+int offsets_chunk(const moe_shape& s);
+int64_t offsets_nchunks(const moe_shape& s);
+size_t offsets_scratch_bytes(const moe_shape& s);
+moe_status launch_build_offsets(const moe_shape& s, const int32_t* topk_idx,
+                                int32_t* counts, int32_t* offsets, int32_t* padded,
+                                int32_t* block_meta, int32_t* num_blocks, int32_t* pos,
+                                int32_t* row_src, int32_t* err_flag, void* scratch,
+                                hipStream_t st);
+
+moe_status launch_permute(const moe_shape& s, const void* x, const int32_t* pos,
+                          void* x_perm, hipStream_t st);
+moe_status launch_combine(const moe_shape& s, const void* y, const int32_t* pos,
+                          const float* topk_w, const void* shared_out, void* out,
+                          hipStream_t st);
+
+// Grouped GEMM.  dense_rows > 0 selects dense mode (the shared expert): rows
+// [0, dense_rows) form consecutive block_m blocks of expert 0 and block_meta /
+// num_blocks are ignored.
+moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const void* B0,
+                               const void* B1, int K, int N, const int32_t* block_meta,
+                               const int32_t* num_blocks, int32_t max_blocks,
+                               int32_t dense_rows, void* C, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,220 @@
+/*
+ * moe.h - C ABI of libmoe: the forward pass of a dropless Mixture-of-Experts layer
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages state the problem:
+ *   x[T, d] tokens, router W_g[d, E], each token picks k of E experts; expert e is a
+ *   SwiGLU MLP with W1[e], W3[e] of shape [d, d_e] and W2[e] of shape [d_e, d];
+ *   an optional shared expert (same form, inner size d_e_shared) sees every token.
+ *   (TileLang tutorial chapter "MoE, MLA and sparse-attention operators", sections
+ *   2.1-2.5; course notes "Dropless and grouped GEMM", sections 1 and 4.)
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is device memory owned by the caller, row-major and
+ *     contiguous, 16-byte aligned.  The library never allocates, frees or
+ *     synchronises; every kernel is enqueued on `stream` (a hipStream_t; NULL is
+ *     the null stream) and the caller synchronises.  Nothing is copied between
+ *     host and device: counts and offsets stay in device memory.
+ *   - Activations and weights are fp32 (dtype 0) or bf16 (dtype 1); router
+ *     logits, routing weights and all accumulation are fp32; integer outputs are
+ *     int32.
+ *   - Host-side validation runs before anything is enqueued and returns a status;
+ *     MOE_EHIP reports a failed kernel launch.  A data error that only the device
+ *     can see (an expert id outside [0, E) handed to moe_build_offsets) sets
+ *     *err_flag to 1 on the device; the outputs are then unspecified.
+ *   - Results are bitwise reproducible run to run: no floating-point atomics, and
+ *     every reduction has a fixed order.
+ *   - Entry points are reentrant; the library keeps no mutable global state.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK          0
+#define MOE_EINVAL      1   /* a shape, pointer, alignment or argument is invalid   */
+#define MOE_ENOTSUP     2   /* valid, but not supported by this build (see below)   */
+#define MOE_EWORKSPACE  3   /* workspace missing or smaller than moe_workspace_bytes */
+#define MOE_EHIP        4   /* a HIP launch or runtime call failed                   */
+
+#define MOE_DTYPE_F32   0
+#define MOE_DTYPE_BF16  1
+
+#define MOE_OP_GATEUP_SWIGLU 0   /* act = silu(A W1[e]) * (A W3[e]), [rows, d_e] */
+#define MOE_OP_DOWN          1   /* y   = A W2[e],                   [rows, d]   */
+
+/*
+ * The layer's shape.
+ *   T >= 0 tokens (T == 0 is a no-op); d, d_e >= 1 with d % 8 == 0 and d_e % 8 == 0
+ *   (bf16) or % 4 == 0 (fp32); 1 <= k <= E <= 1024; T * k < 2^31.
+ *   n_groups, topk_groups: 0, 0 for plain top-k; otherwise E % n_groups == 0,
+ *   1 <= topk_groups <= n_groups and k <= topk_groups * E / n_groups (group-limited
+ *   routing: experts form n_groups contiguous id ranges, a group scores its largest
+ *   logit, only the topk_groups best groups stay eligible; TileLang chapter section
+ *   2.2, dropless notes section 4 step 4).
+ *   renormalize: 1 divides the k routing weights of a token by their sum.
+ *   block_m: every expert's row segment is padded up to a multiple of block_m
+ *   (dropless notes section 3); it is also the row granularity of the grouped GEMM.
+ *   bf16 needs block_m % 128 == 0 (else MOE_ENOTSUP); fp32 takes any block_m >= 1.
+ *   d_e_shared: inner size of the shared expert, 0 = none.
+ */
+typedef struct moe_shape {
+  int32_t T, d, E, k, d_e;
+  int32_t n_groups, topk_groups;
+  int32_t renormalize;
+  int32_t block_m;
+  int32_t d_e_shared;
+  int32_t dtype;
+} moe_shape;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_str(moe_status s);
+
+/* Host-only and pure.  Upper bound on the number of block_m-row blocks:
+ * sum_e ceil(c_e / block_m) <= floor((T*k + min(E, T*k) * (block_m - 1)) / block_m).
+ * Returns -1 for an invalid shape. */
+int32_t moe_max_blocks(const moe_shape* s);
+
+/* Host-only and pure.  moe_max_blocks(s) * block_m: the row count every permuted
+ * buffer (x_perm, act, y, row_src) is sized at - a declared upper bound, since the
+ * real padded total is data (dropless notes sections 1 and 4). -1 if invalid. */
+int64_t moe_max_rows(const moe_shape* s);
+
+/* Host-only and pure.  Bytes of device workspace that moe_layer_fwd needs; the same
+ * amount is enough for moe_route and moe_build_offsets.  0 if the shape is invalid. */
+size_t moe_workspace_bytes(const moe_shape* s);
+
+/*
+ * Router and selection (TileLang chapter section 2.2; dropless notes section 4
+ * steps 2-4).
+ *   logits[t, e] = sum_i x[t, i] * w_gate[i, e] + bias[e], accumulated in fp32.
+ *   Selection runs on those fp32 logits: within the eligible experts, k rounds of
+ *   "largest remaining logit", ties to the lower expert id, so slot j holds the
+ *   j-th largest.  topk_w[t, j] = softmax over all E logits at topk_idx[t, j],
+ *   divided by the sum of the token's k weights when renormalize is set.
+ * In:  x [T, d] (dtype), w_gate [d, E] (dtype), bias [E] fp32 or NULL.
+ * Out: logits [T, E] fp32 (NULL: not stored), topk_idx [T, k] int32,
+ *      topk_w [T, k] fp32.
+ * ws:  device workspace of ws_bytes >= moe_workspace_bytes(s).
+ */
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate,
+                     const float* bias, float* logits, int32_t* topk_idx,
+                     float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Counts, offsets, padded offsets, block metadata and the permutation, all on the
+ * device (TileLang chapter sections 2.2 item 2, 2.3 item 2 and 2.4 (a); dropless
+ * notes sections 3, 5 and 7).  With a = t*k + j and c_e the number of assignments
+ * with expert e:
+ *   counts[e]            = c_e
+ *   offsets[e]           = sum_{e' < e} c_e'                  (E+1 entries)
+ *   padded_offsets[e]    = sum_{e' < e} ceil(c_e'/block_m)*block_m  (E+1 entries)
+ *   num_blocks[0]        = sum_e ceil(c_e / block_m)
+ *   block_meta[b]        = {expert, m_start, valid_m} for b < num_blocks, experts in
+ *                          ascending order, m_start = padded_offsets[e] + i*block_m,
+ *                          valid_m = min(block_m, c_e - i*block_m); entries from
+ *                          num_blocks to max_blocks-1 are left untouched
+ *   pos[a]               = padded_offsets[e] + #{a' < a : topk_idx[a'] = e}
+ *                          (a stable sort by expert id)
+ *   row_src[r]           = a where pos[a] = r, -1 on every other row r < max_rows
+ *   err_flag[0]          = 1 if any id lies outside [0, E) (those assignments are
+ *                          skipped and get pos = -1), else 0
+ * In:  topk_idx [T*k] int32 (duplicates within a token are allowed).
+ * Out: counts [E], offsets [E+1], padded_offsets [E+1], block_meta
+ *      [moe_max_blocks(s)][3], num_blocks [1], pos [T*k], row_src [moe_max_rows(s)],
+ *      err_flag [1], all int32.
+ * ws:  device workspace of ws_bytes >= moe_workspace_bytes(s).
+ */
+moe_status moe_build_offsets(const moe_shape* s, const int32_t* topk_idx,
+                             int32_t* counts, int32_t* offsets,
+                             int32_t* padded_offsets, int32_t* block_meta,
+                             int32_t* num_blocks, int32_t* pos, int32_t* row_src,
+                             int32_t* err_flag, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/*
+ * Permute (in-card dispatch; TileLang chapter section 2.3, dropless notes section 4
+ * steps 5-6): x_perm[pos[t*k + j], :] = x[t, :] for every (t, j) with pos >= 0.
+ * Pad rows of x_perm are neither written nor read.
+ * In:  x [T, d] (dtype), pos [T*k] int32.  Out: x_perm [moe_max_rows(s), d] (dtype).
+ */
+moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* pos,
+                       void* x_perm, void* stream);
+
+/*
+ * Grouped GEMM over the contiguous, block_m-aligned expert segments (TileLang
+ * chapter section 2.4; dropless notes sections 3, 5 and 7): one launch covers every
+ * expert; block b of block_meta computes rows [m_start, m_start + valid_m) against
+ * expert `expert`'s weights only.  Rows past valid_m are neither read nor written.
+ *   op = MOE_OP_GATEUP_SWIGLU: A = x_perm [rows, d], B0 = W1 [E, d, d_e] (gate),
+ *        B1 = W3 [E, d, d_e] (up); C = act [rows, d_e] = silu(A W1[e]) * (A W3[e]),
+ *        the dual GEMM sharing one read of A with a fused SiLU-and-multiply epilogue
+ *        (TileLang chapter section 2.4 (c)).
+ *   op = MOE_OP_DOWN: A = act [rows, d_e], B0 = W2 [E, d_e, d], B1 = NULL;
+ *        C = y [rows, d] = A W2[e].
+ * block_meta and num_blocks are device pointers (as written by moe_build_offsets);
+ * max_blocks (host) bounds num_blocks and sizes the launch, so the host never needs
+ * the real block count; 1 <= max_blocks <= moe_max_blocks(s).  A and C hold
+ * max_blocks * block_m rows.
+ */
+moe_status moe_grouped_gemm(const moe_shape* s, int32_t op, const void* A,
+                            const void* B0, const void* B1,
+                            const int32_t* block_meta, const int32_t* num_blocks,
+                            int32_t max_blocks, void* C, void* stream);
+
+/*
+ * Combine (TileLang chapter section 2.5; dropless notes section 4 steps 10-11):
+ *   out[t, :] = sum_{j = 0..k-1, in this order} topk_w[t, j] * y[pos[t*k + j], :]
+ *               (+ shared_out[t, :])
+ * accumulated in fp32 and rounded once to dtype; slots with pos < 0 are skipped.
+ * In:  y [moe_max_rows(s), d] (dtype), pos [T*k] int32, topk_w [T, k] fp32,
+ *      shared_out [T, d] (dtype) or NULL.   Out: out [T, d] (dtype).
+ */
+moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos,
+                       const float* topk_w, const void* shared_out, void* out,
+                       void* stream);
+
+/*
+ * The whole layer: route -> build offsets -> permute -> grouped GEMM (gate/up with
+ * SiLU*mul) -> grouped GEMM (down) -> [shared expert on the unpermuted x] ->
+ * combine.  The shared expert is a dense SwiGLU MLP on every token, added
+ * unweighted (dropless notes section 1).
+ * In:  x [T, d]; w_gate [d, E] and bias [E] fp32 (or NULL) when routing;
+ *      w1, w3 [E, d, d_e], w2 [E, d_e, d];
+ *      ws1, ws3 [d, d_e_shared], ws2 [d_e_shared, d] when d_e_shared > 0 (else NULL);
+ *      topk_idx_in [T, k] int32 and topk_w_in [T, k] fp32: when both are non-NULL the
+ *      router is skipped and these routes are used as given (rows already routed,
+ *      as on one rank of an expert-parallel group); w_gate may then be NULL.
+ * Out: out [T, d] (dtype).
+ * ws:  device workspace of ws_bytes >= moe_workspace_bytes(s); it holds every
+ *      intermediate, laid out by moe_ws_layout.
+ */
+moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate,
+                         const float* bias, const void* w1, const void* w3,
+                         const void* w2, const void* ws1, const void* ws3,
+                         const void* ws2, const int32_t* topk_idx_in,
+                         const float* topk_w_in, void* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * Byte offsets of the intermediates inside the moe_layer_fwd workspace, so that a
+ * caller (tests, profilers) can inspect them after a call.  Host-only and pure.
+ * Each field is an offset from the workspace base; a field is 0-sized when unused.
+ */
+typedef struct moe_ws_layout {
+  size_t logits, topk_idx, topk_w, counts, offsets, padded_offsets, block_meta,
+         num_blocks, pos, row_src, err_flag, x_perm, act, y, shared_act, shared_out,
+         scratch, total;
+} moe_ws_layout;
+moe_status moe_workspace_layout(const moe_shape* s, moe_ws_layout* layout);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

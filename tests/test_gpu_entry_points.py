@@ -1,0 +1,267 @@
+"""Each C-ABI entry point on its own, against the oracle, on the edge cases of the
+method: empty experts, exact multiples of block_m, everything on one expert,
+T*k < block_m, a single token, duplicate experts within a token, out-of-range ids,
+exact logit ties, many chunks, and the dropless notes' worked example."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from dropless_grouped_gemm_amd import binding as B
+from oracle import moe_oracle as O
+
+from gpu_util import TOL_LOGITS, TOL_STAGE, TOL_W_REL, assert_close, f64, i64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_offsets(idx, E, bm, dtype="fp32"):
+    """moe_build_offsets on a [T, k] id array; returns numpy outputs."""
+    idx = np.asarray(idx, np.int32)
+    T, k = idx.shape
+    s = B.make_shape(T=T, d=8, E=E, k=k, d_e=8, block_m=bm, dtype=dtype)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    M = T * k
+    t = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.reshape(-1).copy()).to(DEV)
+    counts, offs, pad, meta, nblk = t(E), t(E + 1), t(E + 1), t(mb * 3), t(1)
+    pos, row_src, err = t(M), t(rows), t(1)
+    ws = B.alloc_workspace(s)
+    print(f"[offsets] T={T} k={k} E={E} bm={bm}", flush=True)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    torch.cuda.synchronize()
+    nb = int(nblk.item())
+    return dict(counts=i64(counts)[:E], offsets=i64(offs), padded=i64(pad), num_blocks=nb,
+                meta=i64(meta)[:nb * 3].reshape(-1, 3), meta_tail=i64(meta)[nb * 3:],
+                pos=i64(pos)[:M], row_src=i64(row_src)[:rows], err=int(err.item()))
+
+
+def check_offsets(idx, E, bm, dtype="fp32"):
+    g = run_offsets(idx, E, bm, dtype)
+    idx = np.asarray(idx)
+    c = O.expert_counts(idx, E)
+    assert g["err"] == 0
+    assert np.array_equal(g["counts"], c)
+    assert np.array_equal(g["offsets"], O.group_offsets(c))
+    assert np.array_equal(g["padded"], O.padded_offsets(c, bm))
+    meta = O.block_metadata(c, bm)
+    assert g["num_blocks"] == len(meta)
+    assert np.array_equal(g["meta"], meta)
+    assert np.all(g["meta_tail"] == -7), "entries past num_blocks must be left untouched"
+    pos, row_src = O.permutation(idx, E, bm)
+    assert np.array_equal(g["pos"], pos)
+    assert np.array_equal(g["row_src"][:len(row_src)], row_src)
+    assert np.all(g["row_src"][len(row_src):] == -1)
+    return g
+
+
+@pytest.mark.parametrize("name,idx,E,bm", [
+    ("all-on-one-expert", np.full((300, 1), 5), 8, 128),
+    ("exact-multiples", np.repeat(np.array([0] * 128 + [1] * 256 + [3] * 128), 1).reshape(-1, 1), 4, 128),
+    ("empty-first-middle-last", np.array([[1, 2], [2, 1], [1, 1], [2, 2]] * 40), 4, 128),
+    ("single-token", np.array([[3]]), 8, 128),
+    ("single-token-all-experts", np.array([[3, 0, 2, 1]]), 4, 128),
+    ("tk-below-block", np.array([[0, 1], [1, 0], [7, 7]]), 8, 128),
+    ("block-1", np.random.default_rng(0).integers(0, 5, (97, 3)), 5, 1),
+    ("block-7", np.random.default_rng(1).integers(0, 9, (97, 3)), 9, 7),
+])
+def test_offsets_edge_cases(name, idx, E, bm):
+    check_offsets(idx, E, bm)
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(50, 8, 4, 128), (5000, 1, 16, 128), (64, 8, 1024, 128),
+                                      (137500, 8, 64, 128), (4099, 6, 64, 32)])
+def test_offsets_random_with_duplicates_and_many_chunks(T, k, E, bm):
+    rng = np.random.default_rng(T + E)
+    p = rng.dirichlet(np.full(E, 0.5))
+    idx = rng.choice(E, size=(T, k), p=p)      # duplicates within a token allowed
+    check_offsets(idx, E, bm, "bf16" if bm % 128 == 0 else "fp32")
+
+
+def test_offsets_worked_example_on_device():
+    """The dropless notes' per-card example, computed on the device: padded sizes
+    21,760/15,104/18,048/10,880 (65,792 rows) and 514 blocks."""
+    g = json.load(open(os.path.join(GOLDEN, "dropless_padding_worked_example.json")))
+    rng = np.random.default_rng(2)
+    ids = np.repeat(np.arange(4), g["counts"])
+    rng.shuffle(ids)
+    out = check_offsets(ids.reshape(8192, 8), 4, 128, "bf16")
+    assert list(np.diff(out["padded"])) == g["padded_sizes"]
+    assert list(out["offsets"]) == g["group_offsets"]
+    assert out["num_blocks"] == g["blocks_total_derived"]
+
+
+def test_offsets_out_of_range_ids_set_the_flag():
+    idx = np.array([[0, 1], [9, 2], [-1, 1], [2, 2]])
+    g = run_offsets(idx, 4, 128)
+    assert g["err"] == 1
+    flat = idx.reshape(-1)
+    bad = (flat < 0) | (flat >= 4)
+    assert np.all(g["pos"][bad] == -1)
+    assert np.array_equal(g["counts"], O.expert_counts(flat[~bad], 4))
+    # the valid assignments still form a correct stable permutation
+    P = g["padded"]
+    for e in range(4):
+        rows = sorted(g["pos"][(flat == e)])
+        assert rows == list(range(P[e], P[e] + int((flat == e).sum())))
+
+
+# ---------------------------------------------------------------------------
+# moe_route on its own
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,k,ng,tg,renorm,dtype", [
+    (200, 512, 8, 4, 0, 0, False, "bf16"),
+    (64, 1024, 256, 8, 8, 4, False, "bf16"),
+    (33, 520, 64, 6, 0, 0, True, "bf16"),
+    (16, 256, 1024, 8, 16, 2, True, "bf16"),
+    (50, 128, 8, 2, 0, 0, True, "fp32"),
+])
+def test_route_standalone(T, d, E, k, ng, tg, renorm, dtype):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T * 31 + E)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    wg = (torch.randn((d, E), generator=g, device=DEV) / d ** 0.5).to(dt)
+    bias = torch.randn(E, generator=g, device=DEV) * 0.3
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=8, block_m=128 if dtype == "bf16" else 1,
+                     dtype=dtype, n_groups=ng, topk_groups=tg, renormalize=renorm)
+    logits = torch.empty((T, E), device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), device=DEV)
+    ws = B.alloc_workspace(s)
+    B.moe_route(s, x, wg, bias, logits, idx, w, ws)
+    idx2 = torch.empty_like(idx)
+    w2 = torch.empty_like(w)
+    B.moe_route(s, x, wg, bias, None, idx2, w2, ws)          # logits not stored
+    torch.cuda.synchronize()
+    ref = O.router_logits(f64(x), f64(wg), f64(bias))
+    assert_close(f64(logits), ref, TOL_LOGITS[dtype], "logits")
+    dec = logits.cpu().numpy()
+    ridx = O.topk_by_repeated_max(dec, k, O.eligible_experts(dec, ng, tg))
+    assert np.array_equal(i64(idx), ridx)
+    np.testing.assert_allclose(f64(w), O.gate_weights(dec, ridx, renorm), rtol=TOL_W_REL, atol=0)
+    assert torch.equal(idx, idx2) and torch.equal(w, w2)
+
+
+def test_route_exact_ties_go_to_the_lower_id():
+    """Duplicated router columns give bitwise-equal logits; the lower id must win."""
+    T, d, E, k = 64, 256, 16, 4
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    x = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
+    wg = (torch.randn((d, E), generator=g, device=DEV) / 16).to(torch.bfloat16)
+    wg[:, 9] = wg[:, 2]
+    wg[:, 13] = wg[:, 2]
+    wg[:, 7] = wg[:, 11]
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=8, block_m=128)
+    logits = torch.empty((T, E), device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, k), device=DEV)
+    B.moe_route(s, x, wg, None, logits, idx, w, B.alloc_workspace(s))
+    torch.cuda.synchronize()
+    L = logits.cpu().numpy()
+    assert np.array_equal(L[:, 9], L[:, 2]) and np.array_equal(L[:, 7], L[:, 11])
+    assert np.array_equal(i64(idx), O.topk_by_repeated_max(L, k))
+    # whenever both members of a tied pair are chosen, the lower id comes first
+    for row in i64(idx):
+        r = list(row)
+        if 2 in r and 9 in r:
+            assert r.index(2) < r.index(9)
+        if 7 in r and 11 in r:
+            assert r.index(7) < r.index(11)
+
+
+# ---------------------------------------------------------------------------
+# permute -> grouped GEMM x2 -> combine, each entry point called on its own
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,k,d_e,bm,dtype,mode", [
+    (200, 512, 8, 2, 256, 128, "bf16", "random"),
+    (96, 264, 6, 3, 136, 128, "bf16", "one-row-per-block"),
+    (512, 256, 4, 1, 128, 128, "bf16", "full-blocks"),
+    (70, 64, 5, 2, 48, 16, "fp32", "random"),
+])
+def test_stage_entry_points(T, d, E, k, d_e, bm, dtype, mode):
+    rng = np.random.default_rng(T + d)
+    if mode == "random":
+        idx = rng.integers(0, E, size=(T, k))
+    elif mode == "one-row-per-block":
+        # each expert gets few rows: blocks with valid_m of 1..3
+        idx = np.zeros((T, k), np.int64)
+        idx[:] = rng.integers(0, E, size=(T, k))
+        idx[:E, 0] = np.arange(E)
+        idx[E:, :] = 0
+    else:
+        idx = np.repeat(np.arange(E), T // E)[rng.permutation(T)].reshape(T, k)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    sh = (torch.randn((T, d), generator=g, device=DEV)).to(dt)
+    tw = torch.rand((T, k), generator=g, device=DEV)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=bm, dtype=dtype)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    M = T * k
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(M), i32(rows), i32(1))
+    ws = B.alloc_workspace(s)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    x_perm = torch.empty((rows, d), dtype=dt, device=DEV)
+    act = torch.empty((rows, d_e), dtype=dt, device=DEV)
+    y = torch.empty((rows, d), dtype=dt, device=DEV)
+    out = torch.empty((T, d), dtype=dt, device=DEV)
+    out_ns = torch.empty((T, d), dtype=dt, device=DEV)
+    B.moe_permute(s, x, pos, x_perm)
+    B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1, w3, meta, nblk, mb, act)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, w2, None, meta, nblk, mb, y)
+    B.moe_combine(s, y, pos, tw, sh, out)
+    B.moe_combine(s, y, pos, tw, None, out_ns)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref_pos, ref_src = O.permutation(idx, E, bm)
+    assert np.array_equal(i64(pos), ref_pos)
+    c = O.expert_counts(idx, E)
+    xh = f64(x)
+    xp_ref = O.permute(xh, ref_pos, k, len(ref_src))
+    valid = np.nonzero(ref_src >= 0)[0]
+    assert np.array_equal(f64(x_perm)[valid], xp_ref[valid])
+    act_ref, _ = O.grouped_ffn(xp_ref, c, bm, f64(w1), f64(w3), f64(w2))
+    assert_close(f64(act)[valid], act_ref[valid], TOL_STAGE[dtype], "act")
+    _, y_ref = O.grouped_ffn(np.zeros_like(xp_ref), c, bm, f64(w1), f64(w3), f64(w2))
+    act_dev = f64(act)
+    P = O.padded_offsets(c, bm)
+    for e in range(E):
+        lo, hi = P[e], P[e] + c[e]
+        y_ref[lo:hi] = act_dev[lo:hi] @ f64(w2)[e]
+    assert_close(f64(y)[valid], y_ref[valid], TOL_STAGE[dtype], "y")
+    y_dev = f64(y)
+    out_ref = O.combine(y_dev, ref_pos, f64(tw), k, f64(sh))
+    assert_close(f64(out), out_ref, TOL_STAGE[dtype], "out")
+    assert_close(f64(out_ns), O.combine(y_dev, ref_pos, f64(tw), k), TOL_STAGE[dtype], "out")
+
+
+def test_combine_skips_negative_positions():
+    T, d, k = 8, 64, 2
+    s = B.make_shape(T=T, d=d, E=4, k=k, d_e=64, block_m=128)
+    y = torch.randn((B.moe_max_rows(s), d), device=DEV).to(torch.bfloat16)
+    pos = torch.tensor([0, -1, 1, 2, -1, -1, 3, 4, 5, 6, 7, 8, 9, 10, -1, 11], dtype=torch.int32,
+                       device=DEV)
+    w = torch.rand((T, k), device=DEV)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    B.moe_combine(s, y, pos, w, None, out)
+    torch.cuda.synchronize()
+    yh, p, wh = f64(y), i64(pos).reshape(T, k), f64(w)
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            if p[t, j] >= 0:
+                ref[t] += wh[t, j] * yh[p[t, j]]
+    assert_close(f64(out), ref, TOL_STAGE["bf16"], "out")
