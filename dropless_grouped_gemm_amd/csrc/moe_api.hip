@@ -40,7 +40,7 @@ static moe_status check_shape(const moe_shape* sp) {
   const int mult = s.dtype == MOE_DTYPE_BF16 ? 8 : 4;  // 16-byte rows
   if (s.T < 0 || s.d < 1 || s.E < 1 || s.k < 1 || s.d_e < 1) return MOE_EINVAL;
   if (s.d % mult || s.d_e % mult) return MOE_EINVAL;
-  if (s.k > s.E) return MOE_EINVAL;
+  if (s.k > 1024) return MOE_ENOTSUP;
   if (s.E > 1024) return MOE_ENOTSUP;
   if ((int64_t)s.T * s.k >= (int64_t)1 << 31) return MOE_EINVAL;
   if (s.n_groups < 0 || s.topk_groups < 0) return MOE_EINVAL;
@@ -49,17 +49,29 @@ static moe_status check_shape(const moe_shape* sp) {
   } else {
     if (s.E % s.n_groups) return MOE_EINVAL;
     if (s.topk_groups < 1 || s.topk_groups > s.n_groups) return MOE_EINVAL;
-    if ((int64_t)s.k > (int64_t)s.topk_groups * (s.E / s.n_groups)) return MOE_EINVAL;
     if (s.n_groups > 64) return MOE_ENOTSUP;
   }
   if (s.renormalize != 0 && s.renormalize != 1) return MOE_EINVAL;
   if (s.block_m < 1) return MOE_EINVAL;
   if (s.d_e_shared < 0 || (s.d_e_shared % mult)) return MOE_EINVAL;
   if (s.dtype == MOE_DTYPE_BF16 && s.block_m % 128) return MOE_ENOTSUP;
+  // one expert matrix is indexed with 32-bit element offsets
+  const int64_t de_max = s.d_e > s.d_e_shared ? s.d_e : s.d_e_shared;
+  if ((int64_t)s.d * de_max >= (int64_t)1 << 31) return MOE_ENOTSUP;
   // the padded row space must stay addressable with int32 row indices
   const int64_t M = (int64_t)s.T * s.k;
   const int64_t mb = (M + (int64_t)(M < s.E ? M : s.E) * (s.block_m - 1)) / s.block_m;
   if (mb * s.block_m >= (int64_t)1 << 31) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// The router picks k distinct experts, so it needs k <= E (and, with group-limited
+// routing, k <= topk_groups * E / n_groups).  Rows that arrive already routed may
+// repeat an expert within a token, so the other stages accept any k.
+static moe_status check_routing(const moe_shape& s) {
+  if (s.k > s.E) return MOE_EINVAL;
+  if (s.n_groups > 0 && (int64_t)s.k > (int64_t)s.topk_groups * (s.E / s.n_groups))
+    return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -149,6 +161,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate, cons
                      void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
+  if ((st = check_routing(*s)) != MOE_OK) return st;
   if (!x || !w_gate || !topk_idx || !topk_w) return MOE_EINVAL;
   if (!aligned16(x) || !aligned4(w_gate) || !aligned4(topk_idx) || !aligned4(topk_w) ||
       (bias && !aligned4(bias)) || (logits && !aligned4(logits)))
@@ -226,6 +239,7 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
   if ((topk_idx_in != nullptr) != (topk_w_in != nullptr)) return MOE_EINVAL;
   if (!x || !w1 || !w3 || !w2 || !out) return MOE_EINVAL;
   if (!routed && !w_gate) return MOE_EINVAL;
+  if (!routed && (st = check_routing(*s)) != MOE_OK) return st;
   const bool shared = s->d_e_shared > 0;
   if (shared && (!ws1 || !ws3 || !ws2)) return MOE_EINVAL;
   if (!shared && (ws1 || ws3 || ws2)) return MOE_EINVAL;

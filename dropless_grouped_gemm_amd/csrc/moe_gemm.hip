@@ -232,6 +232,219 @@ k_gg_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
 }
 
 // ---------------------------------------------------------------------------
+// bf16 kernel, asynchronous-copy version (K % 32 == 0).
+//
+//   * Work tile 128 rows x 512 B-columns; 4 waves, each owning all 128 rows and 128
+//     B-columns (GATEUP: 64 gate + the 64 matching up columns), i.e. a 4 x 4 grid of
+//     32x32 accumulators per wave (256 fp32 values per lane).
+//   * Operands go HBM -> LDS with global_load_lds (16 bytes per lane, no registers),
+//     into a 3-stage ring of 32-deep K slices; the loads for slice ks+2 are issued
+//     while slice ks is multiplied.
+//   * A (rows, K-contiguous) is read with ds_read_b128.  B stays in its natural
+//     [k][n] layout in LDS and is read with ds_read_b64_tr_b16: in each 16-lane group
+//     lane 4r+c points at row r, columns 4c..4c+3 of a 4 x 16 block and receives
+//     column (lane % 16), so two such reads give a lane the 8 consecutive k values of
+//     one column that the 32x32x16 MFMA takes.
+//   * Both LDS layouts are XOR-swizzled on 16-byte chunks so the A reads (8 rows per
+//     cycle) and the transposed B reads (4 rows x 32 bytes per 16-lane group) hit 32
+//     distinct banks.
+//   * Rows past valid_m and columns past N load a valid row / column instead (their
+//     results are never stored), so every lane issues every copy and the copy count
+//     per slice is uniform - the vmcnt-based wait below relies on that.
+// ---------------------------------------------------------------------------
+static constexpr int kV2BK = 32;                  // K per stage
+static constexpr int kV2NB = 512;                 // B columns per tile
+static constexpr int kV2ABytes = kBM * kV2BK * 2; // 8 KB
+static constexpr int kV2BBytes = kV2BK * kV2NB * 2;  // 32 KB
+static constexpr int kV2Stage = kV2ABytes + kV2BBytes;
+static constexpr int kV2Stages = 3;
+static constexpr int kV2CopiesPerThread = 2 + 8;  // A: 8 windows / 4 waves, B: 32 rows / 4 waves
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#define MOE_LDS __attribute__((address_space(3)))
+#define MOE_GLOBAL __attribute__((address_space(1)))
+
+// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 encoding).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// 16-byte asynchronous copy global -> LDS: lane l's 16 bytes land at lds_base + 16*l
+// (lds_base is wave-uniform and goes through M0).  Issued as inline assembly so the
+// compiler's own counter model does not see it: it would otherwise wait for every
+// outstanding copy before each LDS read.  The caller waits with MOE_WAIT_VMCNT;
+// loads complete in issue order, so compiler-generated waits stay correct (they can
+// only over-wait).
+__device__ __forceinline__ void copy16_to_lds(const void* gsrc, const unsigned char* lds_base) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const MOE_LDS void*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(m0)
+               : "memory", "m0");
+}
+
+template <int OP>
+__global__ void __launch_bounds__(kThreads, 1)
+k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
+             const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int K, int N,
+             const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
+             int max_blocks, int E, int64_t max_rows, int dense_rows, int block_m, int n_tiles) {
+  __shared__ __align__(1024) unsigned char lds[kV2Stages * kV2Stage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int kOutCols = OP == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
+  const int tpb = block_m / kBM;
+  const int nblocks =
+      dense_rows > 0 ? (dense_rows + block_m - 1) / block_m : min(num_blocks_ptr[0], max_blocks);
+  const int total = nblocks * tpb * n_tiles;
+  const int nk = K / kV2BK;
+
+  // B-fragment read geometry (fixed per lane): 16-lane group g, row r, column quad c4.
+  const int g = lane >> 4, gi = lane & 15, tr_r = gi >> 2, tr_c4 = gi & 3;
+  int nb[4];  // first B column of this wave's four 32-column subtiles
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    nb[j] = OP == MOE_OP_GATEUP_SWIGLU ? (j < 2 ? wave * 64 + j * 32 : 256 + wave * 64 + (j - 2) * 32)
+                                       : wave * 128 + j * 32;
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int nt = w % n_tiles;
+    const int mt = w / n_tiles;
+    Tile tile;
+    if (!decode_block(mt / tpb, mt % tpb, kBM, block_m, meta, dense_rows, E, max_rows, tile)) continue;
+    const int n0 = nt * kOutCols;
+    const bf16_t* asrc = A + (size_t)tile.m0 * K;
+    const bf16_t* b0e = B0 + (size_t)tile.e * K * N;
+    const bf16_t* b1e = OP == MOE_OP_GATEUP_SWIGLU ? B1 + (size_t)tile.e * K * N : b0e;
+
+    // Per-lane element offsets of the copies; the bases are wave-uniform, so each copy
+    // is an SGPR base plus one 32-bit VGPR offset.
+    int a_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (wave * 2 + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      const int rr = row < tile.valid ? row : 0;
+      a_off[i] = rr * K + c * 8;
+    }
+    // B row kr of the slice: logical chunk c = lane ^ 2*(kr & 3); lanes 0-31 read the
+    // first 256 columns (GATEUP: W1), lanes 32-63 the next 256 (GATEUP: W3).
+    int b_col[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int c = lane ^ (2 * r4);
+      int col = OP == MOE_OP_GATEUP_SWIGLU ? n0 + (c & 31) * 8 : n0 + c * 8;
+      if (col >= N) col = 0;
+      b_col[r4] = col;
+    }
+    const bf16_t* b_base = (OP == MOE_OP_GATEUP_SWIGLU && lane >= 32) ? b1e : b0e;
+    auto issue = [&](int ks) {
+      unsigned char* st = lds + (ks % kV2Stages) * kV2Stage;
+      const int k0 = ks * kV2BK;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) copy16_to_lds(asrc + k0 + a_off[i], st + (wave * 2 + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kr = wave * 8 + i;
+        copy16_to_lds(b_base + ((k0 + kr) * N + b_col[i & 3]),
+                      st + kV2ABytes + kr * 1024);
+      }
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    bf16x8_t af[2][4], bfr[2][4];
+    auto read_frags = [&](int stage, int kk, bf16x8_t* a, bf16x8_t* b) {
+      const unsigned char* sa = lds + stage * kV2Stage;
+      const unsigned char* sb = sa + kV2ABytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 32 + (lane & 31);
+        const int p = (kk * 2 + (lane >> 5)) ^ ((row >> 1) & 3);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + p * 16);
+      }
+      const int kbase = kk * 16 + (g >> 1) * 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ncol = nb[j] + (g & 1) * 16 + 4 * tr_c4;
+        i16x4_t h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = kbase + hh * 4 + tr_r;
+          const int phys = (ncol >> 3) ^ (2 * tr_r);
+          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (MOE_LDS i16x4_t*)(sb + k * 1024 + phys * 16 + (ncol & 7) * 2));
+        }
+        b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+
+    // prologue: slices 0 and 1 in flight
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 1) { MOE_WAIT_VMCNT(kV2CopiesPerThread); } else { MOE_WAIT_VMCNT(0); }
+    __syncthreads();
+    read_frags(0, 0, af[0], bfr[0]);
+
+
+    for (int ks = 0; ks < nk; ++ks) {
+      const int stage = ks % kV2Stages;
+      if (ks + 2 < nk) issue(ks + 2);
+      read_frags(stage, 1, af[1], bfr[1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
+      if (ks + 1 < nk) {
+        // slice ks+1 has landed once at most the copies of slice ks+2 are outstanding
+        if (ks + 2 < nk) { MOE_WAIT_VMCNT(kV2CopiesPerThread); } else { MOE_WAIT_VMCNT(0); }
+        __syncthreads();
+        read_frags((ks + 1) % kV2Stages, 0, af[0], bfr[0]);
+      }
+    }
+    __syncthreads();  // every wave is done with the ring before the next tile refills it
+
+    // Epilogue.  32x32 accumulator layout: element q of lane l is row
+    // (q/4)*8 + (l/32)*4 + q%4, column l%32 of the 32x32 subtile.
+    const int col_in = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        if (r >= tile.valid) continue;
+        bf16_t* crow = C + (size_t)(tile.m0 + r) * N;
+        if (OP == MOE_OP_GATEUP_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wave * 64 + j * 32 + col_in;
+            if (col < N) crow[col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wave * 128 + j * 32 + col_in;
+            if (col < N) crow[col] = f32_to_bf16(acc[i][j][q]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: LDS-tiled FMA GEMM, 32 rows x 64 output columns per work group.
 // ---------------------------------------------------------------------------
 static constexpr int kFM = 32, kFN = 64, kFK = 16;
@@ -313,7 +526,23 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const 
   const int64_t max_rows = dense_rows > 0 ? (int64_t)dense_rows : (int64_t)max_blocks * s.block_m;
   const int E = dense_rows > 0 ? 1 : s.E;
   const int cus = device_cu_count();
-  if (s.dtype == MOE_DTYPE_BF16) {
+  if (s.dtype == MOE_DTYPE_BF16 && K % kV2BK == 0) {
+    const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
+    const int n_tiles = (int)ceil_div(N, out_cols);
+    int64_t items = blocks_ub * (s.block_m / kBM) * n_tiles;
+    int64_t grid = items < cus ? items : cus;
+    if (grid < 1) grid = 1;
+    if (op == MOE_OP_GATEUP_SWIGLU)
+      hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kThreads), 0,
+                         st, static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B0),
+                         static_cast<const bf16_t*>(B1), static_cast<bf16_t*>(C), K, N, block_meta,
+                         num_blocks, max_blocks, E, max_rows, dense_rows, s.block_m, n_tiles);
+    else
+      hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_DOWN>, dim3((unsigned)grid), dim3(kThreads), 0, st,
+                         static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B0), nullptr,
+                         static_cast<bf16_t*>(C), K, N, block_meta, num_blocks, max_blocks, E,
+                         max_rows, dense_rows, s.block_m, n_tiles);
+  } else if (s.dtype == MOE_DTYPE_BF16) {
     const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 128 : 256;
     const int n_tiles = (int)ceil_div(N, out_cols);
     int64_t items = blocks_ub * (s.block_m / kBM) * n_tiles;

@@ -52,9 +52,13 @@ typedef int32_t moe_status;
 /*
  * The layer's shape.
  *   T >= 0 tokens (T == 0 is a no-op); d, d_e >= 1 with d % 8 == 0 and d_e % 8 == 0
- *   (bf16) or % 4 == 0 (fp32); 1 <= k <= E <= 1024; T * k < 2^31.
+ *   (bf16) or % 4 == 0 (fp32); 1 <= E <= 1024; 1 <= k <= 1024; T * k < 2^31.  The
+ *   router picks k distinct experts, so routing (moe_route, moe_layer_fwd without
+ *   given routes) needs k <= E; rows routed elsewhere may repeat an expert within a
+ *   token (k > E is then allowed).
  *   n_groups, topk_groups: 0, 0 for plain top-k; otherwise E % n_groups == 0,
- *   1 <= topk_groups <= n_groups and k <= topk_groups * E / n_groups (group-limited
+ *   1 <= topk_groups <= n_groups <= 64, and routing needs k <= topk_groups * E /
+ *   n_groups (group-limited
  *   routing: experts form n_groups contiguous id ranges, a group scores its largest
  *   logit, only the topk_groups best groups stay eligible; TileLang chapter section
  *   2.2, dropless notes section 4 step 4).

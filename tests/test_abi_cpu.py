@@ -48,7 +48,7 @@ def good_shape(**kw):
 
 
 BAD_SHAPES = [
-    (dict(k=9), B.MOE_EINVAL),                 # k > E
+    (dict(k=1025), B.MOE_ENOTSUP),
     (dict(k=0), B.MOE_EINVAL),
     (dict(d=12), B.MOE_EINVAL),                # bf16 rows must be 16-byte multiples
     (dict(d_e=4), B.MOE_EINVAL),
@@ -57,13 +57,31 @@ BAD_SHAPES = [
     (dict(n_groups=3), B.MOE_EINVAL),          # E % n_groups
     (dict(n_groups=4, topk_groups=0), B.MOE_EINVAL),
     (dict(n_groups=4, topk_groups=5), B.MOE_EINVAL),
-    (dict(n_groups=4, topk_groups=1, k=3), B.MOE_EINVAL),   # k > topk_groups * E / n_groups
+    (dict(n_groups=128, topk_groups=1, E=128), B.MOE_ENOTSUP),
     (dict(n_groups=0, topk_groups=2), B.MOE_EINVAL),
     (dict(block_m=0), B.MOE_EINVAL),
     (dict(block_m=32), B.MOE_ENOTSUP),         # bf16 grouped GEMM works in 128-row tiles
     (dict(d_e_shared=12), B.MOE_EINVAL),
     (dict(T=1 << 29, k=4), B.MOE_EINVAL),      # T*k >= 2^31
 ]
+
+
+def test_routing_needs_k_at_most_E_but_routed_rows_may_repeat_experts():
+    """k > E is a valid shape for rows that arrive already routed (duplicates within a
+    token), but the router itself cannot pick k distinct experts out of E."""
+    L = B.lib()
+    s = good_shape(k=9)
+    ps = ctypes.byref(s)
+    assert L.moe_max_blocks(ps) > 0
+    assert L.moe_route(ps, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 40, None) == B.MOE_EINVAL
+    need = L.moe_workspace_bytes(ps)
+    # without given routes the layer must route: rejected
+    assert L.moe_layer_fwd(ps, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None, None, None,
+                           FAKE, FAKE, need, None) == B.MOE_EINVAL
+    s2 = good_shape(n_groups=4, topk_groups=1, k=3)
+    assert L.moe_route(ctypes.byref(s2), FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 40,
+                       None) == B.MOE_EINVAL
+    assert L.moe_max_blocks(ctypes.byref(s2)) > 0
 
 
 @pytest.mark.parametrize("kw,status", BAD_SHAPES)

@@ -26,6 +26,10 @@ REDUCED = {
                           fixed_counts=(1357, 938, 1124, 677)),
     "decode": C4.scaled(name="decode-r", d=512, d_e=256, d_e_shared=256),
     "zipf": C5.scaled(name="zipf-r", T=2048, d=512, d_e=352),
+    # column tails inside the asynchronous-copy kernel (K % 32 == 0, N ragged)
+    "gateup-ncols-ragged": C2.scaled(name="gateup-ncols-ragged", T=333, d=1024, d_e=200,
+                                     d_e_shared=72),
+    "down-ncols-ragged": C5.scaled(name="down-ncols-ragged", T=700, d=1000, d_e=384),
     "tiny-fp32-ragged": C1.scaled(name="tiny-fp32-ragged", T=37, d=100, d_e=60, block_m=7,
                                   d_e_shared=44),
 }
