@@ -282,20 +282,28 @@ __device__ __forceinline__ void copy16_to_lds(const void* gsrc, const unsigned c
                : "memory", "m0");
 }
 
-template <int OP>
+// A slice in LDS: 128 rows x 64 bytes; chunk c of row r sits at chunk c ^ ((r >> 2) & 3).
+// B slice: 32 rows (k) x 1 KB; chunk c of row k sits at chunk c ^ (4 * (k & 3)).
+// Both were measured conflict-free on gfx950 for the reads below.
+__device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int swz_b(int k, int chunk) { return chunk ^ (4 * (k & 3)); }
+
+template <int OP, bool DENSE>
 __global__ void __launch_bounds__(kThreads, 1)
 k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
              const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int K, int N,
              const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
-             int max_blocks, int E, int64_t max_rows, int dense_rows, int block_m, int n_tiles) {
+             int max_blocks, int E, int64_t max_rows, int dense_rows_arg, int block_m,
+             int n_tiles) {
   __shared__ __align__(1024) unsigned char lds[kV2Stages * kV2Stage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dense_rows = DENSE ? dense_rows_arg : 0;
   constexpr int kOutCols = OP == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
   const int tpb = block_m / kBM;
   const int nblocks =
-      dense_rows > 0 ? (dense_rows + block_m - 1) / block_m : min(num_blocks_ptr[0], max_blocks);
+      DENSE ? (dense_rows + block_m - 1) / block_m : min(num_blocks_ptr[0], max_blocks);
   const int total = nblocks * tpb * n_tiles;
   const int nk = K / kV2BK;
 
@@ -317,22 +325,22 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
     const bf16_t* b0e = B0 + (size_t)tile.e * K * N;
     const bf16_t* b1e = OP == MOE_OP_GATEUP_SWIGLU ? B1 + (size_t)tile.e * K * N : b0e;
 
-    // Per-lane element offsets of the copies; the bases are wave-uniform, so each copy
-    // is an SGPR base plus one 32-bit VGPR offset.
+    // Per-lane element offsets of the copies.  Rows past valid_m and columns past N
+    // read row 0 / column 0 instead (never stored), so every lane issues every copy.
     int a_off[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = (wave * 2 + i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      const int c = swz_a(row, lane & 3);  // the swizzle is an involution
       const int rr = row < tile.valid ? row : 0;
       a_off[i] = rr * K + c * 8;
     }
-    // B row kr of the slice: logical chunk c = lane ^ 2*(kr & 3); lanes 0-31 read the
-    // first 256 columns (GATEUP: W1), lanes 32-63 the next 256 (GATEUP: W3).
+    // B row kr: lanes 0-31 fetch the first 256 columns (GATEUP: W1), 32-63 the next
+    // 256 (GATEUP: W3); the XOR leaves bit 5 of the chunk index alone.
     int b_col[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const int c = lane ^ (2 * r4);
+      const int c = swz_b(r4, lane);
       int col = OP == MOE_OP_GATEUP_SWIGLU ? n0 + (c & 31) * 8 : n0 + c * 8;
       if (col >= N) col = 0;
       b_col[r4] = col;
@@ -346,8 +354,7 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int kr = wave * 8 + i;
-        copy16_to_lds(b_base + ((k0 + kr) * N + b_col[i & 3]),
-                      st + kV2ABytes + kr * 1024);
+        copy16_to_lds(b_base + ((k0 + kr) * N + b_col[i & 3]), st + kV2ABytes + kr * 1024);
       }
     };
 
@@ -359,15 +366,14 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    bf16x8_t af[2][4], bfr[2][4];
+    bf16x8_t af0[4], bf0[4], af1[4], bf1[4];
     auto read_frags = [&](int stage, int kk, bf16x8_t* a, bf16x8_t* b) {
       const unsigned char* sa = lds + stage * kV2Stage;
       const unsigned char* sb = sa + kV2ABytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = i * 32 + (lane & 31);
-        const int p = (kk * 2 + (lane >> 5)) ^ ((row >> 1) & 3);
-        a[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + p * 16);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
       }
       const int kbase = kk * 16 + (g >> 1) * 8;
 #pragma unroll
@@ -377,70 +383,103 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = kbase + hh * 4 + tr_r;
-          const int phys = (ncol >> 3) ^ (2 * tr_r);
           h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MOE_LDS i16x4_t*)(sb + k * 1024 + phys * 16 + (ncol & 7) * 2));
+              (MOE_LDS i16x4_t*)(sb + k * 1024 + swz_b(k, ncol >> 3) * 16 + (ncol & 7) * 2));
         }
         b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
+    auto mfma_block = [&](const bf16x8_t* a, const bf16x8_t* b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
 
-    // prologue: slices 0 and 1 in flight
+    // Prologue: all three slots in flight, wait for slice 0.
     issue(0);
     if (nk > 1) issue(1);
-    if (nk > 1) { MOE_WAIT_VMCNT(kV2CopiesPerThread); } else { MOE_WAIT_VMCNT(0); }
-    __syncthreads();
-    read_frags(0, 0, af[0], bfr[0]);
-
-
-    for (int ks = 0; ks < nk; ++ks) {
-      const int stage = ks % kV2Stages;
-      if (ks + 2 < nk) issue(ks + 2);
-      read_frags(stage, 1, af[1], bfr[1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[1][i], bfr[1][j], acc[i][j], 0, 0, 0);
-      if (ks + 1 < nk) {
-        // slice ks+1 has landed once at most the copies of slice ks+2 are outstanding
-        if (ks + 2 < nk) { MOE_WAIT_VMCNT(kV2CopiesPerThread); } else { MOE_WAIT_VMCNT(0); }
-        __syncthreads();
-        read_frags((ks + 1) % kV2Stages, 0, af[0], bfr[0]);
-      }
+    if (nk > 2) issue(2);
+    if (nk > 2) {
+      MOE_WAIT_VMCNT(2 * kV2CopiesPerThread);
+    } else if (nk > 1) {
+      MOE_WAIT_VMCNT(kV2CopiesPerThread);
+    } else {
+      MOE_WAIT_VMCNT(0);
     }
-    __syncthreads();  // every wave is done with the ring before the next tile refills it
+    __syncthreads();
+    read_frags(0, 0, af0, bf0);
 
-    // Epilogue.  32x32 accumulator layout: element q of lane l is row
-    // (q/4)*8 + (l/32)*4 + q%4, column l%32 of the 32x32 subtile.
-    const int col_in = lane & 31;
+    // Slice ks: the barrier sits between its two 16-deep halves, so while the waves
+    // sync and fetch slice ks+1's first fragments, the second half's 16 MFMAs are
+    // still to issue.  Slot ks % 3 is refilled with slice ks+3 right after the
+    // barrier, once every wave has read it.
+    for (int ks = 0; ks < nk - 1; ++ks) {
+      read_frags(ks % kV2Stages, 1, af1, bf1);
+      mfma_block(af0, bf0);
+      if (ks + 2 < nk) { MOE_WAIT_VMCNT(kV2CopiesPerThread); } else { MOE_WAIT_VMCNT(0); }
+      __syncthreads();
+      if (ks + 3 < nk) issue(ks + 3);
+      read_frags((ks + 1) % kV2Stages, 0, af0, bf0);
+      mfma_block(af1, bf1);
+    }
+    // last slice (peeled, so the loop body has no branch around its LDS reads)
+    read_frags((nk - 1) % kV2Stages, 1, af1, bf1);
+    mfma_block(af0, bf0);
+    mfma_block(af1, bf1);
+    __syncthreads();  // the ring is reused below as the epilogue's staging area
+
+    // Epilogue through LDS: each wave converts its accumulators to bf16 into a private
+    // [rows][cols + 8] staging tile, then stores whole 16-byte row chunks.  32x32
+    // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
+    // l%32 of the 32x32 subtile.
+    constexpr int kWCols = OP == MOE_OP_GATEUP_SWIGLU ? 64 : 128;  // columns per wave
+    constexpr int kHalves = OP == MOE_OP_GATEUP_SWIGLU ? 1 : 2;     // row passes
+    constexpr int kRowsPer = 128 / kHalves;
+    constexpr int kLd = kWCols + 8;                                  // staging row pitch
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kRowsPer * kLd;
+    const int col0 = n0 + wave * kWCols;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int hv = 0; hv < kHalves; ++hv) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        if (r >= tile.valid) continue;
-        bf16_t* crow = C + (size_t)(tile.m0 + r) * N;
-        if (OP == MOE_OP_GATEUP_SWIGLU) {
+      for (int i = 0; i < 4; ++i) {
+        if (i / (4 / kHalves) != hv) continue;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wave * 64 + j * 32 + col_in;
-            if (col < N) crow[col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
-          }
-        } else {
+        for (int q = 0; q < 16; ++q) {
+          const int r = (i % (4 / kHalves)) * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          if (OP == MOE_OP_GATEUP_SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wave * 128 + j * 32 + col_in;
-            if (col < N) crow[col] = f32_to_bf16(acc[i][j][q]);
+            for (int j = 0; j < 2; ++j)
+              stg[r * kLd + j * 32 + (lane & 31)] =
+                  f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              stg[r * kLd + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][q]);
           }
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int kChunks = kWCols / 8;           // 16-byte chunks per staged row
+      constexpr int kRowsPerPass = 64 / kChunks;
+#pragma unroll 4
+      for (int r0 = 0; r0 < kRowsPer; r0 += kRowsPerPass) {
+        const int r = r0 + lane / kChunks;
+        const int ch = lane % kChunks;
+        const int grow = hv * kRowsPer + r;
+        const int gcol = col0 + ch * 8;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + ch * 8);
+        if (grow < tile.valid && gcol < N)
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * N + gcol) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    __syncthreads();  // staging reads done before the next tile refills the ring
   }
 }
 
@@ -532,16 +571,24 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const 
     int64_t items = blocks_ub * (s.block_m / kBM) * n_tiles;
     int64_t grid = items < cus ? items : cus;
     if (grid < 1) grid = 1;
-    if (op == MOE_OP_GATEUP_SWIGLU)
-      hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kThreads), 0,
-                         st, static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B0),
-                         static_cast<const bf16_t*>(B1), static_cast<bf16_t*>(C), K, N, block_meta,
-                         num_blocks, max_blocks, E, max_rows, dense_rows, s.block_m, n_tiles);
-    else
-      hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_DOWN>, dim3((unsigned)grid), dim3(kThreads), 0, st,
-                         static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(B0), nullptr,
-                         static_cast<bf16_t*>(C), K, N, block_meta, num_blocks, max_blocks, E,
-                         max_rows, dense_rows, s.block_m, n_tiles);
+    const bf16_t* a = static_cast<const bf16_t*>(A);
+    const bf16_t* b0 = static_cast<const bf16_t*>(B0);
+    const bf16_t* b1 = static_cast<const bf16_t*>(B1);
+    bf16_t* c = static_cast<bf16_t*>(C);
+    // The dense (shared-expert) launch is its own instantiation, so profiles list it
+    // apart from the routed one.
+#define MOE_V2_LAUNCH(OPV, DENSEV)                                                             \
+  hipLaunchKernelGGL((k_gg_bf16_v2<OPV, DENSEV>), dim3((unsigned)grid), dim3(kThreads), 0, st, a, \
+                     b0, b1, c, K, N, block_meta, num_blocks, max_blocks, E, max_rows, dense_rows, \
+                     s.block_m, n_tiles)
+    if (op == MOE_OP_GATEUP_SWIGLU) {
+      if (dense_rows > 0) MOE_V2_LAUNCH(MOE_OP_GATEUP_SWIGLU, true);
+      else MOE_V2_LAUNCH(MOE_OP_GATEUP_SWIGLU, false);
+    } else {
+      if (dense_rows > 0) MOE_V2_LAUNCH(MOE_OP_DOWN, true);
+      else MOE_V2_LAUNCH(MOE_OP_DOWN, false);
+    }
+#undef MOE_V2_LAUNCH
   } else if (s.dtype == MOE_DTYPE_BF16) {
     const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 128 : 256;
     const int n_tiles = (int)ceil_div(N, out_cols);
