@@ -234,62 +234,72 @@ k_gg_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
 // ---------------------------------------------------------------------------
 // bf16 kernel, asynchronous-copy version (K % 32 == 0).
 //
-//   * Work tile 128 rows x 512 B-columns; 4 waves, each owning all 128 rows and 128
-//     B-columns (GATEUP: 64 gate + the 64 matching up columns), i.e. a 4 x 4 grid of
-//     32x32 accumulators per wave (256 fp32 values per lane).
-//   * Operands go HBM -> LDS with global_load_lds (16 bytes per lane, no registers),
-//     into a 3-stage ring of 32-deep K slices; the loads for slice ks+2 are issued
-//     while slice ks is multiplied.
-//   * A (rows, K-contiguous) is read with ds_read_b128.  B stays in its natural
-//     [k][n] layout in LDS and is read with ds_read_b64_tr_b16: in each 16-lane group
-//     lane 4r+c points at row r, columns 4c..4c+3 of a 4 x 16 block and receives
-//     column (lane % 16), so two such reads give a lane the 8 consecutive k values of
-//     one column that the 32x32x16 MFMA takes.
-//   * Both LDS layouts are XOR-swizzled on 16-byte chunks so the A reads (8 rows per
-//     cycle) and the transposed B reads (4 rows x 32 bytes per 16-lane group) hit 32
-//     distinct banks.
-//   * Rows past valid_m and columns past N load a valid row / column instead (their
+//   * Work tile 128 rows x 512 B-columns, 8 waves (two per SIMD, so one wave's MFMAs
+//     cover the other's copies, LDS reads and barrier waits).  Wave w owns all 128
+//     rows and 64 B-columns: GATEUP gate columns [32w, 32w+32) with the matching up
+//     columns, DOWN columns [64w, 64w+64); a 4 x 2 grid of 32x32 accumulators.
+//   * Operands go HBM -> LDS with 16-byte global_load_lds copies into a 3-stage ring
+//     of 32-deep K slices.  Every copy has a wave-uniform SGPR base and a per-lane
+//     32-bit offset that is fixed for the whole tile.
+//   * A (rows, K-contiguous) is read with ds_read_b128.  B stays [k][n] in LDS, split
+//     in two 256-column halves (GATEUP: W1 and W3; DOWN: the two halves of the 512
+//     columns), and is read with ds_read_b64_tr_b16: in each 16-lane group lane 4r+c
+//     points at row r, columns 4c..4c+3 of a 4 x 16 block and receives column
+//     (lane % 16), so two such reads give a lane the 8 consecutive k values of one
+//     column that the 32x32x16 MFMA takes.
+//   * LDS swizzles (16-byte chunks) measured conflict-free on gfx950: A chunk c of
+//     row r at c ^ ((r >> 2) & 3); B chunk c of row k at c ^ 4 * (k & 3).
+//   * Rows past valid_m and columns past N copy row 0 / column 0 instead (their
 //     results are never stored), so every lane issues every copy and the copy count
-//     per slice is uniform - the vmcnt-based wait below relies on that.
+//     per slice is uniform - the vmcnt-based waits rely on that.
 // ---------------------------------------------------------------------------
+static constexpr int kV2Threads = 512;            // 8 waves
 static constexpr int kV2BK = 32;                  // K per stage
 static constexpr int kV2NB = 512;                 // B columns per tile
 static constexpr int kV2ABytes = kBM * kV2BK * 2; // 8 KB
-static constexpr int kV2BBytes = kV2BK * kV2NB * 2;  // 32 KB
-static constexpr int kV2Stage = kV2ABytes + kV2BBytes;
+static constexpr int kV2BHalf = kV2BK * 256 * 2;  // 16 KB per 256-column half
+static constexpr int kV2Stage = kV2ABytes + 2 * kV2BHalf;
 static constexpr int kV2Stages = 3;
-static constexpr int kV2CopiesPerThread = 2 + 8;  // A: 8 windows / 4 waves, B: 32 rows / 4 waves
+static constexpr int kV2CopiesPerThread = 1 + 4;  // A: 8 windows / 8 waves, B: 32 / 8
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #define MOE_LDS __attribute__((address_space(3)))
-#define MOE_GLOBAL __attribute__((address_space(1)))
 
 // s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 encoding).
 #define MOE_WAIT_VMCNT(n) \
   __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// 16-byte asynchronous copy global -> LDS: lane l's 16 bytes land at lds_base + 16*l
-// (lds_base is wave-uniform and goes through M0).  Issued as inline assembly so the
-// compiler's own counter model does not see it: it would otherwise wait for every
-// outstanding copy before each LDS read.  The caller waits with MOE_WAIT_VMCNT;
-// loads complete in issue order, so compiler-generated waits stay correct (they can
-// only over-wait).
-__device__ __forceinline__ void copy16_to_lds(const void* gsrc, const unsigned char* lds_base) {
+// Wait until at most n slices' copies (n * kV2CopiesPerThread) are outstanding.
+__device__ __forceinline__ void wait_slices(int n) {
+  switch (n) {
+    case 0: MOE_WAIT_VMCNT(0); break;
+    case 1: MOE_WAIT_VMCNT(kV2CopiesPerThread); break;
+    case 2: MOE_WAIT_VMCNT(2 * kV2CopiesPerThread); break;
+    case 3: MOE_WAIT_VMCNT(3 * kV2CopiesPerThread); break;
+    default: MOE_WAIT_VMCNT(4 * kV2CopiesPerThread); break;
+  }
+}
+
+// 16-byte asynchronous copy global -> LDS: lane l reads gbase + voff_bytes[l] and its
+// 16 bytes land at lds_base + 16*l (gbase and lds_base are wave-uniform; lds_base
+// goes through M0).  Issued as inline assembly so the compiler's own counter model
+// does not see it: it would otherwise wait for every outstanding copy before each
+// LDS read.  The caller waits with MOE_WAIT_VMCNT; loads complete in issue order, so
+// compiler-generated waits stay correct (they can only over-wait).
+__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff_bytes,
+                                              const unsigned char* lds_base) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(const MOE_LDS void*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gsrc), "s"(m0)
+               : "v"(voff_bytes), "s"(gbase), "s"(m0)
                : "memory", "m0");
 }
 
-// A slice in LDS: 128 rows x 64 bytes; chunk c of row r sits at chunk c ^ ((r >> 2) & 3).
-// B slice: 32 rows (k) x 1 KB; chunk c of row k sits at chunk c ^ (4 * (k & 3)).
-// Both were measured conflict-free on gfx950 for the reads below.
 __device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 __device__ __forceinline__ int swz_b(int k, int chunk) { return chunk ^ (4 * (k & 3)); }
 
 template <int OP, bool DENSE>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kV2Threads, 1)
 k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
              const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int K, int N,
              const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
@@ -307,13 +317,15 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
   const int total = nblocks * tpb * n_tiles;
   const int nk = K / kV2BK;
 
-  // B-fragment read geometry (fixed per lane): 16-lane group g, row r, column quad c4.
+  // B-fragment geometry (fixed per lane): 16-lane group g, row r, column quad c4, and
+  // for each of the wave's two 32-column subtiles its LDS half and first column.
   const int g = lane >> 4, gi = lane & 15, tr_r = gi >> 2, tr_c4 = gi & 3;
-  int nb[4];  // first B column of this wave's four 32-column subtiles
+  int bhalf[2], bcol0[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    nb[j] = OP == MOE_OP_GATEUP_SWIGLU ? (j < 2 ? wave * 64 + j * 32 : 256 + wave * 64 + (j - 2) * 32)
-                                       : wave * 128 + j * 32;
+  for (int j = 0; j < 2; ++j) {
+    bhalf[j] = OP == MOE_OP_GATEUP_SWIGLU ? j : wave >> 2;
+    bcol0[j] = OP == MOE_OP_GATEUP_SWIGLU ? wave * 32 : (wave & 3) * 64 + j * 32;
+  }
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     const int nt = w % n_tiles;
@@ -324,49 +336,55 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
     const bf16_t* asrc = A + (size_t)tile.m0 * K;
     const bf16_t* b0e = B0 + (size_t)tile.e * K * N;
     const bf16_t* b1e = OP == MOE_OP_GATEUP_SWIGLU ? B1 + (size_t)tile.e * K * N : b0e;
+    // the two 256-column halves of the tile's B columns: matrix and first column
+    const bf16_t* bh_base[2] = {b0e, OP == MOE_OP_GATEUP_SWIGLU ? b1e : b0e};
+    const int bh_col0[2] = {n0, OP == MOE_OP_GATEUP_SWIGLU ? n0 : n0 + 256};
 
-    // Per-lane element offsets of the copies.  Rows past valid_m and columns past N
-    // read row 0 / column 0 instead (never stored), so every lane issues every copy.
-    int a_off[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (wave * 2 + i) * 16 + (lane >> 2);
-      const int c = swz_a(row, lane & 3);  // the swizzle is an involution
+    // A copy (one per wave per slice): window = this wave's 16 rows.
+    uint32_t a_voff;
+    {
+      const int row = wave * 16 + (lane >> 2);
+      const int c = swz_a(row, lane & 3);   // the swizzle is an involution
       const int rr = row < tile.valid ? row : 0;
-      a_off[i] = rr * K + c * 8;
+      a_voff = (uint32_t)(rr * K + c * 8) * 2u;
     }
-    // B row kr: lanes 0-31 fetch the first 256 columns (GATEUP: W1), 32-63 the next
-    // 256 (GATEUP: W3); the XOR leaves bit 5 of the chunk index alone.
-    int b_col[4];
+    // B copies: instruction i of this wave covers rows 2p, 2p+1 of half h, where
+    // (h, p) = ((wave*4 + i) / 16, (wave*4 + i) % 16); lanes 0-31 take row 2p, lanes
+    // 32-63 row 2p+1.  The lane offset depends on the row parity only through the
+    // swizzle (k & 3 = 2*(p & 1) + lane/32), so two offsets per half suffice.
+    uint32_t b_voff[2][2];  // [half][p & 1]
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int c = swz_b(r4, lane);
-      int col = OP == MOE_OP_GATEUP_SWIGLU ? n0 + (c & 31) * 8 : n0 + c * 8;
-      if (col >= N) col = 0;
-      b_col[r4] = col;
-    }
-    const bf16_t* b_base = (OP == MOE_OP_GATEUP_SWIGLU && lane >= 32) ? b1e : b0e;
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int k = 2 * pp + (lane >> 5);
+        const int c = swz_b(k, lane & 31);
+        int col = bh_col0[h] + c * 8;     // absolute column; past N -> column 0
+        if (col >= N) col = 0;
+        b_voff[h][pp] = (uint32_t)((lane >> 5) * N + col) * 2u;
+      }
     auto issue = [&](int ks) {
       unsigned char* st = lds + (ks % kV2Stages) * kV2Stage;
       const int k0 = ks * kV2BK;
+      copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) copy16_to_lds(asrc + k0 + a_off[i], st + (wave * 2 + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int kr = wave * 8 + i;
-        copy16_to_lds(b_base + ((k0 + kr) * N + b_col[i & 3]), st + kV2ABytes + kr * 1024);
+      for (int i = 0; i < 4; ++i) {
+        const int q = wave * 4 + i;  // 0..31: half q / 16, row pair q % 16
+        const int h = q >> 4, pr = q & 15;
+        copy16_to_lds(bh_base[h] + (size_t)(k0 + 2 * pr) * N, b_voff[h][pr & 1],
+                      st + kV2ABytes + h * kV2BHalf + pr * 1024);
       }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    bf16x8_t af0[4], bf0[4], af1[4], bf1[4];
+    bf16x8_t af0[4], bf0[2], af1[4], bf1[2];
     auto read_frags = [&](int stage, int kk, bf16x8_t* a, bf16x8_t* b) {
       const unsigned char* sa = lds + stage * kV2Stage;
       const unsigned char* sb = sa + kV2ABytes;
@@ -377,50 +395,46 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
       }
       const int kbase = kk * 16 + (g >> 1) * 8;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ncol = nb[j] + (g & 1) * 16 + 4 * tr_c4;
-        i16x4_t h[2];
+      for (int j = 0; j < 2; ++j) {
+        const int ncol = bcol0[j] + (g & 1) * 16 + 4 * tr_c4;
+        const unsigned char* hb = sb + bhalf[j] * kV2BHalf;
+        i16x4_t hv[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = kbase + hh * 4 + tr_r;
-          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (MOE_LDS i16x4_t*)(sb + k * 1024 + swz_b(k, ncol >> 3) * 16 + (ncol & 7) * 2));
+          hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (MOE_LDS i16x4_t*)(hb + k * 512 + swz_b(k, ncol >> 3) * 16 + (ncol & 7) * 2));
         }
-        b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
     };
     auto mfma_block = [&](const bf16x8_t* a, const bf16x8_t* b) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     };
 
-    // Prologue: all three slots in flight, wait for slice 0.
-    issue(0);
-    if (nk > 1) issue(1);
-    if (nk > 2) issue(2);
-    if (nk > 2) {
-      MOE_WAIT_VMCNT(2 * kV2CopiesPerThread);
-    } else if (nk > 1) {
-      MOE_WAIT_VMCNT(kV2CopiesPerThread);
-    } else {
-      MOE_WAIT_VMCNT(0);
-    }
+    // Prologue: every slot in flight, wait for slice 0.
+#pragma unroll
+    for (int p = 0; p < kV2Stages; ++p)
+      if (p < nk) issue(p);
+    wait_slices(min(nk, kV2Stages) - 1);
     __syncthreads();
     read_frags(0, 0, af0, bf0);
 
     // Slice ks: the barrier sits between its two 16-deep halves, so while the waves
-    // sync and fetch slice ks+1's first fragments, the second half's 16 MFMAs are
-    // still to issue.  Slot ks % 3 is refilled with slice ks+3 right after the
-    // barrier, once every wave has read it.
+    // sync and fetch slice ks+1's first fragments, the second half's MFMAs are still
+    // to issue.  Slot ks % S is refilled with slice ks+S right after the barrier,
+    // once every wave has read it.
     for (int ks = 0; ks < nk - 1; ++ks) {
       read_frags(ks % kV2Stages, 1, af1, bf1);
       mfma_block(af0, bf0);
-      if (ks + 2 < nk) { MOE_WAIT_VMCNT(kV2CopiesPerThread); } else { MOE_WAIT_VMCNT(0); }
+      // slice ks+1 has landed once only slices ks+2 .. ks+S-1 may be outstanding
+      wait_slices(min(nk - ks - 2, kV2Stages - 2));
       __syncthreads();
-      if (ks + 3 < nk) issue(ks + 3);
+      if (ks + kV2Stages < nk) issue(ks + kV2Stages);
       read_frags((ks + 1) % kV2Stages, 0, af0, bf0);
       mfma_block(af1, bf1);
     }
@@ -434,12 +448,12 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
     // [rows][cols + 8] staging tile, then stores whole 16-byte row chunks.  32x32
     // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
     // l%32 of the 32x32 subtile.
-    constexpr int kWCols = OP == MOE_OP_GATEUP_SWIGLU ? 64 : 128;  // columns per wave
-    constexpr int kHalves = OP == MOE_OP_GATEUP_SWIGLU ? 1 : 2;     // row passes
+    constexpr int kWCols = OP == MOE_OP_GATEUP_SWIGLU ? 32 : 64;   // output columns per wave
+    constexpr int kHalves = OP == MOE_OP_GATEUP_SWIGLU ? 1 : 2;    // row passes
     constexpr int kRowsPer = 128 / kHalves;
-    constexpr int kLd = kWCols + 8;                                  // staging row pitch
+    constexpr int kLd = kWCols + 8;                                 // staging row pitch
     bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kRowsPer * kLd;
-    const int col0 = n0 + wave * kWCols;
+    const int col0 = n0 + (OP == MOE_OP_GATEUP_SWIGLU ? wave * 32 : (wave >> 2) * 256 + (wave & 3) * 64);
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
 #pragma unroll
@@ -449,13 +463,10 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
         for (int q = 0; q < 16; ++q) {
           const int r = (i % (4 / kHalves)) * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
           if (OP == MOE_OP_GATEUP_SWIGLU) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              stg[r * kLd + j * 32 + (lane & 31)] =
-                  f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+            stg[r * kLd + (lane & 31)] = f32_to_bf16(silu_f32(acc[i][0][q]) * acc[i][1][q]);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
               stg[r * kLd + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][q]);
           }
         }
@@ -578,7 +589,7 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const 
     // The dense (shared-expert) launch is its own instantiation, so profiles list it
     // apart from the routed one.
 #define MOE_V2_LAUNCH(OPV, DENSEV)                                                             \
-  hipLaunchKernelGGL((k_gg_bf16_v2<OPV, DENSEV>), dim3((unsigned)grid), dim3(kThreads), 0, st, a, \
+  hipLaunchKernelGGL((k_gg_bf16_v2<OPV, DENSEV>), dim3((unsigned)grid), dim3(kV2Threads), 0, st, a, \
                      b0, b1, c, K, N, block_meta, num_blocks, max_blocks, E, max_rows, dense_rows, \
                      s.block_m, n_tiles)
     if (op == MOE_OP_GATEUP_SWIGLU) {
