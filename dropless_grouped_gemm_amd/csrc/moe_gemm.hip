@@ -259,8 +259,10 @@ static constexpr int kV2NB = 512;                 // B columns per tile
 static constexpr int kV2ABytes = kBM * kV2BK * 2; // 8 KB
 static constexpr int kV2BHalf = kV2BK * 256 * 2;  // 16 KB per 256-column half
 static constexpr int kV2Stage = kV2ABytes + 2 * kV2BHalf;
-static constexpr int kV2Stages = 3;
+static constexpr int kV2Stages = 4;
 static constexpr int kV2CopiesPerThread = 1 + 4;  // A: 8 windows / 8 waves, B: 32 / 8
+static constexpr bool kUseSuper = false;  // XCD-aware super-tile order
+static constexpr int kGroupM = 16, kGroupN = 2;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #define MOE_LDS __attribute__((address_space(3)))
@@ -327,9 +329,31 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
     bcol0[j] = OP == MOE_OP_GATEUP_SWIGLU ? wave * 32 : (wave & 3) * 64 + j * 32;
   }
 
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int nt = w % n_tiles;
-    const int mt = w / n_tiles;
+  // Work order.  Work groups are dispatched to the 8 XCDs round-robin (group b on
+  // XCD b % 8), and each XCD has its own L2.  Tiles are taken in super-tiles of
+  // kGroupM row blocks x kGroupN column tiles, one super-tile per XCD at a time, so
+  // the 32 groups of an XCD share kGroupM A blocks and kGroupN B panels in its L2.
+  const int nm = nblocks * tpb;
+  const int mgroups = (nm + kGroupM - 1) / kGroupM;
+  const int ngroups = (n_tiles + kGroupN - 1) / kGroupN;
+  const int n_super = mgroups * ngroups;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, slots = gridDim.x / 8;
+  const bool use_super = kUseSuper && gridDim.x % 8 == 0 && slots == kGroupM * kGroupN;
+  const int iters = use_super ? (n_super + 7) / 8 : (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  for (int it = 0; it < iters; ++it) {
+    int nt, mt;
+    if (use_super) {
+      const int sidx = xcd + 8 * it;
+      if (sidx >= n_super) break;
+      const int mg = sidx % mgroups, ng = sidx / mgroups;
+      mt = mg * kGroupM + slot / kGroupN;
+      nt = ng * kGroupN + slot % kGroupN;
+      if (mt >= nm || nt >= n_tiles) continue;
+    } else {
+      const int w = blockIdx.x + it * gridDim.x;
+      nt = w % n_tiles;
+      mt = w / n_tiles;
+    }
     Tile tile;
     if (!decode_block(mt / tpb, mt % tpb, kBM, block_m, meta, dense_rows, E, max_rows, tile)) continue;
     const int n0 = nt * kOutCols;
@@ -363,17 +387,23 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
         if (col >= N) col = 0;
         b_voff[h][pp] = (uint32_t)((lane >> 5) * N + col) * 2u;
       }
-    auto issue = [&](int ks) {
-      unsigned char* st = lds + (ks % kV2Stages) * kV2Stage;
+    // copy `part` (0: this wave's A window, 1..4: its B row pairs) of slice ks into
+    // ring slot `slot`
+    auto issue_part_to = [&](int ks, int slot, int part) {
+      unsigned char* st = lds + slot * kV2Stage;
       const int k0 = ks * kV2BK;
-      copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = wave * 4 + i;  // 0..31: half q / 16, row pair q % 16
+      if (part == 0) {
+        copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
+      } else {
+        const int q = wave * 4 + part - 1;  // 0..31: half q / 16, row pair q % 16
         const int h = q >> 4, pr = q & 15;
         copy16_to_lds(bh_base[h] + (size_t)(k0 + 2 * pr) * N, b_voff[h][pr & 1],
                       st + kV2ABytes + h * kV2BHalf + pr * 1024);
       }
+    };
+    auto issue = [&](int ks) {
+#pragma unroll
+      for (int part = 0; part < kV2CopiesPerThread; ++part) issue_part_to(ks, ks % kV2Stages, part);
     };
 
     f32x16_t acc[4][2];
@@ -416,33 +446,45 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     };
 
-    // Prologue: every slot in flight, wait for slice 0.
+    // Prologue: every slot in flight (slices past the end re-copy the last slice into
+    // a slot that is never read again, so every iteration issues the same number of
+    // copies and the waits below are constants), then wait for slice 0.
 #pragma unroll
-    for (int p = 0; p < kV2Stages; ++p)
-      if (p < nk) issue(p);
-    wait_slices(min(nk, kV2Stages) - 1);
+    for (int p = 0; p < kV2Stages; ++p) issue(min(p, nk - 1));
+    MOE_WAIT_VMCNT((kV2Stages - 1) * kV2CopiesPerThread);
     __syncthreads();
     read_frags(0, 0, af0, bf0);
 
     // Slice ks: the barrier sits between its two 16-deep halves, so while the waves
     // sync and fetch slice ks+1's first fragments, the second half's MFMAs are still
     // to issue.  Slot ks % S is refilled with slice ks+S right after the barrier,
-    // once every wave has read it.
+    // once every wave has read it; the refill copies are spread between the second
+    // half's MFMAs (a burst of copies right after the barrier stalls the waves on the
+    // memory-instruction queue).
     for (int ks = 0; ks < nk - 1; ++ks) {
       read_frags(ks % kV2Stages, 1, af1, bf1);
       mfma_block(af0, bf0);
-      // slice ks+1 has landed once only slices ks+2 .. ks+S-1 may be outstanding
-      wait_slices(min(nk - ks - 2, kV2Stages - 2));
+      // slice ks+1 has landed once only slices ks+2 .. ks+S-1 are outstanding
+      MOE_WAIT_VMCNT((kV2Stages - 2) * kV2CopiesPerThread);
       __syncthreads();
-      if (ks + kV2Stages < nk) issue(ks + kV2Stages);
       read_frags((ks + 1) % kV2Stages, 0, af0, bf0);
-      mfma_block(af1, bf1);
+      const int ksrc = min(ks + kV2Stages, nk - 1);
+      const int slot = ks % kV2Stages;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        issue_part_to(ksrc, slot, i);
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2)
+          acc[i][j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j2], acc[i][j2], 0, 0, 0);
+      }
+      issue_part_to(ksrc, slot, 4);
     }
     // last slice (peeled, so the loop body has no branch around its LDS reads)
     read_frags((nk - 1) % kV2Stages, 1, af1, bf1);
     mfma_block(af0, bf0);
     mfma_block(af1, bf1);
-    __syncthreads();  // the ring is reused below as the epilogue's staging area
+    MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
+    __syncthreads();
 
     // Epilogue through LDS: each wave converts its accumulators to bf16 into a private
     // [rows][cols + 8] staging tile, then stores whole 16-byte row chunks.  32x32
