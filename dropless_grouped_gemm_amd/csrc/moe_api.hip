@@ -203,17 +203,23 @@ moe_status moe_grouped_gemm(const moe_shape* s, int32_t op, const void* A, const
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
-  if (!A || !B0 || !C || !block_meta || !num_blocks) return MOE_EINVAL;
+  if (!A || !B0 || !C) return MOE_EINVAL;
   if (op == MOE_OP_GATEUP_SWIGLU && !B1) return MOE_EINVAL;
   if (op == MOE_OP_DOWN && B1) return MOE_EINVAL;
-  if (!aligned16(A) || !aligned16(B0) || (B1 && !aligned16(B1)) || !aligned16(C) ||
-      !aligned4(block_meta) || !aligned4(num_blocks))
+  if (!aligned16(A) || !aligned16(B0) || (B1 && !aligned16(B1)) || !aligned16(C))
     return MOE_EINVAL;
-  if (max_blocks < 1 || max_blocks > max_blocks_of(*s)) return MOE_EINVAL;
   const int K = op == MOE_OP_GATEUP_SWIGLU ? s->d : s->d_e;
   const int N = op == MOE_OP_GATEUP_SWIGLU ? s->d_e : s->d;
-  return launch_grouped_gemm(*s, op, A, B0, B1, K, N, block_meta, num_blocks, max_blocks, 0, C,
-                             static_cast<hipStream_t>(stream));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!block_meta && !num_blocks) {  // dense mode: one expert over all T rows
+    if (max_blocks != 0) return MOE_EINVAL;
+    if (s->T == 0) return MOE_OK;
+    return launch_grouped_gemm(*s, op, A, B0, B1, K, N, nullptr, nullptr, 0, s->T, C, hs);
+  }
+  if (!block_meta || !num_blocks || !aligned4(block_meta) || !aligned4(num_blocks))
+    return MOE_EINVAL;
+  if (max_blocks < 1 || max_blocks > max_blocks_of(*s)) return MOE_EINVAL;
+  return launch_grouped_gemm(*s, op, A, B0, B1, K, N, block_meta, num_blocks, max_blocks, 0, C, hs);
 }
 
 moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos, const float* topk_w,

@@ -166,6 +166,13 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* pos,
  * max_blocks (host) bounds num_blocks and sizes the launch, so the host never needs
  * the real block count; 1 <= max_blocks <= moe_max_blocks(s).  A and C hold
  * max_blocks * block_m rows.
+ * Dense mode (the shared expert, dropless notes section 1): block_meta and
+ * num_blocks both NULL and max_blocks == 0.  A and C then hold s->T rows, every row
+ * goes through one expert (B0, B1 point at a single [d, d_e] or [d_e, d] matrix) and
+ * s->E, s->k are not used.  This is the launch moe_layer_fwd makes for the shared
+ * expert, with d_e = d_e_shared.
+ * Errors: MOE_EINVAL for a bad op, NULL or misaligned operands, or a max_blocks
+ * outside the range above; nothing is launched then.
  */
 moe_status moe_grouped_gemm(const moe_shape* s, int32_t op, const void* A,
                             const void* B0, const void* B1,

@@ -117,6 +117,14 @@ def test_null_and_misaligned_pointers_rejected():
     mb = L.moe_max_blocks(ps)
     assert L.moe_grouped_gemm(ps, 1, FAKE, FAKE, None, FAKE, FAKE, mb + 1, FAKE, None) == B.MOE_EINVAL
     assert L.moe_grouped_gemm(ps, 1, FAKE, FAKE, None, FAKE, FAKE, 0, FAKE, None) == B.MOE_EINVAL
+    # dense mode: block table and count both NULL, max_blocks 0; half of the pair is an error
+    assert L.moe_grouped_gemm(ps, 1, FAKE, FAKE, None, None, FAKE, 1, FAKE, None) == B.MOE_EINVAL
+    assert L.moe_grouped_gemm(ps, 1, FAKE, FAKE, None, FAKE, None, 1, FAKE, None) == B.MOE_EINVAL
+    assert L.moe_grouped_gemm(ps, 1, FAKE, FAKE, None, None, None, 1, FAKE, None) == B.MOE_EINVAL
+    assert L.moe_grouped_gemm(ps, 1, FAKE, FAKE, None, None, None, -1, FAKE, None) == B.MOE_EINVAL
+    s0 = good_shape(T=0)
+    assert L.moe_grouped_gemm(ctypes.byref(s0), 1, FAKE, FAKE, None, None, None, 0, FAKE,
+                              None) == B.MOE_OK
     # layer: shared-expert pointers must match d_e_shared; routing pair all-or-nothing
     assert L.moe_layer_fwd(ps, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                            FAKE, FAKE, 1 << 40, None) == B.MOE_EINVAL

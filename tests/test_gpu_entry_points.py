@@ -248,6 +248,30 @@ def test_stage_entry_points(T, d, E, k, d_e, bm, dtype, mode):
     assert_close(f64(out_ns), O.combine(y_dev, ref_pos, f64(tw), k), TOL_STAGE[dtype], "out")
 
 
+@pytest.mark.parametrize("T,d,d_e,dtype", [(300, 256, 136, "bf16"), (129, 512, 256, "bf16"),
+                                           (1, 256, 128, "bf16"), (77, 96, 40, "fp32")])
+def test_grouped_gemm_dense_mode_is_the_shared_expert(T, d, d_e, dtype):
+    """Dense mode (no block table): all T rows through one expert, as the shared expert
+    of the layer; rows past T are neither read nor written."""
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    bm = 128 if dtype == "bf16" else 32
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T + d_e)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=1, k=1, d_e=d_e, block_m=bm, dtype=dtype)
+    act = torch.full((T + 1, d_e), 7.0, dtype=dt, device=DEV)
+    y = torch.full((T + 1, d), 7.0, dtype=dt, device=DEV)
+    B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x, w1, w3, None, None, 0, act)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, w2, None, None, None, 0, y)
+    torch.cuda.synchronize()
+    assert_close(f64(act)[:T], O.swiglu_act(f64(x), f64(w1), f64(w3)), TOL_STAGE[dtype], "act")
+    assert_close(f64(y)[:T], f64(act)[:T] @ f64(w2), TOL_STAGE[dtype], "y")
+    assert bool((act[T] == 7.0).all()) and bool((y[T] == 7.0).all())
+
+
 def test_combine_skips_negative_positions():
     T, d, k = 8, 64, 2
     s = B.make_shape(T=T, d=d, E=4, k=k, d_e=64, block_m=128)
