@@ -5,7 +5,8 @@
 
 One step is one pass of the whole layer over one batch already resident in HBM:
 router GEMM + top-k, counts/offsets/permutation, permute, grouped gate/up GEMM with
-SiLU*mul, grouped down GEMM, the shared expert, and combine.  The step is issued as
+SiLU*mul, grouped down GEMM (each GEMM launch also carries the shared expert when
+there is one), and combine.  The step is issued as
 the sequence of C-ABI calls that moe_layer_fwd makes, with HIP events recorded on the
 launch stream between them, so every kernel's average duration is measured inside
 the timed region.  Prints one JSON line.
@@ -95,16 +96,12 @@ def main():
     shared = cfg.d_e_shared > 0
     if shared:
         ds = cfg.d_e_shared
-        # the shared expert: the grouped GEMM's dense mode (no block table), the same
-        # launches moe_layer_fwd makes
-        s_sh = B.make_shape(T=T, d=d, E=1, k=1, d_e=ds, block_m=cfg.block_m, dtype=cfg.dtype)
+        # the shared expert rides in the routed grouped-GEMM launches as a dense
+        # segment (moe_grouped_gemm_shared), the calls moe_layer_fwd makes
         sh_act = torch.empty((T, ds), dtype=dt, device=dev)
         sh_out = torch.empty((T, d), dtype=dt, device=dev)
 
-    stages = (["route"] if not routed else []) + ["offsets", "permute", "gateup", "down"]
-    if shared:
-        stages += ["shared_gateup", "shared_down"]
-    stages += ["combine"]
+    stages = (["route"] if not routed else []) + ["offsets", "permute", "gateup", "down", "combine"]
 
     def step(ev=None):
         i = 0
@@ -123,24 +120,23 @@ def main():
         i += 1
         if ev is not None:
             ev[i].record()
-        B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk, mb, act)
-        i += 1
-        if ev is not None:
-            ev[i].record()
-        B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y)
+        if shared:
+            B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk,
+                                      mb, act, inp.x, inp.ws1, inp.ws3, sh_act)
+        else:
+            B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk, mb,
+                               act)
         i += 1
         if ev is not None:
             ev[i].record()
         if shared:
-            B.moe_grouped_gemm(s_sh, B.MOE_OP_GATEUP_SWIGLU, inp.x, inp.ws1, inp.ws3, None, None,
-                               0, sh_act)
-            i += 1
-            if ev is not None:
-                ev[i].record()
-            B.moe_grouped_gemm(s_sh, B.MOE_OP_DOWN, sh_act, inp.ws2, None, None, None, 0, sh_out)
-            i += 1
-            if ev is not None:
-                ev[i].record()
+            B.moe_grouped_gemm_shared(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y,
+                                      sh_act, inp.ws2, None, sh_out)
+        else:
+            B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y)
+        i += 1
+        if ev is not None:
+            ev[i].record()
         B.moe_combine(s, y, pos, topk_w, sh_out if shared else None, out)
         i += 1
         if ev is not None:
@@ -202,20 +198,19 @@ def main():
     cnt = counts.cpu().tolist()
     active = sum(1 for c in cnt if c > 0)
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    # each launch covers the routed rows and, when there is one, the shared expert
     gu_flops = LG.gateup_flops(M, d, de)
     dn_flops = LG.down_flops(M, d, de)
+    sg = LG.gateup_flops(T, d, cfg.d_e_shared) if shared else 0
+    sd = LG.down_flops(T, d, cfg.d_e_shared) if shared else 0
     gemm = {
-        "gateup": {"tflops": gu_flops / (stage_ms["gateup"] * 1e9),
-                   "flops": gu_flops, "us": stage_ms["gateup"] * 1e3},
-        "down": {"tflops": dn_flops / (stage_ms["down"] * 1e9),
-                 "flops": dn_flops, "us": stage_ms["down"] * 1e3},
+        "gateup": {"tflops": (gu_flops + sg) / (stage_ms["gateup"] * 1e9),
+                   "flops": gu_flops + sg, "routed_flops": gu_flops, "shared_flops": sg,
+                   "us": stage_ms["gateup"] * 1e3},
+        "down": {"tflops": (dn_flops + sd) / (stage_ms["down"] * 1e9),
+                 "flops": dn_flops + sd, "routed_flops": dn_flops, "shared_flops": sd,
+                 "us": stage_ms["down"] * 1e3},
     }
-    if shared:
-        sg, sd = LG.gateup_flops(T, d, cfg.d_e_shared), LG.down_flops(T, d, cfg.d_e_shared)
-        gemm["shared_gateup"] = {"tflops": sg / (stage_ms["shared_gateup"] * 1e9), "flops": sg,
-                                 "us": stage_ms["shared_gateup"] * 1e3}
-        gemm["shared_down"] = {"tflops": sd / (stage_ms["shared_down"] * 1e9), "flops": sd,
-                               "us": stage_ms["shared_down"] * 1e3}
     for v in gemm.values():
         v["frac"] = v["tflops"] / peak
     pb = LG.permute_bytes(T, k, d, eb)
@@ -234,8 +229,7 @@ def main():
         v["frac"] = v["gbps"] / PEAK_HBM_GBPS
 
     # the dominant kernel: the one with the largest share of the step
-    dom = max(("gateup", "down", "shared_gateup", "shared_down"),
-              key=lambda n: stage_ms.get(n, -1.0))
+    dom = max(("gateup", "down"), key=lambda n: stage_ms[n])
     # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
     # copy kernel), taken from the committed summary unless the kernel changed since
     tpath = args.traffic or os.path.join(ROOT, "profiles", f"{dom}_{cfg.name}_hbm_traffic.md")

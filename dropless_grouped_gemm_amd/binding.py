@@ -23,7 +23,7 @@ MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
 
 ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
-                "moe_grouped_gemm", "moe_combine", "moe_layer_fwd")
+                "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_combine", "moe_layer_fwd")
 
 
 class moe_shape(ctypes.Structure):
@@ -78,6 +78,9 @@ def lib():
         L.moe_permute.restype = ctypes.c_int32
         L.moe_grouped_gemm.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
         L.moe_grouped_gemm.restype = ctypes.c_int32
+        L.moe_grouped_gemm_shared.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P,
+                                              P, P, P, P, P]
+        L.moe_grouped_gemm_shared.restype = ctypes.c_int32
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
         L.moe_combine.restype = ctypes.c_int32
         L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -187,6 +190,14 @@ def moe_grouped_gemm(shape, op, A, B0, B1, block_meta, num_blocks, max_blocks, C
     _check("moe_grouped_gemm", lib().moe_grouped_gemm(
         ctypes.byref(shape), op, _p(A), _p(B0), _p(B1), _p(block_meta), _p(num_blocks),
         int(max_blocks), _p(C), _stream(stream)))
+
+
+def moe_grouped_gemm_shared(shape, op, A, B0, B1, block_meta, num_blocks, max_blocks, C,
+                            A_shared, B0_shared, B1_shared, C_shared, stream=None):
+    _check("moe_grouped_gemm_shared", lib().moe_grouped_gemm_shared(
+        ctypes.byref(shape), op, _p(A), _p(B0), _p(B1), _p(block_meta), _p(num_blocks),
+        int(max_blocks), _p(C), _p(A_shared), _p(B0_shared), _p(B1_shared), _p(C_shared),
+        _stream(stream)))
 
 
 def moe_combine(shape, y, pos, topk_w, shared_out, out, stream=None):

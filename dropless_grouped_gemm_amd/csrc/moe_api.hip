@@ -197,29 +197,62 @@ moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* pos, vo
   return launch_permute(*s, x, pos, x_perm, static_cast<hipStream_t>(stream));
 }
 
+// operand rules shared by the grouped-GEMM entry points
+static bool gemm_operands_ok(int32_t op, const void* A, const void* B0, const void* B1,
+                             const void* C) {
+  if (!A || !B0 || !C) return false;
+  if (op == MOE_OP_GATEUP_SWIGLU && !B1) return false;
+  if (op == MOE_OP_DOWN && B1) return false;
+  return aligned16(A) && aligned16(B0) && (!B1 || aligned16(B1)) && aligned16(C);
+}
+
+static bool block_table_ok(const moe_shape& s, const int32_t* block_meta,
+                           const int32_t* num_blocks, int32_t max_blocks) {
+  return block_meta && num_blocks && aligned4(block_meta) && aligned4(num_blocks) &&
+         max_blocks >= 1 && max_blocks <= max_blocks_of(s);
+}
+
 moe_status moe_grouped_gemm(const moe_shape* s, int32_t op, const void* A, const void* B0,
                             const void* B1, const int32_t* block_meta, const int32_t* num_blocks,
                             int32_t max_blocks, void* C, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
-  if (!A || !B0 || !C) return MOE_EINVAL;
-  if (op == MOE_OP_GATEUP_SWIGLU && !B1) return MOE_EINVAL;
-  if (op == MOE_OP_DOWN && B1) return MOE_EINVAL;
-  if (!aligned16(A) || !aligned16(B0) || (B1 && !aligned16(B1)) || !aligned16(C))
-    return MOE_EINVAL;
+  if (!gemm_operands_ok(op, A, B0, B1, C)) return MOE_EINVAL;
   const int K = op == MOE_OP_GATEUP_SWIGLU ? s->d : s->d_e;
   const int N = op == MOE_OP_GATEUP_SWIGLU ? s->d_e : s->d;
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  GemmSegments g{};
   if (!block_meta && !num_blocks) {  // dense mode: one expert over all T rows
     if (max_blocks != 0) return MOE_EINVAL;
     if (s->T == 0) return MOE_OK;
-    return launch_grouped_gemm(*s, op, A, B0, B1, K, N, nullptr, nullptr, 0, s->T, C, hs);
+    g.Ad = A; g.B0d = B0; g.B1d = B1; g.Cd = C; g.Kd = K; g.Nd = N; g.dense_rows = s->T;
+  } else {
+    if (!block_table_ok(*s, block_meta, num_blocks, max_blocks)) return MOE_EINVAL;
+    g.A = A; g.B0 = B0; g.B1 = B1; g.C = C; g.K = K; g.N = N;
+    g.block_meta = block_meta; g.num_blocks = num_blocks; g.max_blocks = max_blocks;
   }
-  if (!block_meta || !num_blocks || !aligned4(block_meta) || !aligned4(num_blocks))
+  return launch_grouped_gemm(*s, op, g, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_gemm_shared(const moe_shape* s, int32_t op, const void* A, const void* B0,
+                                   const void* B1, const int32_t* block_meta,
+                                   const int32_t* num_blocks, int32_t max_blocks, void* C,
+                                   const void* A_shared, const void* B0_shared,
+                                   const void* B1_shared, void* C_shared, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
+  if (s->d_e_shared <= 0) return MOE_EINVAL;
+  if (!gemm_operands_ok(op, A, B0, B1, C) ||
+      !gemm_operands_ok(op, A_shared, B0_shared, B1_shared, C_shared))
     return MOE_EINVAL;
-  if (max_blocks < 1 || max_blocks > max_blocks_of(*s)) return MOE_EINVAL;
-  return launch_grouped_gemm(*s, op, A, B0, B1, K, N, block_meta, num_blocks, max_blocks, 0, C, hs);
+  if (!block_table_ok(*s, block_meta, num_blocks, max_blocks)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  const bool gu = op == MOE_OP_GATEUP_SWIGLU;
+  GemmSegments g{A, B0, B1, C, gu ? s->d : s->d_e, gu ? s->d_e : s->d, block_meta, num_blocks,
+                 max_blocks, A_shared, B0_shared, B1_shared, C_shared,
+                 gu ? s->d : s->d_e_shared, gu ? s->d_e_shared : s->d, s->T};
+  return launch_grouped_gemm(*s, op, g, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos, const float* topk_w,
@@ -282,25 +315,20 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
   if (st != MOE_OK) return st;
   st = launch_permute(*s, x, pos, at(L.x_perm), hs);
   if (st != MOE_OK) return st;
+  // Routed experts and the shared expert go through the grouped GEMM together (one
+  // launch per op when their shapes agree), the shared expert as a dense segment
+  // over the unpermuted x.
   const int32_t mb = (int32_t)max_blocks_of(*s);
-  st = launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, at(L.x_perm), w1, w3, s->d, s->d_e, meta, nblk,
-                           mb, 0, at(L.act), hs);
+  const int des = s->d_e_shared;
+  GemmSegments gu{at(L.x_perm), w1, w3, at(L.act), s->d, s->d_e, meta, nblk, mb,
+                  x, ws1, ws3, at(L.shared_act), s->d, des, shared ? s->T : 0};
+  st = launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, gu, hs);
   if (st != MOE_OK) return st;
-  st = launch_grouped_gemm(*s, MOE_OP_DOWN, at(L.act), w2, nullptr, s->d_e, s->d, meta, nblk, mb, 0,
-                           at(L.y), hs);
+  GemmSegments dn{at(L.act), w2, nullptr, at(L.y), s->d_e, s->d, meta, nblk, mb,
+                  at(L.shared_act), ws2, nullptr, at(L.shared_out), des, s->d, shared ? s->T : 0};
+  st = launch_grouped_gemm(*s, MOE_OP_DOWN, dn, hs);
   if (st != MOE_OK) return st;
-  const void* sh = nullptr;
-  if (shared) {
-    moe_shape ss = *s;
-    ss.d_e = s->d_e_shared;
-    st = launch_grouped_gemm(ss, MOE_OP_GATEUP_SWIGLU, x, ws1, ws3, s->d, s->d_e_shared, nullptr,
-                             nullptr, 0, s->T, at(L.shared_act), hs);
-    if (st != MOE_OK) return st;
-    st = launch_grouped_gemm(ss, MOE_OP_DOWN, at(L.shared_act), ws2, nullptr, s->d_e_shared, s->d,
-                             nullptr, nullptr, 0, s->T, at(L.shared_out), hs);
-    if (st != MOE_OK) return st;
-    sh = at(L.shared_out);
-  }
+  const void* sh = shared ? at(L.shared_out) : nullptr;
   return launch_combine(*s, at(L.y), pos, wts, sh, out, hs);
 }
 

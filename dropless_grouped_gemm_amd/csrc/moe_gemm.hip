@@ -300,22 +300,31 @@ __device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff_b
 __device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 __device__ __forceinline__ int swz_b(int k, int chunk) { return chunk ^ (4 * (k & 3)); }
 
-template <int OP, bool DENSE>
+// Operands of one segment set: A rows, the B matrices (expert-strided) and C rows.
+struct GGOperands {
+  const bf16_t* A;
+  const bf16_t* B0;
+  const bf16_t* B1;
+  bf16_t* C;
+};
+
+// One launch covers two segment sets with the same K and N: a dense segment of
+// dense_rows rows through one expert (the shared expert; dense_rows == 0: none),
+// taken first, then the routed segments of the block table (max_blocks == 0: none).
+template <int OP>
 __global__ void __launch_bounds__(kV2Threads, 1)
-k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
-             const bf16_t* __restrict__ B1, bf16_t* __restrict__ C, int K, int N,
+k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
              const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
-             int max_blocks, int E, int64_t max_rows, int dense_rows_arg, int block_m,
+             int max_blocks, int E, int64_t max_rows, int dense_rows, int block_m,
              int n_tiles) {
   __shared__ __align__(1024) unsigned char lds[kV2Stages * kV2Stage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dense_rows = DENSE ? dense_rows_arg : 0;
   constexpr int kOutCols = OP == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
   const int tpb = block_m / kBM;
-  const int nblocks =
-      DENSE ? (dense_rows + block_m - 1) / block_m : min(num_blocks_ptr[0], max_blocks);
+  const int nb_dense = (dense_rows + block_m - 1) / block_m;
+  const int nblocks = nb_dense + (max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0);
   const int total = nblocks * tpb * n_tiles;
   const int nk = K / kV2BK;
 
@@ -355,11 +364,21 @@ k_gg_bf16_v2(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
       mt = w / n_tiles;
     }
     Tile tile;
-    if (!decode_block(mt / tpb, mt % tpb, kBM, block_m, meta, dense_rows, E, max_rows, tile)) continue;
+    const int blk = mt / tpb;
+    const bool in_dense = blk < nb_dense;
+    if (in_dense) {
+      if (!decode_block(blk, mt % tpb, kBM, block_m, nullptr, dense_rows, 1, dense_rows, tile))
+        continue;
+    } else {
+      if (!decode_block(blk - nb_dense, mt % tpb, kBM, block_m, meta, 0, E, max_rows, tile))
+        continue;
+    }
+    const GGOperands& ops = in_dense ? dense : routed;
+    bf16_t* const C = ops.C;
     const int n0 = nt * kOutCols;
-    const bf16_t* asrc = A + (size_t)tile.m0 * K;
-    const bf16_t* b0e = B0 + (size_t)tile.e * K * N;
-    const bf16_t* b1e = OP == MOE_OP_GATEUP_SWIGLU ? B1 + (size_t)tile.e * K * N : b0e;
+    const bf16_t* asrc = ops.A + (size_t)tile.m0 * K;
+    const bf16_t* b0e = ops.B0 + (size_t)tile.e * K * N;
+    const bf16_t* b1e = OP == MOE_OP_GATEUP_SWIGLU ? ops.B1 + (size_t)tile.e * K * N : b0e;
     // the two 256-column halves of the tile's B columns: matrix and first column
     const bf16_t* bh_base[2] = {b0e, OP == MOE_OP_GATEUP_SWIGLU ? b1e : b0e};
     const int bh_col0[2] = {n0, OP == MOE_OP_GATEUP_SWIGLU ? n0 : n0 + 256};
@@ -607,7 +626,8 @@ k_gg_f32(const float* __restrict__ A, const float* __restrict__ B0, const float*
   }
 }
 
-moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const void* B0,
+// One segment set on the register-staged or fp32 kernels (dense_rows > 0: dense mode).
+static moe_status launch_other(const moe_shape& s, int op, const void* A, const void* B0,
                                const void* B1, int K, int N, const int32_t* block_meta,
                                const int32_t* num_blocks, int32_t max_blocks, int32_t dense_rows,
                                void* C, hipStream_t st) {
@@ -618,31 +638,7 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const 
   const int64_t max_rows = dense_rows > 0 ? (int64_t)dense_rows : (int64_t)max_blocks * s.block_m;
   const int E = dense_rows > 0 ? 1 : s.E;
   const int cus = device_cu_count();
-  if (s.dtype == MOE_DTYPE_BF16 && K % kV2BK == 0) {
-    const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
-    const int n_tiles = (int)ceil_div(N, out_cols);
-    int64_t items = blocks_ub * (s.block_m / kBM) * n_tiles;
-    int64_t grid = items < cus ? items : cus;
-    if (grid < 1) grid = 1;
-    const bf16_t* a = static_cast<const bf16_t*>(A);
-    const bf16_t* b0 = static_cast<const bf16_t*>(B0);
-    const bf16_t* b1 = static_cast<const bf16_t*>(B1);
-    bf16_t* c = static_cast<bf16_t*>(C);
-    // The dense (shared-expert) launch is its own instantiation, so profiles list it
-    // apart from the routed one.
-#define MOE_V2_LAUNCH(OPV, DENSEV)                                                             \
-  hipLaunchKernelGGL((k_gg_bf16_v2<OPV, DENSEV>), dim3((unsigned)grid), dim3(kV2Threads), 0, st, a, \
-                     b0, b1, c, K, N, block_meta, num_blocks, max_blocks, E, max_rows, dense_rows, \
-                     s.block_m, n_tiles)
-    if (op == MOE_OP_GATEUP_SWIGLU) {
-      if (dense_rows > 0) MOE_V2_LAUNCH(MOE_OP_GATEUP_SWIGLU, true);
-      else MOE_V2_LAUNCH(MOE_OP_GATEUP_SWIGLU, false);
-    } else {
-      if (dense_rows > 0) MOE_V2_LAUNCH(MOE_OP_DOWN, true);
-      else MOE_V2_LAUNCH(MOE_OP_DOWN, false);
-    }
-#undef MOE_V2_LAUNCH
-  } else if (s.dtype == MOE_DTYPE_BF16) {
+  if (s.dtype == MOE_DTYPE_BF16) {
     const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 128 : 256;
     const int n_tiles = (int)ceil_div(N, out_cols);
     int64_t items = blocks_ub * (s.block_m / kBM) * n_tiles;
@@ -675,6 +671,64 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const 
                          max_rows, dense_rows, s.block_m, n_tiles);
   }
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g, hipStream_t st) {
+  const bool routed = g.max_blocks > 0;
+  const bool dense = g.dense_rows > 0;
+  if (!routed && !dense) return MOE_OK;
+  const int cus = device_cu_count();
+  const bool v2_routed = s.dtype == MOE_DTYPE_BF16 && g.K % kV2BK == 0;
+  const bool v2_dense = s.dtype == MOE_DTYPE_BF16 && g.Kd % kV2BK == 0;
+  // one launch when both sets fit the async-copy kernel with the same K and N
+  if ((!routed || v2_routed) && (!dense || v2_dense) && (!routed || !dense || (g.K == g.Kd && g.N == g.Nd))) {
+    const int K = routed ? g.K : g.Kd, N = routed ? g.N : g.Nd;
+    const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
+    const int n_tiles = (int)ceil_div(N, out_cols);
+    const int64_t blocks_ub = (routed ? (int64_t)g.max_blocks : 0) +
+                              (dense ? ceil_div(g.dense_rows, s.block_m) : 0);
+    int64_t items = blocks_ub * (s.block_m / kBM) * n_tiles;
+    int64_t grid = items < cus ? items : cus;
+    if (grid < 1) grid = 1;
+    const GGOperands ro{static_cast<const bf16_t*>(g.A), static_cast<const bf16_t*>(g.B0),
+                        static_cast<const bf16_t*>(g.B1), static_cast<bf16_t*>(g.C)};
+    const GGOperands dn{static_cast<const bf16_t*>(g.Ad), static_cast<const bf16_t*>(g.B0d),
+                        static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd)};
+    const int64_t max_rows = (int64_t)g.max_blocks * s.block_m;
+    if (op == MOE_OP_GATEUP_SWIGLU)
+      hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kV2Threads), 0,
+                         st, ro, dn, K, N, g.block_meta, g.num_blocks, g.max_blocks, s.E, max_rows,
+                         g.dense_rows, s.block_m, n_tiles);
+    else
+      hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_DOWN>, dim3((unsigned)grid), dim3(kV2Threads), 0, st,
+                         ro, dn, K, N, g.block_meta, g.num_blocks, g.max_blocks, s.E, max_rows,
+                         g.dense_rows, s.block_m, n_tiles);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  }
+  // otherwise each set on its own launch
+  moe_status st2 = MOE_OK;
+  if (dense) {
+    if (v2_dense) {
+      GemmSegments d = g;
+      d.max_blocks = 0;  // dense set alone: takes the single-launch path above
+      st2 = launch_grouped_gemm(s, op, d, st);
+    } else {
+      st2 = launch_other(s, op, g.Ad, g.B0d, g.B1d, g.Kd, g.Nd, nullptr, nullptr, 0, g.dense_rows,
+                         g.Cd, st);
+    }
+  }
+  if (st2 != MOE_OK) return st2;
+  if (routed) {
+    if (v2_routed) {
+      GemmSegments r = g;
+      r.dense_rows = 0;
+      st2 = launch_grouped_gemm(s, op, r, st);
+    } else {
+      st2 = launch_other(s, op, g.A, g.B0, g.B1, g.K, g.N, g.block_meta, g.num_blocks,
+                         g.max_blocks, 0, g.C, st);
+    }
+  }
+  return st2;
 }
 
 }  // namespace moe

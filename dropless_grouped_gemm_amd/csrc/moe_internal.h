@@ -71,12 +71,26 @@ moe_status launch_combine(const moe_shape& s, const void* y, const int32_t* pos,
                           const float* topk_w, const void* shared_out, void* out,
                           hipStream_t st);
 
-// Grouped GEMM.  dense_rows > 0 selects dense mode (the shared expert): rows
-// [0, dense_rows) form consecutive block_m blocks of expert 0 and block_meta /
-// num_blocks are ignored.
-moe_status launch_grouped_gemm(const moe_shape& s, int op, const void* A, const void* B0,
-                               const void* B1, int K, int N, const int32_t* block_meta,
-                               const int32_t* num_blocks, int32_t max_blocks,
-                               int32_t dense_rows, void* C, hipStream_t st);
+// Grouped GEMM over up to two segment sets with their own operands: the routed
+// segments of a block table (max_blocks == 0: none) and a dense segment of
+// dense_rows rows through a single expert (the shared expert; dense_rows == 0:
+// none).  bf16 sets with the same K and N (K % 32 == 0) share one launch.
+struct GemmSegments {
+  const void* A;
+  const void* B0;
+  const void* B1;
+  void* C;
+  int K, N;
+  const int32_t* block_meta;
+  const int32_t* num_blocks;
+  int32_t max_blocks;
+  const void* Ad;
+  const void* B0d;
+  const void* B1d;
+  void* Cd;
+  int Kd, Nd;
+  int32_t dense_rows;
+};
+moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g, hipStream_t st);
 
 }  // namespace moe

@@ -131,22 +131,31 @@ k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m,
   __shared__ int s_cnt[1025], s_pad[1025], s_boff[1025];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  // per expert: exclusive scan over chunks (chunk bases, in place) -> count
+  // Per column (expert, or E = out-of-range ids): exclusive scan over chunks (chunk
+  // bases, in place) -> total.  Loads go out 16 at a time so the walk down the
+  // chunks is not a chain of load latencies.
   int c = 0;
-  if (tid < E) {
+  for (int col = tid; col <= E; col += kScanThreads) {
     int run = 0;
-    for (int64_t ch = 0; ch < nchunks; ++ch) {
-      const int v = hist[ch * (E + 1) + tid];
-      hist[ch * (E + 1) + tid] = run;
-      run += v;
+    for (int64_t ch0 = 0; ch0 < nchunks; ch0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = ch0 + u < nchunks ? hist[(ch0 + u) * (E + 1) + col] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (ch0 + u < nchunks) {
+          if (col < E) hist[(ch0 + u) * (E + 1) + col] = run;
+          run += v[u];
+        }
+      }
     }
-    c = run;
-    counts[tid] = c;
-  }
-  if (tid == 0) {
-    int bad = 0;
-    for (int64_t ch = 0; ch < nchunks; ++ch) bad += hist[ch * (E + 1) + E];
-    s_bad = bad;
+    if (col < E) {
+      c = run;
+      counts[col] = c;
+    } else {
+      s_bad = run;
+    }
   }
   const int nb = (c + block_m - 1) / block_m;
   const int inc_c = block_inclusive_scan(c, sh_wave);

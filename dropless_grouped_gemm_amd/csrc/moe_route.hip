@@ -6,12 +6,16 @@
 // remaining logit" over the eligible experts (same section; group-limited routing
 // from section 2.2 and the dropless notes, section 4 step 4).
 //
-// bf16 path: each wave owns 16 tokens and computes a 16 x E tile with
+// bf16 path: each wave owns 16 tokens and computes a 16 x (16*NTB) tile with
 // v_mfma_f32_16x16x32_bf16.  x streams from HBM straight into the A operand (its rows
-// are K-contiguous, so no LDS round trip); the block stages W_g^T for its K slice in
-// LDS, shared by the 4 waves.  K is split over blockIdx.y so small-T shapes (decode)
-// still spread over the chip; each split writes fp32 partial logits and the
-// selection kernel adds them in split order, so the result is deterministic.
+// are K-contiguous, so no LDS round trip; each load instruction covers 64 contiguous
+// bytes of 16 rows and a lane keeps 8 loads in flight).  The block stages its slice
+// of W_g in LDS in W_g's own [k][e] layout with 16-byte copies, and the B operand
+// (8 consecutive k of one expert per lane) comes out of it with the gfx950 LDS
+// transpose read ds_read_b64_tr_b16.  K is split over blockIdx.y and experts over
+// blockIdx.z so that small-T shapes (decode) still spread over the chip; each K
+// split writes fp32 partial logits and the selection kernel adds them in split
+// order, so the result is deterministic.
 #include "moe_internal.h"
 
 #include <float.h>
@@ -20,34 +24,41 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 static constexpr int kRouteThreads = 256;   // 4 waves
 static constexpr int kRouteTok = 64;        // tokens per block (16 per wave)
-static constexpr int kRouteLdsElems = 32768;  // W_g^T chunk: 64 KB of bf16
+static constexpr int kRoutePair = 256;      // K per loop step: two 128-deep windows
+static constexpr int kRouteMaxSplit = 8;
 
-// Expert tiles (of 16) per block: enough to cover E up to 256 in one block.
-static inline int route_ntb(int E) {
-  int nt = (E + 15) / 16;
+// Staged W_g rows per chunk and their pitch (16 bytes of pad) per expert-tile count;
+// every chunk but a split's last holds an even number of steps.
+template <int NTB>
+struct RouteTile {
+  static constexpr int kPitch = 32 * NTB + 16;
+  static constexpr int kKC = NTB == 1 ? 1024 : 512;
+  static constexpr int kLds = kKC * kPitch;   // 48 KB, 40 KB, 72 KB
+};
+
+// Expert tiles (of 16) per block.  With many token blocks one block covers up to 64
+// experts, so x is read once for E <= 64; with few (decode) each block takes one
+// tile of 16 experts, and the expert tiles supply the parallelism.
+static inline int route_ntb(const moe_shape& s) {
+  const int nt = (s.E + 15) / 16;
+  if (ceil_div(s.T, kRouteTok) < 64) return 1;
   int b = 1;
-  while (b < nt && b < 16) b *= 2;
+  while (b < nt && b < 4) b *= 2;
   return b;
-}
-
-static inline int route_kc(int ntb) {
-  // K chunk staged in LDS: 16*ntb * (KC + 8) bf16 <= 32768 elements, KC % 32 == 0.
-  int kc = (kRouteLdsElems / (16 * ntb) - 8) / 32 * 32;
-  if (kc > 2048) kc = 2048;
-  if (kc < 32) kc = 32;
-  return kc;
 }
 
 int router_nsplit(const moe_shape& s) {
   if (s.dtype != MOE_DTYPE_BF16) return 1;
-  int64_t tok_blocks = ceil_div(s.T, kRouteTok);
-  int64_t ksteps = ceil_div(s.d, 32);
-  int64_t want = ceil_div(2 * 256, tok_blocks > 0 ? tok_blocks : 1);  // ~2 blocks per CU
-  if (want > ksteps) want = ksteps;
-  if (want > 64) want = 64;
+  const int ntb = route_ntb(s);
+  const int64_t blocks = ceil_div(s.T, kRouteTok) * ceil_div(s.E, 16 * ntb);
+  const int64_t pairs = ceil_div(s.d, kRoutePair);
+  int64_t want = ceil_div(4 * 256, blocks > 0 ? blocks : 1);  // ~4 blocks per CU
+  if (want > pairs) want = pairs;
+  if (want > kRouteMaxSplit) want = kRouteMaxSplit;
   if (want < 1) want = 1;
   return (int)want;
 }
@@ -61,60 +72,122 @@ size_t router_partial_bytes(const moe_shape& s) {
 // Block (x, y, z) covers tokens [64x, 64x + 64), K slice y, experts
 // [16*NTB*z, 16*NTB*(z+1)).
 // ---------------------------------------------------------------------------
+#define MOE_LDS __attribute__((address_space(3)))
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
 template <int NTB>
 __global__ void __launch_bounds__(kRouteThreads)
 k_router_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, int T, int d, int E,
-              int k_per_split, int kc, float* __restrict__ partial) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* wsT = reinterpret_cast<bf16_t*>(smem_raw);  // [16*NTB][kc + 8]
+              int k_per_split, float* __restrict__ partial) {
   constexpr int EB = 16 * NTB;
-  const int ldw = kc + 8;
+  constexpr int EV = EB / 8;               // 16-byte pieces per staged k row
+  constexpr int kPitch = RouteTile<NTB>::kPitch;
+  constexpr int kc = RouteTile<NTB>::kKC;
+  __shared__ __align__(16) unsigned char smem_raw[RouteTile<NTB>::kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int g = lane >> 4;                 // k group of the MFMA operands
   const int t0 = blockIdx.x * kRouteTok + wave * 16;
   const int e0 = blockIdx.z * EB;
   const int kbeg = blockIdx.y * k_per_split;
   const int kend = min(d, kbeg + k_per_split);
 
-  // A operand: row t0 + lane%16, 8 k values at (lane/16)*8 within each 32-wide step.
+  // A operand: row t0 + lane%16, k values g*8 .. g*8+7 of each 32-deep step.  The
+  // loads are unconditional, from a clamped row and column: rows past T produce
+  // results that are never stored, and k positions past the split meet staged W_g
+  // rows that are zero (or a window whose MFMAs are skipped), so no load needs a
+  // branch and the compiler can keep two steps of loads in flight.
   const int arow = t0 + (lane & 15);
-  const int akoff = (lane >> 4) * 8;
-  const bool arow_ok = arow < T;
-  const bf16_t* xrow = x + (size_t)(arow_ok ? arow : 0) * d;
+  const bf16_t* xrow = x + (size_t)min(arow, T - 1) * d;
+  // B operand by transpose read: in each 16-lane group, lane 4r+c addresses k row r
+  // of a 4-row block, experts 4c..4c+3; lane i receives expert i's 4 k values.
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+  const unsigned char* bl = smem_raw + (g * 8 + tr_r) * kPitch + tr_c * 8;
 
   f32x4_t acc[NTB];
 #pragma unroll
   for (int i = 0; i < NTB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc0 = kbeg; kc0 < kend; kc0 += kc) {
+  auto b_operand = [&](int krow, int nt) {
+    i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MOE_LDS i16x4_t*)(bl + krow * kPitch + nt * 32));
+    i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (MOE_LDS i16x4_t*)(bl + (krow + 4) * kPitch + nt * 32));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto load_step = [&](bf16x8_t* a, int kp) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      a[q] = *reinterpret_cast<const bf16x8_t*>(xrow + min(kp + q * 32 + g * 8, d - 8));
+  };
+  // Stage W_g[kc0 .. kc0+kpad)[e0 .. e0+EB) as rows of EB experts, zeros past the
+  // split (kpad = klen rounded up to 128); loads batched, 8 per thread in flight.
+  auto stage = [&](int kc0) {
     const int klen = min(kc, kend - kc0);
-    const int kpad = (klen + 31) / 32 * 32;
+    const int kpad = (klen + 127) / 128 * 128;
     __syncthreads();
-    // Stage W_g[kc0 .. kc0+klen)[e0 .. e0+EB) transposed into wsT[e][k]; zeros outside.
-    for (int i = tid; i < kpad * EB; i += kRouteThreads) {
-      const int e = i % EB;
-      const int kk = i / EB;
-      bf16_t v = 0;
-      if (e0 + e < E && kk < klen) v = wg[(size_t)(kc0 + kk) * E + e0 + e];
-      wsT[e * ldw + kk] = v;
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int ks = 0; ks < kpad; ks += 32) {
-      const int kg = kc0 + ks + akoff;
-      bf16x8_t a;
-      if (arow_ok && kg < kend) {
-        a = *reinterpret_cast<const bf16x8_t*>(xrow + kg);
-      } else {
-        a = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    const int total = kpad * EV;
+    for (int base = 0; base < total; base += kRouteThreads * 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kRouteThreads + tid;
+        const int kk = i / EV, ev = i % EV;
+        v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (i < total && kk < klen) {
+          const bf16_t* src = wg + (size_t)(kc0 + kk) * E + e0 + ev * 8;
+          if ((E & 7) == 0) {
+            if (e0 + ev * 8 < E) v[u] = *reinterpret_cast<const u32x4_t*>(src);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (e0 + ev * 8 + q < E) v[u][q >> 1] |= (uint32_t)src[q] << (16 * (q & 1));
+          }
+        }
       }
 #pragma unroll
-      for (int nt = 0; nt < NTB; ++nt) {
-        const bf16x8_t b =
-            *reinterpret_cast<const bf16x8_t*>(wsT + (nt * 16 + (lane & 15)) * ldw + ks + akoff);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nt], 0, 0, 0);
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kRouteThreads + tid;
+        if (i < total)
+          *reinterpret_cast<u32x4_t*>(smem_raw + (i / EV) * kPitch + (i % EV) * 16) = v[u];
       }
+    }
+    __syncthreads();
+  };
+  // one step: window rows [w, w+128) and, when `two`, [w+128, w+256) of the chunk
+  auto compute = [&](const bf16x8_t* a, int w, bool two) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int nt = 0; nt < NTB; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b_operand(w + q * 32, nt),
+                                                           acc[nt], 0, 0, 0);
+    if (two) {
+#pragma unroll
+      for (int q = 4; q < 8; ++q)
+#pragma unroll
+        for (int nt = 0; nt < NTB; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], b_operand(w + q * 32, nt),
+                                                             acc[nt], 0, 0, 0);
+    }
+  };
+
+  // Chunks of kc staged rows; within a chunk, steps of 256 alternate two register
+  // sets: a step computes from one set while the loads of the next fill the other.
+  // Loads are unconditional (clamped), so the waits stay exact; the last load of a
+  // chunk fetches the first step of the next one, which overlaps its staging.
+  bf16x8_t a0[8], a1[8];
+  load_step(a0, kbeg);
+  for (int kc0 = kbeg; kc0 < kend; kc0 += kc) {
+    stage(kc0);
+    const int nst = (min(kc, kend - kc0) + kRoutePair - 1) / kRoutePair;
+    for (int i = 0; i < nst; i += 2) {
+      load_step(a1, kc0 + (i + 1) * kRoutePair);
+      compute(a0, i * kRoutePair, kc0 + i * kRoutePair + 128 < kend);
+      load_step(a0, kc0 + (i + 2) * kRoutePair);
+      if (i + 1 < nst)
+        compute(a1, (i + 1) * kRoutePair, kc0 + (i + 1) * kRoutePair + 128 < kend);
     }
   }
   // 16x16 output layout: lane holds column lane%16, rows (lane/16)*4 + i.
@@ -144,155 +217,174 @@ __global__ void k_router_f32(const float* __restrict__ x, const float* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Selection: one wave per token.
+// Selection: G lanes per token (G = 8 .. 64, a power of two >= min(E, 64)), so a
+// wave serves 64/G tokens, and each lane holds PER experts lt + G*r.  A candidate is
+// one 64-bit key: the logit's bits mapped to an unsigned order (high word) and the
+// complement of the expert id (low word), so the largest key is the largest logit
+// and, among equal logits, the lowest id.  Each of the k rounds is one butterfly
+// max over xor offsets < G, which stays inside a token's lane group.
 // ---------------------------------------------------------------------------
-struct Cand {
-  float v;
-  int e;
-  int ok;  // 1 = a real candidate
-};
-
-__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-  if (a.ok != b.ok) return a.ok > b.ok;
-  if (a.v != b.v) return a.v > b.v;
-  return a.e < b.e;
+__device__ __forceinline__ uint64_t sel_key(float v, int id) {
+  uint32_t u = __float_as_uint(v == 0.f ? 0.f : v);  // -0 and +0 compare equal
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)id);
 }
 
-__device__ __forceinline__ Cand wave_best(Cand c) {
+__device__ __forceinline__ int sel_id(uint64_t key) {
+  return (int)(0xffffffffu - (uint32_t)key);
+}
+
+template <int G>
+__device__ __forceinline__ uint64_t group_max_key(uint64_t k) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    Cand o;
-    o.v = __shfl_xor(c.v, off, 64);
-    o.e = __shfl_xor(c.e, off, 64);
-    o.ok = __shfl_xor(c.ok, off, 64);
-    if (better(o, c)) c = o;
+  for (int off = G / 2; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)k, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off, 64);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    k = o > k ? o : k;
   }
-  return c;
+  return k;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  for (int off = G / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-static constexpr int kSelMaxPerLane = 16;   // E <= 1024
-static constexpr int kSelWaves = 4;
+static constexpr int kSelThreads = 256;
+static constexpr int kSelLds = 4096;        // floats: (256 / G) tokens x E logits
 
-__global__ void __launch_bounds__(64 * kSelWaves)
+static inline int select_lanes(int E) {
+  int g = 8;
+  while (g < E && g < 64) g *= 2;
+  return g;
+}
+
+template <int G, int PER>
+__global__ void __launch_bounds__(kSelThreads)
 k_select(const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, int T, int E,
          int k, int n_groups, int topk_groups, int renormalize, float* __restrict__ logits_out,
          int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  __shared__ float gl[kSelWaves][1024];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * kSelWaves + wave;
-  if (t >= T) return;  // wave-uniform
-  const int per = (E + 63) / 64;
+  __shared__ float gl[kSelLds];
+  constexpr int kTokPerBlock = kSelThreads / G;
+  const int lt = threadIdx.x % G;          // lane within the token's group
+  const int slot = threadIdx.x / G;        // token within the block
+  const int base_lane = (threadIdx.x & 63) - lt;
+  const int tok = blockIdx.x * kTokPerBlock + slot;
+  // Groups past T compute on the last token (so every lane of a wave takes part in
+  // the butterflies) and write nothing.
+  const bool live = tok < T;
+  const int t = live ? tok : T - 1;
 
-  float l[kSelMaxPerLane];
+  bool has[PER];
+  float l[PER];
 #pragma unroll
-  for (int r = 0; r < kSelMaxPerLane; ++r) {
-    const int e = lane + 64 * r;
-    float v = -FLT_MAX;
-    if (r < per && e < E) {
-      float acc = 0.f;
-      for (int sidx = 0; sidx < nsplit; ++sidx) acc += partial[((size_t)sidx * T + t) * E + e];
-      if (bias) acc += bias[e];
-      v = acc;
-      if (logits_out) logits_out[(size_t)t * E + e] = v;
-    }
-    l[r] = v;
+  for (int r = 0; r < PER; ++r) {
+    const int e = lt + G * r;
+    has[r] = e < E;
+    float pv[kRouteMaxSplit];
+#pragma unroll
+    for (int sidx = 0; sidx < kRouteMaxSplit; ++sidx)
+      pv[sidx] = (has[r] && sidx < nsplit) ? partial[((size_t)sidx * T + t) * E + e] : 0.f;
+    float acc = pv[0];
+#pragma unroll
+    for (int sidx = 1; sidx < kRouteMaxSplit; ++sidx)
+      if (sidx < nsplit) acc += pv[sidx];
+    if (bias && has[r]) acc += bias[e];
+    l[r] = has[r] ? acc : -FLT_MAX;
+    if (logits_out && live && has[r]) logits_out[(size_t)t * E + e] = acc;
   }
   // softmax over all E in fp32 (max-subtracted)
   float m = -FLT_MAX;
 #pragma unroll
-  for (int r = 0; r < kSelMaxPerLane; ++r)
-    if (r < per && lane + 64 * r < E) m = fmaxf(m, l[r]);
-  m = wave_max(m);
-  float z[kSelMaxPerLane];
+  for (int r = 0; r < PER; ++r)
+    if (has[r]) m = fmaxf(m, l[r]);
+  m = group_max<G>(m);
+  float z[PER];
   float zs = 0.f;
 #pragma unroll
-  for (int r = 0; r < kSelMaxPerLane; ++r) {
-    z[r] = 0.f;
-    if (r < per && lane + 64 * r < E) {
-      z[r] = expf(l[r] - m);
-      zs += z[r];
-    }
+  for (int r = 0; r < PER; ++r) {
+    z[r] = has[r] ? expf(l[r] - m) : 0.f;
+    zs += z[r];
   }
-  const float S = wave_sum(zs);
+  const float S = group_sum<G>(zs);
 
-  // eligibility (group-limited routing)
-  unsigned elig = 0;  // bit r: expert lane + 64r eligible
+  // eligibility (group-limited routing; n_groups <= min(E, 64) <= G)
+  bool elig[PER];
 #pragma unroll
-  for (int r = 0; r < kSelMaxPerLane; ++r)
-    if (r < per && lane + 64 * r < E) elig |= 1u << r;
+  for (int r = 0; r < PER; ++r) elig[r] = has[r];
   if (n_groups > 0) {
     const int gs = E / n_groups;
+    float* tl = gl + slot * E;
 #pragma unroll
-    for (int r = 0; r < kSelMaxPerLane; ++r)
-      if (r < per && lane + 64 * r < E) gl[wave][lane + 64 * r] = l[r];
+    for (int r = 0; r < PER; ++r)
+      if (has[r]) tl[lt + G * r] = l[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    Cand g{-FLT_MAX, 0x7fffffff, 0};
-    if (lane < n_groups) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint64_t gkey = 0;
+    if (lt < n_groups) {
       float gm = -FLT_MAX;
-      for (int e = lane * gs; e < (lane + 1) * gs; ++e) gm = fmaxf(gm, gl[wave][e]);
-      g = Cand{gm, lane, 1};
+      for (int e = lt * gs; e < (lt + 1) * gs; ++e) gm = fmaxf(gm, tl[e]);
+      gkey = sel_key(gm, lt);
     }
     uint64_t keep = 0;
     for (int r = 0; r < topk_groups; ++r) {
-      const Cand b = wave_best(g);
-      keep |= 1ull << b.e;
-      if (lane == b.e) g.ok = 0;
+      const uint64_t b = group_max_key<G>(gkey);
+      const int gid = sel_id(b);
+      keep |= 1ull << gid;
+      if (lt == gid) gkey = 0;
     }
-    unsigned el = 0;
 #pragma unroll
-    for (int r = 0; r < kSelMaxPerLane; ++r) {
-      const int e = lane + 64 * r;
-      if (r < per && e < E && ((keep >> (e / gs)) & 1ull)) el |= 1u << r;
-    }
-    elig = el;
+    for (int r = 0; r < PER; ++r) elig[r] = has[r] && ((keep >> ((lt + G * r) / gs)) & 1ull);
   }
 
   // k rounds of "largest remaining eligible logit", ties to the lower id
-  int my_idx[kSelMaxPerLane];
-  float my_w[kSelMaxPerLane];
+  uint64_t key[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) key[r] = elig[r] ? sel_key(l[r], lt + G * r) : 0ull;
+  int my_idx[PER];
+  float my_w[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) { my_idx[r] = 0; my_w[r] = 0.f; }
   float wsum = 0.f;
   for (int j = 0; j < k; ++j) {
-    Cand c{-FLT_MAX, 0x7fffffff, 0};
+    uint64_t c = key[0];
 #pragma unroll
-    for (int r = 0; r < kSelMaxPerLane; ++r) {
-      if ((elig >> r) & 1u) {
-        Cand o{l[r], lane + 64 * r, 1};
-        if (better(o, c)) c = o;
+    for (int r = 1; r < PER; ++r) c = key[r] > c ? key[r] : c;
+    const uint64_t b = group_max_key<G>(c);
+    const int e = sel_id(b);
+    const int owner = e % G, rr = e / G;
+    float zo = 0.f;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      if (r == rr) {
+        zo = z[r];
+        if (lt == owner) key[r] = 0ull;
       }
     }
-    const Cand b = wave_best(c);
-    const int owner = b.e & 63, rr = b.e >> 6;
-    float p = 0.f;
-#pragma unroll
-    for (int r = 0; r < kSelMaxPerLane; ++r)
-      if (r == rr) p = z[r];
-    p = __shfl(p, owner, 64) / S;
-    if (lane == owner) elig &= ~(1u << rr);
+    const float p = __shfl(zo, base_lane + owner, 64) / S;
     wsum += p;
-    if (lane == (j & 63)) {
+    if (lt == j % G) {
 #pragma unroll
-      for (int q = 0; q < kSelMaxPerLane; ++q)
-        if (q == (j >> 6)) { my_idx[q] = b.e; my_w[q] = p; }
+      for (int q = 0; q < PER; ++q)
+        if (q == j / G) { my_idx[q] = e; my_w[q] = p; }
     }
   }
-  const float scale = renormalize ? 1.0f / wsum : 1.0f;
+  if (!live) return;
+  const float scale = 1.0f / wsum;
 #pragma unroll
-  for (int q = 0; q < kSelMaxPerLane; ++q) {
-    const int j = lane + 64 * q;
+  for (int q = 0; q < PER; ++q) {
+    const int j = lt + G * q;
     if (j < k) {
       topk_idx[(size_t)t * k + j] = my_idx[q];
       topk_w[(size_t)t * k + j] = renormalize ? my_w[q] * scale : my_w[q];
@@ -305,22 +397,22 @@ moe_status launch_route(const moe_shape& s, const void* x, const void* w_gate, c
                         hipStream_t st) {
   const int nsplit = router_nsplit(s);
   if (s.dtype == MOE_DTYPE_BF16) {
-    const int ntb = route_ntb(s.E);
-    const int kc = route_kc(ntb);
-    int64_t ksteps = ceil_div(s.d, 32);
-    int k_per_split = (int)(ceil_div(ksteps, nsplit) * 32);
+    const int ntb = route_ntb(s);
+    const int64_t pairs = ceil_div(s.d, kRoutePair);
+    const int k_per_split = (int)(ceil_div(pairs, nsplit) * kRoutePair);
     dim3 grid((unsigned)ceil_div(s.T, kRouteTok), (unsigned)nsplit,
               (unsigned)ceil_div(s.E, 16 * ntb));
-    size_t lds = (size_t)16 * ntb * (kc + 8) * sizeof(bf16_t);
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w_gate);
+#define MOE_ROUTER_LAUNCH(NTBV)                                                               \
+  hipLaunchKernelGGL(k_router_bf16<NTBV>, grid, dim3(kRouteThreads), 0, st, xb, wb, s.T, s.d, \
+                     s.E, k_per_split, partial)
     switch (ntb) {
-      case 1: hipLaunchKernelGGL(k_router_bf16<1>, grid, dim3(kRouteThreads), lds, st, xb, wb, s.T, s.d, s.E, k_per_split, kc, partial); break;
-      case 2: hipLaunchKernelGGL(k_router_bf16<2>, grid, dim3(kRouteThreads), lds, st, xb, wb, s.T, s.d, s.E, k_per_split, kc, partial); break;
-      case 4: hipLaunchKernelGGL(k_router_bf16<4>, grid, dim3(kRouteThreads), lds, st, xb, wb, s.T, s.d, s.E, k_per_split, kc, partial); break;
-      case 8: hipLaunchKernelGGL(k_router_bf16<8>, grid, dim3(kRouteThreads), lds, st, xb, wb, s.T, s.d, s.E, k_per_split, kc, partial); break;
-      default: hipLaunchKernelGGL(k_router_bf16<16>, grid, dim3(kRouteThreads), lds, st, xb, wb, s.T, s.d, s.E, k_per_split, kc, partial); break;
+      case 1: MOE_ROUTER_LAUNCH(1); break;
+      case 2: MOE_ROUTER_LAUNCH(2); break;
+      default: MOE_ROUTER_LAUNCH(4); break;
     }
+#undef MOE_ROUTER_LAUNCH
   } else {
     int64_t n = (int64_t)s.T * s.E;
     hipLaunchKernelGGL(k_router_f32, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st,
@@ -328,9 +420,23 @@ moe_status launch_route(const moe_shape& s, const void* x, const void* w_gate, c
                        s.E, partial);
   }
   if (hipGetLastError() != hipSuccess) return MOE_EHIP;
-  hipLaunchKernelGGL(k_select, dim3((unsigned)ceil_div(s.T, kSelWaves)), dim3(64 * kSelWaves), 0, st,
-                     partial, nsplit, bias, s.T, s.E, s.k, s.n_groups, s.topk_groups, s.renormalize,
-                     logits, topk_idx, topk_w);
+  const int G = select_lanes(s.E);
+  int per = 1;
+  while (per * G < s.E) per *= 2;
+  const dim3 sgrid((unsigned)ceil_div(s.T, kSelThreads / G));
+#define MOE_SELECT_LAUNCH(GV, PV)                                                              \
+  hipLaunchKernelGGL((k_select<GV, PV>), sgrid, dim3(kSelThreads), 0, st, partial, nsplit, bias, \
+                     s.T, s.E, s.k, s.n_groups, s.topk_groups, s.renormalize, logits, topk_idx, \
+                     topk_w)
+  if (G == 8) MOE_SELECT_LAUNCH(8, 1);
+  else if (G == 16) MOE_SELECT_LAUNCH(16, 1);
+  else if (G == 32) MOE_SELECT_LAUNCH(32, 1);
+  else if (per == 1) MOE_SELECT_LAUNCH(64, 1);
+  else if (per == 2) MOE_SELECT_LAUNCH(64, 2);
+  else if (per == 4) MOE_SELECT_LAUNCH(64, 4);
+  else if (per == 8) MOE_SELECT_LAUNCH(64, 8);
+  else MOE_SELECT_LAUNCH(64, 16);
+#undef MOE_SELECT_LAUNCH
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -180,6 +180,29 @@ moe_status moe_grouped_gemm(const moe_shape* s, int32_t op, const void* A,
                             int32_t max_blocks, void* C, void* stream);
 
 /*
+ * The grouped GEMM of the routed experts and the shared expert in one call
+ * (dropless notes section 1: the shared expert is a dense MLP on every token, next
+ * to the routed ones).  The routed half is exactly moe_grouped_gemm with a block
+ * table; the shared half is its dense mode over the T unpermuted rows:
+ *   op = MOE_OP_GATEUP_SWIGLU: A_shared = x [T, d], B0_shared = Ws1 [d, d_e_shared],
+ *        B1_shared = Ws3 [d, d_e_shared]; C_shared = [T, d_e_shared].
+ *   op = MOE_OP_DOWN: A_shared = [T, d_e_shared], B0_shared = Ws2 [d_e_shared, d],
+ *        B1_shared = NULL; C_shared = [T, d].
+ * When d_e_shared == d_e both halves run in one launch, so a small T (decode) does
+ * not leave the shared expert's few row blocks alone on the chip; otherwise they
+ * run back to back.  Requires s->d_e_shared > 0.  This is the call moe_layer_fwd
+ * makes for each op.
+ * Errors: MOE_EINVAL for a bad op, d_e_shared == 0, NULL or misaligned operands, or
+ * a block table as moe_grouped_gemm rejects it; nothing is launched then.
+ */
+moe_status moe_grouped_gemm_shared(const moe_shape* s, int32_t op, const void* A,
+                                   const void* B0, const void* B1,
+                                   const int32_t* block_meta, const int32_t* num_blocks,
+                                   int32_t max_blocks, void* C, const void* A_shared,
+                                   const void* B0_shared, const void* B1_shared,
+                                   void* C_shared, void* stream);
+
+/*
  * Combine (TileLang chapter section 2.5; dropless notes section 4 steps 10-11):
  *   out[t, :] = sum_{j = 0..k-1, in this order} topk_w[t, j] * y[pos[t*k + j], :]
  *               (+ shared_out[t, :])
@@ -193,8 +216,8 @@ moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos,
 
 /*
  * The whole layer: route -> build offsets -> permute -> grouped GEMM (gate/up with
- * SiLU*mul) -> grouped GEMM (down) -> [shared expert on the unpermuted x] ->
- * combine.  The shared expert is a dense SwiGLU MLP on every token, added
+ * SiLU*mul, with the shared expert's gate/up on the unpermuted x when there is one)
+ * -> grouped GEMM (down, likewise) -> combine.  The shared expert is a dense SwiGLU MLP on every token, added
  * unweighted (dropless notes section 1).
  * In:  x [T, d]; w_gate [d, E] and bias [E] fp32 (or NULL) when routing;
  *      w1, w3 [E, d, d_e], w2 [E, d_e, d];

@@ -96,6 +96,8 @@ def test_invalid_shapes_rejected_by_every_entry_point(kw, status):
     assert L.moe_build_offsets(ps, *([FAKE] * 9), FAKE, 1 << 40, None) == status
     assert L.moe_permute(ps, FAKE, FAKE, FAKE, None) == status
     assert L.moe_grouped_gemm(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == status
+    assert L.moe_grouped_gemm_shared(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, None) == status
     assert L.moe_combine(ps, FAKE, FAKE, FAKE, None, FAKE, None) == status
     assert L.moe_layer_fwd(ps, *([FAKE] * 6), None, None, None, None, None, FAKE, FAKE,
                            1 << 40, None) == status
@@ -135,6 +137,35 @@ def test_null_and_misaligned_pointers_rejected():
     s2 = good_shape(d_e_shared=256)
     assert L.moe_layer_fwd(ctypes.byref(s2), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None,
                            None, None, FAKE, FAKE, 1 << 40, None) == B.MOE_EINVAL
+
+
+def test_grouped_gemm_shared_argument_rules():
+    L = B.lib()
+    s = good_shape(d_e_shared=256)
+    ps = ctypes.byref(s)
+    mb = L.moe_max_blocks(ps)
+    g = L.moe_grouped_gemm_shared
+    odd = ctypes.c_void_p(0x10008)
+    # needs a shared expert in the shape
+    s0 = good_shape()
+    assert g(ctypes.byref(s0), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+             None) == B.MOE_EINVAL
+    # op rules apply to both halves
+    assert g(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_EINVAL
+    assert g(ps, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_EINVAL
+    assert g(ps, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, odd, FAKE, None, FAKE, None) == B.MOE_EINVAL
+    assert g(ps, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, None, None) == B.MOE_EINVAL
+    assert g(ps, 2, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_EINVAL
+    # the routed half needs its block table
+    assert g(ps, 1, FAKE, FAKE, None, None, None, 0, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_EINVAL
+    assert g(ps, 1, FAKE, FAKE, None, FAKE, FAKE, mb + 1, FAKE, FAKE, FAKE, None, FAKE,
+             None) == B.MOE_EINVAL
+    assert g(ps, 1, FAKE, FAKE, None, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, FAKE, None) == B.MOE_EINVAL
+    # T == 0: validated, nothing launched
+    sT = good_shape(T=0, d_e_shared=256)
+    assert g(ctypes.byref(sT), 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE,
+             None) == B.MOE_EINVAL      # max_blocks must be <= moe_max_blocks = 0
+    assert L.moe_max_blocks(ctypes.byref(sT)) == 0
 
 
 def test_workspace_too_small_rejected_before_launch():

@@ -119,6 +119,11 @@ def test_offsets_out_of_range_ids_set_the_flag():
     (33, 520, 64, 6, 0, 0, True, "bf16"),
     (16, 256, 1024, 8, 16, 2, True, "bf16"),
     (50, 128, 8, 2, 0, 0, True, "fp32"),
+    (100, 384, 4, 3, 0, 0, False, "bf16"),       # 8 lanes per token, 4 idle
+    (130, 256, 16, 4, 4, 2, True, "bf16"),       # 16 lanes per token, group limit
+    (77, 640, 20, 5, 0, 0, False, "bf16"),       # 32 lanes per token
+    (4500, 256, 96, 6, 0, 0, False, "bf16"),     # many token blocks: all experts per block
+    (4100, 264, 8, 2, 0, 0, True, "bf16"),       # many token blocks, K tail in a window
 ])
 def test_route_standalone(T, d, E, k, ng, tg, renorm, dtype):
     g = torch.Generator(device=DEV)
@@ -183,6 +188,9 @@ def test_route_exact_ties_go_to_the_lower_id():
     (96, 264, 6, 3, 136, 128, "bf16", "one-row-per-block"),
     (512, 256, 4, 1, 128, 128, "bf16", "full-blocks"),
     (70, 64, 5, 2, 48, 16, "fp32", "random"),
+    (40, 256, 4, 70, 128, 128, "bf16", "random"),      # k > 64: slots handed out in two rounds
+    (3, 128, 2, 5, 64, 128, "bf16", "random"),         # k not a multiple of the slot batch
+    (9, 8200, 3, 2, 64, 128, "bf16", "random"),        # row of 1025 vectors: partial chunks
 ])
 def test_stage_entry_points(T, d, E, k, d_e, bm, dtype, mode):
     rng = np.random.default_rng(T + d)
@@ -270,6 +278,60 @@ def test_grouped_gemm_dense_mode_is_the_shared_expert(T, d, d_e, dtype):
     assert_close(f64(act)[:T], O.swiglu_act(f64(x), f64(w1), f64(w3)), TOL_STAGE[dtype], "act")
     assert_close(f64(y)[:T], f64(act)[:T] @ f64(w2), TOL_STAGE[dtype], "y")
     assert bool((act[T] == 7.0).all()) and bool((y[T] == 7.0).all())
+
+
+@pytest.mark.parametrize("T,d,E,k,d_e,d_es,dtype", [
+    (200, 512, 8, 2, 256, 256, "bf16"),      # one launch for both halves
+    (64, 256, 16, 4, 128, 128, "bf16"),      # decode-like: few rows per expert
+    (150, 512, 4, 2, 256, 128, "bf16"),      # d_e_shared != d_e: two launches
+    (90, 264, 6, 3, 136, 136, "bf16"),       # K % 32 != 0 for down: register-staged kernel
+    (70, 64, 5, 2, 48, 32, "fp32"),
+])
+def test_grouped_gemm_shared_matches_separate_calls(T, d, E, k, d_e, d_es, dtype):
+    """moe_grouped_gemm_shared = moe_grouped_gemm on the block table + its dense mode on
+    the shared expert, bit for bit, and the shared half matches the oracle."""
+    rng = np.random.default_rng(T + d_es)
+    idx = rng.integers(0, E, size=(T, k))
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    bm = 128 if dtype == "bf16" else 16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17 + T)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    ws1 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+    ws3 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+    ws2 = (torch.randn((d_es, d), generator=g, device=DEV) / d_es ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=bm, dtype=dtype, d_e_shared=d_es)
+    s_sh = B.make_shape(T=T, d=d, E=1, k=1, d_e=d_es, block_m=bm, dtype=dtype)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    ws = B.alloc_workspace(s)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    x_perm = torch.empty((rows, d), dtype=dt, device=DEV)
+    B.moe_permute(s, x, pos, x_perm)
+    e = lambda *sh: torch.empty(sh, dtype=dt, device=DEV)
+    act, y, sact, sout = e(rows, d_e), e(rows, d), e(T, d_es), e(T, d)
+    act2, y2, sact2, sout2 = e(rows, d_e), e(rows, d), e(T, d_es), e(T, d)
+    B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1, w3, meta, nblk, mb, act,
+                              x, ws1, ws3, sact)
+    B.moe_grouped_gemm_shared(s, B.MOE_OP_DOWN, act, w2, None, meta, nblk, mb, y,
+                              sact, ws2, None, sout)
+    B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1, w3, meta, nblk, mb, act2)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act2, w2, None, meta, nblk, mb, y2)
+    B.moe_grouped_gemm(s_sh, B.MOE_OP_GATEUP_SWIGLU, x, ws1, ws3, None, None, 0, sact2)
+    B.moe_grouped_gemm(s_sh, B.MOE_OP_DOWN, sact2, ws2, None, None, None, 0, sout2)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy(np.nonzero(O.permutation(idx, E, bm)[1] >= 0)[0]).to(DEV)
+    bits = torch.int16 if dtype == "bf16" else torch.int32
+    for a, b in ((act[valid], act2[valid]), (y[valid], y2[valid]), (sact, sact2), (sout, sout2)):
+        assert torch.equal(a.view(bits), b.view(bits))
+    assert_close(f64(sact), O.swiglu_act(f64(x), f64(ws1), f64(ws3)), TOL_STAGE[dtype], "shared act")
+    assert_close(f64(sout), f64(sact) @ f64(ws2), TOL_STAGE[dtype], "shared out")
 
 
 def test_combine_skips_negative_positions():
