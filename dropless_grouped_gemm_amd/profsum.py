@@ -50,7 +50,8 @@ def short_name(name: str) -> str:
         elif ch == "(" and depth == 0:
             name = name[:i]
             break
-    return name[5:] if name.startswith("void ") else name
+    name = name[5:] if name.startswith("void ") else name
+    return name if len(name) <= 96 else name[:93] + "..."
 
 
 def kernels_summary(d: str, command: str, bench_log: str | None) -> str:

@@ -191,6 +191,7 @@ def test_route_exact_ties_go_to_the_lower_id():
     (40, 256, 4, 70, 128, 128, "bf16", "random"),      # k > 64: slots handed out in two rounds
     (3, 128, 2, 5, 64, 128, "bf16", "random"),         # k not a multiple of the slot batch
     (9, 8200, 3, 2, 64, 128, "bf16", "random"),        # row of 1025 vectors: partial chunks
+    (1100, 256, 3, 1, 128, 128, "bf16", "random"),     # 256-row tiles, odd block counts
 ])
 def test_stage_entry_points(T, d, E, k, d_e, bm, dtype, mode):
     rng = np.random.default_rng(T + d)

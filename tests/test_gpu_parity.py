@@ -32,6 +32,13 @@ REDUCED = {
     "down-ncols-ragged": C5.scaled(name="down-ncols-ragged", T=700, d=1000, d_e=384),
     "tiny-fp32-ragged": C1.scaled(name="tiny-fp32-ragged", T=37, d=100, d_e=60, block_m=7,
                                   d_e_shared=44),
+    # 256-row tiles (experts average >= 256 rows): ~375 rows per expert give odd block
+    # counts, so expert boundaries fall inside row pairs (two-pass items); a ragged last
+    # column tile; the shared expert in the same launch (d_e_shared == d_e) ...
+    "wide": C2.scaled(name="wide", T=1500, d=512, k=2, d_e=224, d_e_shared=224),
+    # ... or in launches of its own (d_e_shared != d_e), its 1500 rows in 256-row tiles
+    "wide-split-shared": C2.scaled(name="wide-split-shared", T=1500, d=512, k=2, d_e=224,
+                                   d_e_shared=96),
 }
 
 
