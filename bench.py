@@ -6,7 +6,9 @@
 One step is one pass of the whole layer over one batch already resident in HBM:
 router GEMM + top-k, counts/offsets/permutation, permute, grouped gate/up GEMM with
 SiLU*mul, grouped down GEMM (each GEMM launch also carries the shared expert when
-there is one), and combine.  The step is issued as
+there is one), and combine.  In bf16 the permute is fused into the gate/up launch
+(its A rows are gathered from x through the permutation), as moe_layer_fwd does; the
+standalone permute kernel is then timed separately for its bandwidth figure.  The step is issued as
 the sequence of C-ABI calls that moe_layer_fwd makes, with HIP events recorded on the
 launch stream between them, so every kernel's average duration is measured inside
 the timed region.  Prints one JSON line.
@@ -101,7 +103,11 @@ def main():
         sh_act = torch.empty((T, ds), dtype=dt, device=dev)
         sh_out = torch.empty((T, d), dtype=dt, device=dev)
 
-    stages = (["route"] if not routed else []) + ["offsets", "permute", "gateup", "down", "combine"]
+    # where the kernels can gather gate/up rows straight from x, the permute is fused into
+    # the gate/up launch (the call moe_layer_fwd makes) and x_perm is not written
+    gather = B.gather_supported(s)
+    stages = ((["route"] if not routed else []) + ["offsets"] + ([] if gather else ["permute"]) +
+              ["gateup", "down", "combine"])
 
     def step(ev=None):
         i = 0
@@ -116,16 +122,20 @@ def main():
         i += 1
         if ev is not None:
             ev[i].record()
-        B.moe_permute(s, inp.x, pos, x_perm)
-        i += 1
-        if ev is not None:
-            ev[i].record()
-        if shared:
-            B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk,
-                                      mb, act, inp.x, inp.ws1, inp.ws3, sh_act)
+        if gather:
+            B.moe_grouped_gemm_gather(s, inp.x, row_src, inp.w1, inp.w3, meta, nblk, mb, act,
+                                      inp.ws1, inp.ws3, sh_act if shared else None)
         else:
-            B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk, mb,
-                               act)
+            B.moe_permute(s, inp.x, pos, x_perm)
+            i += 1
+            if ev is not None:
+                ev[i].record()
+            if shared:
+                B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta,
+                                          nblk, mb, act, inp.x, inp.ws1, inp.ws3, sh_act)
+            else:
+                B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk,
+                                   mb, act)
         i += 1
         if ev is not None:
             ev[i].record()
@@ -174,6 +184,20 @@ def main():
         stage_ms[st] /= args.steps
     if int(err.item()) != 0:
         raise RuntimeError("device reported out-of-range expert ids")
+    if gather:
+        # the standalone permute (not on the layer path here: fused into gate/up),
+        # timed on its own for its bandwidth figure
+        for _ in range(2):
+            B.moe_permute(s, inp.x, pos, x_perm)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for _ in range(args.steps):
+            B.moe_permute(s, inp.x, pos, x_perm)
+        p1.record()
+        torch.cuda.synchronize()
+        permute_ms = p0.elapsed_time(p1) / args.steps
+    else:
+        permute_ms = stage_ms["permute"]
 
     # cross-check: the single moe_layer_fwd call runs the same kernels
     out2 = torch.empty_like(out)
@@ -216,8 +240,8 @@ def main():
     pb = LG.permute_bytes(T, k, d, eb)
     cb = LG.combine_bytes(T, k, d, eb, shared)
     moves = {
-        "permute": {"gbps": pb / (stage_ms["permute"] * 1e6), "bytes": pb,
-                    "us": stage_ms["permute"] * 1e3},
+        "permute": {"gbps": pb / (permute_ms * 1e6), "bytes": pb, "us": permute_ms * 1e3,
+                    "on_layer_path": not gather},
         "combine": {"gbps": cb / (stage_ms["combine"] * 1e6), "bytes": cb,
                     "us": stage_ms["combine"] * 1e3},
     }

@@ -23,7 +23,8 @@ MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
 
 ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
-                "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_combine", "moe_layer_fwd")
+                "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_grouped_gemm_gather",
+                "moe_combine", "moe_layer_fwd")
 
 
 class moe_shape(ctypes.Structure):
@@ -81,6 +82,8 @@ def lib():
         L.moe_grouped_gemm_shared.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P,
                                               P, P, P, P, P]
         L.moe_grouped_gemm_shared.restype = ctypes.c_int32
+        L.moe_grouped_gemm_gather.argtypes = [S, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
+        L.moe_grouped_gemm_gather.restype = ctypes.c_int32
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
         L.moe_combine.restype = ctypes.c_int32
         L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -198,6 +201,20 @@ def moe_grouped_gemm_shared(shape, op, A, B0, B1, block_meta, num_blocks, max_bl
         ctypes.byref(shape), op, _p(A), _p(B0), _p(B1), _p(block_meta), _p(num_blocks),
         int(max_blocks), _p(C), _p(A_shared), _p(B0_shared), _p(B1_shared), _p(C_shared),
         _stream(stream)))
+
+
+def moe_grouped_gemm_gather(shape, x, row_src, w1, w3, block_meta, num_blocks, max_blocks, act,
+                            ws1=None, ws3=None, shared_act=None, stream=None):
+    _check("moe_grouped_gemm_gather", lib().moe_grouped_gemm_gather(
+        ctypes.byref(shape), _p(x), _p(row_src), _p(w1), _p(w3), _p(block_meta), _p(num_blocks),
+        int(max_blocks), _p(act), _p(ws1), _p(ws3), _p(shared_act), _stream(stream)))
+
+
+def gather_supported(shape) -> bool:
+    """moe_grouped_gemm_gather (and so moe_layer_fwd's fused permute) applies: bf16,
+    d % 32 == 0 and gathered rows addressable with 32-bit byte offsets."""
+    return (shape.dtype == MOE_DTYPE_BF16 and shape.d % 32 == 0
+            and shape.T * shape.d * 2 + 4096 < 2 ** 32)
 
 
 def moe_combine(shape, y, pos, topk_w, shared_out, out, stream=None):

@@ -255,6 +255,27 @@ moe_status moe_grouped_gemm_shared(const moe_shape* s, int32_t op, const void* A
   return launch_grouped_gemm(*s, op, g, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_grouped_gemm_gather(const moe_shape* s, const void* x, const int32_t* row_src,
+                                   const void* w1, const void* w3, const int32_t* block_meta,
+                                   const int32_t* num_blocks, int32_t max_blocks, void* act,
+                                   const void* ws1, const void* ws3, void* shared_act,
+                                   void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!gather_supported(*s)) return MOE_ENOTSUP;
+  if (!gemm_operands_ok(MOE_OP_GATEUP_SWIGLU, x, w1, w3, act)) return MOE_EINVAL;
+  if (!row_src || !aligned4(row_src)) return MOE_EINVAL;
+  if (!block_table_ok(*s, block_meta, num_blocks, max_blocks)) return MOE_EINVAL;
+  const bool shared = s->d_e_shared > 0;
+  if (shared && !gemm_operands_ok(MOE_OP_GATEUP_SWIGLU, x, ws1, ws3, shared_act)) return MOE_EINVAL;
+  if (!shared && (ws1 || ws3 || shared_act)) return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  GemmSegments g{x, w1, w3, act, s->d, s->d_e, block_meta, num_blocks, max_blocks,
+                 shared ? x : nullptr, ws1, ws3, shared_act, s->d, s->d_e_shared,
+                 shared ? s->T : 0, row_src, s->k, s->T};
+  return launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, g, static_cast<hipStream_t>(stream));
+}
+
 moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos, const float* topk_w,
                        const void* shared_out, void* out, void* stream) {
   moe_status st = check_shape(s);
@@ -313,15 +334,21 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
                             static_cast<int32_t*>(at(L.row_src)),
                             static_cast<int32_t*>(at(L.err_flag)), at(L.scratch), hs);
   if (st != MOE_OK) return st;
-  st = launch_permute(*s, x, pos, at(L.x_perm), hs);
-  if (st != MOE_OK) return st;
+  // Gate/up reads its A rows straight from x through row_src when the kernels can
+  // (the permute fused into the GEMM's loads); otherwise x is permuted first.
+  const bool gather = gather_supported(*s);
+  if (!gather) {
+    st = launch_permute(*s, x, pos, at(L.x_perm), hs);
+    if (st != MOE_OK) return st;
+  }
   // Routed experts and the shared expert go through the grouped GEMM together (one
   // launch per op when their shapes agree), the shared expert as a dense segment
   // over the unpermuted x.
   const int32_t mb = (int32_t)max_blocks_of(*s);
   const int des = s->d_e_shared;
-  GemmSegments gu{at(L.x_perm), w1, w3, at(L.act), s->d, s->d_e, meta, nblk, mb,
-                  x, ws1, ws3, at(L.shared_act), s->d, des, shared ? s->T : 0};
+  GemmSegments gu{gather ? x : at(L.x_perm), w1, w3, at(L.act), s->d, s->d_e, meta, nblk, mb,
+                  x, ws1, ws3, at(L.shared_act), s->d, des, shared ? s->T : 0,
+                  gather ? static_cast<const int32_t*>(at(L.row_src)) : nullptr, s->k, s->T};
   st = launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, gu, hs);
   if (st != MOE_OK) return st;
   GemmSegments dn{at(L.act), w2, nullptr, at(L.y), s->d_e, s->d, meta, nblk, mb,

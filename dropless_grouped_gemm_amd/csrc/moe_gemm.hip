@@ -27,13 +27,13 @@
 //     store, so W never needs a separate transposed copy.
 //   * Rows past valid_m and columns past N are never read or written; K tails are
 //     zero-filled in the staging loads.
-#include "moe_internal.h"
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
+#include "moe_gemm_common.h"
 
 namespace moe {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 static constexpr int kBM = 128;     // rows per tile
 static constexpr int kBK = 64;      // K per pipeline stage
@@ -45,32 +45,6 @@ static constexpr int kStageBytes = kALdsBytes + kBLdsBytes;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-struct Tile {
-  int e, m0, valid;
-};
-
-// Work-item decoding shared by both kernels: returns false if the item is empty.
-__device__ __forceinline__ bool decode_block(int b, int sub, int sub_rows, int block_m,
-                                             const int32_t* __restrict__ meta, int dense_rows,
-                                             int E, int64_t max_rows, Tile& t) {
-  int e, m_start, vm;
-  if (dense_rows > 0) {
-    e = 0;
-    m_start = b * block_m;
-    vm = min(block_m, dense_rows - m_start);
-  } else {
-    e = meta[3 * b + 0];
-    m_start = meta[3 * b + 1];
-    vm = meta[3 * b + 2];
-  }
-  t.e = e;
-  t.m0 = m_start + sub * sub_rows;
-  t.valid = min(sub_rows, vm - sub * sub_rows);
-  // a table entry that does not fit the expert range or the row buffers is skipped
-  if (e < 0 || e >= E || m_start < 0 || vm > block_m || (int64_t)m_start + vm > max_rows)
-    return false;
-  return t.valid > 0;
-}
 
 template <int OP>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -264,49 +238,11 @@ static constexpr int kV2CopiesPerThread = 1 + 4;  // A: 8 windows / 8 waves, B: 
 static constexpr bool kUseSuper = false;  // XCD-aware super-tile order
 static constexpr int kGroupM = 16, kGroupN = 2;
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-#define MOE_LDS __attribute__((address_space(3)))
 
-// s_waitcnt with vmcnt <= n and the other counters unconstrained (gfx9 encoding).
-#define MOE_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// Wait until at most n slices' copies (n * kV2CopiesPerThread) are outstanding.
-__device__ __forceinline__ void wait_slices(int n) {
-  switch (n) {
-    case 0: MOE_WAIT_VMCNT(0); break;
-    case 1: MOE_WAIT_VMCNT(kV2CopiesPerThread); break;
-    case 2: MOE_WAIT_VMCNT(2 * kV2CopiesPerThread); break;
-    case 3: MOE_WAIT_VMCNT(3 * kV2CopiesPerThread); break;
-    default: MOE_WAIT_VMCNT(4 * kV2CopiesPerThread); break;
-  }
-}
 
-// 16-byte asynchronous copy global -> LDS: lane l reads gbase + voff_bytes[l] and its
-// 16 bytes land at lds_base + 16*l (gbase and lds_base are wave-uniform; lds_base
-// goes through M0).  Issued as inline assembly so the compiler's own counter model
-// does not see it: it would otherwise wait for every outstanding copy before each
-// LDS read.  The caller waits with MOE_WAIT_VMCNT; loads complete in issue order, so
-// compiler-generated waits stay correct (they can only over-wait).
-__device__ __forceinline__ void copy16_to_lds(const void* gbase, uint32_t voff_bytes,
-                                              const unsigned char* lds_base) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(const MOE_LDS void*)lds_base;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff_bytes), "s"(gbase), "s"(m0)
-               : "memory", "m0");
-}
 
-__device__ __forceinline__ int swz_a(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
-__device__ __forceinline__ int swz_b(int k, int chunk) { return chunk ^ (4 * (k & 3)); }
 
-// Operands of one segment set: A rows, the B matrices (expert-strided) and C rows.
-struct GGOperands {
-  const bf16_t* A;
-  const bf16_t* B0;
-  const bf16_t* B1;
-  bf16_t* C;
-};
 
 // One launch covers two segment sets with the same K and N: a dense segment of
 // dense_rows rows through one expert (the shared expert; dense_rows == 0: none),
@@ -389,8 +325,11 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
       const int row = wave * 16 + (lane >> 2);
       const int c = swz_a(row, lane & 3);   // the swizzle is an involution
       const int rr = row < tile.valid ? row : 0;
-      a_voff = (uint32_t)(rr * K + c * 8) * 2u;
+      // with a gather: the token behind the permuted row, addressed from the start of A
+      const int src = ops.gather ? gather_row(ops, tile.m0 + rr) : rr;
+      a_voff = (uint32_t)(src * K + c * 8) * 2u;
     }
+    asrc = uniform_ptr(ops.gather ? ops.A : asrc);
     // B copies: instruction i of this wave covers rows 2p, 2p+1 of half h, where
     // (h, p) = ((wave*4 + i) / 16, (wave*4 + i) % 16); lanes 0-31 take row 2p, lanes
     // 32-63 row 2p+1.  The lane offset depends on the row parity only through the
@@ -673,16 +612,50 @@ static moe_status launch_other(const moe_shape& s, int op, const void* A, const 
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// Wide tiles (384-row groups of one expert's blocks) pay off when experts own many
+// 128-row blocks; with a few rows per expert (decode) the 128-row tiles stream the
+// weights with less copy traffic per weight byte.
+// MOE_GG_TILE_ROWS=128 or 384 forces one tile height where both apply (tests use it to
+// cover both kernels on the same shapes); unset or anything else: automatic.
+static bool use_wide_tiles(const moe_shape& s, const GemmSegments& g) {
+  if (s.block_m != 128) return false;
+  if (g.max_blocks > 0 && g.max_blocks > wide_max_blocks()) return false;
+  const char* force = getenv("MOE_GG_TILE_ROWS");
+  if (force && strcmp(force, "128") == 0) return false;
+  if (force && strcmp(force, "384") == 0) return true;
+  if (g.max_blocks > 0) {
+    const int64_t M = (int64_t)s.T * s.k;
+    return g.max_blocks <= wide_max_blocks() && M >= 256 * std::min<int64_t>(s.E, M);
+  }
+  return g.dense_rows >= 384;
+}
+
+bool gather_supported(const moe_shape& s) {
+  // gathered rows are addressed with 32-bit byte offsets from the start of x
+  return s.dtype == MOE_DTYPE_BF16 && s.d % kV2BK == 0 &&
+         (int64_t)s.T * s.d * 2 + 4096 < ((int64_t)1 << 32);
+}
+
 moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g, hipStream_t st) {
   const bool routed = g.max_blocks > 0;
   const bool dense = g.dense_rows > 0;
   if (!routed && !dense) return MOE_OK;
   const int cus = device_cu_count();
   const bool v2_routed = s.dtype == MOE_DTYPE_BF16 && g.K % kV2BK == 0;
+  if (routed && g.gather && !v2_routed) return MOE_ENOTSUP;
   const bool v2_dense = s.dtype == MOE_DTYPE_BF16 && g.Kd % kV2BK == 0;
   // one launch when both sets fit the async-copy kernel with the same K and N
   if ((!routed || v2_routed) && (!dense || v2_dense) && (!routed || !dense || (g.K == g.Kd && g.N == g.Nd))) {
     const int K = routed ? g.K : g.Kd, N = routed ? g.N : g.Nd;
+    if (use_wide_tiles(s, g)) {
+      const GGOperands ro{static_cast<const bf16_t*>(g.A), static_cast<const bf16_t*>(g.B0),
+                          static_cast<const bf16_t*>(g.B1), static_cast<bf16_t*>(g.C),
+                          g.gather, g.gather_div, g.gather_rows};
+      const GGOperands dn{static_cast<const bf16_t*>(g.Ad), static_cast<const bf16_t*>(g.B0d),
+                          static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1};
+      return launch_gg_wide(op, ro, dn, K, N, g.block_meta, g.num_blocks, routed ? g.max_blocks : 0,
+                            s.E, dense ? g.dense_rows : 0, st);
+    }
     const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
     const int n_tiles = (int)ceil_div(N, out_cols);
     const int64_t blocks_ub = (routed ? (int64_t)g.max_blocks : 0) +
@@ -691,9 +664,10 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
     int64_t grid = items < cus ? items : cus;
     if (grid < 1) grid = 1;
     const GGOperands ro{static_cast<const bf16_t*>(g.A), static_cast<const bf16_t*>(g.B0),
-                        static_cast<const bf16_t*>(g.B1), static_cast<bf16_t*>(g.C)};
+                        static_cast<const bf16_t*>(g.B1), static_cast<bf16_t*>(g.C),
+                        g.gather, g.gather_div, g.gather_rows};
     const GGOperands dn{static_cast<const bf16_t*>(g.Ad), static_cast<const bf16_t*>(g.B0d),
-                        static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd)};
+                        static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1};
     const int64_t max_rows = (int64_t)g.max_blocks * s.block_m;
     if (op == MOE_OP_GATEUP_SWIGLU)
       hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kV2Threads), 0,

@@ -1,0 +1,425 @@
+// Grouped GEMM with wide tiles: 384 rows x 256 B-columns per work group (bf16, gfx950).
+//
+// Same contract as the 128-row kernels in moe_gemm.hip (one launch over the block
+// table [expert, m_start, valid_m] plus an optional dense segment; TileLang chapter
+// "MoE, MLA and sparse-attention operators", section 2.4 (a); dropless notes sections
+// 3, 5 and 7), for routing where experts own many 128-row blocks.
+//
+// Why wider tiles.  On gfx950 the global->LDS copies through each CU's vector-memory
+// path, not the MFMAs, bound the 128 x 512 tile: per 32-deep K slice it moves 40 KB
+// for 2 M multiply-adds.  A 384 x 256 tile moves the same 40 KB (24 KB of A, 16 KB of
+// B) for 3 M multiply-adds, a third fewer bytes per FLOP; its 98,304 fp32
+// accumulators fill three quarters of the CU's register file.
+//
+//   * A work item is (group, column tile).  A group is up to three consecutive table
+//     blocks of one expert whose rows are contiguous (every block but the last full),
+//     so all its rows read the same weight panel.  Each work group builds the group
+//     list of the launch in LDS once, from the device-side table: runs of such blocks,
+//     cut into threes from the start of each run.  The dense segment's groups are
+//     384-row spans of its rows.
+//   * NW waves (4: one per SIMD, 384 accumulator registers each; 8: two per SIMD, 192
+//     each).  Wave w owns rows [(w / 2) * 768 / NW, ...) of the tile and column half
+//     w % 2.  GATEUP: 64 act columns, i.e. the matching 64 gate (W1) and 64 up (W3)
+//     columns, so SiLU*mul stays in registers; DOWN: 128 columns.
+//   * Operands move HBM -> LDS with 16-byte global_load_lds copies into a 3-slot ring of
+//     32-deep K slices (40 KB each).  A is [384 rows][64 B] with the chunk swizzle
+//     c ^ ((row >> 2) & 3); B keeps its [k][n] layout (GATEUP: W1 and W3 regions of
+//     [32][128 columns]; DOWN: one [32][256 columns] region) with the swizzle
+//     c ^ 4 * (k & 3), and is read with ds_read_b64_tr_b16.  Both swizzles were
+//     measured conflict-free on gfx950.
+//   * Every lane issues the same copies every slice (rows past the group's valid rows
+//     copy row 0, columns past N copy column 0; those results are never stored), so
+//     the vmcnt waits are constants.
+#include <algorithm>
+
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+static constexpr int kWRows = 384;                    // rows per tile
+static constexpr int kWBK = 32;                       // K per ring slot
+static constexpr int kWABytes = kWRows * kWBK * 2;    // 24 KB
+static constexpr int kWBBytes = kWBK * 256 * 2;       // 16 KB
+static constexpr int kWStage = kWABytes + kWBBytes;   // 40 KB
+static constexpr int kWStages = 3;
+static constexpr int kWACopies = kWRows / 16;         // 1 KB copies per slice: A
+static constexpr int kWBCopies = kWBBytes / 1024;     //                        B
+static constexpr int kWMaxGroups = 8192;              // LDS group-list capacity
+
+// Block table limit of the wide kernel: the group list and the staged table must fit.
+int wide_max_blocks() {
+  const int staged = (kWStages * kWStage) / (3 * (int)sizeof(int32_t));
+  return kWMaxGroups < staged ? kWMaxGroups : staged;
+}
+
+template <int OP, int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
+k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
+          const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
+          int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles) {
+  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU;
+  constexpr int NT = NW * 64;
+  constexpr int WR = kWRows * 2 / NW;     // rows per wave
+  constexpr int MI = WR / 32;             // 32-row subtiles per wave
+  constexpr int CPA = kWACopies / NW;     // copies per wave per slice
+  constexpr int CPB = kWBCopies / NW;
+  constexpr int CPW = CPA + CPB;
+  constexpr int kOutCols = GU ? 128 : 256;
+  constexpr int kBPitch = GU ? 256 : 512; // bytes per staged B row
+  static_assert(kWACopies % NW == 0 && kWBCopies % NW == 0 && WR % 32 == 0, "tile split");
+
+  __shared__ __align__(1024) unsigned char lds[kWStages * kWStage];
+  __shared__ int32_t s_groups[kWMaxGroups];
+  __shared__ int32_t s_ngroups;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0;
+
+  // ---- group list ----------------------------------------------------------------
+  // Stage the table in the (not yet used) ring, then wave 0 forms the groups: lane l
+  // walks blocks [l*per, (l+1)*per); the run start that governs its first block and its
+  // first output slot come from two wave-wide scans.
+  int32_t* s_meta = reinterpret_cast<int32_t*>(lds);
+  for (int i = tid; i < 3 * nb; i += NT) s_meta[i] = meta[i];
+  __syncthreads();
+  if (wave == 0) {
+    auto ok = [&](int b) {
+      const int e = s_meta[3 * b], m = s_meta[3 * b + 1], v = s_meta[3 * b + 2];
+      return e >= 0 && e < E && m >= 0 && v >= 1 && v <= 128 && (int64_t)m + v <= max_rows;
+    };
+    // block b (valid) continues the run of block b-1
+    auto joins = [&](int b) {
+      return b > 0 && ok(b - 1) && s_meta[3 * b] == s_meta[3 * b - 3] &&
+             s_meta[3 * b + 1] == s_meta[3 * b - 2] + 128 && s_meta[3 * b - 1] == 128;
+    };
+    const int per = (nb + 63) / 64;
+    const int lo = min(lane * per, nb), hi = min(lo + per, nb);
+    int last_rs = -1;
+    for (int b = lo; b < hi; ++b)
+      if (ok(b) && !joins(b)) last_rs = b;
+    int incl = last_rs;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl = max(incl, o);
+    }
+    int in_rs = __shfl_up(incl, 1, 64);
+    if (lane == 0) in_rs = -1;
+    int cnt = 0, rs = in_rs;
+    for (int b = lo; b < hi; ++b) {
+      if (!ok(b)) continue;
+      if (!joins(b)) rs = b;
+      if ((b - rs) % 3 == 0) ++cnt;
+    }
+    int inc = cnt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += o;
+    }
+    int idx = inc - cnt;
+    rs = in_rs;
+    for (int b = lo; b < hi; ++b) {
+      if (!ok(b)) continue;
+      if (!joins(b)) rs = b;
+      if ((b - rs) % 3 == 0) {
+        int n = 1;
+        while (n < 3 && b + n < nb && ok(b + n) && joins(b + n)) ++n;
+        s_groups[idx++] = (b << 2) | n;
+      }
+    }
+    if (lane == 63) s_ngroups = inc;
+  }
+  __syncthreads();
+
+  const int ng_dense = (dense_rows + kWRows - 1) / kWRows;
+  const int total = (ng_dense + s_ngroups) * n_tiles;
+  const int nk = K / kWBK;
+
+  // Fixed per-lane parts of the fragment addresses, so that inside the loop an address
+  // is slot base + one of these + an immediate.
+  //   A (ds_read_b128): row rbase + 32i + (l & 31), logical chunk 2kk + (l >> 5); the
+  //   swizzle c ^ ((row >> 2) & 3) sees the row only through (l >> 2) & 7, so subtile i
+  //   is the immediate 2048 * i and kk selects one of two lane offsets.
+  //   B (ds_read_b64_tr_b16): 16-lane group g, row r = (l & 15) >> 2, column quad
+  //   c4 = l & 3; slice row k = 16kk + 8(g >> 1) + 4hh + r and column
+  //   n = 32j' + 16(g & 1) + 4c4 of the wave's columns, at chunk (n >> 3) ^ 4r (k & 3 is r).
+  //   Subtile j's first chunk cj is a multiple of 4, so its swizzled chunk is
+  //   (cj ^ 4r) | (2(g & 1) + (c4 >> 1)): kk and hh are immediates (16 and 4 rows); the
+  //   lane offset depends on j (GATEUP: on j & 1, the W1/W3 region being an immediate).
+  const int g = lane >> 4, tr_r = (lane & 15) >> 2, tr_c4 = lane & 3;
+  const int ch = wave & 1;                 // column half
+  const int rbase = (wave >> 1) * WR;      // first tile row of the wave
+  constexpr int NBL = GU ? 2 : 4;          // distinct B lane offsets
+  uint32_t a_lane[2], b_lane[NBL];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int row = rbase + (lane & 31);
+    a_lane[kk] = (uint32_t)(row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
+  }
+#pragma unroll
+  for (int jb = 0; jb < NBL; ++jb) {
+    const int cj = (GU ? ch * 64 + jb * 32 : ch * 128 + jb * 32) >> 3;
+    const int chunk = (cj ^ (4 * tr_r)) | (2 * (g & 1) + (tr_c4 >> 1));
+    b_lane[jb] = (uint32_t)(((g >> 1) * 8 + tr_r) * kBPitch + chunk * 16 + (tr_c4 & 1) * 8);
+  }
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int nt = w % n_tiles;
+    const int gidx = w / n_tiles;
+    const bool in_dense = gidx < ng_dense;
+    int e, m0, valid;
+    if (in_dense) {
+      e = 0;
+      m0 = gidx * kWRows;
+      valid = min(kWRows, dense_rows - m0);
+    } else {
+      const int it = s_groups[gidx - ng_dense];
+      const int b = it >> 2, n = it & 3;
+      e = meta[3 * b];
+      m0 = meta[3 * b + 1];
+      valid = 128 * (n - 1) + meta[3 * (b + n - 1) + 2];
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    valid = __builtin_amdgcn_readfirstlane(valid);
+    const GGOperands& ops = in_dense ? dense : routed;
+    bf16_t* const C = ops.C;
+    const int n0 = nt * kOutCols;
+    const bf16_t* asrc = ops.A + (size_t)m0 * K;
+    const bf16_t* b0e = ops.B0 + (size_t)e * K * N;
+    const bf16_t* b1e = GU ? ops.B1 + (size_t)e * K * N : b0e;
+
+    // Copies go out in two groups per slice, each behind one M0 load: the wave's A
+    // windows, then its B rows.  Copy i of a group carries the immediate offset 1 KB * i,
+    // which moves its LDS destination; its global source is corrected through the lane
+    // offset, against a base lowered by the group's largest immediate so that every
+    // lane offset stays non-negative.
+    //
+    // A: window t = wave*CPA + i covers tile rows 16t .. 16t+15, four lanes per row;
+    // the logical chunk of lane l is (l & 3) ^ ((l >> 4) & 3) for every window (the
+    // swizzle is an involution and depends on the row only through row >> 2).
+    // With a gather the source row is the token behind the permuted row, addressed from
+    // the start of A (rows of A * K * 2 bytes fit 32 bits; the host checks).
+    const int32_t* gat = ops.gather;
+    uint32_t a_voff[CPA];
+#pragma unroll
+    for (int i = 0; i < CPA; ++i) {
+      const int row = (wave * CPA + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((lane >> 4) & 3);
+      const int rr = row < valid ? row : 0;
+      const int src = gat ? gather_row(ops, m0 + rr) : rr;
+      a_voff[i] = (uint32_t)(src * K + c * 8) * 2u + (uint32_t)(CPA - 1 - i) * 1024u;
+    }
+    const unsigned char* a_gbase =
+        reinterpret_cast<const unsigned char*>(gat ? ops.A : asrc) - (CPA - 1) * 1024;
+    const int a_ldst = wave * CPA * 1024;
+    // B: copy u = wave*CPB + p.  GATEUP: u < 8 moves W1 rows 4u'..4u'+3 (u' = u % 8;
+    // u >= 8: the same rows of W3), 16 lanes per 256-byte row, and the logical chunk of
+    // lane l is (l & 15) ^ 4 * ((l >> 4) & 3) for every u.  DOWN: copy u moves rows 2u,
+    // 2u+1, 32 lanes per 512-byte row; the chunk depends on u through its parity, which
+    // is p's parity (CPB is even).
+    const int u0 = wave * CPB;
+    uint32_t b_voff[CPB];
+#pragma unroll
+    for (int p = 0; p < CPB; ++p) {
+      const int kl = GU ? (lane >> 4) : (lane >> 5);
+      const int k = GU ? kl : 2 * (p & 1) + kl;           // row within the slice, mod 4
+      const int cpos = GU ? (lane & 15) : (lane & 31);
+      int col = n0 + swz_b(k, cpos) * 8;                  // past N -> column 0
+      if (col >= N) col = 0;
+      const int rows_before = (GU ? 4 : 2) * p;           // slice rows of earlier copies
+      b_voff[p] = (uint32_t)((rows_before + kl) * N + col) * 2u + (uint32_t)(CPB - 1 - p) * 1024u;
+    }
+    const unsigned char* b_gbase;
+    int b_ldst;
+    if (GU) {
+      b_gbase = reinterpret_cast<const unsigned char*>((u0 < 8 ? b0e : b1e) + (size_t)4 * (u0 & 7) * N);
+      b_ldst = kWABytes + (u0 >> 3) * (kWBBytes / 2) + (u0 & 7) * 1024;
+    } else {
+      b_gbase = reinterpret_cast<const unsigned char*>(b0e + (size_t)2 * u0 * N);
+      b_ldst = kWABytes + u0 * 1024;
+    }
+    b_gbase -= (CPB - 1) * 1024;
+    // copy i of slice ks's A group (i == 0 loads M0 first) into ring slot `slot`
+    auto issue_a = [&](int ks, int slot, int i) {
+      if (i == 0) set_lds_dma_base(lds + slot * kWStage + a_ldst);
+      copy16_to_lds_nth(i, a_gbase + (size_t)ks * (kWBK * 2), a_voff[i]);
+    };
+    auto issue_b = [&](int ks, int slot, int p) {
+      if (p == 0) set_lds_dma_base(lds + slot * kWStage + b_ldst);
+      copy16_to_lds_nth(p, b_gbase + (size_t)ks * kWBK * N * 2, b_voff[p]);
+    };
+    auto issue = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < CPA; ++i) issue_a(ks, ks % kWStages, i);
+#pragma unroll
+      for (int p = 0; p < CPB; ++p) issue_b(ks, ks % kWStages, p);
+    };
+
+    f32x16_t acc[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    // One set of fragment registers (192 accumulators leave no room for two): the
+    // other wave on the SIMD covers each wave's LDS read latency.
+    bf16x8_t af[MI], bf[4];
+    auto read_frags = [&](int stage, int kk) {
+      const unsigned char* sa = lds + stage * kWStage;
+      const unsigned char* sb = sa + kWABytes;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + a_lane[kk] + i * 2048);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const unsigned char* hb = sb + (GU ? (j >> 1) * (kWBBytes / 2) + b_lane[j & 1] : b_lane[j]) +
+                                  kk * 16 * kBPitch;
+        i16x4_t hv[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(hb + hh * 4 * kBPitch));
+        bf[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    auto mfma_block = [&]() {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
+
+    // Prologue: every slot in flight (slices past the end re-copy the last slice into a
+    // slot that is never read again, so every slice issues the same number of copies
+    // and the waits are constants), then wait for slice 0.
+#pragma unroll
+    for (int p = 0; p < kWStages; ++p) issue(min(p, nk - 1));
+    MOE_WAIT_VMCNT((kWStages - 1) * CPW);
+    __syncthreads();
+
+    // Slice ks: two 16-deep halves, then a barrier once slice ks+1 has landed.  The
+    // barrier ending slice ks-1 freed its slot; slice ks-1+S refills it, the A copies
+    // spread between the first half's MFMAs and the B copies between the second's.
+    for (int ks = 0; ks < nk; ++ks) {
+      const int stage = ks % kWStages;
+      const int ksrc = min(ks - 1 + kWStages, nk - 1);
+      const int slot = (ks + kWStages - 1) % kWStages;
+      read_frags(stage, 0);
+      if (ks > 0) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            // A copy c goes after MFMA floor(c * MI * 4 / CPA)
+#pragma unroll
+            for (int c = 0; c < CPA; ++c)
+              if (c * MI * 4 / CPA == i * 4 + j) issue_a(ksrc, slot, c);
+          }
+        }
+      } else {
+        mfma_block();
+      }
+      read_frags(stage, 1);
+      if (ks > 0) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CPB; ++c)
+              if (c * MI * 4 / CPB == i * 4 + j) issue_b(ksrc, slot, c);
+          }
+        }
+      } else {
+        mfma_block();
+      }
+      if (ks + 1 < nk) {
+        MOE_WAIT_VMCNT((kWStages - 2) * CPW);   // slice ks+1 has landed
+        __syncthreads();
+      }
+    }
+    MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
+    __syncthreads();
+
+    // Epilogue through LDS: each wave converts 64 output columns at a time to bf16 into
+    // a private [WR][64 + 8] staging tile, then stores whole 16-byte row chunks.  32x32
+    // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
+    // l%32 of the subtile.
+    constexpr int kLd = 64 + 8;
+    constexpr int kPasses = GU ? 1 : 2;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * WR * kLd;
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            float v;
+            if (GU)
+              v = silu_f32(acc[i][jj][q]) * acc[i][jj + 2][q];
+            else
+              v = acc[i][ps * 2 + jj][q];
+            stg[r * kLd + jj * 32 + (lane & 31)] = f32_to_bf16(v);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int col0 = n0 + (GU ? ch * 64 : ch * 128 + ps * 64);
+#pragma unroll 4
+      for (int r0 = 0; r0 < WR; r0 += 8) {
+        const int r = r0 + (lane >> 3);
+        const int c8 = lane & 7;
+        const int grow = rbase + r;
+        const int gcol = col0 + c8 * 8;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + c8 * 8);
+        if (grow < valid && gcol < N)
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * N + gcol) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();  // staging reads done before the next item refills the ring
+  }
+}
+
+static constexpr int kWideWaves = 8;
+
+moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, int K, int N,
+                          const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
+                          int E, int32_t dense_rows, hipStream_t st) {
+  const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 128 : 256;
+  const int n_tiles = (int)ceil_div(N, out_cols);
+  // groups: at most one per block, and at most a third of the blocks plus one per expert
+  const int64_t mb = max_blocks > 0 ? max_blocks : 0;
+  const int64_t groups_ub = std::min<int64_t>(mb, ceil_div(mb, 3) + std::min<int64_t>(E, mb)) +
+                            ceil_div(dense_rows, kWRows);
+  const int64_t items = groups_ub * n_tiles;
+  const int cus = device_cu_count();
+  int64_t grid = items < cus ? items : cus;
+  if (grid < 1) grid = 1;
+  const int64_t max_rows = (int64_t)max_blocks * 128;
+  constexpr int NT = kWideWaves * 64;
+  if (op == MOE_OP_GATEUP_SWIGLU)
+    hipLaunchKernelGGL((k_gg_wide<MOE_OP_GATEUP_SWIGLU, kWideWaves>), dim3((unsigned)grid), dim3(NT),
+                       0, st, ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows,
+                       dense_rows, n_tiles);
+  else
+    hipLaunchKernelGGL((k_gg_wide<MOE_OP_DOWN, kWideWaves>), dim3((unsigned)grid), dim3(NT), 0, st,
+                       ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows, dense_rows,
+                       n_tiles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+}  // namespace moe

@@ -90,7 +90,14 @@ struct GemmSegments {
   void* Cd;
   int Kd, Nd;
   int32_t dense_rows;
+  // routed rows gather their A rows: row r reads A row gather[r] / gather_div
+  // (nullptr: A is already permuted); needs gather_supported()
+  const int32_t* gather;
+  int gather_div;
+  int gather_rows;  // rows of the unpermuted A (row indices are clamped into it)
 };
 moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g, hipStream_t st);
+// The bf16 asynchronous-copy kernels can gather gate/up A rows from the unpermuted x.
+bool gather_supported(const moe_shape& s);
 
 }  // namespace moe

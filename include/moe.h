@@ -203,6 +203,29 @@ moe_status moe_grouped_gemm_shared(const moe_shape* s, int32_t op, const void* A
                                    void* C_shared, void* stream);
 
 /*
+ * Gate/up grouped GEMM with the permute fused into its A-operand loads (direct
+ * gather; dropless notes section 4 steps 5-7: the permutation only decides which
+ * token row each GEMM row reads).  Identical to permuting x with moe_permute and
+ * calling moe_grouped_gemm(_shared) with MOE_OP_GATEUP_SWIGLU, bit for bit, without
+ * writing or reading x_perm: row r of the block table's segments reads
+ * x[row_src[r] / k, :] for r below its block's valid_m.
+ * In:  x [T, d] (bf16), row_src [moe_max_rows(s)] int32 (as written by
+ *      moe_build_offsets), w1, w3 [E, d, d_e], the block table as for
+ *      moe_grouped_gemm; when d_e_shared > 0 also ws1, ws3 [d, d_e_shared] (the
+ *      shared expert over the same x, as moe_grouped_gemm_shared), else NULLs.
+ * Out: act [moe_max_rows(s), d_e]; shared_act [T, d_e_shared] when d_e_shared > 0.
+ * Errors: MOE_ENOTSUP unless dtype is bf16, d % 32 == 0 and T * d * 2 + 4096 < 2^32
+ *      (the byte offsets of gathered rows); MOE_EINVAL as for moe_grouped_gemm.
+ *      Nothing is launched then.
+ */
+moe_status moe_grouped_gemm_gather(const moe_shape* s, const void* x,
+                                   const int32_t* row_src, const void* w1,
+                                   const void* w3, const int32_t* block_meta,
+                                   const int32_t* num_blocks, int32_t max_blocks,
+                                   void* act, const void* ws1, const void* ws3,
+                                   void* shared_act, void* stream);
+
+/*
  * Combine (TileLang chapter section 2.5; dropless notes section 4 steps 10-11):
  *   out[t, :] = sum_{j = 0..k-1, in this order} topk_w[t, j] * y[pos[t*k + j], :]
  *               (+ shared_out[t, :])
@@ -217,8 +240,10 @@ moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos,
 /*
  * The whole layer: route -> build offsets -> permute -> grouped GEMM (gate/up with
  * SiLU*mul, with the shared expert's gate/up on the unpermuted x when there is one)
- * -> grouped GEMM (down, likewise) -> combine.  The shared expert is a dense SwiGLU MLP on every token, added
- * unweighted (dropless notes section 1).
+ * -> grouped GEMM (down, likewise) -> combine.  Where moe_grouped_gemm_gather
+ * applies (bf16, d % 32 == 0), the permute is fused into the gate/up loads and
+ * x_perm is not written.  The shared expert is a dense SwiGLU MLP on every token,
+ * added unweighted (dropless notes section 1).
  * In:  x [T, d]; w_gate [d, E] and bias [E] fp32 (or NULL) when routing;
  *      w1, w3 [E, d, d_e], w2 [E, d_e, d];
  *      ws1, ws3 [d, d_e_shared], ws2 [d_e_shared, d] when d_e_shared > 0 (else NULL);

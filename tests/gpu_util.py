@@ -55,6 +55,7 @@ class LayerRun:
 
     def __init__(self, cfg, inp, routed=None):
         self.cfg = cfg
+        self.x = inp.x
         self.shape = B.shape_of_config(cfg)
         dev = inp.x.device
         self.ws = B.alloc_workspace(self.shape, dev)
@@ -106,7 +107,16 @@ class LayerRun:
         return self.view("y", self.dt(), (B.moe_max_rows(self.shape), self.cfg.d))
 
     def x_perm(self):
-        return self.view("x_perm", self.dt(), (B.moe_max_rows(self.shape), self.cfg.d))
+        """x permuted by the layer's own pos.  Where the layer fuses the permute into the
+        gate/up loads (x_perm never written), the standalone moe_permute produces it."""
+        rows = B.moe_max_rows(self.shape)
+        if not B.gather_supported(self.shape):
+            return self.view("x_perm", self.dt(), (rows, self.cfg.d))
+        xp = torch.empty((rows, self.cfg.d), dtype=self.dt(), device=self.x.device)
+        B.moe_permute(self.shape, self.x, self.view("pos", torch.int32, (self.cfg.T * self.cfg.k,)),
+                      xp)
+        torch.cuda.synchronize()
+        return xp
 
 
 def host_inputs(inp):

@@ -101,6 +101,8 @@ def test_invalid_shapes_rejected_by_every_entry_point(kw, status):
     assert L.moe_combine(ps, FAKE, FAKE, FAKE, None, FAKE, None) == status
     assert L.moe_layer_fwd(ps, *([FAKE] * 6), None, None, None, None, None, FAKE, FAKE,
                            1 << 40, None) == status
+    assert L.moe_grouped_gemm_gather(ps, *([FAKE] * 6), 1, FAKE, None, None, None,
+                                     None) == status
 
 
 def test_null_and_misaligned_pointers_rejected():
@@ -228,3 +230,34 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert L["act"] - L["x_perm"] >= rows * s.d * 2
         assert L["y"] - L["act"] >= rows * s.d_e * 2
         assert L["total"] > L["scratch"]
+
+
+def test_grouped_gemm_gather_argument_rules():
+    """The fused-permute gate/up: bf16 with d % 32 == 0 only (else ENOTSUP), the block
+    table as for moe_grouped_gemm, shared-expert operands matching d_e_shared."""
+    L = B.lib()
+    g = L.moe_grouped_gemm_gather
+    odd = ctypes.c_void_p(0x10008)
+    s32 = B.make_shape(T=8, d=64, E=2, k=1, d_e=32, block_m=16, dtype="fp32")
+    s_k = good_shape(d=72)
+    for s in (s32, s_k):
+        assert not B.gather_supported(s)
+        assert g(ctypes.byref(s), *([FAKE] * 6), 1, FAKE, None, None, None, None) == B.MOE_ENOTSUP
+    s = good_shape()
+    ps = ctypes.byref(s)
+    assert B.gather_supported(s)
+    mb = L.moe_max_blocks(ps)
+    ok = lambda *a: g(ps, *a, None)
+    assert ok(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, None, None) == B.MOE_EINVAL
+    assert ok(odd, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, None, None) == B.MOE_EINVAL
+    assert ok(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None, None, None) == B.MOE_EINVAL
+    assert ok(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, FAKE, None, None, None) == B.MOE_EINVAL
+    assert ok(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mb + 1, FAKE, None, None, None) == B.MOE_EINVAL
+    assert ok(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None, None) == B.MOE_EINVAL
+    # no shared expert in the shape: its operands must be NULL
+    assert ok(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    s2 = good_shape(d_e_shared=256)
+    ps2 = ctypes.byref(s2)
+    assert g(ps2, *([FAKE] * 6), 1, FAKE, None, None, None, None) == B.MOE_EINVAL
+    sT = good_shape(T=0)
+    assert g(ctypes.byref(sT), *([FAKE] * 6), 0, FAKE, None, None, None, None) == B.MOE_EINVAL

@@ -5,6 +5,8 @@ exact logit ties, many chunks, and the dropless notes' worked example."""
 import json
 import os
 
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -333,6 +335,65 @@ def test_grouped_gemm_shared_matches_separate_calls(T, d, E, k, d_e, d_es, dtype
         assert torch.equal(a.view(bits), b.view(bits))
     assert_close(f64(sact), O.swiglu_act(f64(x), f64(ws1), f64(ws3)), TOL_STAGE[dtype], "shared act")
     assert_close(f64(sout), f64(sact) @ f64(ws2), TOL_STAGE[dtype], "shared out")
+
+
+@pytest.mark.parametrize("tile", ["128", "384"])
+@pytest.mark.parametrize("T,d,E,k,d_e,d_es", [
+    (200, 512, 8, 2, 256, 256),      # shared expert in the same launch
+    (64, 256, 16, 4, 128, 128),      # decode-like: few rows per expert
+    (150, 512, 4, 2, 256, 0),        # no shared expert
+    (1100, 256, 3, 1, 200, 72),      # column tails; shared expert in launches of its own
+    (900, 1024, 4, 8, 128, 0),       # duplicate experts within a token, many full groups
+])
+def test_grouped_gemm_gather_is_permute_then_gemm(tile, T, d, E, k, d_e, d_es, monkeypatch):
+    """moe_grouped_gemm_gather = moe_permute then moe_grouped_gemm(_shared) gate/up, bit
+    for bit, on both tile heights; it never writes past the valid rows."""
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", tile)
+    rng = np.random.default_rng(T + d + k)
+    idx = rng.integers(0, E, size=(T, k))
+    dt = torch.bfloat16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5 + T)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16", d_e_shared=d_es)
+    assert B.gather_supported(s)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    ws = B.alloc_workspace(s)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    x_perm = torch.empty((rows, d), dtype=dt, device=DEV)
+    B.moe_permute(s, x, pos, x_perm)
+    act = torch.full((rows, d_e), 3.0, dtype=dt, device=DEV)
+    act2 = torch.empty((rows, d_e), dtype=dt, device=DEV)
+    if d_es:
+        ws1 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+        ws3 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+        sact = torch.empty((T, d_es), dtype=dt, device=DEV)
+        sact2 = torch.empty((T, d_es), dtype=dt, device=DEV)
+        B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act, ws1, ws3, sact)
+        B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1, w3, meta, nblk, mb, act2,
+                                  x, ws1, ws3, sact2)
+    else:
+        B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act)
+        B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1, w3, meta, nblk, mb, act2)
+    torch.cuda.synchronize()
+    ref_pos, ref_src = O.permutation(idx, E, 128)
+    valid = np.nonzero(ref_src >= 0)[0]
+    dv = torch.from_numpy(valid).to(DEV)
+    assert torch.equal(act[dv].view(torch.int16), act2[dv].view(torch.int16))
+    pad_rows = torch.from_numpy(np.nonzero(ref_src < 0)[0]).to(DEV)
+    assert bool((act[pad_rows] == 3.0).all())
+    if d_es:
+        assert torch.equal(sact.view(torch.int16), sact2.view(torch.int16))
+    c = O.expert_counts(idx, E)
+    xp_ref = O.permute(f64(x), ref_pos, k, len(ref_src))
+    act_ref, _ = O.grouped_ffn(xp_ref, c, 128, f64(w1), f64(w3), np.zeros((E, d_e, d)))
+    assert_close(f64(act)[valid], act_ref[valid], TOL_STAGE["bf16"], "act")
 
 
 def test_combine_skips_negative_positions():

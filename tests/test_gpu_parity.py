@@ -1,6 +1,8 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded inputs
 shaped like each of the five workloads, at sizes the oracle finishes in seconds
 while still spanning several tiles and ragged tails."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -42,17 +44,36 @@ REDUCED = {
 }
 
 
-@pytest.fixture(scope="module", params=list(REDUCED))
+# bf16 cases with 128-row blocks run twice: grouped GEMMs on 128-row tiles and on
+# 384-row tiles (MOE_GG_TILE_ROWS forces the library's choice; unset, it picks by shape).
+CASES = []
+for _name, _cfg in REDUCED.items():
+    if _cfg.dtype == "bf16" and _cfg.block_m == 128:
+        CASES += [(_name, "128"), (_name, "384")]
+    else:
+        CASES.append((_name, None))
+
+
+@pytest.fixture(scope="module", params=CASES, ids=[f"{n}-t{t}" if t else n for n, t in CASES])
 def case(request):
-    cfg = REDUCED[request.param]
-    torch.manual_seed(0)
-    inp = make_inputs(cfg, device="cuda")
-    run = LayerRun(cfg, inp)
-    h = host_inputs(inp)
-    ref = oracle_layer(cfg, h, run, inp)
-    print(f"[parity case] {cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.k} d_e={cfg.d_e}",
-          flush=True)
-    return cfg, inp, run, h, ref
+    name, tile = request.param
+    cfg = REDUCED[name]
+    old = os.environ.pop("MOE_GG_TILE_ROWS", None)
+    if tile:
+        os.environ["MOE_GG_TILE_ROWS"] = tile
+    try:
+        torch.manual_seed(0)
+        inp = make_inputs(cfg, device="cuda")
+        print(f"[parity case] {cfg.name} tile rows {tile or 'auto'}: T={cfg.T} d={cfg.d} "
+              f"E={cfg.E} k={cfg.k} d_e={cfg.d_e}", flush=True)
+        run = LayerRun(cfg, inp)
+        h = host_inputs(inp)
+        ref = oracle_layer(cfg, h, run, inp)
+        yield cfg, inp, run, h, ref
+    finally:
+        os.environ.pop("MOE_GG_TILE_ROWS", None)
+        if old is not None:
+            os.environ["MOE_GG_TILE_ROWS"] = old
 
 
 def test_router_logits_and_selection(case):
