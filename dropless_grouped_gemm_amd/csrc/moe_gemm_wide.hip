@@ -14,15 +14,15 @@
 //   * A work item is (group, column tile).  A group is up to three consecutive table
 //     blocks of one expert whose rows are contiguous (every block but the last full),
 //     so all its rows read the same weight panel.  Each work group builds the group
-//     list of the launch in LDS once, from the device-side table: runs of such blocks,
-//     cut into threes from the start of each run.  The dense segment's groups are
-//     384-row spans of its rows.
+//     list of the launch from the device-side table, in the LDS ring before its first
+//     item: runs of such blocks, cut into threes from the start of each run.  The
+//     dense segment's groups are 384-row spans of its rows.
 //   * NW waves (4: one per SIMD, 384 accumulator registers each; 8: two per SIMD, 192
 //     each).  Wave w owns rows [(w / 2) * 768 / NW, ...) of the tile and column half
 //     w % 2.  GATEUP: 64 act columns, i.e. the matching 64 gate (W1) and 64 up (W3)
 //     columns, so SiLU*mul stays in registers; DOWN: 128 columns.
-//   * Operands move HBM -> LDS with 16-byte global_load_lds copies into a 3-slot ring of
-//     32-deep K slices (40 KB each).  A is [384 rows][64 B] with the chunk swizzle
+//   * Operands move HBM -> LDS with 16-byte global_load_lds copies into a 4-slot ring of
+//     32-deep K slices (40 KB each, the whole LDS).  A is [384 rows][64 B] with the chunk swizzle
 //     c ^ ((row >> 2) & 3); B keeps its [k][n] layout (GATEUP: W1 and W3 regions of
 //     [32][128 columns]; DOWN: one [32][256 columns] region) with the swizzle
 //     c ^ 4 * (k & 3), and is read with ds_read_b64_tr_b16.  Both swizzles were
@@ -31,6 +31,7 @@
 //     copy row 0, columns past N copy column 0; those results are never stored), so
 //     the vmcnt waits are constants.
 #include <algorithm>
+#include <cstdlib>
 
 #include "moe_gemm_common.h"
 
@@ -41,15 +42,16 @@ static constexpr int kWBK = 32;                       // K per ring slot
 static constexpr int kWABytes = kWRows * kWBK * 2;    // 24 KB
 static constexpr int kWBBytes = kWBK * 256 * 2;       // 16 KB
 static constexpr int kWStage = kWABytes + kWBBytes;   // 40 KB
-static constexpr int kWStages = 3;
+static constexpr int kWStages = 4;
 static constexpr int kWACopies = kWRows / 16;         // 1 KB copies per slice: A
 static constexpr int kWBCopies = kWBBytes / 1024;     //                        B
-static constexpr int kWMaxGroups = 8192;              // LDS group-list capacity
+static constexpr int kWMaxBlocks = 8192;              // block-table limit (see below)
 
-// Block table limit of the wide kernel: the group list and the staged table must fit.
+// Block table limit of the wide kernel: the staged table (3 ints per block), the group
+// list (one int per block at most) and its length must fit the ring while it is idle.
 int wide_max_blocks() {
-  const int staged = (kWStages * kWStage) / (3 * (int)sizeof(int32_t));
-  return kWMaxGroups < staged ? kWMaxGroups : staged;
+  static_assert(kWMaxBlocks * 16 + 16 <= kWStages * kWStage, "group list fits the ring");
+  return kWMaxBlocks;
 }
 
 template <int OP, int NW>
@@ -69,8 +71,6 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   static_assert(kWACopies % NW == 0 && kWBCopies % NW == 0 && WR % 32 == 0, "tile split");
 
   __shared__ __align__(1024) unsigned char lds[kWStages * kWStage];
-  __shared__ int32_t s_groups[kWMaxGroups];
-  __shared__ int32_t s_ngroups;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -78,62 +78,70 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   const int nb = max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0;
 
   // ---- group list ----------------------------------------------------------------
-  // Stage the table in the (not yet used) ring, then wave 0 forms the groups: lane l
-  // walks blocks [l*per, (l+1)*per); the run start that governs its first block and its
-  // first output slot come from two wave-wide scans.
+  // Built in the ring while it is idle: the table is staged at s_meta, then wave 0 forms
+  // the groups into s_groups (lane l walks blocks [l*per, (l+1)*per); the run start that
+  // governs its first block and its first output slot come from two wave-wide scans)
+  // and their number into *s_ngroups.  Every wave then keeps the entries of its next 64
+  // work items in one register (lane j: item j), so the whole LDS holds the ring.
   int32_t* s_meta = reinterpret_cast<int32_t*>(lds);
-  for (int i = tid; i < 3 * nb; i += NT) s_meta[i] = meta[i];
-  __syncthreads();
-  if (wave == 0) {
-    auto ok = [&](int b) {
-      const int e = s_meta[3 * b], m = s_meta[3 * b + 1], v = s_meta[3 * b + 2];
-      return e >= 0 && e < E && m >= 0 && v >= 1 && v <= 128 && (int64_t)m + v <= max_rows;
-    };
-    // block b (valid) continues the run of block b-1
-    auto joins = [&](int b) {
-      return b > 0 && ok(b - 1) && s_meta[3 * b] == s_meta[3 * b - 3] &&
-             s_meta[3 * b + 1] == s_meta[3 * b - 2] + 128 && s_meta[3 * b - 1] == 128;
-    };
-    const int per = (nb + 63) / 64;
-    const int lo = min(lane * per, nb), hi = min(lo + per, nb);
-    int last_rs = -1;
-    for (int b = lo; b < hi; ++b)
-      if (ok(b) && !joins(b)) last_rs = b;
-    int incl = last_rs;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl = max(incl, o);
-    }
-    int in_rs = __shfl_up(incl, 1, 64);
-    if (lane == 0) in_rs = -1;
-    int cnt = 0, rs = in_rs;
-    for (int b = lo; b < hi; ++b) {
-      if (!ok(b)) continue;
-      if (!joins(b)) rs = b;
-      if ((b - rs) % 3 == 0) ++cnt;
-    }
-    int inc = cnt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(inc, off, 64);
-      if (lane >= off) inc += o;
-    }
-    int idx = inc - cnt;
-    rs = in_rs;
-    for (int b = lo; b < hi; ++b) {
-      if (!ok(b)) continue;
-      if (!joins(b)) rs = b;
-      if ((b - rs) % 3 == 0) {
-        int n = 1;
-        while (n < 3 && b + n < nb && ok(b + n) && joins(b + n)) ++n;
-        s_groups[idx++] = (b << 2) | n;
+  int32_t* s_groups = s_meta + 3 * nb;
+  int32_t* s_ngroups = s_groups + nb;
+  auto build_groups = [&]() {
+    for (int i = tid; i < 3 * nb; i += NT) s_meta[i] = meta[i];
+    __syncthreads();
+    if (wave == 0) {
+      auto ok = [&](int b) {
+        const int e = s_meta[3 * b], m = s_meta[3 * b + 1], v = s_meta[3 * b + 2];
+        return e >= 0 && e < E && m >= 0 && v >= 1 && v <= 128 && (int64_t)m + v <= max_rows;
+      };
+      // block b (valid) continues the run of block b-1
+      auto joins = [&](int b) {
+        return b > 0 && ok(b - 1) && s_meta[3 * b] == s_meta[3 * b - 3] &&
+               s_meta[3 * b + 1] == s_meta[3 * b - 2] + 128 && s_meta[3 * b - 1] == 128;
+      };
+      const int per = (nb + 63) / 64;
+      const int lo = min(lane * per, nb), hi = min(lo + per, nb);
+      int last_rs = -1;
+      for (int b = lo; b < hi; ++b)
+        if (ok(b) && !joins(b)) last_rs = b;
+      int incl = last_rs;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl = max(incl, o);
       }
+      int in_rs = __shfl_up(incl, 1, 64);
+      if (lane == 0) in_rs = -1;
+      int cnt = 0, rs = in_rs;
+      for (int b = lo; b < hi; ++b) {
+        if (!ok(b)) continue;
+        if (!joins(b)) rs = b;
+        if ((b - rs) % 3 == 0) ++cnt;
+      }
+      int inc = cnt;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += o;
+      }
+      int idx = inc - cnt;
+      rs = in_rs;
+      for (int b = lo; b < hi; ++b) {
+        if (!ok(b)) continue;
+        if (!joins(b)) rs = b;
+        if ((b - rs) % 3 == 0) {
+          int n = 1;
+          while (n < 3 && b + n < nb && ok(b + n) && joins(b + n)) ++n;
+          s_groups[idx++] = (b << 2) | n;
+        }
+      }
+      if (lane == 63) *s_ngroups = inc;
     }
-    if (lane == 63) s_ngroups = inc;
-  }
-  __syncthreads();
+    __syncthreads();
+  };
+  build_groups();
+  const int ngroups = __builtin_amdgcn_readfirstlane(*s_ngroups);
 
   const int ng_dense = (dense_rows + kWRows - 1) / kWRows;
-  const int total = (ng_dense + s_ngroups) * n_tiles;
+  const int total = (ng_dense + ngroups) * n_tiles;
   const int nk = K / kWBK;
 
   // Fixed per-lane parts of the fragment addresses, so that inside the loop an address
@@ -164,7 +172,17 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     b_lane[jb] = (uint32_t)(((g >> 1) * 8 + tr_r) * kBPitch + chunk * 16 + (tr_c4 & 1) * 8);
   }
 
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+  int my_groups = 0;  // lane j: the group-list entry of this work group's item (batch + j)
+  for (int j = 0;; ++j) {
+    const int w = blockIdx.x + j * gridDim.x;
+    if (w >= total) break;
+    if (j % 64 == 0) {
+      if (j > 0) build_groups();   // the ring is idle between items
+      const int wl = blockIdx.x + (j + lane) * gridDim.x;
+      const int gl = wl / n_tiles - ng_dense;
+      my_groups = (wl < total && gl >= 0) ? s_groups[gl] : 0;
+      __syncthreads();             // every wave has its entries before the ring refills
+    }
     const int nt = w % n_tiles;
     const int gidx = w / n_tiles;
     const bool in_dense = gidx < ng_dense;
@@ -174,7 +192,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       m0 = gidx * kWRows;
       valid = min(kWRows, dense_rows - m0);
     } else {
-      const int it = s_groups[gidx - ng_dense];
+      const int it = __builtin_amdgcn_readlane(my_groups, j % 64);
       const int b = it >> 2, n = it & 3;
       e = meta[3 * b];
       m0 = meta[3 * b + 1];
@@ -408,6 +426,12 @@ moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, in
   const int64_t items = groups_ub * n_tiles;
   const int cus = device_cu_count();
   int64_t grid = items < cus ? items : cus;
+  // MOE_GG_GRID_CAP=n caps the persistent grid (tests use it so that one work group
+  // walks more than 64 items and rebuilds its group list)
+  if (const char* cap = getenv("MOE_GG_GRID_CAP")) {
+    const int64_t c = atoll(cap);
+    if (c >= 1 && c < grid) grid = c;
+  }
   if (grid < 1) grid = 1;
   const int64_t max_rows = (int64_t)max_blocks * 128;
   constexpr int NT = kWideWaves * 64;

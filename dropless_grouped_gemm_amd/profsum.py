@@ -14,8 +14,8 @@ with FETCH_SIZE and one with WRITE_SIZE (KiB per dispatch).  Each counter is sca
 by the ratio of known to counted bytes of a plain elementwise kernel that reads and
 writes 1 GiB (torch.neg over 2^28 fp32 values, launched by the benchmark's
 --copy-probe), giving HBM bytes per launch of kernel K.  The summary ends with a
-JSON block that the benchmark reads; it carries the SHA-256 of the kernel's source
-file so that a figure taken before the kernel changed is not reported.
+JSON block that the benchmark reads; it carries the SHA-256 of the grouped-GEMM
+sources so that a figure taken before the kernels changed is not reported.
 """
 from __future__ import annotations
 
@@ -30,12 +30,23 @@ from collections import defaultdict
 PROBE_KERNEL = "neg_kernel"
 PROBE_BYTES = 1 << 30           # read, and written, by the probe kernel
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SOURCE = os.path.join("dropless_grouped_gemm_amd", "csrc", "moe_gemm.hip")
+# every source the grouped-GEMM kernels are built from
+GEMM_SOURCE = [os.path.join("dropless_grouped_gemm_amd", "csrc", f)
+               for f in ("moe_gemm.hip", "moe_gemm_wide.hip", "moe_gemm_common.h")]
 
 
-def source_digest(rel_path: str) -> str:
-    with open(os.path.join(ROOT, rel_path), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(rel_paths) -> str:
+    """SHA-256 over the concatenated bytes of one source file or a list of them."""
+    if isinstance(rel_paths, str):
+        rel_paths = [rel_paths]
+    h = hashlib.sha256()
+    for rel in rel_paths:
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return ""
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def short_name(name: str) -> str:

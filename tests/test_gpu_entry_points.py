@@ -396,6 +396,49 @@ def test_grouped_gemm_gather_is_permute_then_gemm(tile, T, d, E, k, d_e, d_es, m
     assert_close(f64(act)[valid], act_ref[valid], TOL_STAGE["bf16"], "act")
 
 
+@pytest.mark.parametrize("cap", ["1", "3"])
+def test_wide_tiles_with_a_capped_grid(cap, monkeypatch):
+    """A persistent grid of 1 or 3 work groups: each walks more than 64 items of the
+    384-row kernel (its group list is rebuilt every 64 items); gate/up (gathered) and
+    down match the 128-row kernel bit for bit."""
+    T, d, E, k, d_e = 900, 1024, 4, 8, 128
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, E, size=(T, k))
+    dt = torch.bfloat16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(23)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16")
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    ws = B.alloc_workspace(s)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    e = lambda *sh: torch.empty(sh, dtype=dt, device=DEV)
+    act, y, act2, y2 = e(rows, d_e), e(rows, d), e(rows, d_e), e(rows, d)
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", "384")
+    monkeypatch.setenv("MOE_GG_GRID_CAP", cap)
+    B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, w2, None, meta, nblk, mb, y)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", "128")
+    monkeypatch.delenv("MOE_GG_GRID_CAP")
+    B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act2)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act2, w2, None, meta, nblk, mb, y2)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy(np.nonzero(O.permutation(idx, E, 128)[1] >= 0)[0]).to(DEV)
+    # more than 64 down items per work group at cap 1 (the group list is rebuilt)
+    groups = sum(-(-(-(-int(c) // 128)) // 3) for c in O.expert_counts(idx, E))
+    assert groups * (d // 256) > 64 * int(cap) or cap == "3"
+    assert torch.equal(act[valid].view(torch.int16), act2[valid].view(torch.int16))
+    assert torch.equal(y[valid].view(torch.int16), y2[valid].view(torch.int16))
+
+
 def test_combine_skips_negative_positions():
     T, d, k = 8, 64, 2
     s = B.make_shape(T=T, d=d, E=4, k=k, d_e=64, block_m=128)
