@@ -227,13 +227,22 @@ def main():
     dn_flops = LG.down_flops(M, d, de)
     sg = LG.gateup_flops(T, d, cfg.d_e_shared) if shared else 0
     sd = LG.down_flops(T, d, cfg.d_e_shared) if shared else 0
+    # algorithmic bytes per launch: every tensor the launch needs, once
+    if gather:
+        gu_bytes = LG.gateup_gather_bytes(T, M, active, d, de, eb)
+    else:
+        gu_bytes = LG.gateup_bytes(M, active, d, de, eb)
+    dn_bytes = LG.down_bytes(M, active, d, de, eb)
+    if shared:
+        gu_bytes += LG.shared_gateup_bytes(T, d, cfg.d_e_shared, eb, reads_x=not gather)
+        dn_bytes += LG.shared_down_bytes(T, d, cfg.d_e_shared, eb)
     gemm = {
         "gateup": {"tflops": (gu_flops + sg) / (stage_ms["gateup"] * 1e9),
                    "flops": gu_flops + sg, "routed_flops": gu_flops, "shared_flops": sg,
-                   "us": stage_ms["gateup"] * 1e3},
+                   "bytes": gu_bytes, "us": stage_ms["gateup"] * 1e3},
         "down": {"tflops": (dn_flops + sd) / (stage_ms["down"] * 1e9),
                  "flops": dn_flops + sd, "routed_flops": dn_flops, "shared_flops": sd,
-                 "us": stage_ms["down"] * 1e3},
+                 "bytes": dn_bytes, "us": stage_ms["down"] * 1e3},
     }
     for v in gemm.values():
         v["frac"] = v["tflops"] / peak

@@ -37,6 +37,23 @@ def gateup_bytes(rows, active_experts, d, d_e, b):
     return (rows * d + 2 * active_experts * d * d_e + rows * d_e) * b
 
 
+def gateup_gather_bytes(T, rows, active_experts, d, d_e, b):
+    """Gate/up with the permute fused into its loads: read each token row of x once (the
+    k gathered copies are re-reads of it), W1 and W3 of every expert with rows once;
+    write act."""
+    return (T * d + 2 * active_experts * d * d_e + rows * d_e) * b
+
+
+def shared_gateup_bytes(T, d, d_es, b, reads_x=True):
+    """The shared expert's gate/up: x (unless the routed half already reads it), Ws1,
+    Ws3; write its act."""
+    return ((T * d if reads_x else 0) + 2 * d * d_es + T * d_es) * b
+
+
+def shared_down_bytes(T, d, d_es, b):
+    return (T * d_es + d_es * d + T * d) * b
+
+
 def down_bytes(rows, active_experts, d, d_e, b):
     """Read act and W2 of every expert with rows once; write y."""
     return (rows * d_e + active_experts * d_e * d + rows * d) * b
