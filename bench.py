@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="fusedmoe-8x2048")
+    ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
+                    help="fp8: expert weights quantised to e4m3 with a scale per 128x128 "
+                         "block (quantised once, outside the timed region)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -103,6 +106,18 @@ def main():
         sh_act = torch.empty((T, ds), dtype=dt, device=dev)
         sh_out = torch.empty((T, d), dtype=dt, device=dev)
 
+    fp8 = args.weights == "fp8"
+    if fp8 and not B.fp8_supported(s):
+        print(f"fp8 weights are not supported for {cfg.name}", file=sys.stderr)
+        sys.exit(2)
+    if fp8:
+        # quantised once (weights at rest in fp8), outside the timed region
+        q1, q3, q2 = (B.quantize_fp8(w) for w in (inp.w1, inp.w3, inp.w2))
+        if cfg.d_e_shared > 0:
+            qs1, qs3, qs2 = (B.quantize_fp8(w) for w in (inp.ws1, inp.ws3, inp.ws2))
+        else:
+            qs1 = qs3 = qs2 = (None, None)
+        torch.cuda.synchronize()
     # where the kernels can gather gate/up rows straight from x, the permute is fused into
     # the gate/up launch (the call moe_layer_fwd makes) and x_perm is not written
     gather = B.gather_supported(s)
@@ -122,7 +137,17 @@ def main():
         i += 1
         if ev is not None:
             ev[i].record()
-        if gather:
+        if fp8:
+            if not gather:
+                B.moe_permute(s, inp.x, pos, x_perm)
+                i += 1
+                if ev is not None:
+                    ev[i].record()
+            B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, inp.x if gather else x_perm, *q1,
+                                   *q3, meta, nblk, mb, row_src if gather else None, act,
+                                   inp.x if shared else None, *qs1, *qs3,
+                                   sh_act if shared else None)
+        elif gather:
             B.moe_grouped_gemm_gather(s, inp.x, row_src, inp.w1, inp.w3, meta, nblk, mb, act,
                                       inp.ws1, inp.ws3, sh_act if shared else None)
         else:
@@ -139,7 +164,11 @@ def main():
         i += 1
         if ev is not None:
             ev[i].record()
-        if shared:
+        if fp8:
+            B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, *q2, None, None, meta, nblk, mb, None, y,
+                                   sh_act if shared else None, *qs2, None, None,
+                                   sh_out if shared else None)
+        elif shared:
             B.moe_grouped_gemm_shared(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y,
                                       sh_act, inp.ws2, None, sh_out)
         else:
@@ -202,15 +231,20 @@ def main():
     # cross-check: the single moe_layer_fwd call runs the same kernels
     out2 = torch.empty_like(out)
     ws2 = B.alloc_workspace(s, dev)
-    B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1, inp.ws3,
-                    inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
+    def layer_call():
+        if fp8:
+            B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *q1, *q3, *q2, *qs1, *qs3, *qs2,
+                                inp.topk_idx, inp.topk_w, out2, ws2)
+        else:
+            B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1,
+                            inp.ws3, inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
+    layer_call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nrep = max(3, args.steps // 2)
     e0.record()
     for _ in range(nrep):
-        B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1, inp.ws3,
-                        inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
+        layer_call()
     e1.record()
     torch.cuda.synchronize()
     layer_fwd_ms = e0.elapsed_time(e1) / nrep
@@ -228,14 +262,18 @@ def main():
     sg = LG.gateup_flops(T, d, cfg.d_e_shared) if shared else 0
     sd = LG.down_flops(T, d, cfg.d_e_shared) if shared else 0
     # algorithmic bytes per launch: every tensor the launch needs, once
+    wb = 1 if fp8 else eb                      # bytes per weight
     if gather:
-        gu_bytes = LG.gateup_gather_bytes(T, M, active, d, de, eb)
+        gu_bytes = LG.gateup_gather_bytes(T, M, active, d, de, eb, wb)
     else:
-        gu_bytes = LG.gateup_bytes(M, active, d, de, eb)
-    dn_bytes = LG.down_bytes(M, active, d, de, eb)
+        gu_bytes = LG.gateup_bytes(M, active, d, de, eb, wb)
+    dn_bytes = LG.down_bytes(M, active, d, de, eb, wb)
     if shared:
-        gu_bytes += LG.shared_gateup_bytes(T, d, cfg.d_e_shared, eb, reads_x=not gather)
-        dn_bytes += LG.shared_down_bytes(T, d, cfg.d_e_shared, eb)
+        gu_bytes += LG.shared_gateup_bytes(T, d, cfg.d_e_shared, eb, reads_x=not gather, wb=wb)
+        dn_bytes += LG.shared_down_bytes(T, d, cfg.d_e_shared, eb, wb)
+    if fp8:
+        gu_bytes += LG.fp8_scale_bytes(2 * active + (2 if shared else 0), d, de)
+        dn_bytes += LG.fp8_scale_bytes(active + (1 if shared else 0), de, d)
     gemm = {
         "gateup": {"tflops": (gu_flops + sg) / (stage_ms["gateup"] * 1e9),
                    "flops": gu_flops + sg, "routed_flops": gu_flops, "shared_flops": sg,
@@ -244,8 +282,13 @@ def main():
                  "flops": dn_flops + sd, "routed_flops": dn_flops, "shared_flops": sd,
                  "bytes": dn_bytes, "us": stage_ms["down"] * 1e3},
     }
+    # each launch's bound: MFMA when its arithmetic intensity reaches the ridge point
+    # (peak FLOP/s / HBM bytes/s), HBM otherwise (decode: the launch streams weights)
+    ridge = peak * 1e12 / (PEAK_HBM_GBPS * 1e9)
     for v in gemm.values():
-        v["frac"] = v["tflops"] / peak
+        v["gbps"] = v["bytes"] / (v["us"] * 1e3)
+        v["bound"] = "mfma" if v["flops"] / v["bytes"] >= ridge else "hbm"
+        v["frac"] = (v["tflops"] / peak if v["bound"] == "mfma" else v["gbps"] / PEAK_HBM_GBPS)
     pb = LG.permute_bytes(T, k, d, eb)
     cb = LG.combine_bytes(T, k, d, eb, shared)
     moves = {
@@ -265,10 +308,16 @@ def main():
     dom = max(("gateup", "down"), key=lambda n: stage_ms[n])
     # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
     # copy kernel), taken from the committed summary unless the kernel changed since
-    tpath = args.traffic or os.path.join(ROOT, "profiles", f"{dom}_{cfg.name}_hbm_traffic.md")
-    traffic = PS.read_traffic(tpath, dom, cfg.name)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": gemm[dom]["tflops"], "peak": peak,
-                "unit": "TFLOP/s", "frac": gemm[dom]["frac"], "traffic": traffic}
+    wname = cfg.name + ("-fp8w" if fp8 else "")
+    tpath = args.traffic or os.path.join(ROOT, "profiles", f"{dom}_{wname}_hbm_traffic.md")
+    traffic = PS.read_traffic(tpath, dom, wname)
+    if gemm[dom]["bound"] == "mfma":
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": gemm[dom]["tflops"], "peak": peak,
+                    "unit": "TFLOP/s", "frac": gemm[dom]["frac"], "traffic": traffic}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": gemm[dom]["gbps"],
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gemm[dom]["frac"],
+                    "traffic": traffic}
 
     # ---- CPU oracle on a bounded sample -----------------------------------------
     cpu = None
@@ -287,6 +336,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
+        "weights": "fp8-e4m3, fp32 scale per 128x128 block" if fp8 else cfg.dtype,
         "data": "synthetic (seeded; N(0,1) tokens, N(0,1/fan_in) weights, random-init)",
         "config": {"workload": cfg.description, "name": cfg.name, "T": T, "d": d, "E": E, "k": k,
                    "d_e": de, "d_e_shared": cfg.d_e_shared, "block_m": cfg.block_m,

@@ -24,7 +24,8 @@ MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
 ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
                 "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_grouped_gemm_gather",
-                "moe_combine", "moe_layer_fwd")
+                "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_grouped_gemm_fp8",
+                "moe_layer_fwd_fp8")
 
 
 class moe_shape(ctypes.Structure):
@@ -84,6 +85,13 @@ def lib():
         L.moe_grouped_gemm_shared.restype = ctypes.c_int32
         L.moe_grouped_gemm_gather.argtypes = [S, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
         L.moe_grouped_gemm_gather.restype = ctypes.c_int32
+        L.moe_quantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+        L.moe_quantize_fp8.restype = ctypes.c_int32
+        L.moe_grouped_gemm_fp8.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32,
+                                           P, P, P, P, P, P, P, P, P]
+        L.moe_grouped_gemm_fp8.restype = ctypes.c_int32
+        L.moe_layer_fwd_fp8.argtypes = [S] + [P] * 19 + [ctypes.c_size_t, P]
+        L.moe_layer_fwd_fp8.restype = ctypes.c_int32
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
         L.moe_combine.restype = ctypes.c_int32
         L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -215,6 +223,53 @@ def gather_supported(shape) -> bool:
     d % 32 == 0 and gathered rows addressable with 32-bit byte offsets."""
     return (shape.dtype == MOE_DTYPE_BF16 and shape.d % 32 == 0
             and shape.T * shape.d * 2 + 4096 < 2 ** 32)
+
+
+def moe_quantize_fp8(w, q, scales, stream=None):
+    """w: bf16 [E, K, N] (or [K, N]); q: uint8 of the same shape; scales: fp32
+    [E, ceil(K/128), ceil(N/128)]."""
+    E, K, N = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(E, K, N, _p(w), _p(q), _p(scales),
+                                                      _stream(stream)))
+
+
+def fp8_scale_shape(w_shape):
+    """Scale array shape for a weight of shape [E, K, N] (or [K, N])."""
+    *e, K, N = w_shape
+    return tuple(e) + (-(-K // 128), -(-N // 128))
+
+
+def quantize_fp8(w, stream=None):
+    """(codes, scales) of a bf16 weight tensor, on its device."""
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    s = torch.empty(fp8_scale_shape(w.shape), dtype=torch.float32, device=w.device)
+    moe_quantize_fp8(w, q, s, stream)
+    return q, s
+
+
+def moe_grouped_gemm_fp8(shape, op, A, Q0, S0, Q1, S1, block_meta, num_blocks, max_blocks,
+                         row_src, C, A_shared=None, Q0_shared=None, S0_shared=None,
+                         Q1_shared=None, S1_shared=None, C_shared=None, stream=None):
+    _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
+        ctypes.byref(shape), op, _p(A), _p(Q0), _p(S0), _p(Q1), _p(S1), _p(block_meta),
+        _p(num_blocks), int(max_blocks), _p(row_src), _p(C), _p(A_shared), _p(Q0_shared),
+        _p(S0_shared), _p(Q1_shared), _p(S1_shared), _p(C_shared), _stream(stream)))
+
+
+def moe_layer_fwd_fp8(shape, x, w_gate, bias, q1, s1, q3, s3, q2, s2, qs1, ss1, qs3, ss3,
+                      qs2, ss2, topk_idx_in, topk_w_in, out, ws, stream=None):
+    _check("moe_layer_fwd_fp8", lib().moe_layer_fwd_fp8(
+        ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(q1), _p(s1), _p(q3), _p(s3),
+        _p(q2), _p(s2), _p(qs1), _p(ss1), _p(qs3), _p(ss3), _p(qs2), _p(ss2), _p(topk_idx_in),
+        _p(topk_w_in), _p(out), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def fp8_supported(shape) -> bool:
+    """The fp8-weight path applies: bf16 activations, 128-row blocks, d, d_e (and
+    d_e_shared) multiples of 32 and at most 32768."""
+    dims = [shape.d, shape.d_e] + ([shape.d_e_shared] if shape.d_e_shared else [])
+    return (shape.dtype == MOE_DTYPE_BF16 and shape.block_m == 128
+            and all(v % 32 == 0 and v <= 32768 for v in dims))
 
 
 def moe_combine(shape, y, pos, topk_w, shared_out, out, stream=None):

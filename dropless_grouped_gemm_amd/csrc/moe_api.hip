@@ -276,6 +276,164 @@ moe_status moe_grouped_gemm_gather(const moe_shape* s, const void* x, const int3
   return launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, g, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_quantize_fp8(int32_t E, int32_t K, int32_t N, const void* w, uint8_t* q,
+                            float* scales, void* stream) {
+  if (E < 1 || K < 1 || N < 8 || N % 8) return MOE_EINVAL;
+  if ((int64_t)E * K * N >= ((int64_t)1 << 40)) return MOE_ENOTSUP;
+  if (!w || !q || !scales || !aligned16(w) || (reinterpret_cast<uintptr_t>(q) & 7u) ||
+      !aligned4(scales))
+    return MOE_EINVAL;
+  return launch_quantize_fp8(E, K, N, w, q, scales, static_cast<hipStream_t>(stream));
+}
+
+// The fp8-weight path: bf16 activations, 128-row blocks, K and N the kernel takes.
+static moe_status check_fp8(const moe_shape& s) {
+  if (s.dtype != MOE_DTYPE_BF16 || s.block_m != 128) return MOE_ENOTSUP;
+  if (!fp8_gemm_supported(s.d, s.d_e) || !fp8_gemm_supported(s.d_e, s.d)) return MOE_ENOTSUP;
+  if (s.d_e_shared > 0 &&
+      (!fp8_gemm_supported(s.d, s.d_e_shared) || !fp8_gemm_supported(s.d_e_shared, s.d)))
+    return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+static bool fp8_operands_ok(int32_t op, const void* A, const uint8_t* Q0, const float* S0,
+                            const uint8_t* Q1, const float* S1, const void* C) {
+  if (!A || !Q0 || !S0 || !C) return false;
+  if (op == MOE_OP_GATEUP_SWIGLU && (!Q1 || !S1)) return false;
+  if (op == MOE_OP_DOWN && (Q1 || S1)) return false;
+  return aligned16(A) && aligned16(Q0) && aligned4(S0) && (!Q1 || aligned16(Q1)) &&
+         (!S1 || aligned4(S1)) && aligned16(C);
+}
+
+// One fp8 grouped-GEMM op over the routed segments and (optionally) the shared expert:
+// one launch when their K and N agree, else two.
+static moe_status run_fp8_op(const moe_shape& s, int op, const void* A, const uint8_t* Q0,
+                             const float* S0, const uint8_t* Q1, const float* S1,
+                             const int32_t* meta, const int32_t* nblk, int32_t mb,
+                             const int32_t* row_src, void* C, const void* As,
+                             const uint8_t* Q0s, const float* S0s, const uint8_t* Q1s,
+                             const float* S1s, void* Cs, hipStream_t st) {
+  const bool gu = op == MOE_OP_GATEUP_SWIGLU;
+  const int K = gu ? s.d : s.d_e, N = gu ? s.d_e : s.d;
+  const bool shared = As != nullptr;
+  const int Ks = gu ? s.d : s.d_e_shared, Ns = gu ? s.d_e_shared : s.d;
+  GemmSegmentsF8 g{A, Q0, S0, Q1, S1, C, K, N, meta, nblk, mb,
+                   nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                   row_src, s.k, s.T};
+  if (shared && Ks == K && Ns == N) {
+    g.Ad = As; g.Q0d = Q0s; g.S0d = S0s; g.Q1d = Q1s; g.S1d = S1s; g.Cd = Cs; g.dense_rows = s.T;
+    return launch_grouped_gemm_fp8(op, g, s.E, st);
+  }
+  if (shared) {
+    GemmSegmentsF8 d{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Ks, Ns, nullptr, nullptr,
+                     0, As, Q0s, S0s, Q1s, S1s, Cs, s.T, nullptr, 1, 1};
+    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, st);
+    if (st2 != MOE_OK) return st2;
+  }
+  return launch_grouped_gemm_fp8(op, g, s.E, st);
+}
+
+moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, const uint8_t* Q0,
+                                const float* S0, const uint8_t* Q1, const float* S1,
+                                const int32_t* block_meta, const int32_t* num_blocks,
+                                int32_t max_blocks, const int32_t* row_src, void* C,
+                                const void* A_shared, const uint8_t* Q0_shared,
+                                const float* S0_shared, const uint8_t* Q1_shared,
+                                const float* S1_shared, void* C_shared, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
+  if ((st = check_fp8(*s)) != MOE_OK) return st;
+  if (!fp8_operands_ok(op, A, Q0, S0, Q1, S1, C)) return MOE_EINVAL;
+  if (!block_table_ok(*s, block_meta, num_blocks, max_blocks)) return MOE_EINVAL;
+  if (row_src) {
+    if (op != MOE_OP_GATEUP_SWIGLU || !aligned4(row_src)) return MOE_EINVAL;
+    if (!gather_supported(*s)) return MOE_ENOTSUP;
+  }
+  const bool shared = A_shared || Q0_shared || S0_shared || Q1_shared || S1_shared || C_shared;
+  if (shared) {
+    if (s->d_e_shared <= 0) return MOE_EINVAL;
+    if (!fp8_operands_ok(op, A_shared, Q0_shared, S0_shared, Q1_shared, S1_shared, C_shared))
+      return MOE_EINVAL;
+  }
+  if (s->T == 0) return MOE_OK;
+  return run_fp8_op(*s, op, A, Q0, S0, Q1, S1, block_meta, num_blocks, max_blocks, row_src, C,
+                    shared ? A_shared : nullptr, Q0_shared, S0_shared, Q1_shared, S1_shared,
+                    C_shared, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_gate,
+                             const float* bias, const uint8_t* q1, const float* s1,
+                             const uint8_t* q3, const float* s3, const uint8_t* q2,
+                             const float* s2, const uint8_t* qs1, const float* ss1,
+                             const uint8_t* qs3, const float* ss3, const uint8_t* qs2,
+                             const float* ss2, const int32_t* topk_idx_in,
+                             const float* topk_w_in, void* out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_fp8(*s)) != MOE_OK) return st;
+  const bool routed = topk_idx_in && topk_w_in;
+  if ((topk_idx_in != nullptr) != (topk_w_in != nullptr)) return MOE_EINVAL;
+  if (!x || !out || !aligned16(x) || !aligned16(out)) return MOE_EINVAL;
+  if (!routed && !w_gate) return MOE_EINVAL;
+  if (!routed && (st = check_routing(*s)) != MOE_OK) return st;
+  const bool shared = s->d_e_shared > 0;
+  const void* qptr[] = {q1, q3, q2};
+  const void* sptr[] = {s1, s3, s2};
+  for (int i = 0; i < 3; ++i)
+    if (!qptr[i] || !sptr[i] || !aligned16(qptr[i]) || !aligned4(sptr[i])) return MOE_EINVAL;
+  const void* qs[] = {qs1, qs3, qs2};
+  const void* ss[] = {ss1, ss3, ss2};
+  for (int i = 0; i < 3; ++i) {
+    if (shared && (!qs[i] || !ss[i] || !aligned16(qs[i]) || !aligned4(ss[i]))) return MOE_EINVAL;
+    if (!shared && (qs[i] || ss[i])) return MOE_EINVAL;
+  }
+  if ((w_gate && !aligned4(w_gate)) || (bias && !aligned4(bias)) ||
+      (topk_idx_in && !aligned4(topk_idx_in)) || (topk_w_in && !aligned4(topk_w_in)))
+    return MOE_EINVAL;
+  moe_ws_layout L;
+  layout_of(*s, L);
+  if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (s->T == 0) return MOE_OK;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  int32_t* idx = routed ? const_cast<int32_t*>(topk_idx_in) : static_cast<int32_t*>(at(L.topk_idx));
+  float* wts = routed ? const_cast<float*>(topk_w_in) : static_cast<float*>(at(L.topk_w));
+  if (!routed) {
+    st = launch_route(*s, x, w_gate, bias, static_cast<float*>(at(L.logits)), idx, wts,
+                      static_cast<float*>(at(L.scratch)), hs);
+    if (st != MOE_OK) return st;
+  }
+  int32_t* meta = static_cast<int32_t*>(at(L.block_meta));
+  int32_t* nblk = static_cast<int32_t*>(at(L.num_blocks));
+  int32_t* pos = static_cast<int32_t*>(at(L.pos));
+  int32_t* rsrc = static_cast<int32_t*>(at(L.row_src));
+  st = launch_build_offsets(*s, idx, static_cast<int32_t*>(at(L.counts)),
+                            static_cast<int32_t*>(at(L.offsets)),
+                            static_cast<int32_t*>(at(L.padded_offsets)), meta, nblk, pos, rsrc,
+                            static_cast<int32_t*>(at(L.err_flag)), at(L.scratch), hs);
+  if (st != MOE_OK) return st;
+  const bool gather = gather_supported(*s);
+  if (!gather) {
+    st = launch_permute(*s, x, pos, at(L.x_perm), hs);
+    if (st != MOE_OK) return st;
+  }
+  const int32_t mb = (int32_t)max_blocks_of(*s);
+  st = run_fp8_op(*s, MOE_OP_GATEUP_SWIGLU, gather ? x : at(L.x_perm), q1, s1, q3, s3, meta, nblk,
+                  mb, gather ? rsrc : nullptr, at(L.act), shared ? x : nullptr, qs1, ss1, qs3, ss3,
+                  shared ? at(L.shared_act) : nullptr, hs);
+  if (st != MOE_OK) return st;
+  st = run_fp8_op(*s, MOE_OP_DOWN, at(L.act), q2, s2, nullptr, nullptr, meta, nblk, mb, nullptr,
+                  at(L.y), shared ? at(L.shared_act) : nullptr, qs2, ss2, nullptr, nullptr,
+                  shared ? at(L.shared_out) : nullptr, hs);
+  if (st != MOE_OK) return st;
+  const void* sh = shared ? at(L.shared_out) : nullptr;
+  return launch_combine(*s, at(L.y), pos, wts, sh, out, hs);
+}
+
 moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos, const float* topk_w,
                        const void* shared_out, void* out, void* stream) {
   moe_status st = check_shape(s);

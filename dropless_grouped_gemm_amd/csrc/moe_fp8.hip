@@ -1,0 +1,394 @@
+// fp8 (OCP e4m3) expert weights with a scale per 128 x 128 block (dropless notes
+// section 12: fp8 weights carry a scale per quantisation block; dequantise before
+// the product when the block is narrower than the matrix unit's contraction, else the
+// scale can go after it).  Here the bf16 MFMA takes 16-deep slices, narrower than the
+// 128-deep block, so either order works; the weights are dequantised in registers
+// just before the MFMA (code -> fp32, times the block scale, rounded to bf16), which
+// keeps one accumulator set and costs 16 VALU operations per 32 x 16 B fragment.
+//
+//   * k_quantize_fp8: one work group per 128 x 128 block of one expert matrix:
+//     amax, scale = amax / 448 (1 for an all-zero block), codes = round-to-nearest-
+//     even of clamp(w / scale, -448, 448), all in fp32.
+//   * k_gg_fp8w: the grouped GEMM of the 128-row asynchronous-copy kernel with fp8
+//     B.  The copies move fp8 bytes (half the bf16 bytes), so a 24 KB slice (8 KB of A,
+//     16 KB of B for 32 x 512) fits a six-slot ring.  B stays [k][n] in LDS with the
+//     16-byte chunk swizzle c ^ (k & 15) and is read with ds_read_b64_tr_b8: in each
+//     16-lane group lane i points at row i / 2, bytes 8 (i % 2) .. +7 of an 8 x 16 block
+//     and receives column i's 8 rows, exactly the 8 consecutive k values one lane
+//     supplies to v_mfma_f32_32x32x16_bf16 (lane layout established with a probe).
+//     Rows may be gathered from x through row_src as in the bf16 kernels.
+#include "moe_gemm_common.h"
+
+#include <cmath>
+
+namespace moe {
+
+static constexpr int kQBlock = 128;        // quantisation block (k and n)
+static constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------------------
+// quantiser
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_quantize_fp8(const bf16_t* __restrict__ w, uint8_t* __restrict__ q, float* __restrict__ scales,
+               int K, int N) {
+  __shared__ float s_max[4];
+  const int nb = blockIdx.x, kb = blockIdx.y, e = blockIdx.z;
+  const int NB = gridDim.x, KB = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c8 = tid & 15;          // 8-column chunk of the block
+  const int r0 = tid >> 4;          // rows r0 + 16 i
+  const int col = nb * kQBlock + c8 * 8;
+  const bf16_t* src = w + (size_t)e * K * N;
+  u32x4_t v[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = kb * kQBlock + r0 + 16 * i;
+    if (row < K && col < N) {
+      v[i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)row * N + col);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[i][h] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(v[i][h] & 0xffff0000u)));
+      }
+    } else {
+      v[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (lane == 0) s_max[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+  if (tid == 0) scales[((size_t)e * KB + kb) * NB + nb] = scale;
+  uint8_t* dst = q + (size_t)e * K * N;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = kb * kQBlock + r0 + 16 * i;
+    if (row >= K || col >= N) continue;
+    uint32_t packed[2];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float lo = fminf(fmaxf(__uint_as_float(v[i][h] << 16) / scale, -kE4M3Max), kE4M3Max);
+      const float hi = fminf(fmaxf(__uint_as_float(v[i][h] & 0xffff0000u) / scale, -kE4M3Max),
+                             kE4M3Max);
+      // two codes into bytes 2(h & 1), 2(h & 1) + 1 of packed[h >> 1]
+      const int word = __builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false) & 0xffff;
+      if (h & 1)
+        packed[h >> 1] |= (uint32_t)word << 16;
+      else
+        packed[h >> 1] = (uint32_t)word;
+    }
+    *reinterpret_cast<uint2*>(dst + (size_t)row * N + col) = make_uint2(packed[0], packed[1]);
+  }
+}
+
+moe_status launch_quantize_fp8(int E, int K, int N, const void* w, uint8_t* q, float* scales,
+                               hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(N, kQBlock), (unsigned)ceil_div(K, kQBlock), (unsigned)E);
+  hipLaunchKernelGGL(k_quantize_fp8, grid, dim3(256), 0, st, static_cast<const bf16_t*>(w), q,
+                     scales, K, N);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// grouped GEMM with fp8 B
+// ---------------------------------------------------------------------------
+static constexpr int kFThreads = 512;                 // 8 waves
+static constexpr int kFBK = 32;                       // K per ring slot
+static constexpr int kFABytes = 128 * kFBK * 2;       // 8 KB of A (bf16)
+static constexpr int kFBHalf = kFBK * 256;            // 8 KB per 256-column half (fp8)
+static constexpr int kFStage = kFABytes + 2 * kFBHalf;  // 24 KB
+static constexpr int kFStages = 6;
+static constexpr int kFCopies = 1 + 2;                // per wave per slice: A, B
+static constexpr int kFMaxKB = 256;                   // k-blocks per item held in LDS
+
+// Operands of one segment set with fp8 B: codes and scales per matrix.
+struct GGOperandsF8 {
+  GGOperands base;          // A, C, gather; base.B0 / base.B1 unused
+  const uint8_t* Q0;
+  const uint8_t* Q1;
+  const float* S0;
+  const float* S1;
+};
+
+__device__ __forceinline__ int swz_q(int k, int chunk) { return chunk ^ (k & 15); }
+
+template <int OP>
+__global__ void __launch_bounds__(kFThreads, 1)
+k_gg_fp8w(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
+          const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
+          int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles) {
+  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU;
+  constexpr int kOutCols = GU ? 256 : 512;
+  __shared__ __align__(1024) unsigned char lds[kFStages * kFStage];
+  // the item's block scales: [kb][4] (GATEUP: W1 n-blocks 0, 1 then W3 n-blocks 0, 1
+  // of the tile; DOWN: n-blocks 0..3 of the tile)
+  __shared__ float s_scale[kFMaxKB * 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb_dense = (dense_rows + 127) / 128;
+  const int nblocks = nb_dense + (max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0);
+  const int total = nblocks * n_tiles;
+  const int nk = K / kFBK;
+  const int KB = (K + kQBlock - 1) / kQBlock, NBq = (N + kQBlock - 1) / kQBlock;
+
+  // B fragment reads: 16-lane group g, lane gi of it; subtile j of the wave: LDS half
+  // and first column within the half.
+  const int g = lane >> 4, gi = lane & 15;
+  int bhalf[2], bcol0[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    bhalf[j] = GU ? j : wave >> 2;
+    bcol0[j] = GU ? wave * 32 : (wave & 3) * 64 + j * 32;
+  }
+  uint32_t b_lane[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int k = 8 * (g >> 1) + (gi >> 1);                // row within a 16-deep step
+    const int chunk = bcol0[j] / 16 + (g & 1);
+    b_lane[j] = (uint32_t)(bhalf[j] * kFBHalf + k * 256 + swz_q(k, chunk) * 16 + (gi & 1) * 8);
+  }
+  // the scale slot of subtile j: [kb][4] index
+  int sidx[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    sidx[j] = GU ? j * 2 + (bcol0[j] >> 7) : (bhalf[j] * 256 + bcol0[j]) >> 7;
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int nt = w % n_tiles;
+    const int blk = w / n_tiles;
+    const bool in_dense = blk < nb_dense;
+    Tile tile;
+    if (in_dense) {
+      if (!decode_block(blk, 0, 128, 128, nullptr, dense_rows, 1, dense_rows, tile)) continue;
+    } else {
+      if (!decode_block(blk - nb_dense, 0, 128, 128, meta, 0, E, max_rows, tile)) continue;
+    }
+    const GGOperandsF8& ops = in_dense ? dense : routed;
+    bf16_t* const C = ops.base.C;
+    const int n0 = nt * kOutCols;
+    const int e = tile.e;
+
+    // block scales of this item's columns, every k-block
+    {
+      const float* s0 = ops.S0 + (size_t)e * KB * NBq;
+      const float* s1 = GU ? ops.S1 + (size_t)e * KB * NBq : s0;
+      for (int i = tid; i < KB * 4; i += kFThreads) {
+        const int kb = i >> 2, slot = i & 3;
+        int nb;
+        const float* sp;
+        if (GU) {
+          nb = (n0 >> 7) + (slot & 1);
+          sp = slot < 2 ? s0 : s1;
+        } else {
+          nb = (n0 >> 7) + slot;
+          sp = s0;
+        }
+        s_scale[i] = nb < NBq ? sp[(size_t)kb * NBq + nb] : 1.0f;
+      }
+    }
+
+    // A copy (one per wave per slice): the wave's 16-row window; rows past valid_m
+    // copy row 0, gathered rows come from x.
+    const bf16_t* asrc = ops.base.A + (size_t)tile.m0 * K;
+    uint32_t a_voff;
+    {
+      const int row = wave * 16 + (lane >> 2);
+      const int c = swz_a(row, lane & 3);
+      const int rr = row < tile.valid ? row : 0;
+      const int src = ops.base.gather ? gather_row(ops.base, tile.m0 + rr) : rr;
+      a_voff = (uint32_t)(src * K + c * 8) * 2u;
+    }
+    asrc = uniform_ptr(ops.base.gather ? ops.base.A : asrc);
+    // B copies: copy u = 2 wave + p of 16 moves rows 4u'..4u'+3 (u' = u % 8) of half
+    // u / 8, 16 lanes per 256-byte row; the logical chunk of lane l is
+    // (l & 15) ^ ((4u' + (l >> 4)) & 15).  Columns past N copy column 0.
+    const uint8_t* bh_base[2];
+    int bh_col0[2];
+    bh_base[0] = ops.Q0 + (size_t)e * K * N;
+    bh_base[1] = GU ? ops.Q1 + (size_t)e * K * N : bh_base[0];
+    bh_col0[0] = n0;
+    bh_col0[1] = GU ? n0 : n0 + 256;
+    uint32_t b_voff[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int u = wave * 2 + p;
+      const int uu = u & 7, h = u >> 3;
+      const int k = 4 * uu + (lane >> 4);
+      int col = bh_col0[h] + swz_q(k, lane & 15) * 16;
+      if (col >= N) col = 0;
+      b_voff[p] = (uint32_t)((lane >> 4) * N + col);
+    }
+    const int bu_h = (wave * 2) >> 3;                      // both copies in one half
+    const uint8_t* bsrc = uniform_ptr(bh_base[bu_h]);
+    auto issue = [&](int ks, int slot) {
+      unsigned char* st = lds + slot * kFStage;
+      const int k0 = ks * kFBK;
+      copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int uu = (wave * 2 + p) & 7;
+        copy16_to_lds(bsrc + (size_t)(k0 + 4 * uu) * N, b_voff[p],
+                      st + kFABytes + bu_h * kFBHalf + uu * 1024);
+      }
+    };
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    // 32-row subtiles holding valid rows (decode: usually one): the others are neither
+    // read nor multiplied, so a weight-streaming item does a quarter of the MFMAs.
+    const int nsub = __builtin_amdgcn_readfirstlane(min(4, (tile.valid + 31) >> 5));
+    bf16x8_t af[4], bf[2];
+    auto read_frags = [&](int ks, int kk) {
+      const unsigned char* sa = lds + (ks % kFStages) * kFStage;
+      const unsigned char* sb = sa + kFABytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nsub) break;
+        const int row = i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
+      }
+      const int kb = (ks * kFBK) >> 7;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (MOE_LDS v2i*)(sb + b_lane[j] + kk * 16 * 256));
+        const float sc = s_scale[kb * 4 + sidx[j]];
+        bf16x8_t o;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], false);   // bytes 0, 1
+          const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], true);    // bytes 2, 3
+          o[4 * h + 0] = static_cast<__bf16>(f0[0] * sc);
+          o[4 * h + 1] = static_cast<__bf16>(f0[1] * sc);
+          o[4 * h + 2] = static_cast<__bf16>(f1[0] * sc);
+          o[4 * h + 3] = static_cast<__bf16>(f1[1] * sc);
+        }
+        bf[j] = o;
+      }
+    };
+    auto mfma_block = [&]() {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nsub) break;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    // Prologue: every slot in flight (slices past the end re-copy the last slice into a
+    // slot that is never read), then wait for slice 0.  The scale table was written by
+    // plain LDS stores; the barrier publishes it too.
+#pragma unroll
+    for (int p = 0; p < kFStages; ++p) issue(min(p, nk - 1), p);
+    MOE_WAIT_VMCNT((kFStages - 1) * kFCopies);
+    __syncthreads();
+
+    // Slice ks: two 16-deep halves, then a barrier once slice ks+1 has landed; the
+    // barrier that ended slice ks-1 freed its slot, which slice ks-1+S refills.
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks > 0) issue(min(ks - 1 + kFStages, nk - 1), (ks - 1) % kFStages);
+      read_frags(ks, 0);
+      mfma_block();
+      read_frags(ks, 1);
+      mfma_block();
+      if (ks + 1 < nk) {
+        MOE_WAIT_VMCNT((kFStages - 2) * kFCopies);   // slice ks+1 has landed
+        __syncthreads();
+      }
+    }
+    MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
+    __syncthreads();
+
+    // Epilogue through LDS (as the bf16 kernel): bf16 staging per wave, 16-byte stores.
+    constexpr int kWCols = GU ? 32 : 64;
+    constexpr int kHalves = GU ? 1 : 2;
+    constexpr int kRowsPer = 128 / kHalves;
+    constexpr int kLd = kWCols + 8;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kRowsPer * kLd;
+    const int col0 = n0 + (GU ? wave * 32 : (wave >> 2) * 256 + (wave & 3) * 64);
+#pragma unroll
+    for (int hv = 0; hv < kHalves; ++hv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i / (4 / kHalves) != hv) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = (i % (4 / kHalves)) * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          if (GU) {
+            stg[r * kLd + (lane & 31)] = f32_to_bf16(silu_f32(acc[i][0][q]) * acc[i][1][q]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              stg[r * kLd + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][q]);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int kChunks = kWCols / 8;
+      constexpr int kRowsPerPass = 64 / kChunks;
+#pragma unroll 4
+      for (int r0 = 0; r0 < kRowsPer; r0 += kRowsPerPass) {
+        const int r = r0 + lane / kChunks;
+        const int ch = lane % kChunks;
+        const int grow = hv * kRowsPer + r;
+        const int gcol = col0 + ch * 8;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + ch * 8);
+        if (grow < tile.valid && gcol < N)
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * N + gcol) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();  // staging and scale reads done before the next item refills
+  }
+}
+
+bool fp8_gemm_supported(int K, int N) {
+  return K % kFBK == 0 && N % 16 == 0 && ceil_div(K, kQBlock) <= kFMaxKB;
+}
+
+moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, hipStream_t st) {
+  const bool routed = g.max_blocks > 0, dense = g.dense_rows > 0;
+  if (!routed && !dense) return MOE_OK;
+  const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
+  const int n_tiles = (int)ceil_div(g.N, out_cols);
+  const int64_t blocks_ub = (routed ? (int64_t)g.max_blocks : 0) + (dense ? ceil_div(g.dense_rows, 128) : 0);
+  const int64_t items = blocks_ub * n_tiles;
+  const int cus = device_cu_count();
+  int64_t grid = items < cus ? items : cus;
+  if (grid < 1) grid = 1;
+  const GGOperandsF8 ro{{static_cast<const bf16_t*>(g.A), nullptr, nullptr, static_cast<bf16_t*>(g.C),
+                         g.gather, g.gather_div, g.gather_rows},
+                        g.Q0, g.Q1, g.S0, g.S1};
+  const GGOperandsF8 dn{{static_cast<const bf16_t*>(g.Ad), nullptr, nullptr, static_cast<bf16_t*>(g.Cd),
+                         nullptr, 1, 1},
+                        g.Q0d, g.Q1d, g.S0d, g.S1d};
+  const int64_t max_rows = (int64_t)g.max_blocks * 128;
+  if (op == MOE_OP_GATEUP_SWIGLU)
+    hipLaunchKernelGGL(k_gg_fp8w<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kFThreads), 0, st,
+                       ro, dn, g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E, max_rows,
+                       g.dense_rows, n_tiles);
+  else
+    hipLaunchKernelGGL(k_gg_fp8w<MOE_OP_DOWN>, dim3((unsigned)grid), dim3(kFThreads), 0, st, ro, dn,
+                       g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E, max_rows,
+                       g.dense_rows, n_tiles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+}  // namespace moe

@@ -372,12 +372,16 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+    // 32-row subtiles holding valid rows (decode: usually one): the others are neither
+    // read nor multiplied, so a weight-streaming item does a quarter of the MFMAs.
+    const int nsub = __builtin_amdgcn_readfirstlane(min(4, (tile.valid + 31) >> 5));
     bf16x8_t af0[4], bf0[2], af1[4], bf1[2];
     auto read_frags = [&](int stage, int kk, bf16x8_t* a, bf16x8_t* b) {
       const unsigned char* sa = lds + stage * kV2Stage;
       const unsigned char* sb = sa + kV2ABytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (i >= nsub) break;
         const int row = i * 32 + (lane & 31);
         a[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
       }
@@ -398,10 +402,12 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
     };
     auto mfma_block = [&](const bf16x8_t* a, const bf16x8_t* b) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nsub) break;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
     };
 
     // Prologue: every slot in flight (slices past the end re-copy the last slice into
@@ -431,9 +437,11 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         issue_part_to(ksrc, slot, i);
+        if (i < nsub) {
 #pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2)
-          acc[i][j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j2], acc[i][j2], 0, 0, 0);
+          for (int j2 = 0; j2 < 2; ++j2)
+            acc[i][j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j2], acc[i][j2], 0, 0, 0);
+        }
       }
       issue_part_to(ksrc, slot, 4);
     }

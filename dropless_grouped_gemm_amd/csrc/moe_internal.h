@@ -100,4 +100,35 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
 // The bf16 asynchronous-copy kernels can gather gate/up A rows from the unpermuted x.
 bool gather_supported(const moe_shape& s);
 
+// fp8 (e4m3) weights with fp32 scales per 128 x 128 block (moe_fp8.hip).
+moe_status launch_quantize_fp8(int E, int K, int N, const void* w, uint8_t* q, float* scales,
+                               hipStream_t st);
+// The fp8-weight grouped GEMM applies to this K (contraction) and N.
+bool fp8_gemm_supported(int K, int N);
+struct GemmSegmentsF8 {
+  const void* A;
+  const uint8_t* Q0;
+  const float* S0;
+  const uint8_t* Q1;
+  const float* S1;
+  void* C;
+  int K, N;
+  const int32_t* block_meta;
+  const int32_t* num_blocks;
+  int32_t max_blocks;
+  // dense segment (the shared expert): same K and N, rows of Ad
+  const void* Ad;
+  const uint8_t* Q0d;
+  const float* S0d;
+  const uint8_t* Q1d;
+  const float* S1d;
+  void* Cd;
+  int32_t dense_rows;
+  // routed rows gathered from A (as GemmSegments::gather)
+  const int32_t* gather;
+  int gather_div;
+  int gather_rows;
+};
+moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, hipStream_t st);
+
 }  // namespace moe

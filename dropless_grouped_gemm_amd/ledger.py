@@ -32,31 +32,42 @@ def down_flops(rows, d, d_e):
     return 2 * rows * d_e * d
 
 
-def gateup_bytes(rows, active_experts, d, d_e, b):
-    """Read the permuted rows and W1, W3 of every expert with rows once; write act."""
-    return (rows * d + 2 * active_experts * d * d_e + rows * d_e) * b
+def gateup_bytes(rows, active_experts, d, d_e, b, wb=None):
+    """Read the permuted rows and W1, W3 of every expert with rows once; write act.
+    wb: bytes per weight (default b)."""
+    wb = b if wb is None else wb
+    return (rows * d + rows * d_e) * b + 2 * active_experts * d * d_e * wb
 
 
-def gateup_gather_bytes(T, rows, active_experts, d, d_e, b):
+def gateup_gather_bytes(T, rows, active_experts, d, d_e, b, wb=None):
     """Gate/up with the permute fused into its loads: read each token row of x once (the
     k gathered copies are re-reads of it), W1 and W3 of every expert with rows once;
     write act."""
-    return (T * d + 2 * active_experts * d * d_e + rows * d_e) * b
+    wb = b if wb is None else wb
+    return (T * d + rows * d_e) * b + 2 * active_experts * d * d_e * wb
 
 
-def shared_gateup_bytes(T, d, d_es, b, reads_x=True):
+def shared_gateup_bytes(T, d, d_es, b, reads_x=True, wb=None):
     """The shared expert's gate/up: x (unless the routed half already reads it), Ws1,
     Ws3; write its act."""
-    return ((T * d if reads_x else 0) + 2 * d * d_es + T * d_es) * b
+    wb = b if wb is None else wb
+    return ((T * d if reads_x else 0) + T * d_es) * b + 2 * d * d_es * wb
 
 
-def shared_down_bytes(T, d, d_es, b):
-    return (T * d_es + d_es * d + T * d) * b
+def shared_down_bytes(T, d, d_es, b, wb=None):
+    wb = b if wb is None else wb
+    return (T * d_es + T * d) * b + d_es * d * wb
 
 
-def down_bytes(rows, active_experts, d, d_e, b):
+def fp8_scale_bytes(matrices, K, N, block=128):
+    """fp32 scales of `matrices` fp8 weight matrices [K, N], one per block x block."""
+    return matrices * (-(-K // block)) * (-(-N // block)) * 4
+
+
+def down_bytes(rows, active_experts, d, d_e, b, wb=None):
     """Read act and W2 of every expert with rows once; write y."""
-    return (rows * d_e + active_experts * d_e * d + rows * d) * b
+    wb = b if wb is None else wb
+    return (rows * d_e + rows * d) * b + active_experts * d_e * d * wb
 
 
 def permute_bytes(T, k, d, b):

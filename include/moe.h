@@ -262,6 +262,63 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate,
                          size_t ws_bytes, void* stream);
 
 /*
+ * fp8 expert weights (dropless notes section 12: fp8 weights with a scale per
+ * quantisation block).  Format: OCP 8-bit floating point E4M3 ("e4m3fn": bias 7, no
+ * infinities, 0x7F / 0xFF are NaN, largest finite value 448), one byte per weight in
+ * the bf16 weight's [E, K, N] layout; one fp32 scale per 128 x 128 block,
+ * scales[E][ceil(K/128)][ceil(N/128)].  The weight is code value * scale.
+ */
+
+/*
+ * Quantise bf16 expert matrices w [E, K, N] to fp8: per 128 x 128 block (partial at
+ * the edges), scale = amax / 448 in fp32 (1 for an all-zero block), code =
+ * clamp(w / scale, -448, 448) in fp32, rounded to the nearest e4m3 value (ties to
+ * even).  Requires N % 8 == 0; q 8-byte aligned, w 16-byte aligned.
+ * Out: q [E, K, N] uint8, scales [E, ceil(K/128), ceil(N/128)] fp32.
+ * Errors: MOE_EINVAL for bad sizes or pointers; nothing is launched then.
+ */
+moe_status moe_quantize_fp8(int32_t E, int32_t K, int32_t N, const void* w, uint8_t* q,
+                            float* scales, void* stream);
+
+/*
+ * The grouped GEMM (as moe_grouped_gemm, one op per call) with fp8 weights:
+ * B0 / B1 are (Q0, S0) / (Q1, S1) code and scale arrays of W1 / W3 (gate/up) or W2
+ * (down: Q1 = S1 = NULL).  Each 16-deep weight fragment is dequantised to bf16
+ * (code * scale, rounded to nearest even) just before the bf16 MFMA; accumulation and
+ * the epilogue are fp32, outputs bf16.
+ * row_src: NULL (A is x_perm) or, for op == MOE_OP_GATEUP_SWIGLU only, the
+ * permutation, so that A is x [T, d] and row r reads x[row_src[r] / k] (the permute
+ * fused into the loads, as moe_grouped_gemm_gather).
+ * A_shared, Q0_shared, S0_shared, Q1_shared, S1_shared, C_shared: all NULL, or the
+ * shared expert (needs d_e_shared > 0) as moe_grouped_gemm_shared's second half.
+ * Requires dtype bf16, block_m == 128, d and d_e (and d_e_shared) multiples of 32,
+ * at most 32768 (else MOE_ENOTSUP); the block table as for moe_grouped_gemm.
+ */
+moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A,
+                                const uint8_t* Q0, const float* S0, const uint8_t* Q1,
+                                const float* S1, const int32_t* block_meta,
+                                const int32_t* num_blocks, int32_t max_blocks,
+                                const int32_t* row_src, void* C, const void* A_shared,
+                                const uint8_t* Q0_shared, const float* S0_shared,
+                                const uint8_t* Q1_shared, const float* S1_shared,
+                                void* C_shared, void* stream);
+
+/*
+ * moe_layer_fwd with fp8 weights: (q1, s1), (q3, s3), (q2, s2) replace w1, w3, w2 and
+ * (qs1, ss1), (qs3, ss3), (qs2, ss2) the shared expert's (NULLs when d_e_shared == 0).
+ * Same workspace (moe_workspace_bytes), same pipeline and requirements as
+ * moe_grouped_gemm_fp8.
+ */
+moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_gate,
+                             const float* bias, const uint8_t* q1, const float* s1,
+                             const uint8_t* q3, const float* s3, const uint8_t* q2,
+                             const float* s2, const uint8_t* qs1, const float* ss1,
+                             const uint8_t* qs3, const float* ss3, const uint8_t* qs2,
+                             const float* ss2, const int32_t* topk_idx_in,
+                             const float* topk_w_in, void* out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * Byte offsets of the intermediates inside the moe_layer_fwd workspace, so that a
  * caller (tests, profilers) can inspect them after a call.  Host-only and pure.
  * Each field is an offset from the workspace base; a field is 0-sized when unused.

@@ -21,7 +21,7 @@ FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced (validation f
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -261,3 +261,42 @@ def test_grouped_gemm_gather_argument_rules():
     assert g(ps2, *([FAKE] * 6), 1, FAKE, None, None, None, None) == B.MOE_EINVAL
     sT = good_shape(T=0)
     assert g(ctypes.byref(sT), *([FAKE] * 6), 0, FAKE, None, None, None, None) == B.MOE_EINVAL
+
+
+def test_fp8_entry_point_argument_rules():
+    """fp8 weights: bf16 activations with 128-row blocks only; codes/scales pairs per
+    op; shared-expert operands all or nothing; bad sizes rejected before any launch."""
+    L = B.lib()
+    q = L.moe_quantize_fp8
+    assert q(0, 128, 128, FAKE, FAKE, FAKE, None) == B.MOE_EINVAL
+    assert q(1, 128, 12, FAKE, FAKE, FAKE, None) == B.MOE_EINVAL          # N % 8
+    assert q(1, 128, 128, None, FAKE, FAKE, None) == B.MOE_EINVAL
+    assert q(1, 128, 128, FAKE, ctypes.c_void_p(0x10004), FAKE, None) == B.MOE_EINVAL
+    g = L.moe_grouped_gemm_fp8
+    s = good_shape()
+    ps = ctypes.byref(s)
+    mb = L.moe_max_blocks(ps)
+    n6 = [None] * 6
+    # fp32 activations, or 256-row blocks: not supported
+    for bad in (good_shape(dtype="fp32", block_m=128), good_shape(block_m=256), good_shape(d=272)):
+        assert g(ctypes.byref(bad), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE,
+                 *n6, None) == B.MOE_ENOTSUP
+    assert B.fp8_supported(s) and not B.fp8_supported(good_shape(d=272))
+    ok = lambda op, *a: g(ps, op, *a, None)
+    assert ok(0, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, None, FAKE, *n6) == B.MOE_EINVAL
+    assert ok(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, *n6) == B.MOE_EINVAL
+    assert ok(0, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, *n6) == B.MOE_EINVAL
+    assert ok(1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, mb + 1, None, FAKE, *n6) == B.MOE_EINVAL
+    assert ok(1, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, FAKE, FAKE, *n6) == B.MOE_EINVAL  # gather on down
+    # shared operands with no shared expert in the shape
+    assert ok(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE,
+              FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    lf = L.moe_layer_fwd_fp8
+    need = L.moe_workspace_bytes(ps)
+    # no router weights and no given routes; and a shared-expert pointer without one
+    assert lf(ps, FAKE, None, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE, need,
+              None) == B.MOE_EINVAL
+    assert lf(ps, FAKE, FAKE, None, *([FAKE] * 6), FAKE, *([None] * 5), None, None, FAKE, FAKE,
+              need, None) == B.MOE_EINVAL
+    assert lf(ps, FAKE, FAKE, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE,
+              need - 1, None) == B.MOE_EWORKSPACE

@@ -1,0 +1,167 @@
+"""fp8 (e4m3) expert weights on the GPU, through the C ABI, against the fp8 oracle.
+
+  * the quantiser's codes and scales are integers / fp32 values decided in fp32 on both
+    sides: bit-exact;
+  * a grouped-GEMM stage with fp8 weights is compared with the fp64 product by the
+    exactly dequantised weights.  The device rounds each dequantised weight to bf16
+    (<= 2^-9 relative) before the MFMA and rounds its output to bf16 (<= 2^-9), with
+    fp32 accumulation in between; with random signs the weight roundings add up like
+    a random walk, well inside 1e-2 * max|ref| (TOL_STAGE_FP8);
+  * the layer output keeps the stated bound 2e-2 * max|ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from dropless_grouped_gemm_amd import binding as B
+from oracle import fp8_oracle as F
+from oracle import moe_oracle as O
+from workloads import get_config, make_inputs
+
+from gpu_util import TOL_OUT, assert_close, f64, i64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL_STAGE_FP8 = 1e-2
+
+
+@pytest.mark.parametrize("E,K,N", [(2, 300, 200), (3, 256, 384), (1, 7168, 256), (4, 128, 8)])
+def test_quantize_is_bit_exact(E, K, N):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(E * 1000 + K + N)
+    w = (torch.randn((E, K, N), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+    if K >= 256 and N >= 128:
+        w[0, 128:256, 0:128] = 0                       # an all-zero block
+        w[-1, 3, 5] = 30.0                             # one large weight in a block
+        w[-1, 4, 6] = -1e-30                           # a value that flushes to a zero code
+    q, s = B.quantize_fp8(w)
+    torch.cuda.synchronize()
+    rq, rs = F.quantize(w.float().cpu().numpy())
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+def _routes(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, E, size=(T, k))
+
+
+@pytest.mark.parametrize("T,d,E,k,d_e,d_es", [
+    (200, 512, 8, 2, 256, 256),      # shared expert in the same launch
+    (64, 1024, 16, 4, 128, 0),       # decode-like: few rows per expert
+    (150, 256, 4, 2, 384, 128),      # shared expert in launches of its own; ragged n-blocks
+    (40, 1280, 3, 3, 160, 0),        # partial 128-blocks in both k and n
+])
+def test_grouped_gemm_fp8_against_oracle(T, d, E, k, d_e, d_es):
+    idx = _routes(T, E, k, T + d)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T + d_e)
+    dt = torch.bfloat16
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    (q1, s1), (q3, s3), (q2, s2) = B.quantize_fp8(w1), B.quantize_fp8(w3), B.quantize_fp8(w2)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16", d_e_shared=d_es)
+    assert B.fp8_supported(s)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    ws = B.alloc_workspace(s)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    x_perm = torch.empty((rows, d), dtype=dt, device=DEV)
+    B.moe_permute(s, x, pos, x_perm)
+    e = lambda *sh: torch.empty(sh, dtype=dt, device=DEV)
+    act, act_g, y = e(rows, d_e), e(rows, d_e), e(rows, d)
+    sh = {}
+    if d_es:
+        ws1 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+        ws3 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+        ws2 = (torch.randn((d_es, d), generator=g, device=DEV) / d_es ** 0.5).to(dt)
+        (qa, sa), (qb, sb), (qc, sc) = B.quantize_fp8(ws1), B.quantize_fp8(ws3), B.quantize_fp8(ws2)
+        sact, sact_g, sout = e(T, d_es), e(T, d_es), e(T, d)
+        B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, q1, s1, q3, s3, meta, nblk, mb,
+                               None, act, x, qa, sa, qb, sb, sact)
+        B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, x, q1, s1, q3, s3, meta, nblk, mb,
+                               row_src, act_g, x, qa, sa, qb, sb, sact_g)
+        B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, q2, s2, None, None, meta, nblk, mb, None, y,
+                               sact, qc, sc, None, None, sout)
+    else:
+        B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, q1, s1, q3, s3, meta, nblk, mb,
+                               None, act)
+        B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, x, q1, s1, q3, s3, meta, nblk, mb,
+                               row_src, act_g)
+        B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, q2, s2, None, None, meta, nblk, mb, None, y)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref_pos, ref_src = O.permutation(idx, E, 128)
+    valid = np.nonzero(ref_src >= 0)[0]
+    dv = torch.from_numpy(valid).to(DEV)
+    # the fused gather is the same arithmetic on the same rows: bit-exact
+    assert torch.equal(act[dv].view(torch.int16), act_g[dv].view(torch.int16))
+    c = O.expert_counts(idx, E)
+    xp_ref = O.permute(f64(x), ref_pos, k, len(ref_src))
+    def dq(qq, ss):
+        qn, sn = qq.cpu().numpy(), ss.cpu().numpy()
+        return F.dequantize(qn.reshape((-1,) + qn.shape[-2:]), sn.reshape((-1,) + sn.shape[-2:]))
+    W1, W3, W2 = dq(q1, s1), dq(q3, s3), dq(q2, s2)
+    act_ref, _ = O.grouped_ffn(xp_ref, c, 128, W1, W3, W2)
+    assert_close(f64(act)[valid], act_ref[valid], TOL_STAGE_FP8, "act")
+    # down on the device's own act
+    act_dev = f64(act)
+    P = O.padded_offsets(c, 128)
+    y_ref = np.zeros((len(ref_src), d))
+    for ex in range(E):
+        lo, hi = P[ex], P[ex] + c[ex]
+        y_ref[lo:hi] = act_dev[lo:hi] @ W2[ex]
+    assert_close(f64(y)[valid], y_ref[valid], TOL_STAGE_FP8, "y")
+    if d_es:
+        assert torch.equal(sact.view(torch.int16), sact_g.view(torch.int16))
+        Ws1, Ws3, Ws2 = (dq(qa, sa)[0], dq(qb, sb)[0], dq(qc, sc)[0])
+        assert_close(f64(sact), O.swiglu_act(f64(x), Ws1, Ws3), TOL_STAGE_FP8, "shared act")
+        assert_close(f64(sout), f64(sact) @ Ws2, TOL_STAGE_FP8, "shared out")
+
+
+@pytest.mark.parametrize("name,scale", [
+    ("decode-256x2048", dict(name="decode-fp8-r", d=512, d_e=256, d_e_shared=256)),
+    ("fusedmoe-8x2048", dict(name="fusedmoe-fp8-r", T=600, d=1024, d_e=384, d_e_shared=256)),
+    ("ep-share-4x2048", dict(name="ep-share-fp8-r", T=512, d=1024, d_e=256,
+                             fixed_counts=(1357, 938, 1124, 677))),
+])
+def test_layer_fwd_fp8(name, scale):
+    """The layer with fp8 weights against the oracle layer evaluated with the exactly
+    dequantised weights, at the stated output bound."""
+    cfg = get_config(name).scaled(**scale)
+    torch.manual_seed(0)
+    inp = make_inputs(cfg, device=DEV)
+    s = B.shape_of_config(cfg)
+    qz = [B.quantize_fp8(w) for w in (inp.w1, inp.w3, inp.w2)]
+    qs = [B.quantize_fp8(w) for w in (inp.ws1, inp.ws3, inp.ws2)] if cfg.d_e_shared else [(None, None)] * 3
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=DEV)
+    ws = B.alloc_workspace(s)
+    routed = inp.topk_idx is not None
+    B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *qz[0], *qz[1], *qz[2], *qs[0], *qs[1],
+                        *qs[2], inp.topk_idx if routed else None, inp.topk_w if routed else None,
+                        out, ws)
+    torch.cuda.synchronize()
+    dq = lambda p: None if p[0] is None else F.dequantize(
+        p[0].cpu().numpy().reshape((-1,) + tuple(p[0].shape[-2:])),
+        p[1].cpu().numpy().reshape((-1,) + tuple(p[1].shape[-2:])))
+    W1, W3, W2 = (dq(p) for p in qz)
+    Ws = [dq(p) for p in qs]
+    kw = dict(k=cfg.k, block_m=cfg.block_m)
+    if cfg.d_e_shared:
+        kw.update(ws1=Ws[0][0], ws3=Ws[1][0], ws2=Ws[2][0])
+    xh = f64(inp.x)
+    if routed:
+        ref = O.moe_layer(xh, W1, W3, W2, topk_idx=i64(inp.topk_idx), topk_w=f64(inp.topk_w), **kw)
+    else:
+        logits = B.ws_view(ws, s, "logits", torch.float32, (cfg.T, cfg.E)).cpu().numpy()
+        ref = O.moe_layer(xh, W1, W3, W2, w_gate=f64(inp.w_gate),
+                          bias=None if inp.bias is None else f64(inp.bias),
+                          n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                          renormalize=cfg.renormalize, decision_logits=logits, **kw)
+    rel = assert_close(f64(out), ref.out, TOL_OUT["bf16"], "out")
+    print(f"[fp8 parity] {cfg.name}: out max|d|/max|ref| = {rel:.2e}")
