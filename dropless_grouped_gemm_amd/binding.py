@@ -25,7 +25,9 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
                 "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_grouped_gemm_gather",
                 "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_grouped_gemm_fp8",
-                "moe_layer_fwd_fp8")
+                "moe_layer_fwd_fp8", "moe_combine_bwd", "moe_swiglu_bwd", "moe_grouped_gemm_dgrad",
+                "moe_grouped_gemm_wgrad", "moe_router_bwd", "moe_bwd_workspace_bytes",
+                "moe_bwd_workspace_layout", "moe_layer_bwd")
 
 
 class moe_shape(ctypes.Structure):
@@ -41,6 +43,14 @@ _LAYOUT_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "padded_o
 
 class moe_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in _LAYOUT_FIELDS]
+
+
+_BWD_LAYOUT_FIELDS = ("dy", "dact", "dgu", "x_perm", "dx_perm", "dtopk_w", "dlogits",
+                      "shared_dact", "shared_dgu", "shared_dx", "router_dx", "total")
+
+
+class moe_bwd_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in _BWD_LAYOUT_FIELDS]
 
 
 class MoEError(RuntimeError):
@@ -96,6 +106,23 @@ def lib():
         L.moe_combine.restype = ctypes.c_int32
         L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_layer_fwd.restype = ctypes.c_int32
+        L.moe_combine_bwd.argtypes = [S, P, P, P, P, P, P, P]
+        L.moe_combine_bwd.restype = ctypes.c_int32
+        L.moe_swiglu_bwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P]
+        L.moe_swiglu_bwd.restype = ctypes.c_int32
+        L.moe_grouped_gemm_dgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
+        L.moe_grouped_gemm_dgrad.restype = ctypes.c_int32
+        L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P]
+        L.moe_grouped_gemm_wgrad.restype = ctypes.c_int32
+        L.moe_router_bwd.argtypes = [S] + [P] * 11
+        L.moe_router_bwd.restype = ctypes.c_int32
+        L.moe_bwd_workspace_bytes.argtypes = [S]
+        L.moe_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_bwd_workspace_layout.argtypes = [S, ctypes.POINTER(moe_bwd_ws_layout)]
+        L.moe_bwd_workspace_layout.restype = ctypes.c_int32
+        L.moe_layer_bwd.argtypes = ([S] + [P] * 12 + [ctypes.c_size_t] + [P] * 11 +
+                                    [ctypes.c_size_t, P])
+        L.moe_layer_bwd.restype = ctypes.c_int32
         _lib = L
     return _lib
 
@@ -282,4 +309,87 @@ def moe_layer_fwd(shape, x, w_gate, bias, w1, w3, w2, ws1, ws3, ws2, topk_idx_in
     _check("moe_layer_fwd", lib().moe_layer_fwd(
         ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2), _p(ws1),
         _p(ws3), _p(ws2), _p(topk_idx_in), _p(topk_w_in), _p(out), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+def moe_bwd_workspace_bytes(shape: moe_shape) -> int:
+    return lib().moe_bwd_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_bwd_workspace_layout(shape: moe_shape) -> dict:
+    L = moe_bwd_ws_layout()
+    _check("moe_bwd_workspace_layout",
+           lib().moe_bwd_workspace_layout(ctypes.byref(shape), ctypes.byref(L)))
+    return {n: getattr(L, n) for n in _BWD_LAYOUT_FIELDS}
+
+
+def alloc_bwd_workspace(shape: moe_shape, device="cuda") -> torch.Tensor:
+    if moe_max_blocks(shape) < 0:                 # invalid shape
+        raise MoEError("moe_bwd_workspace_bytes", MOE_EINVAL)
+    n = moe_bwd_workspace_bytes(shape)            # 0 for T == 0: nothing to hold
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def bwd_ws_view(ws: torch.Tensor, shape: moe_shape, name: str, dtype: torch.dtype, shape_out):
+    """A typed view of one intermediate inside a moe_layer_bwd workspace."""
+    off = moe_bwd_workspace_layout(shape)[name]
+    n = 1
+    for v in shape_out:
+        n *= v
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype).view(*shape_out)
+
+
+def backward_supported(shape) -> bool:
+    """The backward kernels' conditions (mirrors the library's own checks)."""
+    return (shape.dtype == MOE_DTYPE_BF16 and shape.d % 32 == 0 and shape.d_e % 32 == 0
+            and shape.d_e_shared % 32 == 0 and shape.d <= 8192)
+
+
+def moe_combine_bwd(shape, dout, y, pos, topk_w, dy, dtopk_w, stream=None):
+    _check("moe_combine_bwd", lib().moe_combine_bwd(
+        ctypes.byref(shape), _p(dout), _p(y), _p(pos), _p(topk_w), _p(dy), _p(dtopk_w),
+        _stream(stream)))
+
+
+def moe_swiglu_bwd(shape, A, row_src, w1, w3, dact, block_meta, num_blocks, max_blocks, dgu,
+                   x_shared=None, ws1=None, ws3=None, dact_shared=None, dgu_shared=None,
+                   stream=None):
+    _check("moe_swiglu_bwd", lib().moe_swiglu_bwd(
+        ctypes.byref(shape), _p(A), _p(row_src), _p(w1), _p(w3), _p(dact), _p(block_meta),
+        _p(num_blocks), max_blocks, _p(dgu), _p(x_shared), _p(ws1), _p(ws3), _p(dact_shared),
+        _p(dgu_shared), _stream(stream)))
+
+
+def moe_grouped_gemm_dgrad(shape, op, dC, B0, B1, block_meta, num_blocks, max_blocks, dA,
+                           stream=None):
+    _check("moe_grouped_gemm_dgrad", lib().moe_grouped_gemm_dgrad(
+        ctypes.byref(shape), op, _p(dC), _p(B0), _p(B1), _p(block_meta), _p(num_blocks),
+        max_blocks, _p(dA), _stream(stream)))
+
+
+def moe_grouped_gemm_wgrad(shape, op, A, dC, counts, padded_offsets, dB0, dB1, stream=None):
+    _check("moe_grouped_gemm_wgrad", lib().moe_grouped_gemm_wgrad(
+        ctypes.byref(shape), op, _p(A), _p(dC), _p(counts), _p(padded_offsets), _p(dB0),
+        _p(dB1), _stream(stream)))
+
+
+def moe_router_bwd(shape, x, w_gate, logits, topk_idx, dtopk_w, dlogits, dw_gate, dbias, dx_in,
+                   dx_out, stream=None):
+    _check("moe_router_bwd", lib().moe_router_bwd(
+        ctypes.byref(shape), _p(x), _p(w_gate), _p(logits), _p(topk_idx), _p(dtopk_w),
+        _p(dlogits), _p(dw_gate), _p(dbias), _p(dx_in), _p(dx_out), _stream(stream)))
+
+
+def moe_layer_bwd(shape, x, w_gate, w1, w3, w2, ws1, ws3, ws2, topk_idx_in, topk_w_in, dout,
+                  fwd_ws, dx, dw1, dw3, dw2, dws1, dws3, dws2, dw_gate, dbias, dtopk_w, ws,
+                  stream=None):
+    _check("moe_layer_bwd", lib().moe_layer_bwd(
+        ctypes.byref(shape), _p(x), _p(w_gate), _p(w1), _p(w3), _p(w2), _p(ws1), _p(ws3),
+        _p(ws2), _p(topk_idx_in), _p(topk_w_in), _p(dout), _p(fwd_ws),
+        fwd_ws.numel() if fwd_ws is not None else 0, _p(dx), _p(dw1), _p(dw3), _p(dw2),
+        _p(dws1), _p(dws3), _p(dws2), _p(dw_gate), _p(dbias), _p(dtopk_w), _p(ws),
         ws.numel() if ws is not None else 0, _stream(stream)))

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_api.hip", "moe_route.hip", "moe_offsets.hip", "moe_permute.hip", "moe_gemm.hip", "moe_gemm_wide.hip", "moe_fp8.hip"]
+SOURCES = ["moe_api.hip", "moe_route.hip", "moe_offsets.hip", "moe_permute.hip", "moe_gemm.hip", "moe_gemm_wide.hip", "moe_fp8.hip", "moe_backward.hip"]
 
 
 def hipcc() -> str:

@@ -114,6 +114,32 @@ static void layout_of(const moe_shape& s, moe_ws_layout& L) {
   L.total = cur;
 }
 
+// The backward kernels: bf16, contraction sizes in whole 32-deep slices.
+static moe_status check_bwd(const moe_shape& s) {
+  if (s.dtype != MOE_DTYPE_BF16) return MOE_ENOTSUP;
+  if (s.d % 32 || s.d_e % 32 || s.d_e_shared % 32) return MOE_ENOTSUP;
+  return MOE_OK;
+}
+
+static void bwd_layout_of(const moe_shape& s, moe_bwd_ws_layout& L) {
+  const size_t T = s.T, E = s.E, M = (size_t)s.T * s.k;
+  const size_t rows = (size_t)max_blocks_of(s) * s.block_m;
+  const size_t d = s.d, de = s.d_e, ds = s.d_e_shared;
+  size_t cur = 0;
+  L.dy = take(cur, rows * d * 2);
+  L.dact = take(cur, rows * de * 2);
+  L.dgu = take(cur, rows * 2 * de * 2);
+  L.x_perm = take(cur, rows * d * 2);
+  L.dx_perm = take(cur, rows * d * 2);
+  L.dtopk_w = take(cur, M * 4);
+  L.dlogits = take(cur, T * E * 4);
+  L.shared_dact = take(cur, T * ds * 2);
+  L.shared_dgu = take(cur, T * 2 * ds * 2);
+  L.shared_dx = take(cur, ds ? T * d * 2 : 0);
+  L.router_dx = take(cur, T * d * 2);
+  L.total = cur;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -438,8 +464,8 @@ moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos, co
                        const void* shared_out, void* out, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (!y || !pos || !topk_w || !out) return MOE_EINVAL;
-  if (!aligned16(y) || !aligned16(out) || !aligned4(pos) || !aligned4(topk_w) ||
+  if (!y || !pos || !out) return MOE_EINVAL;
+  if (!aligned16(y) || !aligned16(out) || !aligned4(pos) || (topk_w && !aligned4(topk_w)) ||
       (shared_out && !aligned16(shared_out)))
     return MOE_EINVAL;
   if (s->T == 0) return MOE_OK;
@@ -515,6 +541,254 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
   if (st != MOE_OK) return st;
   const void* sh = shared ? at(L.shared_out) : nullptr;
   return launch_combine(*s, at(L.y), pos, wts, sh, out, hs);
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+moe_status moe_combine_bwd(const moe_shape* s, const void* dout, const void* y,
+                           const int32_t* pos, const float* topk_w, void* dy, float* dtopk_w,
+                           void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_bwd(*s)) != MOE_OK) return st;
+  if (s->d > 8192) return MOE_ENOTSUP;
+  if (!dout || !y || !pos || !topk_w || !dy || !dtopk_w) return MOE_EINVAL;
+  if (!aligned16(dout) || !aligned16(y) || !aligned16(dy) || !aligned4(pos) ||
+      !aligned4(topk_w) || !aligned4(dtopk_w))
+    return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  return launch_combine_bwd(*s, dout, y, pos, topk_w, dy, dtopk_w, max_blocks_of(*s) * s->block_m,
+                            static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_swiglu_bwd(const moe_shape* s, const void* A, const int32_t* row_src,
+                          const void* w1, const void* w3, const void* dact,
+                          const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
+                          void* dgu, const void* x_shared, const void* ws1, const void* ws3,
+                          const void* dact_shared, void* dgu_shared, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_bwd(*s)) != MOE_OK) return st;
+  if (!gemm_operands_ok(MOE_OP_GATEUP_SWIGLU, A, w1, w3, dgu) || !dact || !aligned16(dact))
+    return MOE_EINVAL;
+  if (!block_table_ok(*s, block_meta, num_blocks, max_blocks)) return MOE_EINVAL;
+  if (row_src) {
+    if (!aligned4(row_src)) return MOE_EINVAL;
+    if (!gather_supported(*s)) return MOE_ENOTSUP;
+  }
+  const bool shared = x_shared || ws1 || ws3 || dact_shared || dgu_shared;
+  if (shared) {
+    if (s->d_e_shared <= 0) return MOE_EINVAL;
+    if (!gemm_operands_ok(MOE_OP_GATEUP_SWIGLU, x_shared, ws1, ws3, dgu_shared) || !dact_shared ||
+        !aligned16(dact_shared))
+      return MOE_EINVAL;
+  }
+  if (s->T == 0) return MOE_OK;
+  GemmSegments g{A, w1, w3, dgu, s->d, s->d_e, block_meta, num_blocks, max_blocks,
+                 shared ? x_shared : nullptr, ws1, ws3, dgu_shared, s->d, s->d_e_shared,
+                 shared ? s->T : 0, row_src, s->k, s->T, dact, dact_shared};
+  return launch_grouped_gemm(*s, kOpGateUpBwd, g, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC, const void* B0,
+                                  const void* B1, const int32_t* block_meta,
+                                  const int32_t* num_blocks, int32_t max_blocks, void* dA,
+                                  void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_bwd(*s)) != MOE_OK) return st;
+  if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
+  if (!gemm_operands_ok(op, dC, B0, B1, dA)) return MOE_EINVAL;
+  const bool dense = !block_meta && !num_blocks;
+  if (dense ? max_blocks != 0 : !block_table_ok(*s, block_meta, num_blocks, max_blocks))
+    return MOE_EINVAL;
+  if (s->T == 0) return MOE_OK;
+  const bool gu = op == MOE_OP_GATEUP_SWIGLU;
+  const int K = gu ? 2 * s->d_e : s->d, N = gu ? s->d : s->d_e;
+  const int ldb = gu ? s->d_e : s->d;
+  return launch_gg_nt(dC, B0, B1, ldb, gu ? s->d_e : K, dA, K, N, block_meta, num_blocks,
+                      dense ? 0 : max_blocks, dense ? 1 : s->E, s->block_m, dense ? s->T : 0,
+                      static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A, const void* dC,
+                                  const int32_t* counts, const int32_t* padded_offsets, float* dB0,
+                                  float* dB1, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_bwd(*s)) != MOE_OK) return st;
+  if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
+  const bool gu = op == MOE_OP_GATEUP_SWIGLU;
+  if (!A || !dC || !dB0 || (gu && !dB1) || (!gu && dB1)) return MOE_EINVAL;
+  if (!aligned16(A) || !aligned16(dC) || !aligned4(dB0) || (dB1 && !aligned4(dB1)))
+    return MOE_EINVAL;
+  if ((counts == nullptr) != (padded_offsets == nullptr)) return MOE_EINVAL;
+  if (counts && (!aligned4(counts) || !aligned4(padded_offsets))) return MOE_EINVAL;
+  const bool dense = counts == nullptr;
+  const int Km = gu ? s->d : s->d_e, Nn = gu ? 2 * s->d_e : s->d;
+  // T == 0 still writes the (zero) gradients: the counts are not read then
+  return launch_gg_wgrad(A, dC, dB0, dB1, gu ? s->d_e : Nn, Km, Nn, s->T > 0 ? counts : nullptr,
+                         padded_offsets, dense ? 1 : s->E, dense ? s->T : 0,
+                         static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
+                          const float* logits, const int32_t* topk_idx, const float* dtopk_w,
+                          float* dlogits, float* dw_gate, float* dbias, const void* dx_in,
+                          void* dx_out, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_bwd(*s)) != MOE_OK) return st;
+  if (!x || !w_gate || !logits || !topk_idx || !dtopk_w || !dlogits || !dw_gate || !dx_out)
+    return MOE_EINVAL;
+  if (!aligned16(x) || !aligned4(w_gate) || !aligned4(logits) || !aligned4(topk_idx) ||
+      !aligned4(dtopk_w) || !aligned4(dlogits) || !aligned4(dw_gate) || (dbias && !aligned4(dbias)) ||
+      (dx_in && !aligned16(dx_in)) || !aligned16(dx_out))
+    return MOE_EINVAL;
+  return launch_router_bwd(*s, x, w_gate, logits, topk_idx, dtopk_w, dlogits, dw_gate, dbias, dx_in,
+                           dx_out, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_bwd_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  moe_bwd_ws_layout L;
+  bwd_layout_of(*s, L);
+  return L.total;
+}
+
+moe_status moe_bwd_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!layout) return MOE_EINVAL;
+  bwd_layout_of(*s, *layout);
+  return MOE_OK;
+}
+
+moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, const void* w1,
+                         const void* w3, const void* w2, const void* ws1, const void* ws3,
+                         const void* ws2, const int32_t* topk_idx_in, const float* topk_w_in,
+                         const void* dout, const void* fwd_ws, size_t fwd_ws_bytes, void* dx,
+                         float* dw1, float* dw3, float* dw2, float* dws1, float* dws3, float* dws2,
+                         float* dw_gate, float* dbias, float* dtopk_w, void* ws, size_t ws_bytes,
+                         void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if ((st = check_bwd(*s)) != MOE_OK) return st;
+  if (s->d > 8192) return MOE_ENOTSUP;
+  const bool routed = topk_idx_in && topk_w_in;
+  if ((topk_idx_in != nullptr) != (topk_w_in != nullptr)) return MOE_EINVAL;
+  if (!routed && !w_gate) return MOE_EINVAL;
+  if (routed && (dw_gate || dbias)) return MOE_EINVAL;
+  const bool shared = s->d_e_shared > 0;
+  const void* p16[] = {x, w1, w3, w2, dout, dx};
+  for (const void* p : p16)
+    if (!p || !aligned16(p)) return MOE_EINVAL;
+  float* f4[] = {dw1, dw3, dw2};
+  for (float* p : f4)
+    if (!p || !aligned4(p)) return MOE_EINVAL;
+  if (shared) {
+    const void* sp[] = {ws1, ws3, ws2};
+    for (const void* p : sp)
+      if (!p || !aligned16(p)) return MOE_EINVAL;
+    float* sg[] = {dws1, dws3, dws2};
+    for (float* p : sg)
+      if (!p || !aligned4(p)) return MOE_EINVAL;
+  } else if (ws1 || ws3 || ws2 || dws1 || dws3 || dws2) {
+    return MOE_EINVAL;
+  }
+  if ((w_gate && !aligned4(w_gate)) || (dw_gate && !aligned4(dw_gate)) ||
+      (dbias && !aligned4(dbias)) || (dtopk_w && !aligned4(dtopk_w)) ||
+      (topk_idx_in && !aligned4(topk_idx_in)) || (topk_w_in && !aligned4(topk_w_in)))
+    return MOE_EINVAL;
+  moe_ws_layout F;
+  layout_of(*s, F);
+  if (!fwd_ws || !aligned16(fwd_ws) || fwd_ws_bytes < F.total) return MOE_EWORKSPACE;
+  moe_bwd_ws_layout L;
+  bwd_layout_of(*s, L);
+  if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_EWORKSPACE;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int de = s->d_e, des = s->d_e_shared, d = s->d;
+  if (s->T == 0) {
+    // no rows: every weight gradient is zero
+    st = launch_gg_wgrad(x, x, dw1, dw3, de, d, 2 * de, nullptr, nullptr, s->E, 0, hs);
+    if (st == MOE_OK) st = launch_gg_wgrad(x, x, dw2, nullptr, d, de, d, nullptr, nullptr, s->E, 0, hs);
+    if (st == MOE_OK && shared)
+      st = launch_gg_wgrad(x, x, dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1, 0, hs);
+    if (st == MOE_OK && shared)
+      st = launch_gg_wgrad(x, x, dws2, nullptr, d, des, d, nullptr, nullptr, 1, 0, hs);
+    if (st == MOE_OK && (dw_gate || dbias))
+      st = launch_router_bwd(*s, x, w_gate, nullptr, nullptr, nullptr, nullptr, dw_gate, dbias,
+                             nullptr, dx, hs);
+    return st;
+  }
+  const char* fb = static_cast<const char*>(fwd_ws);
+  auto fat = [&](size_t off) { return static_cast<const void*>(fb + off); };
+  char* base = static_cast<char*>(ws);
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  const int32_t* idx = routed ? topk_idx_in : static_cast<const int32_t*>(fat(F.topk_idx));
+  const float* wts = routed ? topk_w_in : static_cast<const float*>(fat(F.topk_w));
+  const int32_t* counts = static_cast<const int32_t*>(fat(F.counts));
+  const int32_t* padded = static_cast<const int32_t*>(fat(F.padded_offsets));
+  const int32_t* meta = static_cast<const int32_t*>(fat(F.block_meta));
+  const int32_t* nblk = static_cast<const int32_t*>(fat(F.num_blocks));
+  const int32_t* pos = static_cast<const int32_t*>(fat(F.pos));
+  const int32_t mb = (int32_t)max_blocks_of(*s);
+  float* dtw = dtopk_w ? dtopk_w : static_cast<float*>(at(L.dtopk_w));
+
+  // combine
+  st = launch_combine_bwd(*s, dout, fat(F.y), pos, wts, at(L.dy), dtw, (int64_t)mb * s->block_m, hs);
+  if (st != MOE_OK) return st;
+  // down: data and weight gradients (routed, then the shared expert on all tokens)
+  st = launch_gg_nt(at(L.dy), w2, nullptr, d, d, at(L.dact), d, de, meta, nblk, mb, s->E,
+                    s->block_m, 0, hs);
+  if (st != MOE_OK) return st;
+  st = launch_gg_wgrad(fat(F.act), at(L.dy), dw2, nullptr, d, de, d, counts, padded, s->E, 0, hs);
+  if (st != MOE_OK) return st;
+  if (shared) {
+    st = launch_gg_nt(dout, ws2, nullptr, d, d, at(L.shared_dact), d, des, nullptr, nullptr, 0, 1,
+                      s->block_m, s->T, hs);
+    if (st != MOE_OK) return st;
+    st = launch_gg_wgrad(fat(F.shared_act), dout, dws2, nullptr, d, des, d, nullptr, nullptr, 1,
+                         s->T, hs);
+    if (st != MOE_OK) return st;
+  }
+  // the weight gradients of gate/up reduce over x_perm's rows
+  st = launch_permute(*s, x, pos, at(L.x_perm), hs);
+  if (st != MOE_OK) return st;
+  // SwiGLU backward with the gate/up products recomputed (both sets in one launch
+  // when their sizes agree)
+  GemmSegments g{at(L.x_perm), w1, w3, at(L.dgu), d, de, meta, nblk, mb,
+                 shared ? x : nullptr, ws1, ws3, shared ? at(L.shared_dgu) : nullptr, d, des,
+                 shared ? s->T : 0, nullptr, 1, 1, at(L.dact), shared ? at(L.shared_dact) : nullptr};
+  st = launch_grouped_gemm(*s, kOpGateUpBwd, g, hs);
+  if (st != MOE_OK) return st;
+  // gate/up: data and weight gradients
+  st = launch_gg_nt(at(L.dgu), w1, w3, de, de, at(L.dx_perm), 2 * de, d, meta, nblk, mb, s->E,
+                    s->block_m, 0, hs);
+  if (st != MOE_OK) return st;
+  st = launch_gg_wgrad(at(L.x_perm), at(L.dgu), dw1, dw3, de, d, 2 * de, counts, padded, s->E, 0, hs);
+  if (st != MOE_OK) return st;
+  if (shared) {
+    st = launch_gg_nt(at(L.shared_dgu), ws1, ws3, des, des, at(L.shared_dx), 2 * des, d, nullptr,
+                      nullptr, 0, 1, s->block_m, s->T, hs);
+    if (st != MOE_OK) return st;
+    st = launch_gg_wgrad(x, at(L.shared_dgu), dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1,
+                         s->T, hs);
+    if (st != MOE_OK) return st;
+  }
+  // router: dlogits, dW_g, dbias, and its dx term on top of the shared expert's
+  const void* extra = shared ? at(L.shared_dx) : nullptr;
+  if (!routed) {
+    st = launch_router_bwd(*s, x, w_gate, static_cast<const float*>(fat(F.logits)), idx, dtw,
+                           static_cast<float*>(at(L.dlogits)), dw_gate, dbias, extra,
+                           at(L.router_dx), hs);
+    if (st != MOE_OK) return st;
+    extra = at(L.router_dx);
+  }
+  // permute backward: dx[t] = sum_j dx_perm[pos[t, j]] (+ the rest)
+  return launch_combine(*s, at(L.dx_perm), pos, nullptr, extra, dx, hs);
 }
 
 }  // extern "C"

@@ -1,0 +1,651 @@
+// Backward pass of the dropless MoE layer (dropless notes: the gradients of grouped
+// GEMMs are grouped GEMMs over the same segments - data gradients through the
+// transposed weights, weight gradients reducing over each expert's rows - and the
+// permutation is replayed from the saved indices).  The chain rule step by step:
+//   combine   dy[pos[t,j]] = w[t,j] dout[t];  dw[t,j] = <dout[t], y[pos[t,j]]>
+//   down      dact = dy W2[e]^T                     (k_gg_nt, data gradient)
+//             dW2[e] = act_e^T dy_e                   (k_gg_wgrad)
+//   SwiGLU    gate/up recomputed, dg | du = SwiGLU'  (the forward kernels, op 2)
+//   gate/up   dx_perm = dg W1[e]^T + du W3[e]^T      (k_gg_nt over K = 2 d_e)
+//             dW1[e] | dW3[e] = x_perm_e^T (dg | du)  (k_gg_wgrad)
+//   permute   dx[t] = sum_j dx_perm[pos[t,j]]        (the combine kernel, unit weights)
+//   router    dlogits through the softmax (and renormalisation), selection fixed
+//             (k_router_bwd); dW_g = x^T dlogits, dbias = sum_t dlogits
+//             (k_router_wgrad); dx += dlogits W_g^T (k_router_dx)
+//
+// The GEMM kernels keep the 128-row kernel's structure (8 waves, 128 x 512 tiles,
+// four 40 KB ring slots of 32-deep slices filled by 16-byte global->LDS copies, fp32
+// accumulators of v_mfma_f32_32x32x16_bf16):
+//   * k_gg_nt: B is read transposed, i.e. the weight is stored [N][K] with K contiguous
+//     (W2[e] as [d_e][d]; W1[e], W3[e] as [d][d_e]), so B slices are staged exactly like
+//     A slices ([n][32 k], 64 bytes per row, chunk swizzle c ^ ((n >> 2) & 3)) and read
+//     with ds_read_b128.  The contraction may switch matrices at ksplit (dg | du against
+//     W1 | W3).
+//   * k_gg_wgrad: C[e] = X_e^T D_e, reducing over the expert's rows: both operands are
+//     row-major slices [32 rows][cols] in LDS, read with ds_read_b64_tr_b16 (X as the A
+//     operand, D as B).  Rows past the expert's count copy its first row and are zeroed
+//     in LDS by the wave that copied them once its copies have landed.  fp32 output;
+//     experts without rows get zeros.
+// No atomics anywhere: every output element has one writer and a fixed summation order.
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// combine backward
+// ---------------------------------------------------------------------------
+static constexpr int kCbWaves = 4;
+static constexpr int kCbVec = 16;   // 16-byte vectors per lane held (rows up to 8192 bf16)
+
+__global__ void __launch_bounds__(64 * kCbWaves)
+k_combine_bwd(const u32x4_t* __restrict__ dout, const u32x4_t* __restrict__ y,
+              const int32_t* __restrict__ pos, const float* __restrict__ w, int T, int k,
+              int nvec, int64_t max_rows, u32x4_t* __restrict__ dy, float* __restrict__ dw) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int t = blockIdx.x * kCbWaves + wave; t < T; t += gridDim.x * kCbWaves) {
+    float g[kCbVec][8];
+#pragma unroll
+    for (int i = 0; i < kCbVec; ++i) {
+      const int v = lane + 64 * i;
+      u32x4_t r = u32x4_t{0u, 0u, 0u, 0u};
+      if (v < nvec) r = dout[(size_t)t * nvec + v];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        g[i][2 * h] = __uint_as_float(r[h] << 16);
+        g[i][2 * h + 1] = __uint_as_float(r[h] & 0xffff0000u);
+      }
+    }
+    for (int j = 0; j < k; ++j) {
+      const int p = pos[(size_t)t * k + j];
+      const float wj = w[(size_t)t * k + j];
+      float dot = 0.f;
+      if (p >= 0 && p < max_rows) {
+#pragma unroll
+        for (int i = 0; i < kCbVec; ++i) {
+          const int v = lane + 64 * i;
+          if (v >= nvec) continue;
+          const u32x4_t r = y[(size_t)p * nvec + v];
+          u32x4_t o;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            dot = fmaf(g[i][2 * h], __uint_as_float(r[h] << 16), dot);
+            dot = fmaf(g[i][2 * h + 1], __uint_as_float(r[h] & 0xffff0000u), dot);
+            o[h] = pack_bf16x2(wj * g[i][2 * h], wj * g[i][2 * h + 1]);
+          }
+          dy[(size_t)p * nvec + v] = o;
+        }
+      }
+      // fixed-order butterfly: the same sum on every run
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+      if (lane == 0) dw[(size_t)t * k + j] = (p >= 0 && p < max_rows) ? dot : 0.f;
+    }
+  }
+}
+
+moe_status launch_combine_bwd(const moe_shape& s, const void* dout, const void* y,
+                              const int32_t* pos, const float* topk_w, void* dy, float* dw,
+                              int64_t max_rows, hipStream_t st) {
+  const int nvec = (int)((int64_t)s.d * 2 / 16);
+  if (nvec > 64 * kCbVec) return MOE_ENOTSUP;
+  int64_t blocks = ceil_div(s.T, kCbWaves);
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_combine_bwd, dim3((unsigned)blocks), dim3(64 * kCbWaves), 0, st,
+                     static_cast<const u32x4_t*>(dout), static_cast<const u32x4_t*>(y), pos, topk_w,
+                     s.T, s.k, nvec, max_rows, static_cast<u32x4_t*>(dy), dw);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// data-gradient grouped GEMM with transposed B
+// ---------------------------------------------------------------------------
+static constexpr int kBThreads = 512;
+static constexpr int kBBK = 32;
+static constexpr int kBABytes = 128 * kBBK * 2;      // 8 KB of A
+static constexpr int kBBBytes = 512 * kBBK * 2;      // 32 KB of B
+static constexpr int kBStage = kBABytes + kBBBytes;  // 40 KB
+static constexpr int kBStages = 4;
+static constexpr int kBCopies = 1 + 4;
+
+struct NTOperands {
+  const bf16_t* A;     // [rows, K]
+  const bf16_t* Bt0;   // per expert [N][ldb]: B[k][n] = Bt0[n][k] for k < ksplit
+  const bf16_t* Bt1;   // ... = Bt1[n][k - ksplit] for k >= ksplit (NULL: unused)
+  bf16_t* C;           // [rows, N]
+  int ldb, ksplit;
+};
+
+__global__ void __launch_bounds__(kBThreads, 1)
+k_gg_nt(NTOperands ops, int K, int N, const int32_t* __restrict__ meta,
+        const int32_t* __restrict__ num_blocks_ptr, int max_blocks, int E, int64_t max_rows,
+        int dense_rows, int block_m, int n_tiles) {
+  __shared__ __align__(1024) unsigned char lds[kBStages * kBStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // items: (block, 128-row sub-tile, 512-column tile); a dense set uses 128-row blocks
+  const int bm = dense_rows > 0 ? 128 : block_m;
+  const int nsub = bm / 128;
+  const int nblocks = dense_rows > 0 ? (dense_rows + 127) / 128 : min(num_blocks_ptr[0], max_blocks);
+  const int total = nblocks * nsub * n_tiles;
+  const int nk = K / kBBK;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int nt = w % n_tiles;
+    const int sub = (w / n_tiles) % nsub;
+    const int blk = w / (n_tiles * nsub);
+    Tile tile;
+    if (!decode_block(blk, sub, 128, bm, meta, dense_rows, E, max_rows, tile)) continue;
+    const int n0 = nt * 512;
+    const bf16_t* asrc = uniform_ptr(ops.A + (size_t)tile.m0 * K);
+    const bf16_t* bt0 = uniform_ptr(ops.Bt0 + (size_t)tile.e * N * ops.ldb);
+    const bf16_t* bt1 = uniform_ptr(ops.Bt1 ? ops.Bt1 + (size_t)tile.e * N * ops.ldb : bt0);
+    // the logical chunk of lane l in every 16-row window: (l & 3) ^ ((l >> 4) & 3)
+    const int c = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t a_voff;
+    {
+      const int row = wave * 16 + (lane >> 2);
+      const int rr = row < tile.valid ? row : 0;
+      a_voff = (uint32_t)(rr * K + c * 8) * 2u;
+    }
+    uint32_t b_voff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int n = n0 + (wave * 4 + p) * 16 + (lane >> 2);
+      const int nn = n < N ? n : 0;        // columns past N copy column 0
+      b_voff[p] = (uint32_t)(nn * ops.ldb + c * 8) * 2u;
+    }
+    auto issue_part_to = [&](int ks, int slot, int part) {
+      unsigned char* st = lds + slot * kBStage;
+      const int k0 = ks * kBBK;
+      if (part == 0) {
+        copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
+      } else {
+        const bool second = k0 >= ops.ksplit;
+        const bf16_t* base = (second ? bt1 : bt0) + (second ? k0 - ops.ksplit : k0);
+        copy16_to_lds(base, b_voff[part - 1], st + kBABytes + (wave * 4 + part - 1) * 1024);
+      }
+    };
+    auto issue = [&](int ks, int slot) {
+#pragma unroll
+      for (int part = 0; part < kBCopies; ++part) issue_part_to(ks, slot, part);
+    };
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    bf16x8_t af0[4], bf0[2], af1[4], bf1[2];
+    auto read_frags = [&](int stage, int kk, bf16x8_t* a, bf16x8_t* b) {
+      const unsigned char* sa = lds + stage * kBStage;
+      const unsigned char* sb = sa + kBABytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = wave * 64 + j * 32 + (lane & 31);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(sb + n * 64 + swz_a(n, kk * 2 + (lane >> 5)) * 16);
+      }
+    };
+    auto mfma_block = [&](const bf16x8_t* a, const bf16x8_t* b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
+
+    // The 128-row kernel's pipeline: every slot in flight, the barrier between the two
+    // 16-deep halves of a slice, the consumed slot refilled between the second half's
+    // MFMAs, constant waits (slots past the last slice take copies of it, never read).
+#pragma unroll
+    for (int p = 0; p < kBStages; ++p) issue(min(p, nk - 1), p);
+    MOE_WAIT_VMCNT((kBStages - 1) * kBCopies);
+    __syncthreads();
+    read_frags(0, 0, af0, bf0);
+    for (int ks = 0; ks < nk - 1; ++ks) {
+      read_frags(ks % kBStages, 1, af1, bf1);
+      mfma_block(af0, bf0);
+      MOE_WAIT_VMCNT((kBStages - 2) * kBCopies);
+      __syncthreads();
+      read_frags((ks + 1) % kBStages, 0, af0, bf0);
+      const int ksrc = min(ks + kBStages, nk - 1);
+      const int slot = ks % kBStages;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        issue_part_to(ksrc, slot, i);
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2)
+          acc[i][j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j2], acc[i][j2], 0, 0, 0);
+      }
+      issue_part_to(ksrc, slot, 4);
+    }
+    read_frags((nk - 1) % kBStages, 1, af1, bf1);
+    mfma_block(af0, bf0);
+    mfma_block(af1, bf1);
+    MOE_WAIT_VMCNT(0);
+    __syncthreads();
+
+    // Epilogue: bf16 staging per wave ([64 rows][64 + 8], two row passes), 16-byte stores.
+    constexpr int kLd = 64 + 8;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * 64 * kLd;
+    const int col0 = n0 + wave * 64;
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i / 2 != hv) continue;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = (i % 2) * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) stg[r * kLd + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][q]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 4
+      for (int r0 = 0; r0 < 64; r0 += 8) {
+        const int r = r0 + (lane >> 3);
+        const int c8 = lane & 7;
+        const int grow = hv * 64 + r;
+        const int gcol = col0 + c8 * 8;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + c8 * 8);
+        if (grow < tile.valid && gcol < N)
+          *reinterpret_cast<u32x4_t*>(ops.C + (size_t)(tile.m0 + grow) * N + gcol) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+  }
+}
+
+moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb, int ksplit,
+                        void* C, int K, int N, const int32_t* meta, const int32_t* num_blocks,
+                        int32_t max_blocks, int E, int block_m, int32_t dense_rows, hipStream_t st) {
+  const int n_tiles = (int)ceil_div(N, 512);
+  const int64_t blocks_ub = dense_rows > 0 ? ceil_div(dense_rows, 128)
+                                           : (int64_t)max_blocks * (block_m / 128);
+  const int64_t items = blocks_ub * n_tiles;
+  const int cus = device_cu_count();
+  int64_t grid = items < cus ? items : cus;
+  if (grid < 1) grid = 1;
+  const NTOperands ops{static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(Bt0),
+                       static_cast<const bf16_t*>(Bt1), static_cast<bf16_t*>(C), ldb,
+                       Bt1 ? ksplit : K};
+  const int64_t max_rows = dense_rows > 0 ? (int64_t)dense_rows : (int64_t)max_blocks * block_m;
+  hipLaunchKernelGGL(k_gg_nt, dim3((unsigned)grid), dim3(kBThreads), 0, st, ops, K, N, meta,
+                     num_blocks, max_blocks, dense_rows > 0 ? 1 : E, max_rows, dense_rows, block_m,
+                     n_tiles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// weight-gradient grouped GEMM: C[e] = X_e^T D_e over each expert's rows
+// ---------------------------------------------------------------------------
+static constexpr int kWgXBytes = kBBK * 128 * 2;     // [32 rows][128 m] = 8 KB
+static constexpr int kWgDBytes = kBBK * 512 * 2;     // [32 rows][512 n] = 32 KB
+static constexpr int kWgStage = kWgXBytes + kWgDBytes;
+
+struct WgOperands {
+  const bf16_t* X;     // [rows, Km]
+  const bf16_t* D;     // [rows, Nn]
+  float* C0;           // per expert [Km][nsplit]      (columns n < nsplit)
+  float* C1;           // per expert [Km][Nn - nsplit] (columns n >= nsplit; NULL: none)
+  int nsplit;
+};
+
+__global__ void __launch_bounds__(kBThreads, 1)
+k_gg_wgrad(WgOperands ops, int Km, int Nn, const int32_t* __restrict__ counts,
+           const int32_t* __restrict__ row_off, int E, int dense_rows, int m_tiles, int n_tiles) {
+  __shared__ __align__(1024) unsigned char lds[kBStages * kWgStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, gi = lane & 15, tr_r = gi >> 2, tr_c4 = gi & 3;
+  const int total = E * m_tiles * n_tiles;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int nt = w % n_tiles;
+    const int mt = (w / n_tiles) % m_tiles;
+    const int e = w / (n_tiles * m_tiles);
+    const int cnt = __builtin_amdgcn_readfirstlane(dense_rows > 0 ? dense_rows : (counts ? counts[e] : 0));
+    const int r0e = __builtin_amdgcn_readfirstlane(dense_rows > 0 || !counts ? 0 : row_off[e]);
+    const int m0 = mt * 128, n0 = nt * 512;
+    const int ns = (cnt + kBBK - 1) / kBBK;   // 32-row slices of this expert
+    // Copies: wave w owns slice rows 4w .. 4w+3: one X copy (4 rows x 256 B, 16 lanes
+    // per row) and four D copies (one 1 KB row each).  A lane's 16 bytes land at
+    // physical chunk (lane & 15) of its X row / lane of its D row, which holds logical
+    // chunk swz_b(row, physical) (the swizzle is an involution).  Rows past the count
+    // read the expert's first row (in bounds) and are zeroed in LDS afterwards.
+    int mcol, ncol[4];
+    {
+      const int rr = 4 * wave + (lane >> 4);
+      mcol = m0 + swz_b(rr, lane & 15) * 8;
+      if (mcol >= Km) mcol = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        ncol[p] = n0 + swz_b(4 * wave + p, lane) * 8;
+        if (ncol[p] >= Nn) ncol[p] = 0;
+      }
+    }
+    const bf16_t* xe = uniform_ptr(ops.X + (size_t)r0e * Km);
+    const bf16_t* de = uniform_ptr(ops.D + (size_t)r0e * Nn);
+    auto issue = [&](int s, int slot) {
+      unsigned char* st = lds + slot * kWgStage;
+      const int rbase = 32 * s + 4 * wave;
+      const int xb = rbase < cnt ? rbase : 0;
+      const int lr = rbase + (lane >> 4) < cnt ? (lane >> 4) : 0;
+      copy16_to_lds(xe + (size_t)xb * Km, (uint32_t)(lr * Km + mcol) * 2u, st + wave * 1024);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = rbase + p;
+        const int rr = r < cnt ? r : 0;
+        copy16_to_lds(de + (size_t)rr * Nn, (uint32_t)ncol[p] * 2u,
+                      st + kWgXBytes + (4 * wave + p) * 1024);
+      }
+    };
+    // zero this wave's rows of slice s that lie past the count (after its copies landed)
+    auto zero_tail = [&](int s) {
+      const int rbase = 32 * s + 4 * wave;
+      if (rbase + 4 <= cnt) return;
+      unsigned char* st = lds + (s % kBStages) * kWgStage;
+      const u32x4_t z = u32x4_t{0u, 0u, 0u, 0u};
+      if (rbase + (lane >> 4) >= cnt) *reinterpret_cast<u32x4_t*>(st + wave * 1024 + lane * 16) = z;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        if (rbase + p >= cnt)
+          *reinterpret_cast<u32x4_t*>(st + kWgXBytes + (4 * wave + p) * 1024 + lane * 16) = z;
+    };
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    // transposed 4 x 16 reads: A (X^T) subtile i reads columns m = 32 i + ..., B (D)
+    // subtile j columns n = 64 wave + 32 j + ...
+    bf16x8_t af[4], bf[2];
+    auto read_frags = [&](int s, int kk) {
+      const unsigned char* sx = lds + (s % kBStages) * kWgStage;
+      const unsigned char* sd = sx + kWgXBytes;
+      const int kbase = kk * 16 + (g >> 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = i * 32 + (g & 1) * 16 + 4 * tr_c4;
+        i16x4_t hv[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = kbase + hh * 4 + tr_r;
+          hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (MOE_LDS i16x4_t*)(sx + k * 256 + swz_b(k, col >> 3) * 16 + (col & 7) * 2));
+        }
+        af[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wave * 64 + j * 32 + (g & 1) * 16 + 4 * tr_c4;
+        i16x4_t hv[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int k = kbase + hh * 4 + tr_r;
+          hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (MOE_LDS i16x4_t*)(sd + k * 1024 + swz_b(k, col >> 3) * 16 + (col & 7) * 2));
+        }
+        bf[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+
+    if (ns > 0) {
+      // every slot in flight (slots past the last slice take copies of it that are
+      // never read: they must not land in the slot that slice really uses, which is
+      // zeroed past the count), then slice 0
+#pragma unroll
+      for (int p = 0; p < kBStages; ++p) issue(min(p, ns - 1), p);
+      MOE_WAIT_VMCNT((kBStages - 1) * kBCopies);
+      zero_tail(0);
+      __syncthreads();
+      for (int s = 0; s < ns; ++s) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          read_frags(s, kk);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < ns) {
+          // slot s % S is free once every wave is past this barrier; slice s+1 must land
+          MOE_WAIT_VMCNT((kBStages - 2) * kBCopies);
+          zero_tail(s + 1);
+          __syncthreads();
+          issue(min(s + kBStages, ns - 1), s % kBStages);
+        }
+      }
+      MOE_WAIT_VMCNT(0);
+      __syncthreads();
+    }
+
+    // fp32 stores straight from the accumulators (32 lanes write 128 contiguous bytes)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = m0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          const int n = n0 + wave * 64 + j * 32 + (lane & 31);
+          if (m >= Km || n >= Nn) continue;
+          if (n < ops.nsplit)
+            ops.C0[((size_t)e * Km + m) * ops.nsplit + n] = acc[i][j][q];
+          else
+            ops.C1[((size_t)e * Km + m) * (Nn - ops.nsplit) + (n - ops.nsplit)] = acc[i][j][q];
+        }
+  }
+}
+
+moe_status launch_gg_wgrad(const void* X, const void* D, float* C0, float* C1, int nsplit, int Km,
+                           int Nn, const int32_t* counts, const int32_t* row_off, int E,
+                           int32_t dense_rows, hipStream_t st) {
+  const int m_tiles = (int)ceil_div(Km, 128), n_tiles = (int)ceil_div(Nn, 512);
+  const int64_t items = (int64_t)E * m_tiles * n_tiles;
+  const int cus = device_cu_count();
+  int64_t grid = items < cus ? items : cus;
+  if (grid < 1) grid = 1;
+  const WgOperands ops{static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(D), C0, C1,
+                       C1 ? nsplit : Nn};
+  hipLaunchKernelGGL(k_gg_wgrad, dim3((unsigned)grid), dim3(kBThreads), 0, st, ops, Km, Nn,
+                     counts, row_off, E, dense_rows, m_tiles, n_tiles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// router backward
+// ---------------------------------------------------------------------------
+// dlogits[t, :] from dw[t, :]: p = softmax(logits[t]) in fp32; the selected experts'
+// probabilities ps_j (renormalised: w_j = ps_j / Z, dps_j = (dw_j - <dw, w>) / Z;
+// otherwise dps = dw); dp[e] = sum of dps_j over the slots choosing e (ascending j);
+// dlogits[e] = p[e] (dp[e] - <dp, p>).  One wave per token, experts strided over
+// lanes, fixed-order reductions.
+static constexpr int kRbMaxPerLane = 16;   // E <= 1024
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+// p[e] of expert e, held by lane e % 64 as element e / 64 (e wave-uniform): each lane
+// selects its element e / 64 without indexing the register array, then lane e % 64's
+// copy is broadcast.
+__device__ __forceinline__ float expert_value(const float (&p)[kRbMaxPerLane], int e) {
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) v = (i == (e >> 6)) ? p[i] : v;
+  return __shfl(v, e & 63, 64);
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__global__ void __launch_bounds__(256)
+k_router_bwd(const float* __restrict__ logits, const int32_t* __restrict__ idx,
+             const float* __restrict__ dw, int T, int E, int k, int renorm,
+             float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* lt = logits + (size_t)t * E;
+  float p[kRbMaxPerLane];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = e < E ? lt[e] : -INFINITY;
+    mx = fmaxf(mx, p[i]);
+  }
+  mx = wave_max(mx);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    p[i] = e < E ? expf(p[i] - mx) : 0.f;
+    sum += p[i];
+  }
+  sum = wave_sum(sum);
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) p[i] /= sum;
+  // selected probabilities and their gradient, slot by slot (lane j holds slot j)
+  float Z = 0.f, dwdotw = 0.f;
+  if (renorm) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      Z += expert_value(p, e);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(size_t)t * k + j];
+      dwdotw += dw[(size_t)t * k + j] * (expert_value(p, e) / Z);
+    }
+  }
+  float dp[kRbMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) dp[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[(size_t)t * k + j];
+    const float g = renorm ? (dw[(size_t)t * k + j] - dwdotw) / Z : dw[(size_t)t * k + j];
+#pragma unroll
+    for (int i = 0; i < kRbMaxPerLane; ++i)
+      if (lane + 64 * i == e) dp[i] += g;
+  }
+  float dotp = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) dotp += dp[i] * p[i];
+  dotp = wave_sum(dotp);
+#pragma unroll
+  for (int i = 0; i < kRbMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) dlogits[(size_t)t * E + e] = p[i] * (dp[i] - dotp);
+  }
+}
+
+// dW_g[c, e] = sum_t x[t, c] dlogits[t, e]; dbias[e] = sum_t dlogits[t, e].  A block
+// owns 64 columns c and up to 64 experts; tokens go through LDS 32 at a time; each
+// thread keeps (c, 16 experts) sums, in ascending t.
+__global__ void __launch_bounds__(256)
+k_router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dl, int T, int d, int E,
+               float* __restrict__ dwg, float* __restrict__ dbias) {
+  __shared__ float sx[32][64];
+  __shared__ float sd[32][64];
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int cl = tid & 63, eg = tid >> 6;   // column, expert group of 16
+  float acc[16], bacc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = bacc[i] = 0.f;
+  for (int t0 = 0; t0 < T; t0 += 32) {
+    for (int i = tid; i < 32 * 64; i += 256) {
+      const int r = i >> 6, cc = i & 63;
+      const int t = t0 + r;
+      sx[r][cc] = (t < T && c0 + cc < d) ? bf16_to_f32(x[(size_t)t * d + c0 + cc]) : 0.f;
+      sd[r][cc] = (t < T && e0 + cc < E) ? dl[(size_t)t * E + e0 + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int r = 0; r < 32; ++r) {
+      const float xv = sx[r][cl];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[i] = fmaf(xv, sd[r][eg * 16 + i], acc[i]);
+        bacc[i] += sd[r][eg * 16 + i];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = e0 + eg * 16 + i;
+    if (dwg && c0 + cl < d && e < E) dwg[(size_t)(c0 + cl) * E + e] = acc[i];
+    if (dbias && blockIdx.x == 0 && cl == 0 && e < E) dbias[e] = bacc[i];
+  }
+}
+
+// dx_add[t, c] = base[t, c] + sum_e dlogits[t, e] W_g[c, e] (base may be NULL: 0),
+// rounded once to bf16.  One block per token.
+__global__ void __launch_bounds__(256)
+k_router_dx(const float* __restrict__ dl, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ base,
+            int T, int d, int E, bf16_t* __restrict__ out) {
+  extern __shared__ float s_dl[];
+  const int t = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) s_dl[e] = dl[(size_t)t * E + e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = base ? bf16_to_f32(base[(size_t)t * d + c]) : 0.f;
+    const bf16_t* wr = wg + (size_t)c * E;
+    for (int e = 0; e < E; ++e) v = fmaf(s_dl[e], bf16_to_f32(wr[e]), v);
+    out[(size_t)t * d + c] = f32_to_bf16(v);
+  }
+}
+
+moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_gate,
+                             const float* logits, const int32_t* idx, const float* dw,
+                             float* dlogits, float* dw_gate, float* dbias, const void* dx_base,
+                             void* dx_out, hipStream_t st) {
+  if (s.E > 64 * kRbMaxPerLane) return MOE_ENOTSUP;
+  if (s.T > 0) {
+    hipLaunchKernelGGL(k_router_bwd, dim3((unsigned)ceil_div(s.T, 4)), dim3(256), 0, st, logits,
+                       idx, dw, s.T, s.E, s.k, s.renormalize, dlogits);
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+  }
+  // with T == 0 the weight gradients are zeros (the kernel reads no rows)
+  if (dw_gate || dbias) {
+    hipLaunchKernelGGL(k_router_wgrad, dim3((unsigned)ceil_div(s.d, 64), (unsigned)ceil_div(s.E, 64)),
+                       dim3(256), 0, st, static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E,
+                       dw_gate, dbias);
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+  }
+  if (s.T > 0) {
+    hipLaunchKernelGGL(k_router_dx, dim3((unsigned)s.T), dim3(256), (size_t)s.E * sizeof(float), st,
+                       dlogits, static_cast<const bf16_t*>(w_gate),
+                       static_cast<const bf16_t*>(dx_base), s.T, s.d, s.E,
+                       static_cast<bf16_t*>(dx_out));
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -254,10 +254,13 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
              int max_blocks, int E, int64_t max_rows, int dense_rows, int block_m,
              int n_tiles) {
   __shared__ __align__(1024) unsigned char lds[kV2Stages * kV2Stage];
+  // op 2 (kOpGateUpBwd) runs the gate/up main loop; its epilogue writes dg | du
+  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU || OP == kOpGateUpBwd;
+  constexpr bool BWD = OP == kOpGateUpBwd;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int kOutCols = OP == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
+  constexpr int kOutCols = GU ? 256 : 512;
   const int tpb = block_m / kBM;
   const int nb_dense = (dense_rows + block_m - 1) / block_m;
   const int nblocks = nb_dense + (max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0);
@@ -270,8 +273,8 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
   int bhalf[2], bcol0[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    bhalf[j] = OP == MOE_OP_GATEUP_SWIGLU ? j : wave >> 2;
-    bcol0[j] = OP == MOE_OP_GATEUP_SWIGLU ? wave * 32 : (wave & 3) * 64 + j * 32;
+    bhalf[j] = GU ? j : wave >> 2;
+    bcol0[j] = GU ? wave * 32 : (wave & 3) * 64 + j * 32;
   }
 
   // Work order.  Work groups are dispatched to the 8 XCDs round-robin (group b on
@@ -314,10 +317,10 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
     const int n0 = nt * kOutCols;
     const bf16_t* asrc = ops.A + (size_t)tile.m0 * K;
     const bf16_t* b0e = ops.B0 + (size_t)tile.e * K * N;
-    const bf16_t* b1e = OP == MOE_OP_GATEUP_SWIGLU ? ops.B1 + (size_t)tile.e * K * N : b0e;
+    const bf16_t* b1e = GU ? ops.B1 + (size_t)tile.e * K * N : b0e;
     // the two 256-column halves of the tile's B columns: matrix and first column
-    const bf16_t* bh_base[2] = {b0e, OP == MOE_OP_GATEUP_SWIGLU ? b1e : b0e};
-    const int bh_col0[2] = {n0, OP == MOE_OP_GATEUP_SWIGLU ? n0 : n0 + 256};
+    const bf16_t* bh_base[2] = {b0e, GU ? b1e : b0e};
+    const int bh_col0[2] = {n0, GU ? n0 : n0 + 256};
 
     // A copy (one per wave per slice): window = this wave's 16 rows.
     uint32_t a_voff;
@@ -456,12 +459,17 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
     // [rows][cols + 8] staging tile, then stores whole 16-byte row chunks.  32x32
     // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
     // l%32 of the 32x32 subtile.
-    constexpr int kWCols = OP == MOE_OP_GATEUP_SWIGLU ? 32 : 64;   // output columns per wave
-    constexpr int kHalves = OP == MOE_OP_GATEUP_SWIGLU ? 1 : 2;    // row passes
+    constexpr int kWCols = GU ? 32 : 64;   // output columns per wave
+    constexpr int kHalves = GU ? 1 : 2;    // row passes
     constexpr int kRowsPer = 128 / kHalves;
     constexpr int kLd = kWCols + 8;                                 // staging row pitch
     bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kRowsPer * kLd;
-    const int col0 = n0 + (OP == MOE_OP_GATEUP_SWIGLU ? wave * 32 : (wave >> 2) * 256 + (wave & 3) * 64);
+    const int col0 = n0 + (GU ? wave * 32 : (wave >> 2) * 256 + (wave & 3) * 64);
+    // op 2 writes two outputs into C = [rows, 2N]: dg (pass 0) then du (pass 1)
+    constexpr int kOutPasses = BWD ? 2 : 1;
+    const int ldc = BWD ? 2 * N : N;
+#pragma unroll
+    for (int pass = 0; pass < kOutPasses; ++pass)
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
 #pragma unroll
@@ -470,7 +478,14 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int r = (i % (4 / kHalves)) * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (OP == MOE_OP_GATEUP_SWIGLU) {
+          if (BWD) {
+            const int grow = hv * kRowsPer + r, gcol = col0 + (lane & 31);
+            const float da = (grow < tile.valid && gcol < N)
+                                 ? bf16_to_f32(ops.D[(size_t)(tile.m0 + grow) * N + gcol]) : 0.f;
+            const float gv = acc[i][0][q], uv = acc[i][1][q];
+            stg[r * kLd + (lane & 31)] = f32_to_bf16(pass == 0 ? swiglu_dgate(gv, uv, da)
+                                                               : swiglu_dup(gv, da));
+          } else if (GU) {
             stg[r * kLd + (lane & 31)] = f32_to_bf16(silu_f32(acc[i][0][q]) * acc[i][1][q]);
           } else {
 #pragma unroll
@@ -492,7 +507,7 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
         const int gcol = col0 + ch * 8;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + ch * 8);
         if (grow < tile.valid && gcol < N)
-          *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * N + gcol) = v;
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * ldc + pass * N + gcol) = v;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -651,6 +666,9 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
   const int cus = device_cu_count();
   const bool v2_routed = s.dtype == MOE_DTYPE_BF16 && g.K % kV2BK == 0;
   if (routed && g.gather && !v2_routed) return MOE_ENOTSUP;
+  if (op == kOpGateUpBwd && ((routed && !v2_routed) ||
+                             (dense && !(s.dtype == MOE_DTYPE_BF16 && g.Kd % kV2BK == 0))))
+    return MOE_ENOTSUP;
   const bool v2_dense = s.dtype == MOE_DTYPE_BF16 && g.Kd % kV2BK == 0;
   // one launch when both sets fit the async-copy kernel with the same K and N
   if ((!routed || v2_routed) && (!dense || v2_dense) && (!routed || !dense || (g.K == g.Kd && g.N == g.Nd))) {
@@ -658,13 +676,14 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
     if (use_wide_tiles(s, g)) {
       const GGOperands ro{static_cast<const bf16_t*>(g.A), static_cast<const bf16_t*>(g.B0),
                           static_cast<const bf16_t*>(g.B1), static_cast<bf16_t*>(g.C),
-                          g.gather, g.gather_div, g.gather_rows};
+                          g.gather, g.gather_div, g.gather_rows, static_cast<const bf16_t*>(g.D)};
       const GGOperands dn{static_cast<const bf16_t*>(g.Ad), static_cast<const bf16_t*>(g.B0d),
-                          static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1};
+                          static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1,
+                          static_cast<const bf16_t*>(g.Dd)};
       return launch_gg_wide(op, ro, dn, K, N, g.block_meta, g.num_blocks, routed ? g.max_blocks : 0,
                             s.E, dense ? g.dense_rows : 0, st);
     }
-    const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
+    const int out_cols = op == MOE_OP_DOWN ? 512 : 256;   // the kernel's kOutCols
     const int n_tiles = (int)ceil_div(N, out_cols);
     const int64_t blocks_ub = (routed ? (int64_t)g.max_blocks : 0) +
                               (dense ? ceil_div(g.dense_rows, s.block_m) : 0);
@@ -673,12 +692,17 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
     if (grid < 1) grid = 1;
     const GGOperands ro{static_cast<const bf16_t*>(g.A), static_cast<const bf16_t*>(g.B0),
                         static_cast<const bf16_t*>(g.B1), static_cast<bf16_t*>(g.C),
-                        g.gather, g.gather_div, g.gather_rows};
+                        g.gather, g.gather_div, g.gather_rows, static_cast<const bf16_t*>(g.D)};
     const GGOperands dn{static_cast<const bf16_t*>(g.Ad), static_cast<const bf16_t*>(g.B0d),
-                        static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1};
+                        static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1,
+                        static_cast<const bf16_t*>(g.Dd)};
     const int64_t max_rows = (int64_t)g.max_blocks * s.block_m;
     if (op == MOE_OP_GATEUP_SWIGLU)
       hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kV2Threads), 0,
+                         st, ro, dn, K, N, g.block_meta, g.num_blocks, g.max_blocks, s.E, max_rows,
+                         g.dense_rows, s.block_m, n_tiles);
+    else if (op == kOpGateUpBwd)
+      hipLaunchKernelGGL(k_gg_bf16_v2<kOpGateUpBwd>, dim3((unsigned)grid), dim3(kV2Threads), 0,
                          st, ro, dn, K, N, g.block_meta, g.num_blocks, g.max_blocks, s.E, max_rows,
                          g.dense_rows, s.block_m, n_tiles);
     else

@@ -71,7 +71,18 @@ struct GGOperands {
   const int32_t* gather;
   int gather_div;
   int gather_rows;
+  // kOpGateUpBwd only: dact [rows, N]; C is then dg | du, [rows, 2 N]
+  const bf16_t* D;
 };
+
+// SwiGLU backward of one element from the recomputed gate g, up u and the incoming
+// gradient da of act = silu(g) u:  dg = da u silu'(g),  du = da silu(g),
+// silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
+__device__ __forceinline__ float swiglu_dgate(float g, float u, float da) {
+  const float s = 1.0f / (1.0f + expf(-g));
+  return da * u * (s * (1.0f + g * (1.0f - s)));
+}
+__device__ __forceinline__ float swiglu_dup(float g, float da) { return da * silu_f32(g); }
 
 // A wave-uniform pointer, held in scalar registers (the copies take an SGPR base).
 template <typename T>

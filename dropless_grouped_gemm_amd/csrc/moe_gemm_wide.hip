@@ -59,7 +59,8 @@ __global__ void __launch_bounds__(NW * 64, 1)
 k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
           const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
           int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles) {
-  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU;
+  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU || OP == kOpGateUpBwd;
+  constexpr bool BWD = OP == kOpGateUpBwd;
   constexpr int NT = NW * 64;
   constexpr int WR = kWRows * 2 / NW;     // rows per wave
   constexpr int MI = WR / 32;             // 32-row subtiles per wave
@@ -369,9 +370,13 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     // a private [WR][64 + 8] staging tile, then stores whole 16-byte row chunks.  32x32
     // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
     // l%32 of the subtile.
+    // The SwiGLU backward (op 2) writes two outputs, dg then du, in two passes; each
+    // element's incoming gradient dact is read from global memory (32 lanes of a row
+    // read 64 contiguous bytes).
     constexpr int kLd = 64 + 8;
-    constexpr int kPasses = GU ? 1 : 2;
+    constexpr int kPasses = (GU && !BWD) ? 1 : 2;
     bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * WR * kLd;
+    const bf16_t* dact = ops.D;
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
 #pragma unroll
@@ -382,10 +387,17 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             float v;
-            if (GU)
+            if (BWD) {
+              const int grow = rbase + r, gcol = n0 + ch * 64 + jj * 32 + (lane & 31);
+              const float da = (grow < valid && gcol < N)
+                                   ? bf16_to_f32(dact[(size_t)(m0 + grow) * N + gcol]) : 0.f;
+              const float gv = acc[i][jj][q], uv = acc[i][jj + 2][q];
+              v = ps == 0 ? swiglu_dgate(gv, uv, da) : swiglu_dup(gv, da);
+            } else if (GU) {
               v = silu_f32(acc[i][jj][q]) * acc[i][jj + 2][q];
-            else
+            } else {
               v = acc[i][ps * 2 + jj][q];
+            }
             stg[r * kLd + jj * 32 + (lane & 31)] = f32_to_bf16(v);
           }
         }
@@ -394,6 +406,9 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int col0 = n0 + (GU ? ch * 64 : ch * 128 + ps * 64);
+      // op 2: C is [rows, 2N], dg in columns [0, N), du in [N, 2N)
+      const int ldc = BWD ? 2 * N : N;
+      const int cofs = BWD ? ps * N : 0;
 #pragma unroll 4
       for (int r0 = 0; r0 < WR; r0 += 8) {
         const int r = r0 + (lane >> 3);
@@ -402,7 +417,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         const int gcol = col0 + c8 * 8;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + c8 * 8);
         if (grow < valid && gcol < N)
-          *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * N + gcol) = v;
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * ldc + cofs + gcol) = v;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -417,7 +432,7 @@ static constexpr int kWideWaves = 8;
 moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, int K, int N,
                           const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
                           int E, int32_t dense_rows, hipStream_t st) {
-  const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 128 : 256;
+  const int out_cols = op == MOE_OP_DOWN ? 256 : 128;
   const int n_tiles = (int)ceil_div(N, out_cols);
   // groups: at most one per block, and at most a third of the blocks plus one per expert
   const int64_t mb = max_blocks > 0 ? max_blocks : 0;
@@ -437,6 +452,10 @@ moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, in
   constexpr int NT = kWideWaves * 64;
   if (op == MOE_OP_GATEUP_SWIGLU)
     hipLaunchKernelGGL((k_gg_wide<MOE_OP_GATEUP_SWIGLU, kWideWaves>), dim3((unsigned)grid), dim3(NT),
+                       0, st, ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows,
+                       dense_rows, n_tiles);
+  else if (op == kOpGateUpBwd)
+    hipLaunchKernelGGL((k_gg_wide<kOpGateUpBwd, kWideWaves>), dim3((unsigned)grid), dim3(NT),
                        0, st, ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows,
                        dense_rows, n_tiles);
   else

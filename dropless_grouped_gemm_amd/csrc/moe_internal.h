@@ -11,6 +11,10 @@ namespace moe {
 
 typedef uint16_t bf16_t;  // raw bf16 bits in memory
 
+// Internal grouped-GEMM op next to MOE_OP_GATEUP_SWIGLU and MOE_OP_DOWN: recompute the
+// gate/up products and apply the SwiGLU backward in the epilogue.
+constexpr int kOpGateUpBwd = 2;
+
 // bf16 <-> fp32.  The widening is exact; the narrowing rounds to nearest even
 // (gfx950 converts in hardware).
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
@@ -69,7 +73,7 @@ moe_status launch_permute(const moe_shape& s, const void* x, const int32_t* pos,
                           void* x_perm, hipStream_t st);
 moe_status launch_combine(const moe_shape& s, const void* y, const int32_t* pos,
                           const float* topk_w, const void* shared_out, void* out,
-                          hipStream_t st);
+                          hipStream_t st);  // topk_w NULL: unit weights
 
 // Grouped GEMM over up to two segment sets with their own operands: the routed
 // segments of a block table (max_blocks == 0: none) and a dense segment of
@@ -95,6 +99,9 @@ struct GemmSegments {
   const int32_t* gather;
   int gather_div;
   int gather_rows;  // rows of the unpermuted A (row indices are clamped into it)
+  // kOpGateUpBwd: the incoming gradient dact of the routed and dense sets
+  const void* D;
+  const void* Dd;
 };
 moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g, hipStream_t st);
 // The bf16 asynchronous-copy kernels can gather gate/up A rows from the unpermuted x.
@@ -130,5 +137,32 @@ struct GemmSegmentsF8 {
   int gather_rows;
 };
 moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, hipStream_t st);
+
+// Backward kernels (moe_backward.hip).
+// dy[pos[t,j]] = w[t,j] dout[t] (bf16), dw[t,j] = <dout[t], y[pos[t,j]]> (fp32); d <= 8192.
+moe_status launch_combine_bwd(const moe_shape& s, const void* dout, const void* y,
+                              const int32_t* pos, const float* topk_w, void* dy, float* dw,
+                              int64_t max_rows, hipStream_t st);
+// C[r] = A[r] B[e] with B stored transposed per expert: B[k][n] = Bt0[e][n][k] for
+// k < ksplit, Bt1[e][n][k - ksplit] beyond (Bt1 NULL: ksplit = K); K % 32 == 0,
+// ksplit % 32 == 0, N % 8 == 0.  Routed rows from the block table, or dense_rows rows
+// of one matrix.
+moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb, int ksplit,
+                        void* C, int K, int N, const int32_t* meta, const int32_t* num_blocks,
+                        int32_t max_blocks, int E, int block_m, int32_t dense_rows, hipStream_t st);
+// C[e] = X_e^T D_e (fp32) over expert e's rows [row_off[e], row_off[e] + counts[e]),
+// columns n < nsplit into C0 [E][Km][nsplit], the rest into C1 (C1 NULL: nsplit = Nn);
+// dense_rows > 0: one expert over rows [0, dense_rows); counts NULL and dense_rows 0:
+// zeros.  Km % 8 == 0, Nn % 8 == 0.
+moe_status launch_gg_wgrad(const void* X, const void* D, float* C0, float* C1, int nsplit, int Km,
+                           int Nn, const int32_t* counts, const int32_t* row_off, int E,
+                           int32_t dense_rows, hipStream_t st);
+// dlogits from dw through the softmax (and renormalisation), selection fixed; then
+// dw_gate = x^T dlogits, dbias = column sums (NULL: skipped), and
+// dx_out = dx_base (NULL: 0) + dlogits w_gate^T in bf16.
+moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_gate,
+                             const float* logits, const int32_t* idx, const float* dw,
+                             float* dlogits, float* dw_gate, float* dbias, const void* dx_base,
+                             void* dx_out, hipStream_t st);
 
 }  // namespace moe

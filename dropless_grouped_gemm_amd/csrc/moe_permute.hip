@@ -123,7 +123,7 @@ k_combine(const u32x4_t* __restrict__ y, const int32_t* __restrict__ pos,
     for (int j0 = 0; j0 < k; j0 += 64) {
       const int nj = min(64, k - j0);
       const int pl = lane < nj ? pos[(size_t)t * k + j0 + lane] : -1;
-      const float wl = lane < nj ? w[(size_t)t * k + j0 + lane] : 0.f;
+      const float wl = lane < nj ? (w ? w[(size_t)t * k + j0 + lane] : 1.f) : 0.f;
       for (int jj = 0; jj < nj; jj += kCombSlots) {
         // issue every load of kCombSlots slots, then accumulate them in slot order
         u32x4_t r[kCombSlots][kCombVec];

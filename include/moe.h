@@ -230,8 +230,9 @@ moe_status moe_grouped_gemm_gather(const moe_shape* s, const void* x,
  *   out[t, :] = sum_{j = 0..k-1, in this order} topk_w[t, j] * y[pos[t*k + j], :]
  *               (+ shared_out[t, :])
  * accumulated in fp32 and rounded once to dtype; slots with pos < 0 are skipped.
- * In:  y [moe_max_rows(s), d] (dtype), pos [T*k] int32, topk_w [T, k] fp32,
- *      shared_out [T, d] (dtype) or NULL.   Out: out [T, d] (dtype).
+ * In:  y [moe_max_rows(s), d] (dtype), pos [T*k] int32, topk_w [T, k] fp32 or NULL
+ *      (unit weights: the sum of each token's k rows, which is the backward of the
+ *      permute), shared_out [T, d] (dtype) or NULL.   Out: out [T, d] (dtype).
  */
 moe_status moe_combine(const moe_shape* s, const void* y, const int32_t* pos,
                        const float* topk_w, const void* shared_out, void* out,
@@ -317,6 +318,127 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
                              const float* ss2, const int32_t* topk_idx_in,
                              const float* topk_w_in, void* out, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * Backward pass (dropless notes: the gradients of the grouped GEMMs are grouped GEMMs
+ * over the same segments - data gradients through the transposed expert weights,
+ * weight gradients reducing over each expert's rows - and the permutation is replayed
+ * from the forward's indices).  The gradient of <dout, out> by the chain rule of the
+ * forward definition, step by step:
+ *   combine  dy[pos[t,j]] = w[t,j] dout[t];  dw[t,j] = <dout[t], y[pos[t,j]]>
+ *   down     dact = dy W2[e]^T;  dW2[e] = act_e^T dy_e
+ *   SwiGLU   g = A W1[e], u = A W3[e] recomputed;  dg = dact u silu'(g),
+ *            du = dact silu(g),  silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
+ *   gate/up  dx_perm = dg W1[e]^T + du W3[e]^T;  dW1[e] | dW3[e] = x_perm_e^T (dg | du)
+ *   permute  dx[t] = sum_j dx_perm[pos[t,j]]   (moe_combine with unit weights)
+ *   shared   the same three GEMM steps over all tokens with output gradient dout
+ *   router   dlogits through the softmax (and renormalisation) with the selection
+ *            held fixed;  dW_g = x^T dlogits;  dbias = sum_t dlogits;  dx += dlogits W_g^T
+ * All backward entry points need dtype bf16 and d, d_e, d_e_shared multiples of 32
+ * (else MOE_ENOTSUP).  Data gradients are bf16 (fp32 accumulation, one rounding);
+ * weight gradients, dtopk_w, dlogits, dW_g and dbias are fp32, each element written
+ * once (no atomics, fixed summation order).
+ */
+
+/*
+ * Combine backward.  In: dout [T, d], y [moe_max_rows(s), d] (the forward's down
+ * output), pos [T*k], topk_w [T, k].  Out: dy [moe_max_rows(s), d] (rows no slot uses
+ * are not written), dtopk_w [T, k] fp32 (0 for slots with pos < 0).  d <= 8192.
+ */
+moe_status moe_combine_bwd(const moe_shape* s, const void* dout, const void* y,
+                           const int32_t* pos, const float* topk_w, void* dy,
+                           float* dtopk_w, void* stream);
+
+/*
+ * SwiGLU backward fused into the gate/up grouped GEMM: the gate and up products are
+ * recomputed from A (x_perm [rows, d], or x [T, d] with row_src as for
+ * moe_grouped_gemm_gather) and the forward's weights, and the epilogue writes
+ * dgu = [dg | du], [rows, 2 d_e] (dg in columns [0, d_e), du in [d_e, 2 d_e)), from
+ * dact [rows, d_e].  The block table as for moe_grouped_gemm.
+ * Shared expert: x_shared (= x [T, d]), ws1, ws3, dact_shared [T, d_e_shared] and
+ * dgu_shared [T, 2 d_e_shared] all given (needs d_e_shared > 0), or all NULL.
+ */
+moe_status moe_swiglu_bwd(const moe_shape* s, const void* A, const int32_t* row_src,
+                          const void* w1, const void* w3, const void* dact,
+                          const int32_t* block_meta, const int32_t* num_blocks,
+                          int32_t max_blocks, void* dgu, const void* x_shared,
+                          const void* ws1, const void* ws3, const void* dact_shared,
+                          void* dgu_shared, void* stream);
+
+/*
+ * Data-gradient grouped GEMM (the weights read transposed):
+ *   op = MOE_OP_DOWN:         dA = dact [rows, d_e] = dC W2[e]^T, dC = dy [rows, d],
+ *                             B0 = W2 [E, d_e, d], B1 = NULL;
+ *   op = MOE_OP_GATEUP_SWIGLU: dA = dx_perm [rows, d] = dC [W1[e] | W3[e]]^T,
+ *                             dC = dgu [rows, 2 d_e], B0 = W1, B1 = W3 [E, d, d_e].
+ * block_meta, num_blocks, max_blocks as for moe_grouped_gemm; block_meta = num_blocks
+ * = NULL with max_blocks = 0 is the dense mode (one expert, E = 1, over T rows: the
+ * shared expert with s->d_e = d_e_shared).  Only rows the table covers are written.
+ */
+moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC,
+                                  const void* B0, const void* B1, const int32_t* block_meta,
+                                  const int32_t* num_blocks, int32_t max_blocks, void* dA,
+                                  void* stream);
+
+/*
+ * Weight-gradient grouped GEMM, reducing over each expert's rows
+ * [padded_offsets[e], padded_offsets[e] + counts[e]) (moe_build_offsets' outputs):
+ *   op = MOE_OP_DOWN:          dB0 = dW2 [E, d_e, d] = A_e^T dC_e, A = act [rows, d_e],
+ *                              dC = dy [rows, d], dB1 = NULL;
+ *   op = MOE_OP_GATEUP_SWIGLU: dB0 = dW1, dB1 = dW3 [E, d, d_e] = A_e^T (dg | du)_e,
+ *                              A = x_perm [rows, d], dC = dgu [rows, 2 d_e].
+ * counts = padded_offsets = NULL: dense mode over all T rows (E = 1, d_e as in s).
+ * fp32 outputs; experts without rows get zeros.
+ */
+moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A,
+                                  const void* dC, const int32_t* counts,
+                                  const int32_t* padded_offsets, float* dB0, float* dB1,
+                                  void* stream);
+
+/*
+ * Router backward (TileLang chapter section 2.2's weights w = softmax(logits)[idx],
+ * divided by their sum when s->renormalize): the selection is piecewise constant and
+ * held fixed.  In: x [T, d], w_gate [d, E] (bf16), logits [T, E] fp32 (the forward's),
+ * topk_idx [T, k], dtopk_w [T, k] fp32; dx_in [T, d] or NULL.
+ * Out: dlogits [T, E] fp32, dw_gate [d, E] fp32, dbias [E] fp32 (or NULL: skipped),
+ *      dx_out [T, d] = dx_in + dlogits w_gate^T (bf16, one rounding).
+ */
+moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
+                          const float* logits, const int32_t* topk_idx, const float* dtopk_w,
+                          float* dlogits, float* dw_gate, float* dbias, const void* dx_in,
+                          void* dx_out, void* stream);
+
+/*
+ * Host-only and pure: bytes of the backward workspace and the offsets of its
+ * intermediates (dy, dact, dgu, x_perm, dx_perm [rows, .]; dtopk_w [T, k] and dlogits
+ * [T, E] fp32; the shared expert's dact, dgu, dx and the router's dx [T, .]).
+ */
+typedef struct moe_bwd_ws_layout {
+  size_t dy, dact, dgu, x_perm, dx_perm, dtopk_w, dlogits, shared_dact, shared_dgu,
+         shared_dx, router_dx, total;
+} moe_bwd_ws_layout;
+size_t moe_bwd_workspace_bytes(const moe_shape* s);
+moe_status moe_bwd_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout);
+
+/*
+ * The layer's backward, after moe_layer_fwd on the same arguments: fwd_ws is that
+ * call's workspace (read only: logits, routes, block table, act, y, shared_act).
+ * In:  x, w_gate (when the forward routed), w1, w3, w2, ws1, ws3, ws2, topk_idx_in and
+ *      topk_w_in exactly as given to moe_layer_fwd; dout [T, d].
+ * Out: dx [T, d] (bf16); dw1, dw3 [E, d, d_e], dw2 [E, d_e, d] fp32; dws1, dws3
+ *      [d, d_e_shared], dws2 [d_e_shared, d] fp32 when d_e_shared > 0 (else NULL);
+ *      dw_gate [d, E] fp32 and dbias [E] fp32 (either may be NULL) when the forward
+ *      routed (NULL otherwise); dtopk_w [T, k] fp32 or NULL (the routing weights'
+ *      gradient; with given routes it is the only gradient they get).
+ * ws:  ws_bytes >= moe_bwd_workspace_bytes(s).
+ */
+moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate,
+                         const void* w1, const void* w3, const void* w2, const void* ws1,
+                         const void* ws3, const void* ws2, const int32_t* topk_idx_in,
+                         const float* topk_w_in, const void* dout, const void* fwd_ws,
+                         size_t fwd_ws_bytes, void* dx, float* dw1, float* dw3, float* dw2,
+                         float* dws1, float* dws3, float* dws2, float* dw_gate, float* dbias,
+                         float* dtopk_w, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Byte offsets of the intermediates inside the moe_layer_fwd workspace, so that a

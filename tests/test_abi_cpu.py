@@ -300,3 +300,95 @@ def test_fp8_entry_point_argument_rules():
               need, None) == B.MOE_EINVAL
     assert lf(ps, FAKE, FAKE, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE,
               need - 1, None) == B.MOE_EWORKSPACE
+
+
+def test_backward_entry_point_argument_rules():
+    """Backward: bf16 with d, d_e, d_e_shared multiples of 32 (else ENOTSUP); operand
+    pairs per op; the block table or the dense mode; workspaces checked before launch.
+    Every call here fails validation, so nothing is launched."""
+    L = B.lib()
+    odd = ctypes.c_void_p(0x10008)
+    s = good_shape()
+    ps = ctypes.byref(s)
+    mb = L.moe_max_blocks(ps)
+    assert B.backward_supported(s)
+    for bad in (good_shape(dtype="fp32"), good_shape(d=264), good_shape(d_e=520),
+                good_shape(d_e_shared=40)):
+        pb = ctypes.byref(bad)
+        assert not B.backward_supported(bad)
+        assert L.moe_combine_bwd(pb, *([FAKE] * 6), None) == B.MOE_ENOTSUP
+        assert L.moe_swiglu_bwd(pb, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
+                                *([None] * 5), None) == B.MOE_ENOTSUP
+        assert L.moe_grouped_gemm_dgrad(pb, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE,
+                                        None) == B.MOE_ENOTSUP
+        assert L.moe_grouped_gemm_wgrad(pb, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                        None) == B.MOE_ENOTSUP
+        assert L.moe_router_bwd(pb, *([FAKE] * 10), None) == B.MOE_ENOTSUP
+    assert L.moe_combine_bwd(ctypes.byref(good_shape(d=8224)), *([FAKE] * 6), None) == B.MOE_ENOTSUP
+    # combine backward: every pointer required
+    assert L.moe_combine_bwd(ps, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
+    assert L.moe_combine_bwd(ps, odd, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_EINVAL
+    # SwiGLU backward: dact required, block table checked, shared operands all or none
+    sb = L.moe_swiglu_bwd
+    assert sb(ps, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, *([None] * 5), None) == B.MOE_EINVAL
+    assert sb(ps, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, 1, FAKE, *([None] * 5), None) == B.MOE_EINVAL
+    assert sb(ps, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, mb + 1, FAKE, *([None] * 5),
+              None) == B.MOE_EINVAL
+    assert sb(ps, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+              None) == B.MOE_EINVAL                        # no shared expert in the shape
+    s2 = good_shape(d_e_shared=256)
+    assert sb(ctypes.byref(s2), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, FAKE,
+              None, FAKE, None) == B.MOE_EINVAL            # shared dact missing
+    # dgrad: op rules, dense mode all-or-nothing
+    dg = L.moe_grouped_gemm_dgrad
+    assert dg(ps, 0, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == B.MOE_EINVAL
+    assert dg(ps, 3, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, None, None, FAKE, 1, FAKE, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, None, None, None, 1, FAKE, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, None, FAKE, FAKE, mb + 1, FAKE, None) == B.MOE_EINVAL
+    # wgrad: dB1 exactly for gate/up; counts and offsets together
+    wg = L.moe_grouped_gemm_wgrad
+    assert wg(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
+    assert wg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_EINVAL
+    assert wg(ps, 1, FAKE, FAKE, FAKE, None, FAKE, None, None) == B.MOE_EINVAL
+    assert wg(ps, 1, odd, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
+    # router backward: dbias and dx_in optional, the rest required
+    rb = L.moe_router_bwd
+    assert rb(ps, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == B.MOE_EINVAL
+    assert rb(ps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == B.MOE_EINVAL
+    # layer backward: workspaces, routing pair, shared operands, router-only outputs
+    lb = L.moe_layer_bwd
+    fwd_need, bwd_need = L.moe_workspace_bytes(ps), L.moe_bwd_workspace_bytes(ps)
+    assert bwd_need > 0
+    args = lambda **o: [o.get(n, v) for n, v in (
+        ("x", FAKE), ("w_gate", FAKE), ("w1", FAKE), ("w3", FAKE), ("w2", FAKE), ("ws1", None),
+        ("ws3", None), ("ws2", None), ("idx", None), ("tw", None), ("dout", FAKE),
+        ("fws", FAKE), ("fwb", fwd_need), ("dx", FAKE), ("dw1", FAKE), ("dw3", FAKE),
+        ("dw2", FAKE), ("dws1", None), ("dws3", None), ("dws2", None), ("dwg", FAKE),
+        ("db", None), ("dtw", None), ("ws", FAKE), ("wsb", bwd_need))]
+    assert lb(ps, *args(fwb=fwd_need - 1), None) == B.MOE_EWORKSPACE
+    assert lb(ps, *args(wsb=bwd_need - 1), None) == B.MOE_EWORKSPACE
+    assert lb(ps, *args(ws=None), None) == B.MOE_EWORKSPACE
+    assert lb(ps, *args(idx=FAKE), None) == B.MOE_EINVAL                  # half a routing pair
+    assert lb(ps, *args(idx=FAKE, tw=FAKE), None) == B.MOE_EINVAL         # dW_g with given routes
+    assert lb(ps, *args(w_gate=None), None) == B.MOE_EINVAL
+    assert lb(ps, *args(dw2=None), None) == B.MOE_EINVAL
+    assert lb(ps, *args(ws1=FAKE), None) == B.MOE_EINVAL                   # no shared expert
+    assert lb(ctypes.byref(s2), *args(), None) == B.MOE_EINVAL            # shared expert missing
+
+
+def test_backward_workspace_layout_is_disjoint_and_aligned():
+    for kw in (dict(), dict(d_e_shared=256), dict(T=8192, d=7168, E=8, k=4, d_e=2048, d_e_shared=2048)):
+        s = good_shape(**kw)
+        L = B.moe_bwd_workspace_layout(s)
+        assert L["total"] == B.moe_bwd_workspace_bytes(s)
+        rows, T, d, de, ds = B.moe_max_rows(s), s.T, s.d, s.d_e, s.d_e_shared
+        sizes = dict(dy=rows * d * 2, dact=rows * de * 2, dgu=rows * 2 * de * 2, x_perm=rows * d * 2,
+                     dx_perm=rows * d * 2, dtopk_w=T * s.k * 4, dlogits=T * s.E * 4,
+                     shared_dact=T * ds * 2, shared_dgu=T * 2 * ds * 2,
+                     shared_dx=T * d * 2 if ds else 0, router_dx=T * d * 2)
+        spans = sorted((L[n], L[n] + sz) for n, sz in sizes.items() if sz)
+        assert all(o % 256 == 0 for o, _ in spans)
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert spans[-1][1] <= L["total"]
