@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: expert weights quantised to e4m3 with a scale per 128x128 "
                          "block (quantised once, outside the timed region)")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the layer's backward pass (per stage and moe_layer_bwd) and "
+                         "report it under 'backward'")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -319,6 +322,17 @@ def main():
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gemm[dom]["frac"],
                     "traffic": traffic}
 
+    bwd = None
+    if args.backward:
+        if fp8 or not B.backward_supported(s):
+            print(f"the backward pass is not supported for {cfg.name} ({args.weights} weights)",
+                  file=sys.stderr)
+            sys.exit(2)
+        bwd = bench_backward(args, cfg, inp, s, B, LG, dict(
+            topk_idx=topk_idx, topk_w=topk_w, counts=counts, pad=pad, meta=meta, nblk=nblk,
+            pos=pos, row_src=row_src, act=act, y=y, logits=logits,
+            sh_act=sh_act if shared else None), ms_per_step)
+
     # ---- CPU oracle on a bounded sample -----------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -351,7 +365,128 @@ def main():
         "active_experts": active,
         "wall_s": wall,
     }
+    if bwd is not None:
+        res["backward"] = bwd
     print(json.dumps(res), flush=True)
+
+
+def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
+    """The backward pass after the staged forward above (whose buffers ``fw`` hold the
+    routes, block table, act, y and logits): each stage timed with events on the
+    current stream, in the order moe_layer_bwd runs them, then moe_layer_bwd itself."""
+    import torch
+    dev = inp.x.device
+    T, d, E, k, de, ds = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_e, cfg.d_e_shared
+    M = T * k
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    bf = torch.bfloat16
+    routed = inp.topk_idx is not None
+    shared = ds > 0
+    e = lambda *sh: torch.empty(sh, dtype=bf, device=dev)
+    f = lambda *sh: torch.empty(sh, dtype=torch.float32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed + 17)
+    dout = torch.randn((T, d), generator=g, device=dev).to(bf)
+    dy, dact, dgu, xp, dxp = e(rows, d), e(rows, de), e(rows, 2 * de), e(rows, d), e(rows, d)
+    dtw, dl = f(T, k), f(T, E)
+    dw1, dw3, dw2 = f(E, d, de), f(E, d, de), f(E, de, d)
+    dwg, db, dxr, dx = f(d, E), f(E), e(T, d), e(T, d)
+    if shared:
+        s1 = B.make_shape(T=T, d=d, E=1, k=1, d_e=ds, block_m=cfg.block_m)
+        sdact, sdgu, sdx = e(T, ds), e(T, 2 * ds), e(T, d)
+        dws1, dws3, dws2 = f(d, ds), f(d, ds), f(ds, d)
+    rws_n = B.moe_router_bwd_workspace_bytes(s)
+    rws = torch.empty(max(rws_n, 256), dtype=torch.uint8, device=dev)
+    stages = (["combine_bwd", "dgrad_down", "wgrad_down", "permute", "swiglu_bwd", "dgrad_gateup",
+               "wgrad_gateup"] + ([] if routed else ["router_bwd"]) + ["unpermute"])
+
+    def step(ev=None):
+        i = 0
+        mark = lambda: ev[i].record() if ev is not None else None
+        mark()
+        B.moe_combine_bwd(s, dout, fw["y"], fw["pos"], fw["topk_w"], dy, dtw)
+        i += 1; mark()
+        B.moe_grouped_gemm_dgrad(s, B.MOE_OP_DOWN, dy, inp.w2, None, fw["meta"], fw["nblk"], mb,
+                                 dact)
+        if shared:
+            B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_DOWN, dout, inp.ws2, None, None, None, 0, sdact)
+        i += 1; mark()
+        B.moe_grouped_gemm_wgrad(s, B.MOE_OP_DOWN, fw["act"], dy, fw["counts"], fw["pad"], dw2, None)
+        if shared:
+            B.moe_grouped_gemm_wgrad(s1, B.MOE_OP_DOWN, fw["sh_act"], dout, None, None, dws2, None)
+        i += 1; mark()
+        B.moe_permute(s, inp.x, fw["pos"], xp)
+        i += 1; mark()
+        B.moe_swiglu_bwd(s, xp, None, inp.w1, inp.w3, dact, fw["meta"], fw["nblk"], mb, dgu,
+                         inp.x if shared else None, inp.ws1, inp.ws3, sdact if shared else None,
+                         sdgu if shared else None)
+        i += 1; mark()
+        B.moe_grouped_gemm_dgrad(s, B.MOE_OP_GATEUP_SWIGLU, dgu, inp.w1, inp.w3, fw["meta"],
+                                 fw["nblk"], mb, dxp)
+        if shared:
+            B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_GATEUP_SWIGLU, sdgu, inp.ws1, inp.ws3, None, None,
+                                     0, sdx)
+        i += 1; mark()
+        B.moe_grouped_gemm_wgrad(s, B.MOE_OP_GATEUP_SWIGLU, xp, dgu, fw["counts"], fw["pad"], dw1,
+                                 dw3)
+        if shared:
+            B.moe_grouped_gemm_wgrad(s1, B.MOE_OP_GATEUP_SWIGLU, inp.x, sdgu, None, None, dws1, dws3)
+        i += 1; mark()
+        extra = sdx if shared else None
+        if not routed:
+            B.moe_router_bwd(s, inp.x, inp.w_gate, fw["logits"], fw["topk_idx"], dtw, dl, dwg, db,
+                             extra, dxr, rws)
+            extra = dxr
+            i += 1; mark()
+        B.moe_combine(s, dxp, fw["pos"], None, extra, dx)
+        i += 1; mark()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nst = len(stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    for kk in range(args.steps):
+        step(evs[kk])
+    torch.cuda.synchronize()
+    st_ms = {n: sum(evs[kk][j].elapsed_time(evs[kk][j + 1]) for kk in range(args.steps)) / args.steps
+             for j, n in enumerate(stages)}
+    total = sum(evs[kk][0].elapsed_time(evs[kk][nst]) for kk in range(args.steps)) / args.steps
+
+    # the single moe_layer_bwd call (after a moe_layer_fwd that fills its workspace)
+    fws, bws = B.alloc_workspace(s, dev), B.alloc_bwd_workspace(s, dev)
+    out = e(T, d)
+    B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1, inp.ws3,
+                    inp.ws2, inp.topk_idx, inp.topk_w, out, fws)
+    call = lambda: B.moe_layer_bwd(
+        s, inp.x, None if routed else inp.w_gate, inp.w1, inp.w3, inp.w2, inp.ws1, inp.ws3,
+        inp.ws2, inp.topk_idx, inp.topk_w, dout, fws, dx, dw1, dw3, dw2,
+        dws1 if shared else None, dws3 if shared else None, dws2 if shared else None,
+        None if routed else dwg, None if routed else db, dtw, bws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nrep = max(3, args.steps // 2)
+    e0.record()
+    for _ in range(nrep):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    layer_ms = e0.elapsed_time(e1) / nrep
+
+    # algorithmic FLOPs per stage: every GEMM launch and its shared-expert twin
+    gu = LG.gateup_flops(M, d, de) + (LG.gateup_flops(T, d, ds) if shared else 0)
+    dn = LG.down_flops(M, d, de) + (LG.down_flops(T, d, ds) if shared else 0)
+    flops = {"dgrad_down": dn, "wgrad_down": dn, "swiglu_bwd": gu, "dgrad_gateup": gu,
+             "wgrad_gateup": gu}
+    peak = PEAK_BF16_TFLOPS
+    gemm = {n: {"us": round(st_ms[n] * 1e3, 2), "tflops": v / (st_ms[n] * 1e9),
+                "frac": v / (st_ms[n] * 1e9) / peak} for n, v in flops.items()}
+    return {"ms_per_step": total, "tokens_per_s": T / (total / 1e3),
+            "layer_bwd_ms_per_call": layer_ms,
+            "fwd_plus_bwd_tokens_per_s": T / ((total + fwd_ms) / 1e3),
+            "stages_us": {n: round(v * 1e3, 2) for n, v in st_ms.items()}, "gemm": gemm,
+            "gemm_tflops_total": sum(flops.values()) / (sum(st_ms[n] for n in flops) * 1e9)}
 
 
 def cpu_baseline(cfg, inp, target_s):

@@ -26,7 +26,8 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
                 "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_grouped_gemm_gather",
                 "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_grouped_gemm_fp8",
                 "moe_layer_fwd_fp8", "moe_combine_bwd", "moe_swiglu_bwd", "moe_grouped_gemm_dgrad",
-                "moe_grouped_gemm_wgrad", "moe_router_bwd", "moe_bwd_workspace_bytes",
+                "moe_grouped_gemm_wgrad", "moe_router_bwd", "moe_router_bwd_workspace_bytes",
+                "moe_bwd_workspace_bytes",
                 "moe_bwd_workspace_layout", "moe_layer_bwd")
 
 
@@ -46,7 +47,8 @@ class moe_ws_layout(ctypes.Structure):
 
 
 _BWD_LAYOUT_FIELDS = ("dy", "dact", "dgu", "x_perm", "dx_perm", "dtopk_w", "dlogits",
-                      "shared_dact", "shared_dgu", "shared_dx", "router_dx", "total")
+                      "shared_dact", "shared_dgu", "shared_dx", "router_dx", "router_scratch",
+                      "total")
 
 
 class moe_bwd_ws_layout(ctypes.Structure):
@@ -114,7 +116,9 @@ def lib():
         L.moe_grouped_gemm_dgrad.restype = ctypes.c_int32
         L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P]
         L.moe_grouped_gemm_wgrad.restype = ctypes.c_int32
-        L.moe_router_bwd.argtypes = [S] + [P] * 11
+        L.moe_router_bwd.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
+        L.moe_router_bwd_workspace_bytes.argtypes = [S]
+        L.moe_router_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.moe_router_bwd.restype = ctypes.c_int32
         L.moe_bwd_workspace_bytes.argtypes = [S]
         L.moe_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -377,11 +381,21 @@ def moe_grouped_gemm_wgrad(shape, op, A, dC, counts, padded_offsets, dB0, dB1, s
         _p(dB1), _stream(stream)))
 
 
+def moe_router_bwd_workspace_bytes(shape: moe_shape) -> int:
+    return lib().moe_router_bwd_workspace_bytes(ctypes.byref(shape))
+
+
 def moe_router_bwd(shape, x, w_gate, logits, topk_idx, dtopk_w, dlogits, dw_gate, dbias, dx_in,
-                   dx_out, stream=None):
+                   dx_out, ws=None, stream=None):
+    """ws: scratch of moe_router_bwd_workspace_bytes(shape) bytes (allocated here when
+    None)."""
+    if ws is None:
+        n = moe_router_bwd_workspace_bytes(shape)
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
     _check("moe_router_bwd", lib().moe_router_bwd(
         ctypes.byref(shape), _p(x), _p(w_gate), _p(logits), _p(topk_idx), _p(dtopk_w),
-        _p(dlogits), _p(dw_gate), _p(dbias), _p(dx_in), _p(dx_out), _stream(stream)))
+        _p(dlogits), _p(dw_gate), _p(dbias), _p(dx_in), _p(dx_out), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def moe_layer_bwd(shape, x, w_gate, w1, w3, w2, ws1, ws3, ws2, topk_idx_in, topk_w_in, dout,

@@ -137,6 +137,7 @@ static void bwd_layout_of(const moe_shape& s, moe_bwd_ws_layout& L) {
   L.shared_dgu = take(cur, T * 2 * ds * 2);
   L.shared_dx = take(cur, ds ? T * d * 2 : 0);
   L.router_dx = take(cur, T * d * 2);
+  L.router_scratch = take(cur, router_bwd_scratch_bytes(s));
   L.total = cur;
 }
 
@@ -633,10 +634,15 @@ moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A,
                          static_cast<hipStream_t>(stream));
 }
 
+size_t moe_router_bwd_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return router_bwd_scratch_bytes(*s);
+}
+
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
                           const float* logits, const int32_t* topk_idx, const float* dtopk_w,
                           float* dlogits, float* dw_gate, float* dbias, const void* dx_in,
-                          void* dx_out, void* stream) {
+                          void* dx_out, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if ((st = check_bwd(*s)) != MOE_OK) return st;
@@ -646,8 +652,10 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
       !aligned4(dtopk_w) || !aligned4(dlogits) || !aligned4(dw_gate) || (dbias && !aligned4(dbias)) ||
       (dx_in && !aligned16(dx_in)) || !aligned16(dx_out))
     return MOE_EINVAL;
+  const size_t need = router_bwd_scratch_bytes(*s);
+  if (need && (!ws || !aligned16(ws) || ws_bytes < need)) return MOE_EWORKSPACE;
   return launch_router_bwd(*s, x, w_gate, logits, topk_idx, dtopk_w, dlogits, dw_gate, dbias, dx_in,
-                           dx_out, static_cast<hipStream_t>(stream));
+                           dx_out, need ? ws : nullptr, static_cast<hipStream_t>(stream));
 }
 
 size_t moe_bwd_workspace_bytes(const moe_shape* s) {
@@ -720,7 +728,7 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
       st = launch_gg_wgrad(x, x, dws2, nullptr, d, des, d, nullptr, nullptr, 1, 0, hs);
     if (st == MOE_OK && (dw_gate || dbias))
       st = launch_router_bwd(*s, x, w_gate, nullptr, nullptr, nullptr, nullptr, dw_gate, dbias,
-                             nullptr, dx, hs);
+                             nullptr, dx, nullptr, hs);
     return st;
   }
   const char* fb = static_cast<const char*>(fwd_ws);
@@ -783,7 +791,7 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
   if (!routed) {
     st = launch_router_bwd(*s, x, w_gate, static_cast<const float*>(fat(F.logits)), idx, dtw,
                            static_cast<float*>(at(L.dlogits)), dw_gate, dbias, extra,
-                           at(L.router_dx), hs);
+                           at(L.router_dx), at(L.router_scratch), hs);
     if (st != MOE_OK) return st;
     extra = at(L.router_dx);
   }

@@ -564,67 +564,135 @@ k_router_bwd(const float* __restrict__ logits, const int32_t* __restrict__ idx,
   }
 }
 
-// dW_g[c, e] = sum_t x[t, c] dlogits[t, e]; dbias[e] = sum_t dlogits[t, e].  A block
-// owns 64 columns c and up to 64 experts; tokens go through LDS 32 at a time; each
-// thread keeps (c, 16 experts) sums, in ascending t.
-__global__ void __launch_bounds__(256)
+// dW_g[c, e] = sum_t x[t, c] dlogits[t, e]; dbias[e] = sum_t dlogits[t, e].  The tokens
+// are cut into contiguous chunks of tchunk (blockIdx.z); a block owns 32 columns c and 16
+// experts of one chunk, its 256 threads being 32 columns x 8 token phases: a thread sums
+// tokens t = begin + phase, + 8, ... in ascending order, and the 8 phase sums are added in
+// phase order through LDS.  Chunk z's sums go to ow + z * ow_stride ([d][E]) and
+// ob + z * ob_stride ([E]; ob NULL: not written); k_router_wgrad_reduce adds the chunks
+// in order when there are several.  The 32 lanes of a phase read one dlogits row (a
+// broadcast) and 64 contiguous bytes of x.
+static constexpr int kRwCols = 32, kRwExp = 16, kRwPhases = 8;
+
+__global__ void __launch_bounds__(kRwCols * kRwPhases)
 k_router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dl, int T, int d, int E,
-               float* __restrict__ dwg, float* __restrict__ dbias) {
-  __shared__ float sx[32][64];
-  __shared__ float sd[32][64];
-  const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int cl = tid & 63, eg = tid >> 6;   // column, expert group of 16
-  float acc[16], bacc[16];
+               int tchunk, float* __restrict__ ow, size_t ow_stride, float* __restrict__ ob,
+               size_t ob_stride) {
+  __shared__ float part[kRwPhases][kRwExp][kRwCols + 1];
+  __shared__ float bpart[kRwPhases][kRwExp];
+  const int cl = threadIdx.x % kRwCols, ph = threadIdx.x / kRwCols;
+  const int c = blockIdx.x * kRwCols + cl, e0 = blockIdx.y * kRwExp;
+  const int ne = min(kRwExp, E - e0);
+  const int tb = blockIdx.z * tchunk, te = min(T, tb + tchunk);
+  float acc[kRwExp], bacc[kRwExp];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = bacc[i] = 0.f;
-  for (int t0 = 0; t0 < T; t0 += 32) {
-    for (int i = tid; i < 32 * 64; i += 256) {
-      const int r = i >> 6, cc = i & 63;
-      const int t = t0 + r;
-      sx[r][cc] = (t < T && c0 + cc < d) ? bf16_to_f32(x[(size_t)t * d + c0 + cc]) : 0.f;
-      sd[r][cc] = (t < T && e0 + cc < E) ? dl[(size_t)t * E + e0 + cc] : 0.f;
-    }
-    __syncthreads();
-    for (int r = 0; r < 32; ++r) {
-      const float xv = sx[r][cl];
+  for (int i = 0; i < kRwExp; ++i) acc[i] = bacc[i] = 0.f;
+#pragma unroll 4
+  for (int t = tb + ph; t < te; t += kRwPhases) {
+    const float xv = c < d ? bf16_to_f32(x[(size_t)t * d + c]) : 0.f;
+    const float* dr = dl + (size_t)t * E + e0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc[i] = fmaf(xv, sd[r][eg * 16 + i], acc[i]);
-        bacc[i] += sd[r][eg * 16 + i];
-      }
+    for (int i = 0; i < kRwExp; ++i) {
+      const float gv = i < ne ? dr[i] : 0.f;
+      acc[i] = fmaf(xv, gv, acc[i]);
+      bacc[i] += gv;
     }
-    __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = e0 + eg * 16 + i;
-    if (dwg && c0 + cl < d && e < E) dwg[(size_t)(c0 + cl) * E + e] = acc[i];
-    if (dbias && blockIdx.x == 0 && cl == 0 && e < E) dbias[e] = bacc[i];
+  for (int i = 0; i < kRwExp; ++i) part[ph][i][cl] = acc[i];
+  if (cl == 0) {
+#pragma unroll
+    for (int i = 0; i < kRwExp; ++i) bpart[ph][i] = bacc[i];
+  }
+  __syncthreads();
+  float* const w = ow + blockIdx.z * ow_stride;
+  for (int o = threadIdx.x; o < kRwCols * kRwExp; o += kRwCols * kRwPhases) {
+    const int oc = o % kRwCols, oi = o / kRwCols;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < kRwPhases; ++p) v += part[p][oi][oc];
+    const int cc = blockIdx.x * kRwCols + oc;
+    if (ow && cc < d && oi < ne) w[(size_t)cc * E + e0 + oi] = v;
+  }
+  if (ob && blockIdx.x == 0 && threadIdx.x < ne) {
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < kRwPhases; ++p) v += bpart[p][threadIdx.x];
+    ob[blockIdx.z * ob_stride + e0 + threadIdx.x] = v;
   }
 }
 
-// dx_add[t, c] = base[t, c] + sum_e dlogits[t, e] W_g[c, e] (base may be NULL: 0),
-// rounded once to bf16.  One block per token.
+// dW_g = sum over the chunks in order (and dbias likewise; either output may be NULL).
+__global__ void __launch_bounds__(256)
+k_router_wgrad_reduce(const float* __restrict__ pw, const float* __restrict__ pb, int nchunks,
+                      int64_t n, int E, float* __restrict__ dwg, float* __restrict__ dbias) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (dwg && i < n) {
+    float v = 0.f;
+    for (int z = 0; z < nchunks; ++z) v += pw[(size_t)z * n + i];
+    dwg[i] = v;
+  }
+  if (dbias && i < E) {
+    float v = 0.f;
+    for (int z = 0; z < nchunks; ++z) v += pb[(size_t)z * E + i];
+    dbias[i] = v;
+  }
+}
+
+// Token chunks of the router's weight gradient: enough blocks to fill the chip (about
+// 2048), chunks of at least 256 tokens.
+static int router_wgrad_chunks(const moe_shape& s) {
+  const int64_t blocks2d = ceil_div(s.d, kRwCols) * ceil_div(s.E, kRwExp);
+  const int64_t want = ceil_div(2048, blocks2d);
+  const int64_t most = ceil_div(s.T, 256);
+  int64_t n = want < most ? want : most;
+  return (int)(n < 1 ? 1 : n);
+}
+
+size_t router_bwd_scratch_bytes(const moe_shape& s) {
+  const int n = router_wgrad_chunks(s);
+  return n > 1 ? (size_t)n * ((size_t)s.d * s.E + s.E) * sizeof(float) : 0;
+}
+
+// dx_out[t, c] = (base[t, c] if base) + sum_e dlogits[t, e] W_g[c, e], rounded once to
+// bf16.  A block owns 16 tokens (their dlogits rows in LDS, read as broadcasts) and 256
+// columns (one per thread, its W_g row read once for all 16 tokens).
+static constexpr int kRdTok = 16;
+
 __global__ void __launch_bounds__(256)
 k_router_dx(const float* __restrict__ dl, const bf16_t* __restrict__ wg, const bf16_t* __restrict__ base,
             int T, int d, int E, bf16_t* __restrict__ out) {
-  extern __shared__ float s_dl[];
-  const int t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += 256) s_dl[e] = dl[(size_t)t * E + e];
+  extern __shared__ float s_dl[];   // [kRdTok][E]
+  const int t0 = blockIdx.x * kRdTok;
+  const int nt = min(kRdTok, T - t0);
+  for (int i = threadIdx.x; i < kRdTok * E; i += 256) {
+    const int tt = i / E;
+    s_dl[i] = tt < nt ? dl[(size_t)(t0 + tt) * E + i % E] : 0.f;
+  }
   __syncthreads();
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float v = base ? bf16_to_f32(base[(size_t)t * d + c]) : 0.f;
-    const bf16_t* wr = wg + (size_t)c * E;
-    for (int e = 0; e < E; ++e) v = fmaf(s_dl[e], bf16_to_f32(wr[e]), v);
-    out[(size_t)t * d + c] = f32_to_bf16(v);
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= d) return;
+  float v[kRdTok];
+#pragma unroll
+  for (int tt = 0; tt < kRdTok; ++tt) v[tt] = 0.f;
+  const bf16_t* wr = wg + (size_t)c * E;
+  for (int e = 0; e < E; ++e) {
+    const float w = bf16_to_f32(wr[e]);
+#pragma unroll
+    for (int tt = 0; tt < kRdTok; ++tt) v[tt] = fmaf(s_dl[tt * E + e], w, v[tt]);
+  }
+#pragma unroll
+  for (int tt = 0; tt < kRdTok; ++tt) {
+    if (tt >= nt) break;
+    const size_t o = (size_t)(t0 + tt) * d + c;
+    out[o] = f32_to_bf16(base ? bf16_to_f32(base[o]) + v[tt] : v[tt]);
   }
 }
 
 moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_gate,
                              const float* logits, const int32_t* idx, const float* dw,
                              float* dlogits, float* dw_gate, float* dbias, const void* dx_base,
-                             void* dx_out, hipStream_t st) {
+                             void* dx_out, void* scratch, hipStream_t st) {
   if (s.E > 64 * kRbMaxPerLane) return MOE_ENOTSUP;
   if (s.T > 0) {
     hipLaunchKernelGGL(k_router_bwd, dim3((unsigned)ceil_div(s.T, 4)), dim3(256), 0, st, logits,
@@ -633,13 +701,32 @@ moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_ga
   }
   // with T == 0 the weight gradients are zeros (the kernel reads no rows)
   if (dw_gate || dbias) {
-    hipLaunchKernelGGL(k_router_wgrad, dim3((unsigned)ceil_div(s.d, 64), (unsigned)ceil_div(s.E, 64)),
-                       dim3(256), 0, st, static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E,
-                       dw_gate, dbias);
+    const int nch = router_wgrad_chunks(s);
+    const int tchunk = (int)(ceil_div(ceil_div(s.T, nch), kRwPhases) * kRwPhases);
+    const dim3 grid((unsigned)ceil_div(s.d, kRwCols), (unsigned)ceil_div(s.E, kRwExp),
+                    (unsigned)nch);
+    const int64_t n = (int64_t)s.d * s.E;
+    if (nch == 1) {
+      // one chunk: the sums go straight to the outputs (either may be NULL)
+      hipLaunchKernelGGL(k_router_wgrad, grid, dim3(kRwCols * kRwPhases), 0, st,
+                         static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E, tchunk,
+                         dw_gate, (size_t)0, dbias, (size_t)0);
+    } else {
+      if (!scratch) return MOE_EWORKSPACE;
+      float* pw = static_cast<float*>(scratch);
+      float* pb = pw + (size_t)nch * n;
+      hipLaunchKernelGGL(k_router_wgrad, grid, dim3(kRwCols * kRwPhases), 0, st,
+                         static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E, tchunk, pw,
+                         (size_t)n, pb, (size_t)s.E);
+      if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+      hipLaunchKernelGGL(k_router_wgrad_reduce, dim3((unsigned)ceil_div(n > s.E ? n : s.E, 256)),
+                         dim3(256), 0, st, pw, pb, nch, n, s.E, dw_gate, dbias);
+    }
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   }
   if (s.T > 0) {
-    hipLaunchKernelGGL(k_router_dx, dim3((unsigned)s.T), dim3(256), (size_t)s.E * sizeof(float), st,
+    hipLaunchKernelGGL(k_router_dx, dim3((unsigned)ceil_div(s.T, kRdTok), (unsigned)ceil_div(s.d, 256)),
+                       dim3(256), (size_t)kRdTok * s.E * sizeof(float), st,
                        dlogits, static_cast<const bf16_t*>(w_gate),
                        static_cast<const bf16_t*>(dx_base), s.T, s.d, s.E,
                        static_cast<bf16_t*>(dx_out));

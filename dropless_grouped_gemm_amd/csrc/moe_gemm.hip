@@ -459,17 +459,63 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
     // [rows][cols + 8] staging tile, then stores whole 16-byte row chunks.  32x32
     // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
     // l%32 of the 32x32 subtile.
+    if constexpr (BWD) {
+      // SwiGLU backward (op 2): per 32-row subtile, the wave's [32][32] block of dact is
+      // copied to LDS (two 16-byte copies per lane; rows past the valid ones and columns
+      // past N read row 0 / column 0, never stored), then dg and du come from one
+      // sigmoid, are staged side by side and stored into C = [rows, 2N] (dg in columns
+      // [0, N), du in [N, 2N)).
+      constexpr int kLd = 32 + 8;
+      bf16_t* so = reinterpret_cast<bf16_t*>(lds) + wave * 2 * 32 * kLd;
+      unsigned char* sda = lds + kV2Threads / 64 * 2 * 32 * kLd * 2 + wave * 2048;
+      const bf16_t* dbase = uniform_ptr(ops.D + (size_t)tile.m0 * N);
+      const int dcol = n0 + wave * 32 + (lane & 3) * 8;
+      const int dcc = dcol < N ? dcol : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i * 32 >= tile.valid) break;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = i * 32 + 16 * j + (lane >> 2);
+          const int rr = r < tile.valid ? r : 0;
+          copy16_to_lds(dbase, (uint32_t)(rr * N + dcc) * 2u, sda + j * 1024);
+        }
+        MOE_WAIT_VMCNT(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          const int c = lane & 31;
+          const float da = bf16_to_f32(*reinterpret_cast<const bf16_t*>(sda + (r * 32 + c) * 2));
+          const float gv = acc[i][0][q], uv = acc[i][1][q];
+          const float sg = 1.0f / (1.0f + expf(-gv));
+          so[r * kLd + c] = f32_to_bf16(da * uv * (sg * (1.0f + gv * (1.0f - sg))));
+          so[(32 + r) * kLd + c] = f32_to_bf16(da * gv * sg);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+          for (int r0 = 0; r0 < 32; r0 += 16) {
+            const int r = r0 + (lane >> 2);
+            const int grow = i * 32 + r;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(so + (ps * 32 + r) * kLd + (lane & 3) * 8);
+            if (grow < tile.valid && dcol < N)
+              *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * 2 * N + ps * N + dcol) = v;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    } else {
     constexpr int kWCols = GU ? 32 : 64;   // output columns per wave
     constexpr int kHalves = GU ? 1 : 2;    // row passes
     constexpr int kRowsPer = 128 / kHalves;
     constexpr int kLd = kWCols + 8;                                 // staging row pitch
     bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kRowsPer * kLd;
     const int col0 = n0 + (GU ? wave * 32 : (wave >> 2) * 256 + (wave & 3) * 64);
-    // op 2 writes two outputs into C = [rows, 2N]: dg (pass 0) then du (pass 1)
-    constexpr int kOutPasses = BWD ? 2 : 1;
-    const int ldc = BWD ? 2 * N : N;
-#pragma unroll
-    for (int pass = 0; pass < kOutPasses; ++pass)
 #pragma unroll
     for (int hv = 0; hv < kHalves; ++hv) {
 #pragma unroll
@@ -478,14 +524,7 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int r = (i % (4 / kHalves)) * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (BWD) {
-            const int grow = hv * kRowsPer + r, gcol = col0 + (lane & 31);
-            const float da = (grow < tile.valid && gcol < N)
-                                 ? bf16_to_f32(ops.D[(size_t)(tile.m0 + grow) * N + gcol]) : 0.f;
-            const float gv = acc[i][0][q], uv = acc[i][1][q];
-            stg[r * kLd + (lane & 31)] = f32_to_bf16(pass == 0 ? swiglu_dgate(gv, uv, da)
-                                                               : swiglu_dup(gv, da));
-          } else if (GU) {
+          if (GU) {
             stg[r * kLd + (lane & 31)] = f32_to_bf16(silu_f32(acc[i][0][q]) * acc[i][1][q]);
           } else {
 #pragma unroll
@@ -507,11 +546,12 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
         const int gcol = col0 + ch * 8;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + ch * 8);
         if (grow < tile.valid && gcol < N)
-          *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * ldc + pass * N + gcol) = v;
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + grow) * N + gcol) = v;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     }
     __syncthreads();  // staging reads done before the next tile refills the ring
   }

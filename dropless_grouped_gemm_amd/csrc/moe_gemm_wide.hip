@@ -370,13 +370,63 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     // a private [WR][64 + 8] staging tile, then stores whole 16-byte row chunks.  32x32
     // accumulator layout: element q of lane l is row (q/4)*8 + (l/32)*4 + q%4, column
     // l%32 of the subtile.
-    // The SwiGLU backward (op 2) writes two outputs, dg then du, in two passes; each
-    // element's incoming gradient dact is read from global memory (32 lanes of a row
-    // read 64 contiguous bytes).
+    if constexpr (BWD) {
+      // SwiGLU backward (op 2): per 32-row subtile, the wave's [32][64] block of the
+      // incoming gradient dact is copied to LDS (four 16-byte copies per lane; rows past
+      // the valid ones and columns past N read row 0 / column 0, never stored), then dg
+      // and du are computed from one sigmoid, staged side by side and stored into
+      // C = [rows, 2N] (dg in columns [0, N), du in [N, 2N)).
+      constexpr int kLd = 64 + 8;
+      bf16_t* so = reinterpret_cast<bf16_t*>(lds) + wave * 2 * 32 * kLd;
+      unsigned char* sda = lds + NW * 2 * 32 * kLd * 2 + wave * 4096;
+      const bf16_t* dbase = uniform_ptr(ops.D + (size_t)m0 * N);
+      const int dcol = n0 + ch * 64 + (lane & 7) * 8;
+      const int dcc = dcol < N ? dcol : 0;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int rsub = rbase + i * 32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = rsub + 8 * j + (lane >> 3);
+          const int rr = r < valid ? r : 0;
+          copy16_to_lds(dbase, (uint32_t)(rr * N + dcc) * 2u, sda + j * 1024);
+        }
+        MOE_WAIT_VMCNT(0);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int r = (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int c = jj * 32 + (lane & 31);
+            const float da = bf16_to_f32(*reinterpret_cast<const bf16_t*>(sda + (r * 64 + c) * 2));
+            const float gv = acc[i][jj][q], uv = acc[i][jj + 2][q];
+            const float sg = 1.0f / (1.0f + expf(-gv));
+            so[r * kLd + c] = f32_to_bf16(da * uv * (sg * (1.0f + gv * (1.0f - sg))));
+            so[(32 + r) * kLd + c] = f32_to_bf16(da * gv * sg);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+#pragma unroll
+          for (int r0 = 0; r0 < 32; r0 += 8) {
+            const int r = r0 + (lane >> 3);
+            const int grow = rsub + r;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(so + (ps * 32 + r) * kLd + (lane & 7) * 8);
+            if (grow < valid && dcol < N)
+              *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * 2 * N + ps * N + dcol) = v;
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    } else {
     constexpr int kLd = 64 + 8;
-    constexpr int kPasses = (GU && !BWD) ? 1 : 2;
+    constexpr int kPasses = GU ? 1 : 2;
     bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * WR * kLd;
-    const bf16_t* dact = ops.D;
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
 #pragma unroll
@@ -387,13 +437,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             float v;
-            if (BWD) {
-              const int grow = rbase + r, gcol = n0 + ch * 64 + jj * 32 + (lane & 31);
-              const float da = (grow < valid && gcol < N)
-                                   ? bf16_to_f32(dact[(size_t)(m0 + grow) * N + gcol]) : 0.f;
-              const float gv = acc[i][jj][q], uv = acc[i][jj + 2][q];
-              v = ps == 0 ? swiglu_dgate(gv, uv, da) : swiglu_dup(gv, da);
-            } else if (GU) {
+            if (GU) {
               v = silu_f32(acc[i][jj][q]) * acc[i][jj + 2][q];
             } else {
               v = acc[i][ps * 2 + jj][q];
@@ -406,9 +450,6 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int col0 = n0 + (GU ? ch * 64 : ch * 128 + ps * 64);
-      // op 2: C is [rows, 2N], dg in columns [0, N), du in [N, 2N)
-      const int ldc = BWD ? 2 * N : N;
-      const int cofs = BWD ? ps * N : 0;
 #pragma unroll 4
       for (int r0 = 0; r0 < WR; r0 += 8) {
         const int r = r0 + (lane >> 3);
@@ -417,11 +458,12 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         const int gcol = col0 + c8 * 8;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + c8 * 8);
         if (grow < valid && gcol < N)
-          *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * ldc + cofs + gcol) = v;
+          *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * N + gcol) = v;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     }
     __syncthreads();  // staging reads done before the next item refills the ring
   }

@@ -158,11 +158,13 @@ moe_status launch_gg_wgrad(const void* X, const void* D, float* C0, float* C1, i
                            int Nn, const int32_t* counts, const int32_t* row_off, int E,
                            int32_t dense_rows, hipStream_t st);
 // dlogits from dw through the softmax (and renormalisation), selection fixed; then
-// dw_gate = x^T dlogits, dbias = column sums (NULL: skipped), and
-// dx_out = dx_base (NULL: 0) + dlogits w_gate^T in bf16.
+// dw_gate = x^T dlogits, dbias = column sums (either NULL: skipped), and
+// dx_out = dx_base (NULL: 0) + dlogits w_gate^T in bf16.  scratch: router_bwd_scratch_bytes
+// (the per-chunk partial sums of dw_gate and dbias).
+size_t router_bwd_scratch_bytes(const moe_shape& s);
 moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_gate,
                              const float* logits, const int32_t* idx, const float* dw,
                              float* dlogits, float* dw_gate, float* dbias, const void* dx_base,
-                             void* dx_out, hipStream_t st);
+                             void* dx_out, void* scratch, hipStream_t st);
 
 }  // namespace moe

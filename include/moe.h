@@ -402,20 +402,24 @@ moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A,
  * topk_idx [T, k], dtopk_w [T, k] fp32; dx_in [T, d] or NULL.
  * Out: dlogits [T, E] fp32, dw_gate [d, E] fp32, dbias [E] fp32 (or NULL: skipped),
  *      dx_out [T, d] = dx_in + dlogits w_gate^T (bf16, one rounding).
+ * ws:  device scratch of ws_bytes >= moe_router_bwd_workspace_bytes(s) (the token-chunk
+ *      partial sums of dw_gate and dbias; may be 0 bytes, ws then NULL).
  */
+size_t moe_router_bwd_workspace_bytes(const moe_shape* s);
 moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
                           const float* logits, const int32_t* topk_idx, const float* dtopk_w,
                           float* dlogits, float* dw_gate, float* dbias, const void* dx_in,
-                          void* dx_out, void* stream);
+                          void* dx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Host-only and pure: bytes of the backward workspace and the offsets of its
  * intermediates (dy, dact, dgu, x_perm, dx_perm [rows, .]; dtopk_w [T, k] and dlogits
- * [T, E] fp32; the shared expert's dact, dgu, dx and the router's dx [T, .]).
+ * [T, E] fp32; the shared expert's dact, dgu, dx and the router's dx [T, .]; the
+ * router's scratch).
  */
 typedef struct moe_bwd_ws_layout {
   size_t dy, dact, dgu, x_perm, dx_perm, dtopk_w, dlogits, shared_dact, shared_dgu,
-         shared_dx, router_dx, total;
+         shared_dx, router_dx, router_scratch, total;
 } moe_bwd_ws_layout;
 size_t moe_bwd_workspace_bytes(const moe_shape* s);
 moe_status moe_bwd_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout);

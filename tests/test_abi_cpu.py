@@ -323,7 +323,7 @@ def test_backward_entry_point_argument_rules():
                                         None) == B.MOE_ENOTSUP
         assert L.moe_grouped_gemm_wgrad(pb, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                         None) == B.MOE_ENOTSUP
-        assert L.moe_router_bwd(pb, *([FAKE] * 10), None) == B.MOE_ENOTSUP
+        assert L.moe_router_bwd(pb, *([FAKE] * 10), FAKE, 1 << 40, None) == B.MOE_ENOTSUP
     assert L.moe_combine_bwd(ctypes.byref(good_shape(d=8224)), *([FAKE] * 6), None) == B.MOE_ENOTSUP
     # combine backward: every pointer required
     assert L.moe_combine_bwd(ps, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
@@ -355,8 +355,17 @@ def test_backward_entry_point_argument_rules():
     assert wg(ps, 1, odd, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
     # router backward: dbias and dx_in optional, the rest required
     rb = L.moe_router_bwd
-    assert rb(ps, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None) == B.MOE_EINVAL
-    assert rb(ps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None) == B.MOE_EINVAL
+    big = 1 << 40
+    assert rb(ps, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, big,
+              None) == B.MOE_EINVAL
+    assert rb(ps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, big,
+              None) == B.MOE_EINVAL
+    # the token-chunk partial sums need their scratch once the tokens are split
+    sw = good_shape(T=8192, d=7168, E=8, k=4)
+    need = L.moe_router_bwd_workspace_bytes(ctypes.byref(sw))
+    assert need > 0
+    assert rb(ctypes.byref(sw), *([FAKE] * 10), FAKE, need - 1, None) == B.MOE_EWORKSPACE
+    assert rb(ctypes.byref(sw), *([FAKE] * 10), None, need, None) == B.MOE_EWORKSPACE
     # layer backward: workspaces, routing pair, shared operands, router-only outputs
     lb = L.moe_layer_bwd
     fwd_need, bwd_need = L.moe_workspace_bytes(ps), L.moe_bwd_workspace_bytes(ps)
@@ -387,7 +396,8 @@ def test_backward_workspace_layout_is_disjoint_and_aligned():
         sizes = dict(dy=rows * d * 2, dact=rows * de * 2, dgu=rows * 2 * de * 2, x_perm=rows * d * 2,
                      dx_perm=rows * d * 2, dtopk_w=T * s.k * 4, dlogits=T * s.E * 4,
                      shared_dact=T * ds * 2, shared_dgu=T * 2 * ds * 2,
-                     shared_dx=T * d * 2 if ds else 0, router_dx=T * d * 2)
+                     shared_dx=T * d * 2 if ds else 0, router_dx=T * d * 2,
+                     router_scratch=B.moe_router_bwd_workspace_bytes(s))
         spans = sorted((L[n], L[n] + sz) for n, sz in sizes.items() if sz)
         assert all(o % 256 == 0 for o, _ in spans)
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
