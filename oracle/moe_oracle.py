@@ -14,7 +14,8 @@ the order the pages give the steps.  Sources, cited by page title and section:
   [DG]  Course notes "Dropless and grouped GEMM" (topic-01-dropless): section 1
         (shared expert, received rows), 3 (pad every segment to a multiple of 128),
         4 (the per-step tensor table), 5 (offsets as a prefix sum, tile -> expert
-        tables), 7 (the per-expert for-loop formulation), 10 (decode boundary cases).
+        tables), 7 (the per-expert for-loop formulation), 10 (decode boundary cases),
+        11 (the unpadded alternative: boundary tiles executed once per group).
 
 Readings taken where the pages are silent or ambiguous (each one is also listed in
 the design notes):
@@ -210,6 +211,38 @@ def permutation(idx, E: int, block_m: int):
     row_src = np.full(int(P[-1]), -1, dtype=np.int64)
     row_src[pos] = np.arange(M)
     return pos, row_src
+
+
+# ----------------------------------------------------------------------------
+# Step 3' - unpadded segments  [DG §11: a boundary tile executed once per group]
+# ----------------------------------------------------------------------------
+def unpadded_tile_table(counts, tile: int):
+    """The executions of the unpadded layout, rows (expert, m_start, valid_m).
+
+    [DG §11]: no segment is rounded up; expert e keeps rows [off[e], off[e+1]) of the
+    M = sum(c) rows (off = group_offsets).  The row space is cut into tiles of ``tile``
+    rows (the last one may be short), and a tile holding rows of several experts is
+    executed once for each of them with that expert's weights, restricted to that
+    expert's rows.  Executions are listed tile by tile and, inside a tile, by expert;
+    m_start is the expert's first row in the tile, valid_m its number of rows there.
+    """
+    off = group_offsets(counts)
+    M = int(off[-1])
+    out = []
+    for t0 in range(0, M, tile):
+        t1 = min(t0 + tile, M)
+        for e in range(len(off) - 1):
+            lo, hi = max(t0, int(off[e])), min(t1, int(off[e + 1]))
+            if hi > lo:
+                out.append((e, lo, hi - lo))
+    return np.asarray(out, dtype=np.int64).reshape(-1, 3)
+
+
+def permutation_unpadded(idx, E: int):
+    """pos / row_src of the unpadded layout: the stable sort of ``permutation`` with
+    every segment at its real length (a padding multiple of 1), so row_src covers
+    exactly the M assignments."""
+    return permutation(idx, E, 1)
 
 
 # ----------------------------------------------------------------------------

@@ -429,3 +429,62 @@ def test_waste_report_definition():
     assert rep["padded_rows"] == 64 + 7 * 32
     assert math.isclose(rep["waste"], (288 - 128) / 128)
     assert math.isclose(rep["hottest_over_mean"], 53 / 16)
+
+
+# ---------------------------------------------------------------------------
+# Unpadded segments ([DG] §11)
+# ---------------------------------------------------------------------------
+def test_unpadded_tiles_worked_example():
+    """[DG] §11's example: 65,536 rows in tiles of 128 for the counts of §3; the three
+    segment starts 21,733 / 36,737 / 54,719 are off the tile grid, so 512 tiles become
+    515 executions (65,920 rows' worth, +0.59 %) against the padded layout's 65,792
+    rows (+0.39 %).  Tile 169 holds e0's rows 21,632-21,732 and then e1's."""
+    counts = [21733, 15004, 17982, 10817]
+    tab = O.unpadded_tile_table(counts, 128)
+    assert list(O.group_offsets(counts)) == [0, 21733, 36737, 54719, 65536]
+    assert 65536 // 128 == 512 and len(tab) == 515
+    assert len(tab) * 128 == 65920
+    assert round(100 * (65920 - 65536) / 65536, 2) == 0.59
+    assert int(O.padded_offsets(counts, 128)[-1]) == 65792
+    assert round(100 * (65792 - 65536) / 65536, 2) == 0.39
+    at169 = [tuple(r) for r in tab if r[1] // 128 == 169]
+    assert at169 == [(0, 21632, 101), (1, 21733, 27)]
+    # the padded layout pays the same boundary with 27 pad rows
+    assert 21760 - 21733 == 27
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_unpadded_tiles_partition_the_rows(seed):
+    """Brute force: label every row with its expert; the executions cover each row once,
+    in order, each inside one tile and one expert's rows, and their number is the count
+    of distinct experts over the tiles, between tiles_m and tiles_m + E_nonempty - 1."""
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 9))
+    tile = int(rng.choice([1, 2, 3, 4, 8, 16, 128]))
+    counts = rng.integers(0, 3 * tile, size=E) * rng.integers(0, 2, size=E)
+    counts[rng.integers(0, E)] += 1
+    tab = O.unpadded_tile_table(counts, tile)
+    label = np.repeat(np.arange(E), counts)
+    M = label.size
+    nxt = 0
+    for e, m, v in tab:
+        assert m == nxt and v >= 1
+        assert (m // tile) == ((m + v - 1) // tile)            # one tile
+        assert np.all(label[m:m + v] == e)                     # one expert
+        nxt = m + v
+    assert nxt == M
+    distinct = sum(len(set(label[t:t + tile])) for t in range(0, M, tile))
+    tiles_m = -(-M // tile)
+    assert len(tab) == distinct
+    assert tiles_m <= len(tab) <= tiles_m + int(np.count_nonzero(counts)) - 1
+
+
+def test_unpadded_permutation_is_the_stable_sort_without_gaps():
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, 5, size=(37, 3))
+    pos, row_src = O.permutation_unpadded(idx, 5)
+    flat = idx.ravel()
+    assert row_src.size == flat.size and np.all(row_src >= 0)
+    assert np.array_equal(flat[row_src], np.sort(flat, kind="stable"))
+    assert np.array_equal(row_src, np.argsort(flat, kind="stable"))
+    assert np.array_equal(pos[row_src], np.arange(flat.size))
