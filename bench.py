@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--weights", choices=("bf16", "fp8"), default="bf16",
                     help="fp8: expert weights quantised to e4m3 with a scale per 128x128 "
                          "block (quantised once, outside the timed region)")
+    ap.add_argument("--unpadded", action="store_true",
+                    help="unpadded segments: tiles straddling an expert boundary get one "
+                         "block-table entry per expert, no pad rows")
     ap.add_argument("--backward", action="store_true",
                     help="also time the layer's backward pass (per stage and moe_layer_bwd) and "
                          "report it under 'backward'")
@@ -77,6 +80,8 @@ def main():
     from workloads import get_config, make_inputs
 
     cfg = get_config(args.config)
+    if args.unpadded:
+        cfg = cfg.scaled(name=cfg.name, unpadded=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = make_inputs(cfg, device=dev)
@@ -354,7 +359,8 @@ def main():
         "data": "synthetic (seeded; N(0,1) tokens, N(0,1/fan_in) weights, random-init)",
         "config": {"workload": cfg.description, "name": cfg.name, "T": T, "d": d, "E": E, "k": k,
                    "d_e": de, "d_e_shared": cfg.d_e_shared, "block_m": cfg.block_m,
-                   "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "seed": cfg.seed},
+                   "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "seed": cfg.seed,
+                   "layout": "unpadded" if cfg.unpadded else "padded"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages_us": {st: round(v * 1e3, 2) for st, v in stage_ms.items()},
@@ -363,6 +369,8 @@ def main():
         "layer_fwd_ms_per_call": layer_fwd_ms,
         "layer_fwd_matches_staged": same,
         "active_experts": active,
+        "blocks": int(nblk.item()),
+        "rows": int(pad[E].item()),
         "wall_s": wall,
     }
     if bwd is not None:

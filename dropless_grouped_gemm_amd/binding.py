@@ -34,7 +34,7 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
 class moe_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("T", "d", "E", "k", "d_e", "n_groups", "topk_groups", "renormalize",
-                 "block_m", "d_e_shared", "dtype")]
+                 "block_m", "d_e_shared", "dtype", "unpadded")]
 
 
 _LAYOUT_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "padded_offsets",
@@ -136,17 +136,17 @@ def status_str(status: int) -> str:
 
 
 def make_shape(T, d, E, k, d_e, block_m, dtype="bf16", n_groups=0, topk_groups=0,
-               renormalize=False, d_e_shared=0) -> moe_shape:
+               renormalize=False, d_e_shared=0, unpadded=False) -> moe_shape:
     dt = {"bf16": MOE_DTYPE_BF16, "fp32": MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16,
           torch.float32: MOE_DTYPE_F32}[dtype]
     return moe_shape(T, d, E, k, d_e, n_groups, topk_groups, int(bool(renormalize)), block_m,
-                     d_e_shared, dt)
+                     d_e_shared, dt, int(bool(unpadded)))
 
 
 def shape_of_config(cfg) -> moe_shape:
     """moe_shape of a workloads.MoEConfig."""
     return make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_e, cfg.block_m, cfg.dtype, cfg.n_groups,
-                      cfg.topk_groups, cfg.renormalize, cfg.d_e_shared)
+                      cfg.topk_groups, cfg.renormalize, cfg.d_e_shared, cfg.unpadded)
 
 
 def _p(t: Optional[torch.Tensor]):

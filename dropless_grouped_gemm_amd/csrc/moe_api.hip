@@ -52,6 +52,7 @@ static moe_status check_shape(const moe_shape* sp) {
     if (s.n_groups > 64) return MOE_ENOTSUP;
   }
   if (s.renormalize != 0 && s.renormalize != 1) return MOE_EINVAL;
+  if (s.unpadded != 0 && s.unpadded != 1) return MOE_EINVAL;
   if (s.block_m < 1) return MOE_EINVAL;
   if (s.d_e_shared < 0 || (s.d_e_shared % mult)) return MOE_EINVAL;
   if (s.dtype == MOE_DTYPE_BF16 && s.block_m % 128) return MOE_ENOTSUP;
@@ -78,8 +79,13 @@ static moe_status check_routing(const moe_shape& s) {
 static int64_t max_blocks_of(const moe_shape& s) {
   const int64_t M = (int64_t)s.T * s.k;
   const int64_t ne = M < s.E ? M : s.E;
+  // unpadded: one entry per tile plus one per expert boundary inside a tile
+  if (s.unpadded) return M == 0 ? 0 : ceil_div(M, s.block_m) + ne - 1;
   return (M + ne * (s.block_m - 1)) / s.block_m;
 }
+
+// Rows of every permuted buffer (x_perm, act, y, row_src).
+static int64_t max_rows_of(const moe_shape& s) { return routed_rows_bound(s, max_blocks_of(s)); }
 
 static size_t take(size_t& cur, size_t bytes) {
   const size_t off = cur;
@@ -91,7 +97,7 @@ static void layout_of(const moe_shape& s, moe_ws_layout& L) {
   const size_t b = elem_bytes(s);
   const size_t T = s.T, E = s.E, M = (size_t)s.T * s.k;
   const size_t mb = (size_t)max_blocks_of(s);
-  const size_t rows = mb * s.block_m;
+  const size_t rows = (size_t)max_rows_of(s);
   size_t cur = 0;
   L.logits = take(cur, T * E * 4);
   L.topk_idx = take(cur, M * 4);
@@ -123,7 +129,7 @@ static moe_status check_bwd(const moe_shape& s) {
 
 static void bwd_layout_of(const moe_shape& s, moe_bwd_ws_layout& L) {
   const size_t T = s.T, E = s.E, M = (size_t)s.T * s.k;
-  const size_t rows = (size_t)max_blocks_of(s) * s.block_m;
+  const size_t rows = (size_t)max_rows_of(s);
   const size_t d = s.d, de = s.d_e, ds = s.d_e_shared;
   size_t cur = 0;
   L.dy = take(cur, rows * d * 2);
@@ -165,7 +171,7 @@ int32_t moe_max_blocks(const moe_shape* s) {
 
 int64_t moe_max_rows(const moe_shape* s) {
   if (check_shape(s) != MOE_OK) return -1;
-  return max_blocks_of(*s) * s->block_m;
+  return max_rows_of(*s);
 }
 
 size_t moe_workspace_bytes(const moe_shape* s) {
@@ -349,15 +355,15 @@ static moe_status run_fp8_op(const moe_shape& s, int op, const void* A, const ui
                    row_src, s.k, s.T};
   if (shared && Ks == K && Ns == N) {
     g.Ad = As; g.Q0d = Q0s; g.S0d = S0s; g.Q1d = Q1s; g.S1d = S1s; g.Cd = Cs; g.dense_rows = s.T;
-    return launch_grouped_gemm_fp8(op, g, s.E, st);
+    return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), st);
   }
   if (shared) {
     GemmSegmentsF8 d{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Ks, Ns, nullptr, nullptr,
                      0, As, Q0s, S0s, Q1s, S1s, Cs, s.T, nullptr, 1, 1};
-    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, st);
+    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, s.T, st);
     if (st2 != MOE_OK) return st2;
   }
-  return launch_grouped_gemm_fp8(op, g, s.E, st);
+  return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), st);
 }
 
 moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, const uint8_t* Q0,
@@ -559,7 +565,7 @@ moe_status moe_combine_bwd(const moe_shape* s, const void* dout, const void* y,
       !aligned4(topk_w) || !aligned4(dtopk_w))
     return MOE_EINVAL;
   if (s->T == 0) return MOE_OK;
-  return launch_combine_bwd(*s, dout, y, pos, topk_w, dy, dtopk_w, max_blocks_of(*s) * s->block_m,
+  return launch_combine_bwd(*s, dout, y, pos, topk_w, dy, dtopk_w, max_rows_of(*s),
                             static_cast<hipStream_t>(stream));
 }
 
@@ -609,7 +615,8 @@ moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC
   const int K = gu ? 2 * s->d_e : s->d, N = gu ? s->d : s->d_e;
   const int ldb = gu ? s->d_e : s->d;
   return launch_gg_nt(dC, B0, B1, ldb, gu ? s->d_e : K, dA, K, N, block_meta, num_blocks,
-                      dense ? 0 : max_blocks, dense ? 1 : s->E, s->block_m, dense ? s->T : 0,
+                      dense ? 0 : max_blocks, dense ? 1 : s->E, s->block_m,
+                      routed_rows_bound(*s, max_blocks), dense ? s->T : 0,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -746,17 +753,17 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
   float* dtw = dtopk_w ? dtopk_w : static_cast<float*>(at(L.dtopk_w));
 
   // combine
-  st = launch_combine_bwd(*s, dout, fat(F.y), pos, wts, at(L.dy), dtw, (int64_t)mb * s->block_m, hs);
+  st = launch_combine_bwd(*s, dout, fat(F.y), pos, wts, at(L.dy), dtw, max_rows_of(*s), hs);
   if (st != MOE_OK) return st;
   // down: data and weight gradients (routed, then the shared expert on all tokens)
   st = launch_gg_nt(at(L.dy), w2, nullptr, d, d, at(L.dact), d, de, meta, nblk, mb, s->E,
-                    s->block_m, 0, hs);
+                    s->block_m, max_rows_of(*s), 0, hs);
   if (st != MOE_OK) return st;
   st = launch_gg_wgrad(fat(F.act), at(L.dy), dw2, nullptr, d, de, d, counts, padded, s->E, 0, hs);
   if (st != MOE_OK) return st;
   if (shared) {
     st = launch_gg_nt(dout, ws2, nullptr, d, d, at(L.shared_dact), d, des, nullptr, nullptr, 0, 1,
-                      s->block_m, s->T, hs);
+                      s->block_m, max_rows_of(*s), s->T, hs);
     if (st != MOE_OK) return st;
     st = launch_gg_wgrad(fat(F.shared_act), dout, dws2, nullptr, d, des, d, nullptr, nullptr, 1,
                          s->T, hs);
@@ -774,13 +781,13 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
   if (st != MOE_OK) return st;
   // gate/up: data and weight gradients
   st = launch_gg_nt(at(L.dgu), w1, w3, de, de, at(L.dx_perm), 2 * de, d, meta, nblk, mb, s->E,
-                    s->block_m, 0, hs);
+                    s->block_m, max_rows_of(*s), 0, hs);
   if (st != MOE_OK) return st;
   st = launch_gg_wgrad(at(L.x_perm), at(L.dgu), dw1, dw3, de, d, 2 * de, counts, padded, s->E, 0, hs);
   if (st != MOE_OK) return st;
   if (shared) {
     st = launch_gg_nt(at(L.shared_dgu), ws1, ws3, des, des, at(L.shared_dx), 2 * des, d, nullptr,
-                      nullptr, 0, 1, s->block_m, s->T, hs);
+                      nullptr, 0, 1, s->block_m, max_rows_of(*s), s->T, hs);
     if (st != MOE_OK) return st;
     st = launch_gg_wgrad(x, at(L.shared_dgu), dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1,
                          s->T, hs);

@@ -274,7 +274,8 @@ k_gg_nt(NTOperands ops, int K, int N, const int32_t* __restrict__ meta,
 
 moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb, int ksplit,
                         void* C, int K, int N, const int32_t* meta, const int32_t* num_blocks,
-                        int32_t max_blocks, int E, int block_m, int32_t dense_rows, hipStream_t st) {
+                        int32_t max_blocks, int E, int block_m, int64_t max_rows,
+                        int32_t dense_rows, hipStream_t st) {
   const int n_tiles = (int)ceil_div(N, 512);
   const int64_t blocks_ub = dense_rows > 0 ? ceil_div(dense_rows, 128)
                                            : (int64_t)max_blocks * (block_m / 128);
@@ -285,7 +286,7 @@ moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb
   const NTOperands ops{static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(Bt0),
                        static_cast<const bf16_t*>(Bt1), static_cast<bf16_t*>(C), ldb,
                        Bt1 ? ksplit : K};
-  const int64_t max_rows = dense_rows > 0 ? (int64_t)dense_rows : (int64_t)max_blocks * block_m;
+  if (dense_rows > 0) max_rows = dense_rows;
   hipLaunchKernelGGL(k_gg_nt, dim3((unsigned)grid), dim3(kBThreads), 0, st, ops, K, N, meta,
                      num_blocks, max_blocks, dense_rows > 0 ? 1 : E, max_rows, dense_rows, block_m,
                      n_tiles);

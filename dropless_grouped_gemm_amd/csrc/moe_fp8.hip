@@ -363,7 +363,8 @@ bool fp8_gemm_supported(int K, int N) {
   return K % kFBK == 0 && N % 16 == 0 && ceil_div(K, kQBlock) <= kFMaxKB;
 }
 
-moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, hipStream_t st) {
+moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64_t max_rows,
+                                   hipStream_t st) {
   const bool routed = g.max_blocks > 0, dense = g.dense_rows > 0;
   if (!routed && !dense) return MOE_OK;
   const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
@@ -379,7 +380,6 @@ moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, hipSt
   const GGOperandsF8 dn{{static_cast<const bf16_t*>(g.Ad), nullptr, nullptr, static_cast<bf16_t*>(g.Cd),
                          nullptr, 1, 1},
                         g.Q0d, g.Q1d, g.S0d, g.S1d};
-  const int64_t max_rows = (int64_t)g.max_blocks * 128;
   if (op == MOE_OP_GATEUP_SWIGLU)
     hipLaunchKernelGGL(k_gg_fp8w<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kFThreads), 0, st,
                        ro, dn, g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E, max_rows,

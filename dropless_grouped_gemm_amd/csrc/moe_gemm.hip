@@ -637,7 +637,7 @@ static moe_status launch_other(const moe_shape& s, int op, const void* A, const 
       dense_rows > 0 ? ceil_div(dense_rows, s.block_m) : (int64_t)max_blocks;
   // rows of A and C: the dense operand has dense_rows rows, the permuted ones
   // max_blocks * block_m
-  const int64_t max_rows = dense_rows > 0 ? (int64_t)dense_rows : (int64_t)max_blocks * s.block_m;
+  const int64_t max_rows = dense_rows > 0 ? (int64_t)dense_rows : routed_rows_bound(s, max_blocks);
   const int E = dense_rows > 0 ? 1 : s.E;
   const int cus = device_cu_count();
   if (s.dtype == MOE_DTYPE_BF16) {
@@ -721,7 +721,8 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
                           static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1,
                           static_cast<const bf16_t*>(g.Dd)};
       return launch_gg_wide(op, ro, dn, K, N, g.block_meta, g.num_blocks, routed ? g.max_blocks : 0,
-                            s.E, dense ? g.dense_rows : 0, st);
+                            routed_rows_bound(s, routed ? g.max_blocks : 0), s.E,
+                            dense ? g.dense_rows : 0, st);
     }
     const int out_cols = op == MOE_OP_DOWN ? 512 : 256;   // the kernel's kOutCols
     const int n_tiles = (int)ceil_div(N, out_cols);
@@ -736,7 +737,7 @@ moe_status launch_grouped_gemm(const moe_shape& s, int op, const GemmSegments& g
     const GGOperands dn{static_cast<const bf16_t*>(g.Ad), static_cast<const bf16_t*>(g.B0d),
                         static_cast<const bf16_t*>(g.B1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1,
                         static_cast<const bf16_t*>(g.Dd)};
-    const int64_t max_rows = (int64_t)g.max_blocks * s.block_m;
+    const int64_t max_rows = routed_rows_bound(s, g.max_blocks);
     if (op == MOE_OP_GATEUP_SWIGLU)
       hipLaunchKernelGGL(k_gg_bf16_v2<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kV2Threads), 0,
                          st, ro, dn, K, N, g.block_meta, g.num_blocks, g.max_blocks, s.E, max_rows,

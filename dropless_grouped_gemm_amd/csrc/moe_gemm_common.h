@@ -130,6 +130,6 @@ __device__ __forceinline__ bool decode_block(int b, int sub, int sub_rows, int b
 int wide_max_blocks();
 moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, int K, int N,
                           const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
-                          int E, int32_t dense_rows, hipStream_t st);
+                          int64_t max_rows, int E, int32_t dense_rows, hipStream_t st);
 
 }  // namespace moe

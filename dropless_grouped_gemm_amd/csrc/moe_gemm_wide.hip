@@ -95,10 +95,12 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         const int e = s_meta[3 * b], m = s_meta[3 * b + 1], v = s_meta[3 * b + 2];
         return e >= 0 && e < E && m >= 0 && v >= 1 && v <= 128 && (int64_t)m + v <= max_rows;
       };
-      // block b (valid) continues the run of block b-1
+      // block b (valid) continues the run of block b-1: same expert, and its rows start
+      // where b-1's end (padded layout: b-1 is full; unpadded: b-1 may be the expert's
+      // partial first entry)
       auto joins = [&](int b) {
         return b > 0 && ok(b - 1) && s_meta[3 * b] == s_meta[3 * b - 3] &&
-               s_meta[3 * b + 1] == s_meta[3 * b - 2] + 128 && s_meta[3 * b - 1] == 128;
+               s_meta[3 * b + 1] == s_meta[3 * b - 2] + s_meta[3 * b - 1];
       };
       const int per = (nb + 63) / 64;
       const int lo = min(lane * per, nb), hi = min(lo + per, nb);
@@ -197,7 +199,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       const int b = it >> 2, n = it & 3;
       e = meta[3 * b];
       m0 = meta[3 * b + 1];
-      valid = 128 * (n - 1) + meta[3 * (b + n - 1) + 2];
+      valid = meta[3 * (b + n - 1) + 1] + meta[3 * (b + n - 1) + 2] - m0;
     }
     e = __builtin_amdgcn_readfirstlane(e);
     m0 = __builtin_amdgcn_readfirstlane(m0);
@@ -473,7 +475,7 @@ static constexpr int kWideWaves = 8;
 
 moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, int K, int N,
                           const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
-                          int E, int32_t dense_rows, hipStream_t st) {
+                          int64_t max_rows, int E, int32_t dense_rows, hipStream_t st) {
   const int out_cols = op == MOE_OP_DOWN ? 256 : 128;
   const int n_tiles = (int)ceil_div(N, out_cols);
   // groups: at most one per block, and at most a third of the blocks plus one per expert
@@ -490,7 +492,6 @@ moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, in
     if (c >= 1 && c < grid) grid = c;
   }
   if (grid < 1) grid = 1;
-  const int64_t max_rows = (int64_t)max_blocks * 128;
   constexpr int NT = kWideWaves * 64;
   if (op == MOE_OP_GATEUP_SWIGLU)
     hipLaunchKernelGGL((k_gg_wide<MOE_OP_GATEUP_SWIGLU, kWideWaves>), dim3((unsigned)grid), dim3(NT),

@@ -51,6 +51,12 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Number of compute units of the current device (queried once per device).
 int device_cu_count();
 
+// Rows of the permuted buffers that a block table of max_blocks entries addresses:
+// max_blocks * block_m in the padded layout, the T*k rows in the unpadded one.
+inline int64_t routed_rows_bound(const moe_shape& s, int64_t max_blocks) {
+  return s.unpadded ? (int64_t)s.T * s.k : max_blocks * s.block_m;
+}
+
 // ---- launchers (each returns MOE_OK or MOE_EHIP) -------------------------------
 // Router: partial logits over nsplit slices of d, then selection.
 int router_nsplit(const moe_shape& s);
@@ -136,7 +142,8 @@ struct GemmSegmentsF8 {
   int gather_div;
   int gather_rows;
 };
-moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, hipStream_t st);
+moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64_t max_rows,
+                                   hipStream_t st);
 
 // Backward kernels (moe_backward.hip).
 // dy[pos[t,j]] = w[t,j] dout[t] (bf16), dw[t,j] = <dout[t], y[pos[t,j]]> (fp32); d <= 8192.
@@ -149,7 +156,8 @@ moe_status launch_combine_bwd(const moe_shape& s, const void* dout, const void* 
 // of one matrix.
 moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb, int ksplit,
                         void* C, int K, int N, const int32_t* meta, const int32_t* num_blocks,
-                        int32_t max_blocks, int E, int block_m, int32_t dense_rows, hipStream_t st);
+                        int32_t max_blocks, int E, int block_m, int64_t max_rows,
+                        int32_t dense_rows, hipStream_t st);
 // C[e] = X_e^T D_e (fp32) over expert e's rows [row_off[e], row_off[e] + counts[e]),
 // columns n < nsplit into C0 [E][Km][nsplit], the rest into C1 (C1 NULL: nsplit = Nn);
 // dense_rows > 0: one expert over rows [0, dense_rows); counts NULL and dense_rows 0:

@@ -5,7 +5,10 @@
 // block table [expert, m_start, valid_m] and the block count all stay in device
 // memory and the grouped GEMM reads them (TileLang chapter "MoE, MLA and
 // sparse-attention operators", sections 2.2 item 2 and 2.3 item 2; dropless notes
-// sections 3, 5 and 7).  Segments are padded to ceil(c / block_m) * block_m rows.
+// sections 3, 5 and 7).  Segments are padded to ceil(c / block_m) * block_m rows, or,
+// in the unpadded layout (dropless notes section 11), keep their c rows: the row space
+// is cut into block_m-row tiles and a tile holding rows of several experts gets one
+// table entry per expert.
 //
 // Three kernels:
 //   k_count     one block per chunk of assignments: per-wave counters in LDS give
@@ -123,7 +126,7 @@ __device__ int block_inclusive_scan(int v, int* sh_wave /*[16]*/) {
 }
 
 __global__ void __launch_bounds__(kScanThreads)
-k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m,
+k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m, int unpadded,
             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
             int32_t* __restrict__ padded, int32_t* __restrict__ meta,
             int32_t* __restrict__ num_blocks, int32_t* __restrict__ err_flag) {
@@ -157,16 +160,21 @@ k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m,
       s_bad = run;
     }
   }
-  const int nb = (c + block_m - 1) / block_m;
   const int inc_c = block_inclusive_scan(c, sh_wave);
-  const int inc_p = block_inclusive_scan(nb * block_m, sh_wave);
+  // entries of expert e: padded, ceil(c / block_m) blocks; unpadded, the tiles its rows
+  // [o, o + c) touch, floor((o + c - 1) / block_m) - floor(o / block_m) + 1
+  const int o = inc_c - c;
+  const int nb = unpadded ? (c > 0 ? (o + c - 1) / block_m - o / block_m + 1 : 0)
+                          : (c + block_m - 1) / block_m;
+  const int seg = unpadded ? c : nb * block_m;   // rows of the expert's segment
+  const int inc_p = block_inclusive_scan(seg, sh_wave);
   const int inc_b = block_inclusive_scan(nb, sh_wave);
   if (tid < E) {
     s_cnt[tid] = c;
-    s_pad[tid] = inc_p - nb * block_m;
+    s_pad[tid] = inc_p - seg;
     s_boff[tid] = inc_b - nb;
     offsets[tid] = inc_c - c;
-    padded[tid] = inc_p - nb * block_m;
+    padded[tid] = inc_p - seg;
   }
   if (tid == E - 1) {
     s_pad[E] = inc_p;
@@ -188,16 +196,25 @@ k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m,
     const int e = lo;
     const int i = b - s_boff[e];
     meta[3 * b + 0] = e;
-    meta[3 * b + 1] = s_pad[e] + i * block_m;
-    meta[3 * b + 2] = min(block_m, s_cnt[e] - i * block_m);
+    if (unpadded) {
+      // the expert's rows inside tile floor(o / block_m) + i
+      const int o = s_pad[e], t0 = (o / block_m + i) * block_m;
+      const int m0 = max(t0, o), m1 = min(t0 + block_m, o + s_cnt[e]);
+      meta[3 * b + 1] = m0;
+      meta[3 * b + 2] = m1 - m0;
+    } else {
+      meta[3 * b + 1] = s_pad[e] + i * block_m;
+      meta[3 * b + 2] = min(block_m, s_cnt[e] - i * block_m);
+    }
   }
 }
 
 __global__ void k_scatter(const int32_t* __restrict__ idx, int64_t M, int E, int chunk,
                           const int32_t* __restrict__ hist, const int32_t* __restrict__ lrank,
                           const int32_t* __restrict__ padded, const int32_t* __restrict__ meta,
-                          const int32_t* __restrict__ num_blocks, int block_m, int64_t max_rows,
-                          int32_t* __restrict__ pos, int32_t* __restrict__ row_src) {
+                          const int32_t* __restrict__ num_blocks, int block_m, int unpadded,
+                          int64_t max_rows, int32_t* __restrict__ pos,
+                          int32_t* __restrict__ row_src) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (int64_t a = i0; a < M; a += stride) {
@@ -210,6 +227,12 @@ __global__ void k_scatter(const int32_t* __restrict__ idx, int64_t M, int E, int
     } else {
       pos[a] = -1;
     }
+  }
+  if (unpadded) {
+    // rows past the routed total (only when some ids were out of range) hold nothing
+    const int total = padded[E];
+    for (int64_t r = i0 + total; r < max_rows; r += stride) row_src[r] = -1;
+    return;
   }
   const int nb = num_blocks[0];
   for (int64_t r = i0; r < max_rows; r += stride) {
@@ -237,7 +260,7 @@ moe_status launch_build_offsets(const moe_shape& s, const int32_t* topk_idx, int
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   }
   hipLaunchKernelGGL(k_scan_meta, dim3(1), dim3(kScanThreads), 0, st, hist, nchunks, s.E, s.block_m,
-                     counts, offsets, padded, block_meta, num_blocks, err_flag);
+                     s.unpadded, counts, offsets, padded, block_meta, num_blocks, err_flag);
   if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   const int64_t max_rows = (int64_t)moe_max_rows(&s);
   const int64_t work = M > max_rows ? M : max_rows;
@@ -246,8 +269,8 @@ moe_status launch_build_offsets(const moe_shape& s, const int32_t* topk_idx, int
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_scatter, dim3((unsigned)blocks), dim3(256), 0, st, topk_idx, M, s.E, chunk,
-                     hist, lrank, padded, block_meta, num_blocks, s.block_m, max_rows, pos,
-                     row_src);
+                     hist, lrank, padded, block_meta, num_blocks, s.block_m, s.unpadded, max_rows,
+                     pos, row_src);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -67,6 +67,11 @@ typedef int32_t moe_status;
  *   (dropless notes section 3); it is also the row granularity of the grouped GEMM.
  *   bf16 needs block_m % 128 == 0 (else MOE_ENOTSUP); fp32 takes any block_m >= 1.
  *   d_e_shared: inner size of the shared expert, 0 = none.
+ *   unpadded: 0 = the padded layout above.  1 = unpadded segments (dropless notes
+ *   section 11): expert e keeps rows [offsets[e], offsets[e+1]) of the T*k rows with no
+ *   padding, the row space is cut into block_m-row tiles, and a tile holding rows of
+ *   several experts gets one block-table entry per expert (executed once for each,
+ *   restricted to that expert's rows).  Every permuted buffer then has T*k rows.
  */
 typedef struct moe_shape {
   int32_t T, d, E, k, d_e;
@@ -75,19 +80,22 @@ typedef struct moe_shape {
   int32_t block_m;
   int32_t d_e_shared;
   int32_t dtype;
+  int32_t unpadded;
 } moe_shape;
 
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_str(moe_status s);
 
-/* Host-only and pure.  Upper bound on the number of block_m-row blocks:
- * sum_e ceil(c_e / block_m) <= floor((T*k + min(E, T*k) * (block_m - 1)) / block_m).
+/* Host-only and pure.  Upper bound on the number of block-table entries: padded,
+ * sum_e ceil(c_e / block_m) <= floor((T*k + min(E, T*k) * (block_m - 1)) / block_m);
+ * unpadded, tiles + (experts with rows) - 1 <= ceil(T*k / block_m) + min(E, T*k) - 1.
  * Returns -1 for an invalid shape. */
 int32_t moe_max_blocks(const moe_shape* s);
 
-/* Host-only and pure.  moe_max_blocks(s) * block_m: the row count every permuted
- * buffer (x_perm, act, y, row_src) is sized at - a declared upper bound, since the
- * real padded total is data (dropless notes sections 1 and 4). -1 if invalid. */
+/* Host-only and pure.  The row count every permuted buffer (x_perm, act, y, row_src)
+ * is sized at: padded, moe_max_blocks(s) * block_m - a declared upper bound, since the
+ * real padded total is data (dropless notes sections 1 and 4); unpadded, T*k.
+ * -1 if invalid. */
 int64_t moe_max_rows(const moe_shape* s);
 
 /* Host-only and pure.  Bytes of device workspace that moe_layer_fwd needs; the same
@@ -124,6 +132,10 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate,
  *                          ascending order, m_start = padded_offsets[e] + i*block_m,
  *                          valid_m = min(block_m, c_e - i*block_m); entries from
  *                          num_blocks to max_blocks-1 are left untouched
+ * With s->unpadded: padded_offsets = offsets; the block table lists, tile by tile
+ * (tiles [i*block_m, (i+1)*block_m) of the T*k rows) and inside a tile by expert, one
+ * entry per expert with rows in the tile: m_start = its first row there, valid_m its
+ * row count there; num_blocks = the number of entries (dropless notes section 11).
  *   pos[a]               = padded_offsets[e] + #{a' < a : topk_idx[a'] = e}
  *                          (a stable sort by expert id)
  *   row_src[r]           = a where pos[a] = r, -1 on every other row r < max_rows

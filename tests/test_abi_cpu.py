@@ -402,3 +402,30 @@ def test_backward_workspace_layout_is_disjoint_and_aligned():
         assert all(o % 256 == 0 for o, _ in spans)
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
         assert spans[-1][1] <= L["total"]
+
+
+@pytest.mark.parametrize("M,E,bm", [(M, E, bm) for M in range(1, 8) for E in (1, 2, 3)
+                                    for bm in (1, 2, 3, 4)])
+def test_unpadded_max_blocks_bounds_every_table(M, E, bm):
+    """Unpadded layout: moe_max_blocks bounds the number of (tile, expert) entries of every
+    way of splitting M rows over E experts (brute force over the oracle's table), is
+    reached whenever tiles can hold every boundary, and the permuted buffers have M rows."""
+    from oracle import moe_oracle as O
+    s = B.make_shape(T=M, d=4, E=E, k=1, d_e=4, block_m=bm, dtype="fp32", unpadded=True)
+    worst = 0
+    for c in itertools.product(range(M + 1), repeat=E):
+        if sum(c) == M:
+            worst = max(worst, len(O.unpadded_tile_table(c, bm)))
+    assert worst <= B.moe_max_blocks(s)
+    if bm > 1 and M >= bm * min(E, M):
+        assert worst == B.moe_max_blocks(s)
+    assert B.moe_max_rows(s) == M
+    L = B.moe_workspace_layout(s)
+    assert L["act"] - L["x_perm"] >= M * s.d * 4
+
+
+def test_unpadded_flag_is_validated():
+    L = B.lib()
+    s = good_shape()
+    s.unpadded = 2
+    assert L.moe_max_blocks(ctypes.byref(s)) == -1

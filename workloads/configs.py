@@ -41,6 +41,9 @@ class MoEConfig:
     n_dead: int = 0
     # fixed routing (router bypassed): per-expert row counts; ids shuffled, weights Dirichlet(1)
     fixed_counts: Optional[Tuple[int, ...]] = None
+    # row layout: padded segments (False) or unpadded segments with per-expert entries
+    # for tiles that straddle an expert boundary (True)
+    unpadded: bool = False
     description: str = ""
 
     @property
