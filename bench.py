@@ -403,6 +403,20 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
         s1 = B.make_shape(T=T, d=d, E=1, k=1, d_e=ds, block_m=cfg.block_m)
         sdact, sdgu, sdx = e(T, ds), e(T, 2 * ds), e(T, d)
         dws1, dws3, dws2 = f(d, ds), f(d, ds), f(ds, d)
+    # the data gradients run on the forward kernels against transposed weights where
+    # experts average >= 256 rows (the choice moe_layer_bwd makes)
+    tw = M >= 256 * min(E, M)
+    wt_dn = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s, B.MOE_OP_DOWN),
+                        dtype=torch.uint8, device=dev) if tw else None
+    wt_gu = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s, B.MOE_OP_GATEUP_SWIGLU),
+                        dtype=torch.uint8, device=dev) if tw else None
+    if shared and tw:
+        wts_dn = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s1, B.MOE_OP_DOWN),
+                             dtype=torch.uint8, device=dev)
+        wts_gu = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s1, B.MOE_OP_GATEUP_SWIGLU),
+                             dtype=torch.uint8, device=dev)
+    else:
+        wts_dn = wts_gu = None
     rws_n = B.moe_router_bwd_workspace_bytes(s)
     rws = torch.empty(max(rws_n, 256), dtype=torch.uint8, device=dev)
     stages = (["combine_bwd", "dgrad_down", "wgrad_down", "permute", "swiglu_bwd", "dgrad_gateup",
@@ -415,9 +429,10 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
         B.moe_combine_bwd(s, dout, fw["y"], fw["pos"], fw["topk_w"], dy, dtw)
         i += 1; mark()
         B.moe_grouped_gemm_dgrad(s, B.MOE_OP_DOWN, dy, inp.w2, None, fw["meta"], fw["nblk"], mb,
-                                 dact)
+                                 dact, wt_dn)
         if shared:
-            B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_DOWN, dout, inp.ws2, None, None, None, 0, sdact)
+            B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_DOWN, dout, inp.ws2, None, None, None, 0, sdact,
+                                     wts_dn)
         i += 1; mark()
         B.moe_grouped_gemm_wgrad(s, B.MOE_OP_DOWN, fw["act"], dy, fw["counts"], fw["pad"], dw2, None)
         if shared:
@@ -430,10 +445,10 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
                          sdgu if shared else None)
         i += 1; mark()
         B.moe_grouped_gemm_dgrad(s, B.MOE_OP_GATEUP_SWIGLU, dgu, inp.w1, inp.w3, fw["meta"],
-                                 fw["nblk"], mb, dxp)
+                                 fw["nblk"], mb, dxp, wt_gu)
         if shared:
             B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_GATEUP_SWIGLU, sdgu, inp.ws1, inp.ws3, None, None,
-                                     0, sdx)
+                                     0, sdx, wts_gu)
         i += 1; mark()
         B.moe_grouped_gemm_wgrad(s, B.MOE_OP_GATEUP_SWIGLU, xp, dgu, fw["counts"], fw["pad"], dw1,
                                  dw3)

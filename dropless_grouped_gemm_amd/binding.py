@@ -27,6 +27,7 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
                 "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_grouped_gemm_fp8",
                 "moe_layer_fwd_fp8", "moe_combine_bwd", "moe_swiglu_bwd", "moe_grouped_gemm_dgrad",
                 "moe_grouped_gemm_wgrad", "moe_router_bwd", "moe_router_bwd_workspace_bytes",
+                "moe_grouped_gemm_dgrad_workspace_bytes",
                 "moe_bwd_workspace_bytes",
                 "moe_bwd_workspace_layout", "moe_layer_bwd")
 
@@ -48,7 +49,7 @@ class moe_ws_layout(ctypes.Structure):
 
 _BWD_LAYOUT_FIELDS = ("dy", "dact", "dgu", "x_perm", "dx_perm", "dtopk_w", "dlogits",
                       "shared_dact", "shared_dgu", "shared_dx", "router_dx", "router_scratch",
-                      "total")
+                      "w2_t", "w13_t", "ws2_t", "ws13_t", "total")
 
 
 class moe_bwd_ws_layout(ctypes.Structure):
@@ -112,7 +113,10 @@ def lib():
         L.moe_combine_bwd.restype = ctypes.c_int32
         L.moe_swiglu_bwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P]
         L.moe_swiglu_bwd.restype = ctypes.c_int32
-        L.moe_grouped_gemm_dgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
+        L.moe_grouped_gemm_dgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P,
+                                             ctypes.c_size_t, P]
+        L.moe_grouped_gemm_dgrad_workspace_bytes.argtypes = [S, ctypes.c_int32]
+        L.moe_grouped_gemm_dgrad_workspace_bytes.restype = ctypes.c_size_t
         L.moe_grouped_gemm_dgrad.restype = ctypes.c_int32
         L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P]
         L.moe_grouped_gemm_wgrad.restype = ctypes.c_int32
@@ -368,11 +372,17 @@ def moe_swiglu_bwd(shape, A, row_src, w1, w3, dact, block_meta, num_blocks, max_
         _p(dgu_shared), _stream(stream)))
 
 
+def moe_grouped_gemm_dgrad_workspace_bytes(shape, op) -> int:
+    return lib().moe_grouped_gemm_dgrad_workspace_bytes(ctypes.byref(shape), op)
+
+
 def moe_grouped_gemm_dgrad(shape, op, dC, B0, B1, block_meta, num_blocks, max_blocks, dA,
-                           stream=None):
+                           ws=None, stream=None):
+    """ws: None - the weights are read transposed in place; a device buffer of
+    moe_grouped_gemm_dgrad_workspace_bytes(shape, op) bytes - transposed into it first."""
     _check("moe_grouped_gemm_dgrad", lib().moe_grouped_gemm_dgrad(
         ctypes.byref(shape), op, _p(dC), _p(B0), _p(B1), _p(block_meta), _p(num_blocks),
-        max_blocks, _p(dA), _stream(stream)))
+        max_blocks, _p(dA), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def moe_grouped_gemm_wgrad(shape, op, A, dC, counts, padded_offsets, dB0, dB1, stream=None):

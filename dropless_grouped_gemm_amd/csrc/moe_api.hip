@@ -120,6 +120,14 @@ static void layout_of(const moe_shape& s, moe_ws_layout& L) {
   L.total = cur;
 }
 
+// The layer's backward runs its data gradients on the forward grouped-GEMM kernels,
+// against weights transposed once per call, where experts average at least 256 rows
+// (where the wide forward kernel applies); otherwise k_gg_nt reads them transposed.
+static bool transposed_dgrad(const moe_shape& s) {
+  const int64_t M = (int64_t)s.T * s.k;
+  return M > 0 && M >= 256 * (M < s.E ? M : (int64_t)s.E);
+}
+
 // The backward kernels: bf16, contraction sizes in whole 32-deep slices.
 static moe_status check_bwd(const moe_shape& s) {
   if (s.dtype != MOE_DTYPE_BF16) return MOE_ENOTSUP;
@@ -144,6 +152,13 @@ static void bwd_layout_of(const moe_shape& s, moe_bwd_ws_layout& L) {
   L.shared_dx = take(cur, ds ? T * d * 2 : 0);
   L.router_dx = take(cur, T * d * 2);
   L.router_scratch = take(cur, router_bwd_scratch_bytes(s));
+  // the expert weights transposed for the data gradients, when the forward kernels run
+  // them (transposed_dgrad)
+  const bool tw = transposed_dgrad(s);
+  L.w2_t = take(cur, tw ? E * d * de * 2 : 0);
+  L.w13_t = take(cur, tw ? E * 2 * de * d * 2 : 0);
+  L.ws2_t = take(cur, tw ? d * ds * 2 : 0);
+  L.ws13_t = take(cur, tw ? 2 * ds * d * 2 : 0);
   L.total = cur;
 }
 
@@ -598,10 +613,59 @@ moe_status moe_swiglu_bwd(const moe_shape* s, const void* A, const int32_t* row_
   return launch_grouped_gemm(*s, kOpGateUpBwd, g, static_cast<hipStream_t>(stream));
 }
 
+// A data gradient on the forward kernels: the weights transposed into wt, then the
+// plain grouped product (op DOWN: no epilogue) C = A (B^T).
+//   DOWN:   W2 [E][d_e][d] -> wt [E][d][d_e];     dA [rows, d_e] = dC [rows, d] wt[e]
+//   GATEUP: W1, W3 [E][d][d_e] -> wt [E][2 d_e][d] (W1^T rows, then W3^T rows);
+//           dA [rows, d] = dC [rows, 2 d_e] wt[e]
+static moe_status dgrad_on_forward_kernels(const moe_shape& s, int op, const void* dC,
+                                           const void* B0, const void* B1,
+                                           const int32_t* meta, const int32_t* nblk, int32_t mb,
+                                           void* dA, const void* dC_d, const void* B0_d,
+                                           const void* B1_d, void* dA_d, int de_d, void* wt,
+                                           void* wt_d, hipStream_t st) {
+  const bool gu = op == MOE_OP_GATEUP_SWIGLU;
+  const bool routed = mb > 0, dense = dC_d != nullptr;
+  const int d = s.d, de = s.d_e;
+  moe_status r = MOE_OK;
+  if (routed) {
+    r = gu ? launch_transpose_bf16(s.E, d, de, B0, wt, (int64_t)2 * de * d, d, st)
+           : launch_transpose_bf16(s.E, de, d, B0, wt, (int64_t)d * de, de, st);
+    if (r == MOE_OK && gu)
+      r = launch_transpose_bf16(s.E, d, de, B1, static_cast<bf16_t*>(wt) + (size_t)de * d,
+                                (int64_t)2 * de * d, d, st);
+    if (r != MOE_OK) return r;
+  }
+  if (dense) {
+    r = gu ? launch_transpose_bf16(1, d, de_d, B0_d, wt_d, (int64_t)2 * de_d * d, d, st)
+           : launch_transpose_bf16(1, de_d, d, B0_d, wt_d, (int64_t)d * de_d, de_d, st);
+    if (r == MOE_OK && gu)
+      r = launch_transpose_bf16(1, d, de_d, B1_d, static_cast<bf16_t*>(wt_d) + (size_t)de_d * d,
+                                (int64_t)2 * de_d * d, d, st);
+    if (r != MOE_OK) return r;
+  }
+  GemmSegments g{};
+  if (routed) {
+    g.A = dC; g.B0 = wt; g.C = dA; g.K = gu ? 2 * de : d; g.N = gu ? d : de;
+    g.block_meta = meta; g.num_blocks = nblk; g.max_blocks = mb;
+  }
+  if (dense) {
+    g.Ad = dC_d; g.B0d = wt_d; g.Cd = dA_d; g.Kd = gu ? 2 * de_d : d; g.Nd = gu ? d : de_d;
+    g.dense_rows = s.T;
+  }
+  return launch_grouped_gemm(s, MOE_OP_DOWN, g, st);
+}
+
+size_t moe_grouped_gemm_dgrad_workspace_bytes(const moe_shape* s, int32_t op) {
+  if (check_shape(s) != MOE_OK) return 0;
+  if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return 0;
+  return align_up((size_t)s->E * s->d * s->d_e * 2 * (op == MOE_OP_GATEUP_SWIGLU ? 2 : 1), 256);
+}
+
 moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC, const void* B0,
                                   const void* B1, const int32_t* block_meta,
                                   const int32_t* num_blocks, int32_t max_blocks, void* dA,
-                                  void* stream) {
+                                  void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if ((st = check_bwd(*s)) != MOE_OK) return st;
@@ -610,14 +674,25 @@ moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC
   const bool dense = !block_meta && !num_blocks;
   if (dense ? max_blocks != 0 : !block_table_ok(*s, block_meta, num_blocks, max_blocks))
     return MOE_EINVAL;
+  // with a workspace the weights are transposed into it and the forward kernels run
+  const bool tw = ws != nullptr;
+  if (tw && (!aligned16(ws) || ws_bytes < moe_grouped_gemm_dgrad_workspace_bytes(s, op)))
+    return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool gu = op == MOE_OP_GATEUP_SWIGLU;
+  if (tw) {
+    if (dense)
+      return dgrad_on_forward_kernels(*s, op, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                      nullptr, dC, B0, B1, dA, s->d_e, nullptr, ws, hs);
+    return dgrad_on_forward_kernels(*s, op, dC, B0, B1, block_meta, num_blocks, max_blocks, dA,
+                                    nullptr, nullptr, nullptr, nullptr, 0, ws, nullptr, hs);
+  }
   const int K = gu ? 2 * s->d_e : s->d, N = gu ? s->d : s->d_e;
   const int ldb = gu ? s->d_e : s->d;
   return launch_gg_nt(dC, B0, B1, ldb, gu ? s->d_e : K, dA, K, N, block_meta, num_blocks,
                       dense ? 0 : max_blocks, dense ? 1 : s->E, s->block_m,
-                      routed_rows_bound(*s, max_blocks), dense ? s->T : 0,
-                      static_cast<hipStream_t>(stream));
+                      routed_rows_bound(*s, max_blocks), dense ? s->T : 0, hs);
 }
 
 moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A, const void* dC,
@@ -756,15 +831,25 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
   st = launch_combine_bwd(*s, dout, fat(F.y), pos, wts, at(L.dy), dtw, max_rows_of(*s), hs);
   if (st != MOE_OK) return st;
   // down: data and weight gradients (routed, then the shared expert on all tokens)
-  st = launch_gg_nt(at(L.dy), w2, nullptr, d, d, at(L.dact), d, de, meta, nblk, mb, s->E,
-                    s->block_m, max_rows_of(*s), 0, hs);
+  const bool tw = transposed_dgrad(*s);
+  if (tw) {
+    st = dgrad_on_forward_kernels(*s, MOE_OP_DOWN, at(L.dy), w2, nullptr, meta, nblk, mb,
+                                  at(L.dact), shared ? dout : nullptr, ws2, nullptr,
+                                  shared ? at(L.shared_dact) : nullptr, des, at(L.w2_t),
+                                  at(L.ws2_t), hs);
+  } else {
+    st = launch_gg_nt(at(L.dy), w2, nullptr, d, d, at(L.dact), d, de, meta, nblk, mb, s->E,
+                      s->block_m, max_rows_of(*s), 0, hs);
+  }
   if (st != MOE_OK) return st;
   st = launch_gg_wgrad(fat(F.act), at(L.dy), dw2, nullptr, d, de, d, counts, padded, s->E, 0, hs);
   if (st != MOE_OK) return st;
   if (shared) {
-    st = launch_gg_nt(dout, ws2, nullptr, d, d, at(L.shared_dact), d, des, nullptr, nullptr, 0, 1,
-                      s->block_m, max_rows_of(*s), s->T, hs);
-    if (st != MOE_OK) return st;
+    if (!tw) {
+      st = launch_gg_nt(dout, ws2, nullptr, d, d, at(L.shared_dact), d, des, nullptr, nullptr, 0, 1,
+                        s->block_m, max_rows_of(*s), s->T, hs);
+      if (st != MOE_OK) return st;
+    }
     st = launch_gg_wgrad(fat(F.shared_act), dout, dws2, nullptr, d, des, d, nullptr, nullptr, 1,
                          s->T, hs);
     if (st != MOE_OK) return st;
@@ -780,15 +865,24 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
   st = launch_grouped_gemm(*s, kOpGateUpBwd, g, hs);
   if (st != MOE_OK) return st;
   // gate/up: data and weight gradients
-  st = launch_gg_nt(at(L.dgu), w1, w3, de, de, at(L.dx_perm), 2 * de, d, meta, nblk, mb, s->E,
-                    s->block_m, max_rows_of(*s), 0, hs);
+  if (tw) {
+    st = dgrad_on_forward_kernels(*s, MOE_OP_GATEUP_SWIGLU, at(L.dgu), w1, w3, meta, nblk, mb,
+                                  at(L.dx_perm), shared ? at(L.shared_dgu) : nullptr, ws1, ws3,
+                                  shared ? at(L.shared_dx) : nullptr, des, at(L.w13_t),
+                                  at(L.ws13_t), hs);
+  } else {
+    st = launch_gg_nt(at(L.dgu), w1, w3, de, de, at(L.dx_perm), 2 * de, d, meta, nblk, mb, s->E,
+                      s->block_m, max_rows_of(*s), 0, hs);
+  }
   if (st != MOE_OK) return st;
   st = launch_gg_wgrad(at(L.x_perm), at(L.dgu), dw1, dw3, de, d, 2 * de, counts, padded, s->E, 0, hs);
   if (st != MOE_OK) return st;
   if (shared) {
-    st = launch_gg_nt(at(L.shared_dgu), ws1, ws3, des, des, at(L.shared_dx), 2 * des, d, nullptr,
-                      nullptr, 0, 1, s->block_m, max_rows_of(*s), s->T, hs);
-    if (st != MOE_OK) return st;
+    if (!tw) {
+      st = launch_gg_nt(at(L.shared_dgu), ws1, ws3, des, des, at(L.shared_dx), 2 * des, d, nullptr,
+                        nullptr, 0, 1, s->block_m, max_rows_of(*s), s->T, hs);
+      if (st != MOE_OK) return st;
+    }
     st = launch_gg_wgrad(x, at(L.shared_dgu), dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1,
                          s->T, hs);
     if (st != MOE_OK) return st;

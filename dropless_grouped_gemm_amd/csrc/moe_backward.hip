@@ -294,6 +294,64 @@ moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb
 }
 
 // ---------------------------------------------------------------------------
+// weight transpose: wt[e][c][r] = w[e][r][c]
+// ---------------------------------------------------------------------------
+// With the weights transposed once, a data gradient C = A B^T is the plain product
+// C = A (B^T) that the forward grouped-GEMM kernels compute.  64 x 64 tiles through LDS:
+// 16-byte row loads, then each thread gathers 8 consecutive r of one column c from LDS
+// and stores them as one 16-byte chunk of wt's row c.
+static constexpr int kTrTile = 64;
+
+__global__ void __launch_bounds__(256)
+k_transpose_bf16(const bf16_t* __restrict__ w, int R, int C, bf16_t* __restrict__ wt,
+                 int64_t wt_estride, int wt_ld) {
+  __shared__ bf16_t tile[kTrTile][kTrTile + 2];
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * kTrTile, c0 = blockIdx.x * kTrTile;
+  const bf16_t* src = w + (size_t)e * R * C;
+  bf16_t* dst = wt + (size_t)e * wt_estride;
+  // load: 64 rows x 8 chunks of 8 columns, two per thread
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + h * 256;
+    const int rr = i >> 3, cc = (i & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+    if (r < R && c < C) v = *reinterpret_cast<const u32x4_t*>(src + (size_t)r * C + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tile[rr][cc + 2 * q] = (bf16_t)(v[q] & 0xffffu);
+      tile[rr][cc + 2 * q + 1] = (bf16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+  // store: 64 columns x 8 chunks of 8 rows, two per thread
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = threadIdx.x + h * 256;
+    const int cc = i >> 3, rr = (i & 7) * 8;
+    const int c = c0 + cc, r = r0 + rr;
+    if (c < C && r < R) {
+      u32x4_t v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] = (uint32_t)tile[rr + 2 * q][cc] | ((uint32_t)tile[rr + 2 * q + 1][cc] << 16);
+      *reinterpret_cast<u32x4_t*>(dst + (size_t)c * wt_ld + r) = v;
+    }
+  }
+}
+
+moe_status launch_transpose_bf16(int E, int R, int C, const void* w, void* wt, int64_t wt_estride,
+                                 int wt_ld, hipStream_t st) {
+  if (E <= 0 || R <= 0 || C <= 0) return MOE_OK;
+  hipLaunchKernelGGL(k_transpose_bf16,
+                     dim3((unsigned)ceil_div(C, kTrTile), (unsigned)ceil_div(R, kTrTile), (unsigned)E),
+                     dim3(256), 0, st, static_cast<const bf16_t*>(w), R, C, static_cast<bf16_t*>(wt),
+                     wt_estride, wt_ld);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
 // weight-gradient grouped GEMM: C[e] = X_e^T D_e over each expert's rows
 // ---------------------------------------------------------------------------
 static constexpr int kWgXBytes = kBBK * 128 * 2;     // [32 rows][128 m] = 8 KB

@@ -158,6 +158,10 @@ moe_status launch_gg_nt(const void* A, const void* Bt0, const void* Bt1, int ldb
                         void* C, int K, int N, const int32_t* meta, const int32_t* num_blocks,
                         int32_t max_blocks, int E, int block_m, int64_t max_rows,
                         int32_t dense_rows, hipStream_t st);
+// wt[e][c][r] = w[e][r][c] (bf16; R % 8 == 0, C % 8 == 0): wt's expert e starts at
+// e * wt_estride elements and its rows are wt_ld elements apart.
+moe_status launch_transpose_bf16(int E, int R, int C, const void* w, void* wt, int64_t wt_estride,
+                                 int wt_ld, hipStream_t st);
 // C[e] = X_e^T D_e (fp32) over expert e's rows [row_off[e], row_off[e] + counts[e]),
 // columns n < nsplit into C0 [E][Km][nsplit], the rest into C1 (C1 NULL: nsplit = Nn);
 // dense_rows > 0: one expert over rows [0, dense_rows); counts NULL and dense_rows 0:

@@ -386,11 +386,15 @@ moe_status moe_swiglu_bwd(const moe_shape* s, const void* A, const int32_t* row_
  * block_meta, num_blocks, max_blocks as for moe_grouped_gemm; block_meta = num_blocks
  * = NULL with max_blocks = 0 is the dense mode (one expert, E = 1, over T rows: the
  * shared expert with s->d_e = d_e_shared).  Only rows the table covers are written.
+ * ws: NULL - a kernel reads the weights transposed in place; or device scratch of
+ * ws_bytes >= moe_grouped_gemm_dgrad_workspace_bytes(s, op) - the weights are first
+ * transposed into it and the forward grouped-GEMM kernels compute the plain product.
  */
+size_t moe_grouped_gemm_dgrad_workspace_bytes(const moe_shape* s, int32_t op);
 moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC,
                                   const void* B0, const void* B1, const int32_t* block_meta,
                                   const int32_t* num_blocks, int32_t max_blocks, void* dA,
-                                  void* stream);
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Weight-gradient grouped GEMM, reducing over each expert's rows
@@ -427,11 +431,13 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
  * Host-only and pure: bytes of the backward workspace and the offsets of its
  * intermediates (dy, dact, dgu, x_perm, dx_perm [rows, .]; dtopk_w [T, k] and dlogits
  * [T, E] fp32; the shared expert's dact, dgu, dx and the router's dx [T, .]; the
- * router's scratch).
+ * router's scratch; where experts average >= 256 rows, the expert weights transposed for
+ * the data gradients: W2^T [E][d][d_e], [W1^T; W3^T] [E][2 d_e][d] and the shared
+ * expert's likewise).
  */
 typedef struct moe_bwd_ws_layout {
   size_t dy, dact, dgu, x_perm, dx_perm, dtopk_w, dlogits, shared_dact, shared_dgu,
-         shared_dx, router_dx, router_scratch, total;
+         shared_dx, router_dx, router_scratch, w2_t, w13_t, ws2_t, ws13_t, total;
 } moe_bwd_ws_layout;
 size_t moe_bwd_workspace_bytes(const moe_shape* s);
 moe_status moe_bwd_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout);

@@ -320,7 +320,7 @@ def test_backward_entry_point_argument_rules():
         assert L.moe_swiglu_bwd(pb, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE,
                                 *([None] * 5), None) == B.MOE_ENOTSUP
         assert L.moe_grouped_gemm_dgrad(pb, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE,
-                                        None) == B.MOE_ENOTSUP
+                                        None, 0, None) == B.MOE_ENOTSUP
         assert L.moe_grouped_gemm_wgrad(pb, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                         None) == B.MOE_ENOTSUP
         assert L.moe_router_bwd(pb, *([FAKE] * 10), FAKE, 1 << 40, None) == B.MOE_ENOTSUP
@@ -341,12 +341,18 @@ def test_backward_entry_point_argument_rules():
               None, FAKE, None) == B.MOE_EINVAL            # shared dact missing
     # dgrad: op rules, dense mode all-or-nothing
     dg = L.moe_grouped_gemm_dgrad
-    assert dg(ps, 0, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None) == B.MOE_EINVAL
-    assert dg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None) == B.MOE_EINVAL
-    assert dg(ps, 3, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None) == B.MOE_EINVAL
-    assert dg(ps, 1, FAKE, FAKE, None, None, FAKE, 1, FAKE, None) == B.MOE_EINVAL
-    assert dg(ps, 1, FAKE, FAKE, None, None, None, 1, FAKE, None) == B.MOE_EINVAL
-    assert dg(ps, 1, FAKE, FAKE, None, FAKE, FAKE, mb + 1, FAKE, None) == B.MOE_EINVAL
+    assert dg(ps, 0, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert dg(ps, 3, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, None, None, FAKE, 1, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, None, None, None, 1, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert dg(ps, 1, FAKE, FAKE, None, FAKE, FAKE, mb + 1, FAKE, None, 0, None) == B.MOE_EINVAL
+    # a workspace selects the transposed-weight path and must hold the transposed weights
+    need = L.moe_grouped_gemm_dgrad_workspace_bytes(ps, 0)
+    assert need == -(-2 * s.E * s.d * s.d_e * 2 // 256) * 256
+    assert dg(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, need - 1, None) == B.MOE_EWORKSPACE
+    assert dg(ps, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, ctypes.c_void_p(0x10008),
+              1 << 40, None) == B.MOE_EWORKSPACE
     # wgrad: dB1 exactly for gate/up; counts and offsets together
     wg = L.moe_grouped_gemm_wgrad
     assert wg(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
@@ -398,6 +404,9 @@ def test_backward_workspace_layout_is_disjoint_and_aligned():
                      shared_dact=T * ds * 2, shared_dgu=T * 2 * ds * 2,
                      shared_dx=T * d * 2 if ds else 0, router_dx=T * d * 2,
                      router_scratch=B.moe_router_bwd_workspace_bytes(s))
+        tw = T * s.k >= 256 * min(s.E, T * s.k)           # data gradients on transposed weights
+        sizes.update(w2_t=s.E * d * de * 2 if tw else 0, w13_t=2 * s.E * de * d * 2 if tw else 0,
+                     ws2_t=d * ds * 2 if tw else 0, ws13_t=2 * ds * d * 2 if tw else 0)
         spans = sorted((L[n], L[n] + sz) for n, sz in sizes.items() if sz)
         assert all(o % 256 == 0 for o, _ in spans)
         assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))

@@ -108,6 +108,14 @@ def test_backward_stages_against_oracle(name, scale):
         dw2_ref[ex] = act_h[r].T @ dy_h[r]
     assert_close(f64(dact)[valid], dact_ref[valid], TOL_STAGE["bf16"], "dact")
     assert_close(f64(dw2), dw2_ref, TOL_WGRAD, "dW2")
+    # the same data gradient on the forward kernels against weights transposed into a
+    # workspace
+    dact_t = e(rows, de)
+    wt = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s, B.MOE_OP_DOWN), dtype=torch.uint8,
+                     device=DEV)
+    B.moe_grouped_gemm_dgrad(s, B.MOE_OP_DOWN, dy, inp.w2, None, meta, nblk, mb, dact_t, wt)
+    torch.cuda.synchronize()
+    assert_close(f64(dact_t)[valid], dact_ref[valid], TOL_STAGE["bf16"], "dact (transposed)")
     for ex in np.nonzero(counts == 0)[0]:
         assert not torch.any(dw2[ex] != 0), f"expert {ex} has no rows: dW2 must be 0"
 
@@ -142,6 +150,13 @@ def test_backward_stages_against_oracle(name, scale):
         dw1_ref[ex] = xp_h[r].T @ dgu_h[r, :de]
         dw3_ref[ex] = xp_h[r].T @ dgu_h[r, de:]
     assert_close(f64(dxp)[valid], dxp_ref[valid], TOL_STAGE["bf16"], "dx_perm")
+    dxp_t = e(rows, d)
+    wt = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s, B.MOE_OP_GATEUP_SWIGLU),
+                     dtype=torch.uint8, device=DEV)
+    B.moe_grouped_gemm_dgrad(s, B.MOE_OP_GATEUP_SWIGLU, dgu, inp.w1, inp.w3, meta, nblk, mb, dxp_t,
+                             wt)
+    torch.cuda.synchronize()
+    assert_close(f64(dxp_t)[valid], dxp_ref[valid], TOL_STAGE["bf16"], "dx_perm (transposed)")
     assert_close(f64(dw1), dw1_ref, TOL_WGRAD, "dW1")
     assert_close(f64(dw3), dw3_ref, TOL_WGRAD, "dW3")
 
@@ -176,6 +191,14 @@ def test_backward_stages_against_oracle(name, scale):
         sdgu_h = f64(sdgu)
         assert_close(f64(sdx), sdgu_h[:, :ds] @ h["ws1"].T + sdgu_h[:, ds:] @ h["ws3"].T,
                      TOL_STAGE["bf16"], "shared dx")
+        sdx_t = e(T, d)
+        wt = torch.empty(B.moe_grouped_gemm_dgrad_workspace_bytes(s1, B.MOE_OP_GATEUP_SWIGLU),
+                         dtype=torch.uint8, device=DEV)
+        B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_GATEUP_SWIGLU, sdgu, inp.ws1, inp.ws3, None, None, 0,
+                                 sdx_t, wt)
+        torch.cuda.synchronize()
+        assert_close(f64(sdx_t), sdgu_h[:, :ds] @ h["ws1"].T + sdgu_h[:, ds:] @ h["ws3"].T,
+                     TOL_STAGE["bf16"], "shared dx (transposed)")
         assert_close(f64(dws1), h["x"].T @ sdgu_h[:, :ds], TOL_WGRAD, "dWs1")
         assert_close(f64(dws3), h["x"].T @ sdgu_h[:, ds:], TOL_WGRAD, "dWs3")
 
@@ -219,6 +242,9 @@ LAYER_CASES = [
     ("fusedmoe-8x2048", dict(name="fusedmoe-bwd-bm256", T=200, d=256, d_e=192, d_e_shared=1088,
                              block_m=256), None),
     ("zipf-skew-64x1408", dict(name="zipf-bwd-l", T=300, d=256, d_e=160), None),
+    # experts averaging >= 256 rows: data gradients on transposed weights, shared expert
+    # of another size in launches of its own
+    ("fusedmoe-8x2048", dict(name="fusedmoe-bwd-tw", T=640, d=256, d_e=192, d_e_shared=320), None),
     ("ep-share-4x2048", dict(name="ep-share-bwd-l", T=128, d=512, d_e=256,
                              fixed_counts=(400, 0, 333, 291)), None),
     ("decode-256x2048", dict(name="decode-bwd-l", T=16, d=512, E=64, d_e=128, d_e_shared=192), None),
