@@ -90,6 +90,12 @@ def kernels_summary(d: str, command: str, bench_log: str | None) -> str:
             out += ["", "Event-timed stage averages printed by the benchmark in the same run (us):",
                     "", "```", json.dumps(b.get("stages_us")), "```",
                     f"roofline: {json.dumps(b.get('roofline'))}"]
+            bw = b.get("backward")
+            if bw:
+                out += ["", "Backward stages in the same run (us), and each backward GEMM launch's "
+                        "TFLOP/s:", "", "```", json.dumps(bw.get("stages_us")),
+                        json.dumps({k: round(v["tflops"], 1) for k, v in bw.get("gemm", {}).items()}),
+                        "```"]
     return "\n".join(out) + "\n"
 
 
