@@ -38,6 +38,7 @@
 namespace moe {
 
 static constexpr int kWRows = 384;                    // rows per tile
+static constexpr int kWideLagFrom = 4;                 // waves >= this run half a step late
 static constexpr int kWBK = 32;                       // K per ring slot
 static constexpr int kWABytes = kWRows * kWBK * 2;    // 24 KB
 static constexpr int kWBBytes = kWBK * 256 * 2;       // 16 KB
@@ -322,49 +323,55 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     MOE_WAIT_VMCNT((kWStages - 1) * CPW);
     __syncthreads();
 
-    // Slice ks: two 16-deep halves, then a barrier once slice ks+1 has landed.  The
-    // barrier ending slice ks-1 freed its slot; slice ks-1+S refills it, the A copies
-    // spread between the first half's MFMAs and the B copies between the second's.
-    for (int ks = 0; ks < nk; ++ks) {
-      const int stage = ks % kWStages;
+    // Ping-pong over half-slices t = 2 ks + kk: every wave runs MEM(t), barrier,
+    // MFMA(t), barrier.  Waves 4-7 (the second wave on each SIMD) start one barrier
+    // late and waves 0-3 end one barrier late, so on every SIMD one wave issues its
+    // MFMAs while the other reads its fragments (and issues copies): the LDS reads of
+    // half the waves overlap the other half's MFMAs instead of all waves reading at
+    // once after a shared barrier.  Every wave executes 4 nk + 1 barriers.
+    //   MEM(2 ks), ks >= 1: slice ks+1 has landed for this wave (then, before any wave
+    //   reads it, at least two barriers pass); every wave has read slice ks-1 (its
+    //   reads completed before the barriers since), so its slot takes slice ks-1+S
+    //   (down: its B copies in MEM(2 ks + 1)).  The wait counts whole slices: at
+    //   MEM(2 ks) every slice up to ks-2+S has been issued in full.
+    const bool lag = wave >= kWideLagFrom;
+    if (lag) __syncthreads();
+    for (int t = 0; t < 2 * nk; ++t) {
+      const int ks = t >> 1, kk = t & 1;
+      // the refill of slice ks-1's slot (after every wave's last read of slice ks-1):
+      // gate/up issues all its copies in the first half's memory phase, down its A
+      // copies there and its B copies in the second half's (measured: each op's faster
+      // split)
+      constexpr bool kSplitCopies = !GU;
       const int ksrc = min(ks - 1 + kWStages, nk - 1);
       const int slot = (ks + kWStages - 1) % kWStages;
-      read_frags(stage, 0);
-      if (ks > 0) {
+      if (kk == 0) {
+        if (ks == 0) {
+          MOE_WAIT_VMCNT((kWStages - 2) * CPW);   // slice 1 has landed
+        } else {
+          MOE_WAIT_VMCNT((kWStages - 3) * CPW);   // slice ks+1 has landed
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+          for (int i = 0; i < CPA; ++i) issue_a(ksrc, slot, i);
+          if (!kSplitCopies) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-            // A copy c goes after MFMA floor(c * MI * 4 / CPA)
-#pragma unroll
-            for (int c = 0; c < CPA; ++c)
-              if (c * MI * 4 / CPA == i * 4 + j) issue_a(ksrc, slot, c);
+            for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
           }
         }
-      } else {
-        mfma_block();
-      }
-      read_frags(stage, 1);
-      if (ks > 0) {
+      } else if (kSplitCopies && ks > 0) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-            for (int c = 0; c < CPB; ++c)
-              if (c * MI * 4 / CPB == i * 4 + j) issue_b(ksrc, slot, c);
-          }
-        }
-      } else {
-        mfma_block();
+        for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
       }
-      if (ks + 1 < nk) {
-        MOE_WAIT_VMCNT((kWStages - 2) * CPW);   // slice ks+1 has landed
-        __syncthreads();
-      }
+      read_frags(ks % kWStages, kk);
+      // scheduling barriers keep each phase's instructions on its side of the barriers
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (!lag) __syncthreads();
     MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
     __syncthreads();
 
