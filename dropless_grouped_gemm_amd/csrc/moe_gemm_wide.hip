@@ -323,6 +323,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     MOE_WAIT_VMCNT((kWStages - 1) * CPW);
     __syncthreads();
 
+    if constexpr (!BWD) {
     // Ping-pong over half-slices t = 2 ks + kk: every wave runs MEM(t), barrier,
     // MFMA(t), barrier.  Waves 4-7 (the second wave on each SIMD) start one barrier
     // late and waves 0-3 end one barrier late, so on every SIMD one wave issues its
@@ -372,6 +373,54 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       __builtin_amdgcn_sched_barrier(0);
     }
     if (!lag) __syncthreads();
+    } else {
+    // The SwiGLU-backward op keeps the one-barrier slice loop: its epilogue's register
+    // pressure spills a value that the ping-pong loop reloads every half-slice, and
+    // the wait for that reload also drains the copies in flight.
+    // Slice ks: two 16-deep halves, then a barrier once slice ks+1 has landed.  The
+    // barrier ending slice ks-1 freed its slot; slice ks-1+S refills it, the A copies
+    // spread between the first half's MFMAs and the B copies between the second's.
+    for (int ks = 0; ks < nk; ++ks) {
+      const int stage = ks % kWStages;
+      const int ksrc = min(ks - 1 + kWStages, nk - 1);
+      const int slot = (ks + kWStages - 1) % kWStages;
+      read_frags(stage, 0);
+      if (ks > 0) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            // A copy c goes after MFMA floor(c * MI * 4 / CPA)
+#pragma unroll
+            for (int c = 0; c < CPA; ++c)
+              if (c * MI * 4 / CPA == i * 4 + j) issue_a(ksrc, slot, c);
+          }
+        }
+      } else {
+        mfma_block();
+      }
+      read_frags(stage, 1);
+      if (ks > 0) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < CPB; ++c)
+              if (c * MI * 4 / CPB == i * 4 + j) issue_b(ksrc, slot, c);
+          }
+        }
+      } else {
+        mfma_block();
+      }
+      if (ks + 1 < nk) {
+        MOE_WAIT_VMCNT((kWStages - 2) * CPW);   // slice ks+1 has landed
+        __syncthreads();
+      }
+    }
+    }
     MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
     __syncthreads();
 
