@@ -126,11 +126,23 @@ def main():
         else:
             qs1 = qs3 = qs2 = (None, None)
         torch.cuda.synchronize()
+    # with enough rows per expert the fp8 layer dequantises its weights (one pass) and
+    # runs the bf16 kernels on them; the staged step does the same
+    deq = fp8 and B.fp8_dequantises(s)
+    fp8k = fp8 and not deq
+    w1_, w3_, w2_ = inp.w1, inp.w3, inp.w2
+    ws1_, ws3_, ws2_ = inp.ws1, inp.ws3, inp.ws2
+    if deq:
+        w1_, w3_, w2_ = (torch.empty_like(inp.w1), torch.empty_like(inp.w3),
+                         torch.empty_like(inp.w2))
+        if shared:
+            ws1_, ws3_, ws2_ = (torch.empty_like(inp.ws1), torch.empty_like(inp.ws3),
+                                torch.empty_like(inp.ws2))
     # where the kernels can gather gate/up rows straight from x, the permute is fused into
     # the gate/up launch (the call moe_layer_fwd makes) and x_perm is not written
     gather = B.gather_supported(s)
     stages = ((["route"] if not routed else []) + ["offsets"] + ([] if gather else ["permute"]) +
-              ["gateup", "down", "combine"])
+              (["dequant"] if deq else []) + ["gateup", "down", "combine"])
 
     def step(ev=None):
         i = 0
@@ -145,7 +157,21 @@ def main():
         i += 1
         if ev is not None:
             ev[i].record()
-        if fp8:
+        if deq:
+            if not gather:
+                B.moe_permute(s, inp.x, pos, x_perm)
+                i += 1
+                if ev is not None:
+                    ev[i].record()
+            for (qq, sc), wd in ((q1, w1_), (q3, w3_), (q2, w2_)):
+                B.moe_dequantize_fp8(qq, sc, wd)
+            if shared:
+                for (qq, sc), wd in ((qs1, ws1_), (qs3, ws3_), (qs2, ws2_)):
+                    B.moe_dequantize_fp8(qq, sc, wd)
+            i += 1
+            if ev is not None:
+                ev[i].record()
+        if fp8k:
             if not gather:
                 B.moe_permute(s, inp.x, pos, x_perm)
                 i += 1
@@ -156,31 +182,32 @@ def main():
                                    inp.x if shared else None, *qs1, *qs3,
                                    sh_act if shared else None)
         elif gather:
-            B.moe_grouped_gemm_gather(s, inp.x, row_src, inp.w1, inp.w3, meta, nblk, mb, act,
-                                      inp.ws1, inp.ws3, sh_act if shared else None)
+            B.moe_grouped_gemm_gather(s, inp.x, row_src, w1_, w3_, meta, nblk, mb, act,
+                                      ws1_, ws3_, sh_act if shared else None)
         else:
-            B.moe_permute(s, inp.x, pos, x_perm)
-            i += 1
-            if ev is not None:
-                ev[i].record()
+            if not deq:
+                B.moe_permute(s, inp.x, pos, x_perm)
+                i += 1
+                if ev is not None:
+                    ev[i].record()
             if shared:
-                B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta,
-                                          nblk, mb, act, inp.x, inp.ws1, inp.ws3, sh_act)
+                B.moe_grouped_gemm_shared(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1_, w3_, meta,
+                                          nblk, mb, act, inp.x, ws1_, ws3_, sh_act)
             else:
-                B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, inp.w1, inp.w3, meta, nblk,
+                B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, w1_, w3_, meta, nblk,
                                    mb, act)
         i += 1
         if ev is not None:
             ev[i].record()
-        if fp8:
+        if fp8k:
             B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, *q2, None, None, meta, nblk, mb, None, y,
                                    sh_act if shared else None, *qs2, None, None,
                                    sh_out if shared else None)
         elif shared:
-            B.moe_grouped_gemm_shared(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y,
-                                      sh_act, inp.ws2, None, sh_out)
+            B.moe_grouped_gemm_shared(s, B.MOE_OP_DOWN, act, w2_, None, meta, nblk, mb, y,
+                                      sh_act, ws2_, None, sh_out)
         else:
-            B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, inp.w2, None, meta, nblk, mb, y)
+            B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, w2_, None, meta, nblk, mb, y)
         i += 1
         if ev is not None:
             ev[i].record()
@@ -238,7 +265,7 @@ def main():
 
     # cross-check: the single moe_layer_fwd call runs the same kernels
     out2 = torch.empty_like(out)
-    ws2 = B.alloc_workspace(s, dev)
+    ws2 = B.alloc_workspace(s, dev, fp8=fp8)
     def layer_call():
         if fp8:
             B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *q1, *q3, *q2, *qs1, *qs3, *qs2,
@@ -270,7 +297,7 @@ def main():
     sg = LG.gateup_flops(T, d, cfg.d_e_shared) if shared else 0
     sd = LG.down_flops(T, d, cfg.d_e_shared) if shared else 0
     # algorithmic bytes per launch: every tensor the launch needs, once
-    wb = 1 if fp8 else eb                      # bytes per weight
+    wb = 1 if fp8k else eb                     # bytes per weight the GEMM kernels read
     if gather:
         gu_bytes = LG.gateup_gather_bytes(T, M, active, d, de, eb, wb)
     else:
@@ -279,7 +306,7 @@ def main():
     if shared:
         gu_bytes += LG.shared_gateup_bytes(T, d, cfg.d_e_shared, eb, reads_x=not gather, wb=wb)
         dn_bytes += LG.shared_down_bytes(T, d, cfg.d_e_shared, eb, wb)
-    if fp8:
+    if fp8k:
         gu_bytes += LG.fp8_scale_bytes(2 * active + (2 if shared else 0), d, de)
         dn_bytes += LG.fp8_scale_bytes(active + (1 if shared else 0), de, d)
     gemm = {
@@ -305,6 +332,13 @@ def main():
         "combine": {"gbps": cb / (stage_ms["combine"] * 1e6), "bytes": cb,
                     "us": stage_ms["combine"] * 1e3},
     }
+    if deq:
+        # every weight: its code read, its bf16 value written, and the block scales
+        nw = 3 * E * d * de + (3 * d * cfg.d_e_shared if shared else 0)
+        qb = 3 * nw + LG.fp8_scale_bytes(3 * E, d, de) + (
+            LG.fp8_scale_bytes(3, d, cfg.d_e_shared) if shared else 0)
+        moves["dequant"] = {"gbps": qb / (stage_ms["dequant"] * 1e6), "bytes": qb,
+                            "us": stage_ms["dequant"] * 1e3}
     if not routed:
         rb = LG.router_bytes(T, d, E, eb)
         moves["route"] = {"gbps": rb / (stage_ms["route"] * 1e6), "bytes": rb,
@@ -316,7 +350,7 @@ def main():
     dom = max(("gateup", "down"), key=lambda n: stage_ms[n])
     # measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a
     # copy kernel), taken from the committed summary unless the kernel changed since
-    wname = cfg.name + ("-fp8w" if fp8 else "")
+    wname = cfg.name + ("-fp8w" if fp8k else "")
     tpath = args.traffic or os.path.join(ROOT, "profiles", f"{dom}_{wname}_hbm_traffic.md")
     traffic = PS.read_traffic(tpath, dom, wname)
     if gemm[dom]["bound"] == "mfma":
@@ -356,6 +390,7 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "weights": "fp8-e4m3, fp32 scale per 128x128 block" if fp8 else cfg.dtype,
+        **({"fp8_path": "dequantised to bf16, bf16 kernels" if deq else "fp8 kernels"} if fp8 else {}),
         "data": "synthetic (seeded; N(0,1) tokens, N(0,1/fan_in) weights, random-init)",
         "config": {"workload": cfg.description, "name": cfg.name, "T": T, "d": d, "E": E, "k": k,
                    "d_e": de, "d_e_shared": cfg.d_e_shared, "block_m": cfg.block_m,

@@ -24,8 +24,9 @@ MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
 ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
                 "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_grouped_gemm_gather",
-                "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_grouped_gemm_fp8",
-                "moe_layer_fwd_fp8", "moe_combine_bwd", "moe_swiglu_bwd", "moe_grouped_gemm_dgrad",
+                "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_dequantize_fp8",
+                "moe_grouped_gemm_fp8", "moe_fp8_workspace_bytes", "moe_layer_fwd_fp8",
+                "moe_combine_bwd", "moe_swiglu_bwd", "moe_grouped_gemm_dgrad",
                 "moe_grouped_gemm_wgrad", "moe_router_bwd", "moe_router_bwd_workspace_bytes",
                 "moe_grouped_gemm_dgrad_workspace_bytes",
                 "moe_bwd_workspace_bytes",
@@ -100,6 +101,10 @@ def lib():
         L.moe_grouped_gemm_gather.restype = ctypes.c_int32
         L.moe_quantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
         L.moe_quantize_fp8.restype = ctypes.c_int32
+        L.moe_dequantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+        L.moe_dequantize_fp8.restype = ctypes.c_int32
+        L.moe_fp8_workspace_bytes.argtypes = [S]
+        L.moe_fp8_workspace_bytes.restype = ctypes.c_size_t
         L.moe_grouped_gemm_fp8.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32,
                                            P, P, P, P, P, P, P, P, P]
         L.moe_grouped_gemm_fp8.restype = ctypes.c_int32
@@ -193,10 +198,11 @@ def moe_workspace_layout(shape: moe_shape) -> dict:
     return {n: getattr(L, n) for n in _LAYOUT_FIELDS}
 
 
-def alloc_workspace(shape: moe_shape, device="cuda") -> torch.Tensor:
-    n = moe_workspace_bytes(shape)
+def alloc_workspace(shape: moe_shape, device="cuda", fp8: bool = False) -> torch.Tensor:
+    """A workspace for moe_layer_fwd (fp8=False) or moe_layer_fwd_fp8 (fp8=True)."""
+    n = moe_fp8_workspace_bytes(shape) if fp8 else moe_workspace_bytes(shape)
     if n == 0:
-        raise MoEError("moe_workspace_bytes", MOE_EINVAL)
+        raise MoEError("moe_fp8_workspace_bytes" if fp8 else "moe_workspace_bytes", MOE_EINVAL)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
@@ -266,6 +272,31 @@ def moe_quantize_fp8(w, q, scales, stream=None):
     E, K, N = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
     _check("moe_quantize_fp8", lib().moe_quantize_fp8(E, K, N, _p(w), _p(q), _p(scales),
                                                       _stream(stream)))
+
+
+def moe_dequantize_fp8(q, scales, w, stream=None):
+    """q: uint8 [E, K, N] (or [K, N]); scales: fp32 [E, ceil(K/128), ceil(N/128)];
+    w: bf16 of q's shape, written."""
+    E, K, N = (1,) + tuple(q.shape) if q.dim() == 2 else tuple(q.shape)
+    _check("moe_dequantize_fp8", lib().moe_dequantize_fp8(E, K, N, _p(q), _p(scales), _p(w),
+                                                          _stream(stream)))
+
+
+def dequantize_fp8(q, scales, stream=None):
+    """The bf16 weights (code * block scale, rounded to nearest even) of an fp8 pair."""
+    w = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    moe_dequantize_fp8(q, scales, w, stream)
+    return w
+
+
+def moe_fp8_workspace_bytes(shape: moe_shape) -> int:
+    return lib().moe_fp8_workspace_bytes(ctypes.byref(shape))
+
+
+def fp8_dequantises(shape: moe_shape) -> bool:
+    """moe_layer_fwd_fp8 dequantises the weights into its workspace and runs the bf16
+    kernels (its workspace then holds room for them)."""
+    return moe_fp8_workspace_bytes(shape) > moe_workspace_bytes(shape)
 
 
 def fp8_scale_shape(w_shape):

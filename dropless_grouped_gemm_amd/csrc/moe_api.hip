@@ -410,6 +410,74 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, c
                     C_shared, static_cast<hipStream_t>(stream));
 }
 
+// The bf16 gate/up (rows gathered from x where the kernels can) and down launches of
+// the layer, routed experts and the shared expert together, on the workspace laid out
+// by layout_of (routes, block table and the permutation already built).
+static moe_status run_bf16_experts(const moe_shape& s, const void* x, char* base,
+                                   const moe_ws_layout& L, bool gather, const void* w1,
+                                   const void* w3, const void* w2, const void* ws1,
+                                   const void* ws3, const void* ws2, hipStream_t hs) {
+  auto at = [&](size_t off) { return static_cast<void*>(base + off); };
+  const bool shared = s.d_e_shared > 0;
+  const int32_t mb = (int32_t)max_blocks_of(s);
+  const int des = s.d_e_shared;
+  int32_t* meta = static_cast<int32_t*>(at(L.block_meta));
+  int32_t* nblk = static_cast<int32_t*>(at(L.num_blocks));
+  GemmSegments gu{gather ? x : at(L.x_perm), w1, w3, at(L.act), s.d, s.d_e, meta, nblk, mb,
+                  x, ws1, ws3, at(L.shared_act), s.d, des, shared ? s.T : 0,
+                  gather ? static_cast<const int32_t*>(at(L.row_src)) : nullptr, s.k, s.T};
+  moe_status st = launch_grouped_gemm(s, MOE_OP_GATEUP_SWIGLU, gu, hs);
+  if (st != MOE_OK) return st;
+  GemmSegments dn{at(L.act), w2, nullptr, at(L.y), s.d_e, s.d, meta, nblk, mb,
+                  at(L.shared_act), ws2, nullptr, at(L.shared_out), des, s.d, shared ? s.T : 0};
+  return launch_grouped_gemm(s, MOE_OP_DOWN, dn, hs);
+}
+
+// With fp8 weights, where experts average at least 256 rows (the wide bf16 kernel's
+// regime, compute-bound), the layer dequantises the weights once into its workspace and
+// runs the bf16 kernels: the same bf16 weights as the fp8 kernels' own in-register
+// dequantisation; below that (decode-like routing, weight streaming) the fp8 kernels
+// read half the bytes.
+static bool fp8_dequantised_path(const moe_shape& s) {
+  const int64_t M = (int64_t)s.T * s.k;
+  return M > 0 && M >= 256 * (M < s.E ? M : (int64_t)s.E);
+}
+
+struct Fp8Layout {
+  size_t w1, w3, w2, ws1, ws3, ws2, total;
+};
+static void fp8_layout_of(const moe_shape& s, const moe_ws_layout& L, Fp8Layout& F) {
+  size_t cur = L.total;
+  const bool deq = fp8_dequantised_path(s);
+  const size_t E = s.E, d = s.d, de = s.d_e, ds = s.d_e_shared;
+  F.w1 = take(cur, deq ? E * d * de * 2 : 0);
+  F.w3 = take(cur, deq ? E * d * de * 2 : 0);
+  F.w2 = take(cur, deq ? E * de * d * 2 : 0);
+  F.ws1 = take(cur, deq ? d * ds * 2 : 0);
+  F.ws3 = take(cur, deq ? d * ds * 2 : 0);
+  F.ws2 = take(cur, deq ? ds * d * 2 : 0);
+  F.total = cur;
+}
+
+size_t moe_fp8_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  moe_ws_layout L;
+  layout_of(*s, L);
+  Fp8Layout F;
+  fp8_layout_of(*s, L, F);
+  return F.total;
+}
+
+moe_status moe_dequantize_fp8(int32_t E, int32_t K, int32_t N, const uint8_t* q,
+                              const float* scales, void* w, void* stream) {
+  if (E < 1 || K < 1 || N < 8 || N % 8) return MOE_EINVAL;
+  if ((int64_t)E * K * N >= ((int64_t)1 << 40)) return MOE_ENOTSUP;
+  if (!w || !q || !scales || !aligned16(w) || (reinterpret_cast<uintptr_t>(q) & 7u) ||
+      !aligned4(scales))
+    return MOE_EINVAL;
+  return launch_dequantize_fp8(E, K, N, q, scales, w, static_cast<hipStream_t>(stream));
+}
+
 moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_gate,
                              const float* bias, const uint8_t* q1, const float* s1,
                              const uint8_t* q3, const float* s3, const uint8_t* q2,
@@ -442,7 +510,9 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
     return MOE_EINVAL;
   moe_ws_layout L;
   layout_of(*s, L);
-  if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_EWORKSPACE;
+  Fp8Layout F8;
+  fp8_layout_of(*s, L, F8);
+  if (!ws || !aligned16(ws) || ws_bytes < F8.total) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -468,6 +538,21 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
   if (!gather) {
     st = launch_permute(*s, x, pos, at(L.x_perm), hs);
     if (st != MOE_OK) return st;
+  }
+  if (fp8_dequantised_path(*s)) {
+    const int E = s->E, d = s->d, de = s->d_e, des = s->d_e_shared;
+    st = launch_dequantize_fp8(E, d, de, q1, s1, at(F8.w1), hs);
+    if (st == MOE_OK) st = launch_dequantize_fp8(E, d, de, q3, s3, at(F8.w3), hs);
+    if (st == MOE_OK) st = launch_dequantize_fp8(E, de, d, q2, s2, at(F8.w2), hs);
+    if (st == MOE_OK && shared) st = launch_dequantize_fp8(1, d, des, qs1, ss1, at(F8.ws1), hs);
+    if (st == MOE_OK && shared) st = launch_dequantize_fp8(1, d, des, qs3, ss3, at(F8.ws3), hs);
+    if (st == MOE_OK && shared) st = launch_dequantize_fp8(1, des, d, qs2, ss2, at(F8.ws2), hs);
+    if (st != MOE_OK) return st;
+    st = run_bf16_experts(*s, x, base, L, gather, at(F8.w1), at(F8.w3), at(F8.w2),
+                          shared ? at(F8.ws1) : nullptr, shared ? at(F8.ws3) : nullptr,
+                          shared ? at(F8.ws2) : nullptr, hs);
+    if (st != MOE_OK) return st;
+    return launch_combine(*s, at(L.y), pos, wts, shared ? at(L.shared_out) : nullptr, out, hs);
   }
   const int32_t mb = (int32_t)max_blocks_of(*s);
   st = run_fp8_op(*s, MOE_OP_GATEUP_SWIGLU, gather ? x : at(L.x_perm), q1, s1, q3, s3, meta, nblk,
@@ -550,16 +635,7 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
   // Routed experts and the shared expert go through the grouped GEMM together (one
   // launch per op when their shapes agree), the shared expert as a dense segment
   // over the unpermuted x.
-  const int32_t mb = (int32_t)max_blocks_of(*s);
-  const int des = s->d_e_shared;
-  GemmSegments gu{gather ? x : at(L.x_perm), w1, w3, at(L.act), s->d, s->d_e, meta, nblk, mb,
-                  x, ws1, ws3, at(L.shared_act), s->d, des, shared ? s->T : 0,
-                  gather ? static_cast<const int32_t*>(at(L.row_src)) : nullptr, s->k, s->T};
-  st = launch_grouped_gemm(*s, MOE_OP_GATEUP_SWIGLU, gu, hs);
-  if (st != MOE_OK) return st;
-  GemmSegments dn{at(L.act), w2, nullptr, at(L.y), s->d_e, s->d, meta, nblk, mb,
-                  at(L.shared_act), ws2, nullptr, at(L.shared_out), des, s->d, shared ? s->T : 0};
-  st = launch_grouped_gemm(*s, MOE_OP_DOWN, dn, hs);
+  st = run_bf16_experts(*s, x, base, L, gather, w1, w3, w2, ws1, ws3, ws2, hs);
   if (st != MOE_OK) return st;
   const void* sh = shared ? at(L.shared_out) : nullptr;
   return launch_combine(*s, at(L.y), pos, wts, sh, out, hs);

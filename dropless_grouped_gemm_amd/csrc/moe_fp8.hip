@@ -93,6 +93,51 @@ moe_status launch_quantize_fp8(int E, int K, int N, const void* w, uint8_t* q, f
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// Dequantisation to bf16: w[e][k][n] = bf16(code * scale[e][k / 128][n / 128]), the code
+// decoded to fp32 by the hardware conversion and the product rounded to nearest even -
+// exactly what the fp8 grouped GEMM does to each fragment before its MFMA.  One thread
+// per 8 consecutive codes of a row (N % 8 == 0, so 8 codes never straddle a block).
+__global__ void __launch_bounds__(256)
+k_dequantize_fp8(const uint8_t* __restrict__ q, const float* __restrict__ scales, int64_t n8,
+                 int K, int N, int KB, int NB, bf16_t* __restrict__ w) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const int64_t el = i * 8;                 // first element of the 8
+    const int n = (int)(el % N);
+    const int64_t ek = el / N;                // e * K + k
+    const int k = (int)(ek % K);
+    const int64_t e = ek / K;
+    const float sc = scales[((size_t)e * KB + k / 128) * NB + n / 128];
+    const uint2 raw = *reinterpret_cast<const uint2*>(q + el);
+    const uint32_t rw[2] = {raw.x, raw.y};
+    u32x4_t o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(rw[h], false);   // bytes 0, 1
+      const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(rw[h], true);    // bytes 2, 3
+      const __bf16 b0 = static_cast<__bf16>(f0[0] * sc), b1 = static_cast<__bf16>(f0[1] * sc);
+      const __bf16 b2 = static_cast<__bf16>(f1[0] * sc), b3 = static_cast<__bf16>(f1[1] * sc);
+      o[2 * h] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      o[2 * h + 1] = (uint32_t)__builtin_bit_cast(uint16_t, b2) |
+                     ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(w + el) = o;
+  }
+}
+
+moe_status launch_dequantize_fp8(int E, int K, int N, const uint8_t* q, const float* scales,
+                                 void* w, hipStream_t st) {
+  const int64_t n8 = (int64_t)E * K * N / 8;
+  if (n8 == 0) return MOE_OK;
+  int64_t blocks = ceil_div(n8, 256);
+  const int64_t cap = (int64_t)device_cu_count() * 32;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(k_dequantize_fp8, dim3((unsigned)blocks), dim3(256), 0, st, q, scales, n8, K,
+                     N, (int)ceil_div(K, 128), (int)ceil_div(N, 128), static_cast<bf16_t*>(w));
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 // ---------------------------------------------------------------------------
 // grouped GEMM with fp8 B
 // ---------------------------------------------------------------------------

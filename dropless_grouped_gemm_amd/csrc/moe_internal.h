@@ -116,6 +116,9 @@ bool gather_supported(const moe_shape& s);
 // fp8 (e4m3) weights with fp32 scales per 128 x 128 block (moe_fp8.hip).
 moe_status launch_quantize_fp8(int E, int K, int N, const void* w, uint8_t* q, float* scales,
                                hipStream_t st);
+// bf16 weights from codes and scales, bit-identical to the fp8 GEMM's own dequantisation.
+moe_status launch_dequantize_fp8(int E, int K, int N, const uint8_t* q, const float* scales,
+                                 void* w, hipStream_t st);
 // The fp8-weight grouped GEMM applies to this K (contraction) and N.
 bool fp8_gemm_supported(int K, int N);
 struct GemmSegmentsF8 {

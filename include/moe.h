@@ -294,6 +294,17 @@ moe_status moe_quantize_fp8(int32_t E, int32_t K, int32_t N, const void* w, uint
                             float* scales, void* stream);
 
 /*
+ * The inverse map of moe_quantize_fp8's format: w[e][i][j] = bf16(fp32(code) * scale
+ * of its 128 x 128 block), the product rounded to nearest even - the same bf16 value
+ * that moe_grouped_gemm_fp8 builds in registers for each weight before its MFMA.
+ * q [E, K, N] uint8 (8-byte aligned), scales [E, ceil(K/128), ceil(N/128)] fp32,
+ * w [E, K, N] bf16 (16-byte aligned, caller-owned).  Requires N % 8 == 0.
+ * Errors: MOE_EINVAL for bad sizes or pointers; nothing is launched then.
+ */
+moe_status moe_dequantize_fp8(int32_t E, int32_t K, int32_t N, const uint8_t* q,
+                              const float* scales, void* w, void* stream);
+
+/*
  * The grouped GEMM (as moe_grouped_gemm, one op per call) with fp8 weights:
  * B0 / B1 are (Q0, S0) / (Q1, S1) code and scale arrays of W1 / W3 (gate/up) or W2
  * (down: Q1 = S1 = NULL).  Each 16-deep weight fragment is dequantised to bf16
@@ -319,9 +330,17 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A,
 /*
  * moe_layer_fwd with fp8 weights: (q1, s1), (q3, s3), (q2, s2) replace w1, w3, w2 and
  * (qs1, ss1), (qs3, ss3), (qs2, ss2) the shared expert's (NULLs when d_e_shared == 0).
- * Same workspace (moe_workspace_bytes), same pipeline and requirements as
- * moe_grouped_gemm_fp8.
+ * Same pipeline and requirements as moe_grouped_gemm_fp8.  Where the routed rows
+ * M = T * k reach 256 * min(E, M) (experts average at least 256 rows: compute-bound
+ * GEMMs), the layer first dequantises every weight into its workspace
+ * (moe_dequantize_fp8) and runs moe_layer_fwd's bf16 kernels on them; below that it
+ * runs moe_grouped_gemm_fp8, which reads half the weight bytes.  Both use the same
+ * bf16 weight values, so the outputs agree to the order of the fp32 sums.
+ * Workspace: moe_fp8_workspace_bytes(s) bytes (moe_workspace_bytes's layout, then the
+ * dequantised weights where they are used), 16-byte aligned.
  */
+size_t moe_fp8_workspace_bytes(const moe_shape* s);
+
 moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_gate,
                              const float* bias, const uint8_t* q1, const float* s1,
                              const uint8_t* q3, const float* s3, const uint8_t* q2,

@@ -292,7 +292,7 @@ def test_fp8_entry_point_argument_rules():
     assert ok(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE,
               FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
     lf = L.moe_layer_fwd_fp8
-    need = L.moe_workspace_bytes(ps)
+    need = L.moe_fp8_workspace_bytes(ps)
     # no router weights and no given routes; and a shared-expert pointer without one
     assert lf(ps, FAKE, None, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE, need,
               None) == B.MOE_EINVAL
@@ -300,6 +300,41 @@ def test_fp8_entry_point_argument_rules():
               need, None) == B.MOE_EINVAL
     assert lf(ps, FAKE, FAKE, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE,
               need - 1, None) == B.MOE_EWORKSPACE
+
+
+def test_fp8_workspace_size_rule():
+    """moe_fp8_workspace_bytes: moe_workspace_bytes's layout, plus room for the
+    dequantised bf16 weights exactly where the layer takes the dequantised path (routed
+    rows M = T * k at least 256 * min(E, M))."""
+    L = B.lib()
+    for kw in (dict(T=64), dict(T=1023), dict(T=1024), dict(T=4096, d_e_shared=512),
+               dict(T=0), dict(T=70, E=1, k=4), dict(T=512, E=300, k=8)):
+        s = good_shape(**kw)
+        base, f8 = L.moe_workspace_bytes(ctypes.byref(s)), L.moe_fp8_workspace_bytes(ctypes.byref(s))
+        M = s.T * s.k
+        wide = M > 0 and M >= 256 * min(s.E, M)
+        w = 2 * (3 * s.E * s.d * s.d_e + 3 * s.d * s.d_e_shared)
+        if wide:
+            assert w <= f8 - base <= w + 6 * 256, kw
+        else:
+            assert f8 == base, kw
+    assert L.moe_fp8_workspace_bytes(ctypes.byref(good_shape(k=0))) == 0
+
+
+def test_dequantize_fp8_argument_rules():
+    """Sizes and pointers checked before any launch: N a multiple of 8, q 8-byte and w
+    16-byte aligned, scales 4-byte aligned."""
+    L = B.lib()
+    dq = L.moe_dequantize_fp8
+    F16 = ctypes.c_void_p(0x10000)
+    assert dq(1, 128, 12, F16, F16, F16, None) == B.MOE_EINVAL
+    assert dq(0, 128, 16, F16, F16, F16, None) == B.MOE_EINVAL
+    assert dq(1, 0, 16, F16, F16, F16, None) == B.MOE_EINVAL
+    assert dq(1, 128, 16, None, F16, F16, None) == B.MOE_EINVAL
+    assert dq(1, 128, 16, F16, F16, None, None) == B.MOE_EINVAL
+    assert dq(1, 128, 16, ctypes.c_void_p(0x10004), F16, F16, None) == B.MOE_EINVAL
+    assert dq(1, 128, 16, F16, F16, ctypes.c_void_p(0x10008), None) == B.MOE_EINVAL
+    assert dq(1, 128, 16, F16, ctypes.c_void_p(0x10002), F16, None) == B.MOE_EINVAL
 
 
 def test_backward_entry_point_argument_rules():

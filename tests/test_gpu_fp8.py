@@ -41,6 +41,25 @@ def test_quantize_is_bit_exact(E, K, N):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
+@pytest.mark.parametrize("E,K,N", [(2, 300, 200), (1, 7168, 256), (3, 128, 8)])
+def test_dequantize_is_bit_exact(E, K, N):
+    """Every e4m3 code (NaNs aside) times fp32 block scales, rounded once to fp32 and
+    then to bf16 (nearest even): the decode is the oracle's code table, the two
+    roundings numpy's and torch's CPU casts."""
+    rng = np.random.default_rng(E + K + N)
+    codes = rng.integers(0, 256, size=(E, K, N)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x00
+    kb, nb = -(-K // 128), -(-N // 128)
+    scales = (rng.uniform(0.5, 2.0, size=(E, kb, nb)) *
+              2.0 ** rng.integers(-12, 4, size=(E, kb, nb))).astype(np.float32)
+    w = B.dequantize_fp8(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    full = np.repeat(np.repeat(scales, 128, axis=1), 128, axis=2)[:, :K, :N]
+    prod = F.e4m3_decode(codes).astype(np.float32) * full          # fp32 product, RNE
+    ref = torch.from_numpy(prod).to(torch.bfloat16)
+    assert torch.equal(w.cpu().view(torch.int16), ref.view(torch.int16))
+
+
 def _routes(T, E, k, seed):
     rng = np.random.default_rng(seed)
     return rng.integers(0, E, size=(T, k))
@@ -140,7 +159,7 @@ def test_layer_fwd_fp8(name, scale):
     qz = [B.quantize_fp8(w) for w in (inp.w1, inp.w3, inp.w2)]
     qs = [B.quantize_fp8(w) for w in (inp.ws1, inp.ws3, inp.ws2)] if cfg.d_e_shared else [(None, None)] * 3
     out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=DEV)
-    ws = B.alloc_workspace(s)
+    ws = B.alloc_workspace(s, fp8=True)
     routed = inp.topk_idx is not None
     B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *qz[0], *qz[1], *qz[2], *qs[0], *qs[1],
                         *qs[2], inp.topk_idx if routed else None, inp.topk_w if routed else None,
@@ -165,3 +184,44 @@ def test_layer_fwd_fp8(name, scale):
                           renormalize=cfg.renormalize, decision_logits=logits, **kw)
     rel = assert_close(f64(out), ref.out, TOL_OUT["bf16"], "out")
     print(f"[fp8 parity] {cfg.name}: out max|d|/max|ref| = {rel:.2e}")
+
+
+@pytest.mark.parametrize("name,scale,wide", [
+    ("ep-share-4x2048", dict(name="ep-fp8-wide", T=512, d=512, d_e=256,
+                             fixed_counts=(1357, 938, 1124, 677)), True),
+    ("fusedmoe-8x2048", dict(name="fm-fp8-wide", T=600, d=512, d_e=256, d_e_shared=256), True),
+    ("fusedmoe-8x2048", dict(name="fm-fp8-narrow", T=400, d=512, d_e=256, d_e_shared=256), False),
+    ("decode-256x2048", dict(name="decode-fp8-dq", d=512, d_e=256, d_e_shared=256), False),
+])
+def test_layer_fwd_fp8_against_bf16_layer_on_dequantised_weights(name, scale, wide):
+    """Where experts average >= 256 rows the fp8 layer dequantises its weights and runs
+    the bf16 layer's kernels: bitwise equal to moe_layer_fwd on moe_dequantize_fp8's
+    weights.  Below that it runs the fp8 kernels, which build the same bf16 weights in
+    registers: equal up to the order of the fp32 sums (5e-3 * max|out|)."""
+    cfg = get_config(name).scaled(**scale)
+    inp = make_inputs(cfg, device=DEV)
+    s = B.shape_of_config(cfg)
+    M = cfg.T * cfg.k
+    assert (M >= 256 * min(cfg.E, M)) == wide
+    extra = B.moe_fp8_workspace_bytes(s) - B.moe_workspace_bytes(s)
+    wbytes = 2 * 3 * cfg.E * cfg.d * cfg.d_e + 2 * 3 * cfg.d * cfg.d_e_shared
+    assert extra >= wbytes if wide else extra == 0
+    qz = [B.quantize_fp8(w) for w in (inp.w1, inp.w3, inp.w2)]
+    qs = [B.quantize_fp8(w) for w in (inp.ws1, inp.ws3, inp.ws2)] if cfg.d_e_shared else [(None, None)] * 3
+    dqz = [B.dequantize_fp8(*p) for p in qz]
+    dqs = [None if p[0] is None else B.dequantize_fp8(*p) for p in qs]
+    routed = inp.topk_idx is not None
+    ri, rw = (inp.topk_idx, inp.topk_w) if routed else (None, None)
+    out8 = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=DEV)
+    out16 = torch.empty_like(out8)
+    ws8 = torch.full((B.moe_fp8_workspace_bytes(s),), 0xFF, dtype=torch.uint8, device=DEV)
+    B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *qz[0], *qz[1], *qz[2], *qs[0], *qs[1],
+                        *qs[2], ri, rw, out8, ws8)
+    B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, *dqz, *dqs, ri, rw, out16,
+                    B.alloc_workspace(s))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out8.float()).all()
+    if wide:
+        assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+    else:
+        assert_close(f64(out8), f64(out16), 5e-3, "fp8 kernels vs bf16 kernels")

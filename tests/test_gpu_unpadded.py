@@ -92,7 +92,7 @@ def test_build_offsets_unpadded_worked_example():
 def _layer(cfg, inp, unpadded, fp8=False):
     c = cfg.scaled(name=cfg.name + ("-unpadded" if unpadded else "-padded"), unpadded=unpadded)
     s = B.shape_of_config(c)
-    ws = B.alloc_workspace(s)
+    ws = B.alloc_workspace(s, fp8=fp8)
     out = torch.empty((c.T, c.d), dtype=inp.x.dtype, device=DEV)
     routed = inp.topk_idx is not None
     ri, rw = (inp.topk_idx, inp.topk_w) if routed else (None, None)
