@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import json
 import math
+import statistics
 import os
 import sys
 import time
@@ -50,6 +51,10 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time the layer's backward pass (per stage and moe_layer_bwd) and "
                          "report it under 'backward'")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not write the 1 GiB scratch buffer between timed steps (by default "
+                         "every step starts with L2 and the 256 MB Infinity Cache holding "
+                         "none of its inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -231,18 +236,25 @@ def main():
 
     nst = len(stages)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    # a 1 GiB write before each timed step evicts L2 and the Infinity Cache, so no step
+    # reads what the previous one left cached; it lies outside the step's events
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for kk in range(args.steps):
+        if flush is not None:
+            flush.fill_(kk & 0x7F)
         step(evs[kk])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = {st: 0.0 for st in stages}
     total_ms = 0.0
+    per_step = []
     for kk in range(args.steps):
         for j, st in enumerate(stages):
             stage_ms[st] += evs[kk][j].elapsed_time(evs[kk][j + 1])
-        total_ms += evs[kk][0].elapsed_time(evs[kk][nst])
+        per_step.append(evs[kk][0].elapsed_time(evs[kk][nst]))
+        total_ms += per_step[-1]
     ms_per_step = total_ms / args.steps
     for st in stages:
         stage_ms[st] /= args.steps
@@ -253,13 +265,16 @@ def main():
         # timed on its own for its bandwidth figure
         for _ in range(2):
             B.moe_permute(s, inp.x, pos, x_perm)
-        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        p0.record()
-        for _ in range(args.steps):
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for p0, p1 in pev:
+            if flush is not None:
+                flush.fill_(0x2A)
+            p0.record()
             B.moe_permute(s, inp.x, pos, x_perm)
-        p1.record()
+            p1.record()
         torch.cuda.synchronize()
-        permute_ms = p0.elapsed_time(p1) / args.steps
+        permute_ms = sum(p0.elapsed_time(p1) for p0, p1 in pev) / args.steps
     else:
         permute_ms = stage_ms["permute"]
 
@@ -275,14 +290,17 @@ def main():
                             inp.ws3, inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
     layer_call()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nrep = max(3, args.steps // 2)
-    e0.record()
-    for _ in range(nrep):
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nrep)]
+    for a0, a1 in lev:
+        if flush is not None:
+            flush.fill_(0x55)
+        a0.record()
         layer_call()
-    e1.record()
+        a1.record()
     torch.cuda.synchronize()
-    layer_fwd_ms = e0.elapsed_time(e1) / nrep
+    layer_fwd_ms = sum(a0.elapsed_time(a1) for a0, a1 in lev) / nrep
     same = bool(torch.equal(out.view(torch.int16) if eb == 2 else out.view(torch.int32),
                             out2.view(torch.int16) if eb == 2 else out2.view(torch.int32)))
     del ws2, out2
@@ -385,6 +403,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": statistics.median(per_step),
+        "caches": "cold: 1 GiB written before each timed step" if flush is not None else "warm",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -504,7 +524,10 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
     torch.cuda.synchronize()
     nst = len(stages)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     for kk in range(args.steps):
+        if flush is not None:
+            flush.fill_(kk & 0x7F)
         step(evs[kk])
     torch.cuda.synchronize()
     st_ms = {n: sum(evs[kk][j].elapsed_time(evs[kk][j + 1]) for kk in range(args.steps)) / args.steps
@@ -523,14 +546,17 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
         None if routed else dwg, None if routed else db, dtw, bws)
     call()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nrep = max(3, args.steps // 2)
-    e0.record()
-    for _ in range(nrep):
+    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nrep)]
+    for a0, a1 in lev:
+        if flush is not None:
+            flush.fill_(0x55)
+        a0.record()
         call()
-    e1.record()
+        a1.record()
     torch.cuda.synchronize()
-    layer_ms = e0.elapsed_time(e1) / nrep
+    layer_ms = sum(a0.elapsed_time(a1) for a0, a1 in lev) / nrep
 
     # algorithmic FLOPs per stage: every GEMM launch and its shared-expert twin
     gu = LG.gateup_flops(M, d, de) + (LG.gateup_flops(T, d, ds) if shared else 0)
