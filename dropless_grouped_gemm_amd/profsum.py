@@ -81,7 +81,7 @@ def kernels_summary(d: str, command: str, bench_log: str | None) -> str:
         lines.append(f"| `{short_name(n)}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{med.get(n, float('nan')):.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
-    out = ["Command (from the repository root; profiler output under gpurun_out/):", "",
+    out = ["Command (from the repository root):", "",
            "```", command, "```", ""] + lines
     if bench_log and os.path.exists(bench_log):
         js = [l for l in open(bench_log).read().splitlines() if l.startswith("{")]
@@ -125,7 +125,7 @@ def traffic_summary(fetch_dir, write_dir, kernel, label, workload, command, algo
         res[counter] = dict(kib=kib, dispatches=n, probe_kib=probe_kib, factor=factor,
                             bytes=kib * 1024.0 * factor, name=name)
     total = res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]
-    out = ["Command (from the repository root; profiler output under gpurun_out/):", "",
+    out = ["Command (from the repository root):", "",
            "```", command, "```", "",
            f"Kernel `{short_name(res['FETCH_SIZE']['name'])}` ({label}), workload {workload}.", "",
            "| counter | KiB / dispatch | dispatches | probe KiB | scale | bytes / launch |",
