@@ -309,3 +309,23 @@ def test_layer_bwd_without_tokens_zeroes_the_weight_gradients():
     torch.cuda.synchronize()
     for n, v in g.items():
         assert torch.count_nonzero(v).item() == 0, n
+
+
+@pytest.mark.parametrize("name,scale", [
+    ("fusedmoe-8x2048", dict(name="fusedmoe-bwd-det", T=640, d=256, d_e=192, d_e_shared=320)),
+    ("zipf-skew-64x1408", dict(name="zipf-bwd-det", T=300, d=256, d_e=160)),
+])
+def test_layer_bwd_is_deterministic(name, scale):
+    """Two backward passes of the same layer produce bitwise-equal gradients: every sum
+    (weight gradients over an expert's rows, the router's chunked weight gradient, dx
+    over a token's k rows) runs in a fixed order, with no atomics."""
+    cfg = get_config(name).scaled(**scale)
+    inp = make_inputs(cfg, device=DEV)
+    dout = _dout(cfg, 13)
+    _, g1 = _layer_grads(cfg, inp, dout)
+    _, g2 = _layer_grads(cfg, inp, dout)
+    for n, a in g1.items():
+        if a is None:
+            continue
+        v = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(v), g2[n].view(v)), n

@@ -225,3 +225,25 @@ def test_layer_fwd_fp8_against_bf16_layer_on_dequantised_weights(name, scale, wi
         assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
     else:
         assert_close(f64(out8), f64(out16), 5e-3, "fp8 kernels vs bf16 kernels")
+
+
+@pytest.mark.parametrize("name,scale", [
+    ("decode-256x2048", dict(name="decode-fp8-det", d=512, d_e=256, d_e_shared=256)),
+    ("fusedmoe-8x2048", dict(name="fm-fp8-det", T=600, d=512, d_e=256, d_e_shared=256)),
+])
+def test_layer_fwd_fp8_is_deterministic(name, scale):
+    """Both fp8 layer paths (fp8 kernels; dequantise then bf16 kernels) give bitwise-equal
+    outputs run to run."""
+    cfg = get_config(name).scaled(**scale)
+    inp = make_inputs(cfg, device=DEV)
+    s = B.shape_of_config(cfg)
+    qz = [B.quantize_fp8(w) for w in (inp.w1, inp.w3, inp.w2)]
+    qs = [B.quantize_fp8(w) for w in (inp.ws1, inp.ws3, inp.ws2)]
+    outs = []
+    for _ in range(2):
+        out = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=DEV)
+        B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *qz[0], *qz[1], *qz[2], *qs[0],
+                            *qs[1], *qs[2], None, None, out, B.alloc_workspace(s, fp8=True))
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
