@@ -34,53 +34,91 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // combine backward
 // ---------------------------------------------------------------------------
-static constexpr int kCbWaves = 4;
-static constexpr int kCbVec = 16;   // 16-byte vectors per lane held (rows up to 8192 bf16)
+static constexpr int kCbWaves = 8;    // kCbSplit waves per token
+static constexpr int kCbSplit = 4;
+static constexpr int kCbVec = 4;      // 16-byte vectors per lane per wave (rows up to 8192 bf16)
+static constexpr int kCbMaxK = 1024;
 
+// kCbSplit waves per token, wave q of them over vectors [256 q, 256 q + 256) of the row.
+// dout's part stays packed (bf16 pairs widen exactly to fp32 on use); the token's k rows
+// of y stream through two register buffers, row j+1's loads in flight while row j is
+// used.  Each wave's dot is a fixed-order lane sum of its fma chain; dw is the sum of
+// the parts in wave order, through LDS: the same sums on every run.
 __global__ void __launch_bounds__(64 * kCbWaves)
 k_combine_bwd(const u32x4_t* __restrict__ dout, const u32x4_t* __restrict__ y,
               const int32_t* __restrict__ pos, const float* __restrict__ w, int T, int k,
               int nvec, int64_t max_rows, u32x4_t* __restrict__ dy, float* __restrict__ dw) {
+  __shared__ float s_part[kCbWaves][kCbMaxK];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  for (int t = blockIdx.x * kCbWaves + wave; t < T; t += gridDim.x * kCbWaves) {
-    float g[kCbVec][8];
+  const int tok = wave / kCbSplit, part = wave % kCbSplit;
+  constexpr int kTok = kCbWaves / kCbSplit;      // tokens per block and iteration
+  const int v0 = part * kCbVec * 64 + lane;      // this lane's first vector
+  for (int tb = blockIdx.x * kTok; tb < T; tb += gridDim.x * kTok) {
+    const int t = tb + tok;
+    if (t < T) {
+      u32x4_t gv[kCbVec];
 #pragma unroll
-    for (int i = 0; i < kCbVec; ++i) {
-      const int v = lane + 64 * i;
-      u32x4_t r = u32x4_t{0u, 0u, 0u, 0u};
-      if (v < nvec) r = dout[(size_t)t * nvec + v];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        g[i][2 * h] = __uint_as_float(r[h] << 16);
-        g[i][2 * h + 1] = __uint_as_float(r[h] & 0xffff0000u);
+      for (int i = 0; i < kCbVec; ++i) {
+        const int v = v0 + 64 * i;
+        gv[i] = v < nvec ? dout[(size_t)t * nvec + v] : u32x4_t{0u, 0u, 0u, 0u};
       }
-    }
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[(size_t)t * k + j];
-      const float wj = w[(size_t)t * k + j];
-      float dot = 0.f;
-      if (p >= 0 && p < max_rows) {
+      auto load_row = [&](int j, u32x4_t* yv) {
+        const int p = pos[(size_t)t * k + j];
+        const bool ok = p >= 0 && p < max_rows;
 #pragma unroll
         for (int i = 0; i < kCbVec; ++i) {
-          const int v = lane + 64 * i;
-          if (v >= nvec) continue;
-          const u32x4_t r = y[(size_t)p * nvec + v];
-          u32x4_t o;
+          const int v = v0 + 64 * i;
+          yv[i] = (ok && v < nvec) ? y[(size_t)p * nvec + v] : u32x4_t{0u, 0u, 0u, 0u};
+        }
+      };
+      auto use_row = [&](int j, const u32x4_t* yv) {
+        const int p = pos[(size_t)t * k + j];
+        const bool ok = p >= 0 && p < max_rows;
+        const float wj = w[(size_t)t * k + j];
+        float dot = 0.f;
+        if (ok) {
 #pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            dot = fmaf(g[i][2 * h], __uint_as_float(r[h] << 16), dot);
-            dot = fmaf(g[i][2 * h + 1], __uint_as_float(r[h] & 0xffff0000u), dot);
-            o[h] = pack_bf16x2(wj * g[i][2 * h], wj * g[i][2 * h + 1]);
+          for (int i = 0; i < kCbVec; ++i) {
+            const int v = v0 + 64 * i;
+            if (v >= nvec) continue;
+            u32x4_t o;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const float g0 = __uint_as_float(gv[i][h] << 16);
+              const float g1 = __uint_as_float(gv[i][h] & 0xffff0000u);
+              dot = fmaf(g0, __uint_as_float(yv[i][h] << 16), dot);
+              dot = fmaf(g1, __uint_as_float(yv[i][h] & 0xffff0000u), dot);
+              o[h] = pack_bf16x2(wj * g0, wj * g1);
+            }
+            dy[(size_t)p * nvec + v] = o;
           }
-          dy[(size_t)p * nvec + v] = o;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+        if (lane == 0) s_part[wave][j] = dot;
+      };
+      u32x4_t ya[kCbVec], yb[kCbVec];
+      load_row(0, ya);
+      for (int j = 0; j < k; j += 2) {
+        if (j + 1 < k) load_row(j + 1, yb);
+        use_row(j, ya);
+        if (j + 1 < k) {
+          if (j + 2 < k) load_row(j + 2, ya);
+          use_row(j + 1, yb);
         }
       }
-      // fixed-order butterfly: the same sum on every run
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-      if (lane == 0) dw[(size_t)t * k + j] = (p >= 0 && p < max_rows) ? dot : 0.f;
     }
+    __syncthreads();
+    if (t < T && part == 0) {
+      for (int j = lane; j < k; j += 64) {
+        float sum = s_part[wave][j];
+#pragma unroll
+        for (int q = 1; q < kCbSplit; ++q) sum += s_part[wave + q][j];
+        dw[(size_t)t * k + j] = sum;
+      }
+    }
+    __syncthreads();   // partials read before the next tokens overwrite them
   }
 }
 
@@ -88,9 +126,9 @@ moe_status launch_combine_bwd(const moe_shape& s, const void* dout, const void* 
                               const int32_t* pos, const float* topk_w, void* dy, float* dw,
                               int64_t max_rows, hipStream_t st) {
   const int nvec = (int)((int64_t)s.d * 2 / 16);
-  if (nvec > 64 * kCbVec) return MOE_ENOTSUP;
-  int64_t blocks = ceil_div(s.T, kCbWaves);
-  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (nvec > kCbSplit * 64 * kCbVec || s.k > kCbMaxK) return MOE_ENOTSUP;
+  int64_t blocks = ceil_div(s.T, kCbWaves / kCbSplit);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_combine_bwd, dim3((unsigned)blocks), dim3(64 * kCbWaves), 0, st,
