@@ -55,6 +55,25 @@ int wide_max_blocks() {
   return kWMaxBlocks;
 }
 
+// Work order.  Items (row group g, column tile t) are numbered in supertiles of
+// Gs x Ts = 32 items (Ts = min(n_tiles, 8) consecutive tiles of Gs consecutive groups,
+// group-major inside), supertiles row by row; the slot j * grid + q of a persistent
+// grid's iteration j goes to work group (q % (grid / 8)) * 8 + q / (grid / 8).  Work
+// groups are dealt to the 8 XCDs in turn, so each XCD runs 32 consecutive items - one
+// supertile: a few A panels and B panels shared through that XCD's L2, instead of up to
+// 32 of each.
+__device__ __forceinline__ void wide_item(int slot, int ngt, int n_tiles, int& g, int& t) {
+  const int Ts = min(n_tiles, 8);
+  const int Gs = 32 / Ts;
+  const int row_items = Gs * n_tiles;
+  const int sr = slot / row_items, rem = slot - sr * row_items;
+  const int gr = min(Gs, ngt - sr * Gs);
+  const int sc = rem / (gr * Ts), within = rem - sc * gr * Ts;
+  const int tc = min(Ts, n_tiles - sc * Ts);
+  g = sr * Gs + within / tc;
+  t = sc * Ts + within % tc;
+}
+
 template <int OP, int NW>
 __global__ void __launch_bounds__(NW * 64, 1)
 k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
@@ -176,19 +195,24 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     b_lane[jb] = (uint32_t)(((g >> 1) * 8 + tr_r) * kBPitch + chunk * 16 + (tr_c4 & 1) * 8);
   }
 
+  const int ngt = ng_dense + ngroups;
+  const int per_xcd = gridDim.x / 8;
+  const int q = (gridDim.x % 8 == 0) ? (blockIdx.x % 8) * per_xcd + blockIdx.x / 8 : blockIdx.x;
   int my_groups = 0;  // lane j: the group-list entry of this work group's item (batch + j)
   for (int j = 0;; ++j) {
-    const int w = blockIdx.x + j * gridDim.x;
+    const int w = q + j * gridDim.x;
     if (w >= total) break;
     if (j % 64 == 0) {
       if (j > 0) build_groups();   // the ring is idle between items
-      const int wl = blockIdx.x + (j + lane) * gridDim.x;
-      const int gl = wl / n_tiles - ng_dense;
+      const int wl = q + (j + lane) * gridDim.x;
+      int gl_g = 0, gl_t = 0;
+      if (wl < total) wide_item(wl, ngt, n_tiles, gl_g, gl_t);
+      const int gl = gl_g - ng_dense;
       my_groups = (wl < total && gl >= 0) ? s_groups[gl] : 0;
       __syncthreads();             // every wave has its entries before the ring refills
     }
-    const int nt = w % n_tiles;
-    const int gidx = w / n_tiles;
+    int gidx, nt;
+    wide_item(w, ngt, n_tiles, gidx, nt);
     const bool in_dense = gidx < ng_dense;
     int e, m0, valid;
     if (in_dense) {
