@@ -137,8 +137,11 @@ def test_layer_unpadded_equals_padded(name, scale, tile, monkeypatch):
     assert_close(f64(out_u), ref.out, TOL_OUT[cu.dtype], "out")
 
 
-def test_layer_fp8_unpadded_equals_padded():
-    cfg = get_config("fusedmoe-8x2048").scaled(name="fm-u-fp8", T=300, d=512, d_e=256,
+@pytest.mark.parametrize("T", [300, 600])
+def test_layer_fp8_unpadded_equals_padded(T):
+    """T = 300: the fp8 kernels; T = 600 (experts average 300 rows): the weights
+    dequantised, then the bf16 kernels."""
+    cfg = get_config("fusedmoe-8x2048").scaled(name=f"fm-u-fp8-{T}", T=T, d=512, d_e=256,
                                                d_e_shared=256)
     inp = make_inputs(cfg, device=DEV)
     _, _, _, out_p = _layer(cfg, inp, False, fp8=True)
