@@ -150,3 +150,41 @@ def test_layer_is_deterministic(case):
     valid = torch.from_numpy(np.nonzero(ref.row_src >= 0)[0]).to(run.out.device)
     assert torch.equal(run.act()[valid].view(bits), run2.act()[valid].view(bits))
     assert torch.equal(run.y()[valid].view(bits), run2.y()[valid].view(bits))
+
+
+@pytest.mark.parametrize("name,scale,tile", [
+    # one expert chosen by every token: the layer is a dense SwiGLU MLP with weight 1
+    ("fusedmoe-8x2048", dict(name="one-expert", T=200, d=256, E=1, k=1, d_e=128,
+                             d_e_shared=0), None),
+    ("fusedmoe-8x2048", dict(name="one-expert-wide", T=900, d=256, E=1, k=1, d_e=128,
+                             d_e_shared=128), "384"),
+    # every token chooses every expert (k = E)
+    ("fusedmoe-8x2048", dict(name="all-experts", T=150, d=256, E=4, k=4, d_e=128,
+                             d_e_shared=0), None),
+    # a single token
+    ("decode-256x2048", dict(name="one-token", T=1, d=512, d_e=256, d_e_shared=256), None),
+])
+def test_layer_degenerate_routing(name, scale, tile, monkeypatch):
+    """Degenerate routings through moe_layer_fwd against the oracle; with one expert and
+    k = 1 also against the dense SwiGLU MLP (routing weight 1) computed by torch in fp32."""
+    if tile:
+        monkeypatch.setenv("MOE_GG_TILE_ROWS", tile)
+    cfg = get_config(name).scaled(**scale)
+    inp = make_inputs(cfg, device="cuda")
+    run = LayerRun(cfg, inp)
+    h = host_inputs(inp)
+    ref = oracle_layer(cfg, h, run, inp)
+    assert_close(f64(run.out), ref.out, TOL_OUT[cfg.dtype], "out")
+    ints = run.ints()
+    assert ints["counts"].sum() == cfg.T * cfg.k
+    if cfg.E == 1:
+        w = run.view("topk_w", torch.float32, (cfg.T, 1))
+        assert torch.all(w == 1.0)
+        x = inp.x.float()
+        dense = (torch.nn.functional.silu(x @ inp.w1[0].float()) * (x @ inp.w3[0].float())) @ inp.w2[0].float()
+        if cfg.d_e_shared:
+            dense += (torch.nn.functional.silu(x @ inp.ws1.float()) * (x @ inp.ws3.float())) @ inp.ws2.float()
+        assert_close(f64(run.out), dense.double().cpu().numpy(), TOL_OUT[cfg.dtype], "dense MLP")
+    if cfg.k == cfg.E:
+        idx = run.view("topk_idx", torch.int32, (cfg.T, cfg.k)).cpu().numpy()
+        assert all(sorted(r) == list(range(cfg.E)) for r in idx)
