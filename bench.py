@@ -477,6 +477,9 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
     stages = (["combine_bwd", "dgrad_down", "wgrad_down", "permute", "swiglu_bwd", "dgrad_gateup",
                "wgrad_gateup"] + ([] if routed else ["router_bwd"]) + ["unpermute"])
 
+    # the weight gradients' work queue (largest expert first), as moe_layer_bwd runs them
+    wsched = torch.empty(B.moe_grouped_gemm_wgrad_workspace_bytes(s), dtype=torch.uint8, device=dev)
+
     def step(ev=None):
         i = 0
         mark = lambda: ev[i].record() if ev is not None else None
@@ -489,7 +492,8 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
             B.moe_grouped_gemm_dgrad(s1, B.MOE_OP_DOWN, dout, inp.ws2, None, None, None, 0, sdact,
                                      wts_dn)
         i += 1; mark()
-        B.moe_grouped_gemm_wgrad(s, B.MOE_OP_DOWN, fw["act"], dy, fw["counts"], fw["pad"], dw2, None)
+        B.moe_grouped_gemm_wgrad(s, B.MOE_OP_DOWN, fw["act"], dy, fw["counts"], fw["pad"], dw2, None,
+                                 wsched)
         if shared:
             B.moe_grouped_gemm_wgrad(s1, B.MOE_OP_DOWN, fw["sh_act"], dout, None, None, dws2, None)
         i += 1; mark()
@@ -506,7 +510,7 @@ def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):
                                      0, sdx, wts_gu)
         i += 1; mark()
         B.moe_grouped_gemm_wgrad(s, B.MOE_OP_GATEUP_SWIGLU, xp, dgu, fw["counts"], fw["pad"], dw1,
-                                 dw3)
+                                 dw3, wsched)
         if shared:
             B.moe_grouped_gemm_wgrad(s1, B.MOE_OP_GATEUP_SWIGLU, inp.x, sdgu, None, None, dws1, dws3)
         i += 1; mark()

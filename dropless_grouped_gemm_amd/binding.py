@@ -27,7 +27,8 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
                 "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_dequantize_fp8",
                 "moe_grouped_gemm_fp8", "moe_fp8_workspace_bytes", "moe_layer_fwd_fp8",
                 "moe_combine_bwd", "moe_swiglu_bwd", "moe_grouped_gemm_dgrad",
-                "moe_grouped_gemm_wgrad", "moe_router_bwd", "moe_router_bwd_workspace_bytes",
+                "moe_grouped_gemm_wgrad", "moe_grouped_gemm_wgrad_workspace_bytes",
+                "moe_router_bwd", "moe_router_bwd_workspace_bytes",
                 "moe_grouped_gemm_dgrad_workspace_bytes",
                 "moe_bwd_workspace_bytes",
                 "moe_bwd_workspace_layout", "moe_layer_bwd")
@@ -50,7 +51,7 @@ class moe_ws_layout(ctypes.Structure):
 
 _BWD_LAYOUT_FIELDS = ("dy", "dact", "dgu", "x_perm", "dx_perm", "dtopk_w", "dlogits",
                       "shared_dact", "shared_dgu", "shared_dx", "router_dx", "router_scratch",
-                      "w2_t", "w13_t", "ws2_t", "ws13_t", "total")
+                      "wgrad_sched", "w2_t", "w13_t", "ws2_t", "ws13_t", "total")
 
 
 class moe_bwd_ws_layout(ctypes.Structure):
@@ -123,7 +124,10 @@ def lib():
         L.moe_grouped_gemm_dgrad_workspace_bytes.argtypes = [S, ctypes.c_int32]
         L.moe_grouped_gemm_dgrad_workspace_bytes.restype = ctypes.c_size_t
         L.moe_grouped_gemm_dgrad.restype = ctypes.c_int32
-        L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P]
+        L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        L.moe_grouped_gemm_wgrad_workspace_bytes.argtypes = [S]
+        L.moe_grouped_gemm_wgrad_workspace_bytes.restype = ctypes.c_size_t
         L.moe_grouped_gemm_wgrad.restype = ctypes.c_int32
         L.moe_router_bwd.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
         L.moe_router_bwd_workspace_bytes.argtypes = [S]
@@ -416,10 +420,18 @@ def moe_grouped_gemm_dgrad(shape, op, dC, B0, B1, block_meta, num_blocks, max_bl
         max_blocks, _p(dA), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
-def moe_grouped_gemm_wgrad(shape, op, A, dC, counts, padded_offsets, dB0, dB1, stream=None):
+def moe_grouped_gemm_wgrad_workspace_bytes(shape: moe_shape) -> int:
+    return lib().moe_grouped_gemm_wgrad_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_grouped_gemm_wgrad(shape, op, A, dC, counts, padded_offsets, dB0, dB1, ws=None,
+                           stream=None):
+    """ws: None (static order) or a uint8 device tensor of at least
+    moe_grouped_gemm_wgrad_workspace_bytes(shape) bytes (work queue, largest expert
+    first)."""
     _check("moe_grouped_gemm_wgrad", lib().moe_grouped_gemm_wgrad(
         ctypes.byref(shape), op, _p(A), _p(dC), _p(counts), _p(padded_offsets), _p(dB0),
-        _p(dB1), _stream(stream)))
+        _p(dB1), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def moe_router_bwd_workspace_bytes(shape: moe_shape) -> int:

@@ -152,6 +152,7 @@ static void bwd_layout_of(const moe_shape& s, moe_bwd_ws_layout& L) {
   L.shared_dx = take(cur, ds ? T * d * 2 : 0);
   L.router_dx = take(cur, T * d * 2);
   L.router_scratch = take(cur, router_bwd_scratch_bytes(s));
+  L.wgrad_sched = take(cur, wgrad_sched_bytes(s.E));
   // the expert weights transposed for the data gradients, when the forward kernels run
   // them (transposed_dgrad)
   const bool tw = transposed_dgrad(s);
@@ -771,9 +772,14 @@ moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC
                       routed_rows_bound(*s, max_blocks), dense ? s->T : 0, hs);
 }
 
+size_t moe_grouped_gemm_wgrad_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return align_up(wgrad_sched_bytes(s->E), 256);
+}
+
 moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A, const void* dC,
                                   const int32_t* counts, const int32_t* padded_offsets, float* dB0,
-                                  float* dB1, void* stream) {
+                                  float* dB1, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if ((st = check_bwd(*s)) != MOE_OK) return st;
@@ -785,10 +791,11 @@ moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A,
   if ((counts == nullptr) != (padded_offsets == nullptr)) return MOE_EINVAL;
   if (counts && (!aligned4(counts) || !aligned4(padded_offsets))) return MOE_EINVAL;
   const bool dense = counts == nullptr;
+  if (ws && (!aligned16(ws) || ws_bytes < wgrad_sched_bytes(s->E))) return MOE_EWORKSPACE;
   const int Km = gu ? s->d : s->d_e, Nn = gu ? 2 * s->d_e : s->d;
   // T == 0 still writes the (zero) gradients: the counts are not read then
   return launch_gg_wgrad(A, dC, dB0, dB1, gu ? s->d_e : Nn, Km, Nn, s->T > 0 ? counts : nullptr,
-                         padded_offsets, dense ? 1 : s->E, dense ? s->T : 0,
+                         padded_offsets, dense ? 1 : s->E, dense ? s->T : 0, dense ? nullptr : ws,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -878,12 +885,13 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
   const int de = s->d_e, des = s->d_e_shared, d = s->d;
   if (s->T == 0) {
     // no rows: every weight gradient is zero
-    st = launch_gg_wgrad(x, x, dw1, dw3, de, d, 2 * de, nullptr, nullptr, s->E, 0, hs);
-    if (st == MOE_OK) st = launch_gg_wgrad(x, x, dw2, nullptr, d, de, d, nullptr, nullptr, s->E, 0, hs);
+    st = launch_gg_wgrad(x, x, dw1, dw3, de, d, 2 * de, nullptr, nullptr, s->E, 0, nullptr, hs);
+    if (st == MOE_OK)
+      st = launch_gg_wgrad(x, x, dw2, nullptr, d, de, d, nullptr, nullptr, s->E, 0, nullptr, hs);
     if (st == MOE_OK && shared)
-      st = launch_gg_wgrad(x, x, dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1, 0, hs);
+      st = launch_gg_wgrad(x, x, dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1, 0, nullptr, hs);
     if (st == MOE_OK && shared)
-      st = launch_gg_wgrad(x, x, dws2, nullptr, d, des, d, nullptr, nullptr, 1, 0, hs);
+      st = launch_gg_wgrad(x, x, dws2, nullptr, d, des, d, nullptr, nullptr, 1, 0, nullptr, hs);
     if (st == MOE_OK && (dw_gate || dbias))
       st = launch_router_bwd(*s, x, w_gate, nullptr, nullptr, nullptr, nullptr, dw_gate, dbias,
                              nullptr, dx, nullptr, hs);
@@ -918,7 +926,8 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
                       s->block_m, max_rows_of(*s), 0, hs);
   }
   if (st != MOE_OK) return st;
-  st = launch_gg_wgrad(fat(F.act), at(L.dy), dw2, nullptr, d, de, d, counts, padded, s->E, 0, hs);
+  st = launch_gg_wgrad(fat(F.act), at(L.dy), dw2, nullptr, d, de, d, counts, padded, s->E, 0,
+                       at(L.wgrad_sched), hs);
   if (st != MOE_OK) return st;
   if (shared) {
     if (!tw) {
@@ -927,7 +936,7 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
       if (st != MOE_OK) return st;
     }
     st = launch_gg_wgrad(fat(F.shared_act), dout, dws2, nullptr, d, des, d, nullptr, nullptr, 1,
-                         s->T, hs);
+                         s->T, nullptr, hs);
     if (st != MOE_OK) return st;
   }
   // the weight gradients of gate/up reduce over x_perm's rows
@@ -951,7 +960,8 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
                       s->block_m, max_rows_of(*s), 0, hs);
   }
   if (st != MOE_OK) return st;
-  st = launch_gg_wgrad(at(L.x_perm), at(L.dgu), dw1, dw3, de, d, 2 * de, counts, padded, s->E, 0, hs);
+  st = launch_gg_wgrad(at(L.x_perm), at(L.dgu), dw1, dw3, de, d, 2 * de, counts, padded, s->E, 0,
+                       at(L.wgrad_sched), hs);
   if (st != MOE_OK) return st;
   if (shared) {
     if (!tw) {
@@ -960,7 +970,7 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate, 
       if (st != MOE_OK) return st;
     }
     st = launch_gg_wgrad(x, at(L.shared_dgu), dws1, dws3, des, d, 2 * des, nullptr, nullptr, 1,
-                         s->T, hs);
+                         s->T, nullptr, hs);
     if (st != MOE_OK) return st;
   }
   // router: dlogits, dW_g, dbias, and its dx term on top of the shared expert's

@@ -404,19 +404,56 @@ struct WgOperands {
   int nsplit;
 };
 
+// Largest expert first: order[r] is the expert of rank r by row count (ties: lower id),
+// and the work queue counter starts at zero.  One block; counts staged in LDS.
+__global__ void __launch_bounds__(256)
+k_wgrad_order(const int32_t* __restrict__ counts, int E, int32_t* __restrict__ order,
+              int32_t* __restrict__ queue) {
+  __shared__ int32_t s_cnt[1024];
+  for (int e = threadIdx.x; e < E; e += 256) s_cnt[e] = counts[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const int c = s_cnt[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) rank += (s_cnt[f] > c) || (s_cnt[f] == c && f < e);
+    order[rank] = e;
+  }
+  if (threadIdx.x == 0) *queue = 0;
+}
+
+// Items (expert, m tile, n tile).  Without a queue, work group b takes items b, b + grid,
+// ...  in expert order.  With one, items are numbered largest expert first (order[]) and
+// each work group takes the next number from the queue counter when it starts an item:
+// the longest items go first and the short ones fill in behind them, so experts of
+// unequal size do not leave work groups idle at the end.  Which work group computes an
+// item does not change its result.
 __global__ void __launch_bounds__(kBThreads, 1)
 k_gg_wgrad(WgOperands ops, int Km, int Nn, const int32_t* __restrict__ counts,
-           const int32_t* __restrict__ row_off, int E, int dense_rows, int m_tiles, int n_tiles) {
+           const int32_t* __restrict__ row_off, int E, int dense_rows, int m_tiles, int n_tiles,
+           int32_t* __restrict__ queue, const int32_t* __restrict__ order) {
   __shared__ __align__(1024) unsigned char lds[kBStages * kWgStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, gi = lane & 15, tr_r = gi >> 2, tr_c4 = gi & 3;
   const int total = E * m_tiles * n_tiles;
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+  // the next item number, handed to every wave through the (idle) first LDS word
+  auto take_next = [&](int v) {
+    __syncthreads();
+    if (tid == 0) *reinterpret_cast<int*>(lds) = v;
+    __syncthreads();
+    const int r = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(lds));
+    __syncthreads();   // read by all before the next item's copies land there
+    return r;
+  };
+  int w = blockIdx.x;
+  if (queue) w = take_next(tid == 0 ? atomicAdd(queue, 1) : 0);
+  while (w < total) {
+    int nxt = 0;
+    if (queue && tid == 0) nxt = atomicAdd(queue, 1);   // fetched while this item runs
     const int nt = w % n_tiles;
     const int mt = (w / n_tiles) % m_tiles;
-    const int e = w / (n_tiles * m_tiles);
+    const int e = queue ? order[w / (n_tiles * m_tiles)] : w / (n_tiles * m_tiles);
     const int cnt = __builtin_amdgcn_readfirstlane(dense_rows > 0 ? dense_rows : (counts ? counts[e] : 0));
     const int r0e = __builtin_amdgcn_readfirstlane(dense_rows > 0 || !counts ? 0 : row_off[e]);
     const int m0 = mt * 128, n0 = nt * 512;
@@ -553,12 +590,15 @@ k_gg_wgrad(WgOperands ops, int Km, int Nn, const int32_t* __restrict__ counts,
           else
             ops.C1[((size_t)e * Km + m) * (Nn - ops.nsplit) + (n - ops.nsplit)] = acc[i][j][q];
         }
+    w = queue ? take_next(nxt) : w + (int)gridDim.x;
   }
 }
 
+size_t wgrad_sched_bytes(int E) { return (size_t)(E + 64) * 4; }
+
 moe_status launch_gg_wgrad(const void* X, const void* D, float* C0, float* C1, int nsplit, int Km,
                            int Nn, const int32_t* counts, const int32_t* row_off, int E,
-                           int32_t dense_rows, hipStream_t st) {
+                           int32_t dense_rows, void* sched, hipStream_t st) {
   const int m_tiles = (int)ceil_div(Km, 128), n_tiles = (int)ceil_div(Nn, 512);
   const int64_t items = (int64_t)E * m_tiles * n_tiles;
   const int cus = device_cu_count();
@@ -566,8 +606,18 @@ moe_status launch_gg_wgrad(const void* X, const void* D, float* C0, float* C1, i
   if (grid < 1) grid = 1;
   const WgOperands ops{static_cast<const bf16_t*>(X), static_cast<const bf16_t*>(D), C0, C1,
                        C1 ? nsplit : Nn};
+  // the work queue applies to the routed experts (counts given) when scratch is given:
+  // [0, 64) the counter (its own 256-byte line), then order[E]
+  int32_t* queue = nullptr;
+  int32_t* order = nullptr;
+  if (sched && counts && dense_rows == 0 && E > 1 && E <= 1024) {
+    queue = static_cast<int32_t*>(sched);
+    order = queue + 64;
+    hipLaunchKernelGGL(k_wgrad_order, dim3(1), dim3(256), 0, st, counts, E, order, queue);
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+  }
   hipLaunchKernelGGL(k_gg_wgrad, dim3((unsigned)grid), dim3(kBThreads), 0, st, ops, Km, Nn,
-                     counts, row_off, E, dense_rows, m_tiles, n_tiles);
+                     counts, row_off, E, dense_rows, m_tiles, n_tiles, queue, order);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

@@ -169,9 +169,12 @@ moe_status launch_transpose_bf16(int E, int R, int C, const void* w, void* wt, i
 // columns n < nsplit into C0 [E][Km][nsplit], the rest into C1 (C1 NULL: nsplit = Nn);
 // dense_rows > 0: one expert over rows [0, dense_rows); counts NULL and dense_rows 0:
 // zeros.  Km % 8 == 0, Nn % 8 == 0.
+// sched: NULL, or wgrad_sched_bytes(E) bytes of device scratch: the routed experts' items
+// then go through a work queue, largest expert first.
 moe_status launch_gg_wgrad(const void* X, const void* D, float* C0, float* C1, int nsplit, int Km,
                            int Nn, const int32_t* counts, const int32_t* row_off, int E,
-                           int32_t dense_rows, hipStream_t st);
+                           int32_t dense_rows, void* sched, hipStream_t st);
+size_t wgrad_sched_bytes(int E);
 // dlogits from dw through the softmax (and renormalisation), selection fixed; then
 // dw_gate = x^T dlogits, dbias = column sums (either NULL: skipped), and
 // dx_out = dx_base (NULL: 0) + dlogits w_gate^T in bf16.  scratch: router_bwd_scratch_bytes

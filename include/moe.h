@@ -424,11 +424,18 @@ moe_status moe_grouped_gemm_dgrad(const moe_shape* s, int32_t op, const void* dC
  *                              A = x_perm [rows, d], dC = dgu [rows, 2 d_e].
  * counts = padded_offsets = NULL: dense mode over all T rows (E = 1, d_e as in s).
  * fp32 outputs; experts without rows get zeros.
+ * ws: NULL - work group b computes output tiles b, b + grid, ... in expert order; or
+ * device scratch of ws_bytes >= moe_grouped_gemm_wgrad_workspace_bytes(s), 16-byte
+ * aligned - the routed experts' tiles are handed out through a work queue, largest
+ * expert first (a one-block kernel ranks the experts by count and clears the queue
+ * first), so experts of unequal size do not leave work groups idle at the end.  The
+ * results are bitwise the same either way.  Errors: MOE_EWORKSPACE for a short ws.
  */
+size_t moe_grouped_gemm_wgrad_workspace_bytes(const moe_shape* s);
 moe_status moe_grouped_gemm_wgrad(const moe_shape* s, int32_t op, const void* A,
                                   const void* dC, const int32_t* counts,
                                   const int32_t* padded_offsets, float* dB0, float* dB1,
-                                  void* stream);
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Router backward (TileLang chapter section 2.2's weights w = softmax(logits)[idx],
@@ -456,7 +463,7 @@ moe_status moe_router_bwd(const moe_shape* s, const void* x, const void* w_gate,
  */
 typedef struct moe_bwd_ws_layout {
   size_t dy, dact, dgu, x_perm, dx_perm, dtopk_w, dlogits, shared_dact, shared_dgu,
-         shared_dx, router_dx, router_scratch, w2_t, w13_t, ws2_t, ws13_t, total;
+         shared_dx, router_dx, router_scratch, wgrad_sched, w2_t, w13_t, ws2_t, ws13_t, total;
 } moe_bwd_ws_layout;
 size_t moe_bwd_workspace_bytes(const moe_shape* s);
 moe_status moe_bwd_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout);

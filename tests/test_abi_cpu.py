@@ -357,7 +357,7 @@ def test_backward_entry_point_argument_rules():
         assert L.moe_grouped_gemm_dgrad(pb, 1, FAKE, FAKE, None, FAKE, FAKE, 1, FAKE,
                                         None, 0, None) == B.MOE_ENOTSUP
         assert L.moe_grouped_gemm_wgrad(pb, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                                        None) == B.MOE_ENOTSUP
+                                        None, 0, None) == B.MOE_ENOTSUP
         assert L.moe_router_bwd(pb, *([FAKE] * 10), FAKE, 1 << 40, None) == B.MOE_ENOTSUP
     assert L.moe_combine_bwd(ctypes.byref(good_shape(d=8224)), *([FAKE] * 6), None) == B.MOE_ENOTSUP
     # combine backward: every pointer required
@@ -390,10 +390,16 @@ def test_backward_entry_point_argument_rules():
               1 << 40, None) == B.MOE_EWORKSPACE
     # wgrad: dB1 exactly for gate/up; counts and offsets together
     wg = L.moe_grouped_gemm_wgrad
-    assert wg(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
-    assert wg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_EINVAL
-    assert wg(ps, 1, FAKE, FAKE, FAKE, None, FAKE, None, None) == B.MOE_EINVAL
-    assert wg(ps, 1, odd, FAKE, FAKE, FAKE, FAKE, None, None) == B.MOE_EINVAL
+    assert wg(ps, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_EINVAL
+    assert wg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.MOE_EINVAL
+    assert wg(ps, 1, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == B.MOE_EINVAL
+    assert wg(ps, 1, odd, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.MOE_EINVAL
+    # the work-queue scratch: (E + 64) int32, 16-byte aligned, or NULL
+    wneed = L.moe_grouped_gemm_wgrad_workspace_bytes(ps)
+    assert wneed == -(-(s.E + 64) * 4 // 256) * 256
+    assert wg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, (s.E + 64) * 4 - 1,
+              None) == B.MOE_EWORKSPACE
+    assert wg(ps, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None, odd, wneed, None) == B.MOE_EWORKSPACE
     # router backward: dbias and dx_in optional, the rest required
     rb = L.moe_router_bwd
     big = 1 << 40
@@ -438,7 +444,8 @@ def test_backward_workspace_layout_is_disjoint_and_aligned():
                      dx_perm=rows * d * 2, dtopk_w=T * s.k * 4, dlogits=T * s.E * 4,
                      shared_dact=T * ds * 2, shared_dgu=T * 2 * ds * 2,
                      shared_dx=T * d * 2 if ds else 0, router_dx=T * d * 2,
-                     router_scratch=B.moe_router_bwd_workspace_bytes(s))
+                     router_scratch=B.moe_router_bwd_workspace_bytes(s),
+                     wgrad_sched=(s.E + 64) * 4)
         tw = T * s.k >= 256 * min(s.E, T * s.k)           # data gradients on transposed weights
         sizes.update(w2_t=s.E * d * de * 2 if tw else 0, w13_t=2 * s.E * de * d * 2 if tw else 0,
                      ws2_t=d * ds * 2 if tw else 0, ws13_t=2 * ds * d * 2 if tw else 0)

@@ -108,6 +108,12 @@ def test_backward_stages_against_oracle(name, scale):
         dw2_ref[ex] = act_h[r].T @ dy_h[r]
     assert_close(f64(dact)[valid], dact_ref[valid], TOL_STAGE["bf16"], "dact")
     assert_close(f64(dw2), dw2_ref, TOL_WGRAD, "dW2")
+    # the same weight gradient through the work queue (largest expert first): bitwise
+    sched = torch.empty(B.moe_grouped_gemm_wgrad_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    dw2_q = torch.full_like(dw2, float("nan"))
+    B.moe_grouped_gemm_wgrad(s, B.MOE_OP_DOWN, run.act(), dy, dcounts, dpad, dw2_q, None, sched)
+    torch.cuda.synchronize()
+    assert torch.equal(dw2.view(torch.int32), dw2_q.view(torch.int32))
     # the same data gradient on the forward kernels against weights transposed into a
     # workspace
     dact_t = e(rows, de)
@@ -140,7 +146,11 @@ def test_backward_stages_against_oracle(name, scale):
     dxp, dw1, dw3 = e(rows, d), f(E, d, de), f(E, d, de)
     B.moe_grouped_gemm_dgrad(s, B.MOE_OP_GATEUP_SWIGLU, dgu, inp.w1, inp.w3, meta, nblk, mb, dxp)
     B.moe_grouped_gemm_wgrad(s, B.MOE_OP_GATEUP_SWIGLU, xp, dgu, dcounts, dpad, dw1, dw3)
+    dw1_q, dw3_q = torch.full_like(dw1, float("nan")), torch.full_like(dw3, float("nan"))
+    B.moe_grouped_gemm_wgrad(s, B.MOE_OP_GATEUP_SWIGLU, xp, dgu, dcounts, dpad, dw1_q, dw3_q, sched)
     torch.cuda.synchronize()
+    assert torch.equal(dw1.view(torch.int32), dw1_q.view(torch.int32))
+    assert torch.equal(dw3.view(torch.int32), dw3_q.view(torch.int32))
     dgu_h = f64(dgu)
     dxp_ref = np.zeros((rows, d))
     dw1_ref, dw3_ref = np.zeros((E, d, de)), np.zeros((E, d, de))
