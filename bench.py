@@ -301,6 +301,29 @@ def main():
         a1.record()
     torch.cuda.synchronize()
     layer_fwd_ms = sum(a0.elapsed_time(a1) for a0, a1 in lev) / nrep
+    # the same call captured once in a HIP graph and replayed (the library only enqueues
+    # kernels: no allocation, memset or host synchronisation), which removes the
+    # per-launch host overhead
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer_call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        layer_call()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nrep)]
+    for a0, a1 in gev:
+        if flush is not None:
+            flush.fill_(0x3C)
+        a0.record()
+        graph.replay()
+        a1.record()
+    torch.cuda.synchronize()
+    layer_graph_ms = sum(a0.elapsed_time(a1) for a0, a1 in gev) / nrep
+    del graph
     same = bool(torch.equal(out.view(torch.int16) if eb == 2 else out.view(torch.int32),
                             out2.view(torch.int16) if eb == 2 else out2.view(torch.int32)))
     del ws2, out2
@@ -422,6 +445,7 @@ def main():
         "gemm": gemm,
         "moves": moves,
         "layer_fwd_ms_per_call": layer_fwd_ms,
+        "layer_fwd_graph_ms_per_call": layer_graph_ms,
         "layer_fwd_matches_staged": same,
         "active_experts": active,
         "blocks": int(nblk.item()),
