@@ -190,6 +190,9 @@ def test_layer_fwd_fp8(name, scale):
     ("ep-share-4x2048", dict(name="ep-fp8-wide", T=512, d=512, d_e=256,
                              fixed_counts=(1357, 938, 1124, 677)), True),
     ("fusedmoe-8x2048", dict(name="fm-fp8-wide", T=600, d=512, d_e=256, d_e_shared=256), True),
+    # a shared expert of another width: its own launches on both paths
+    ("fusedmoe-8x2048", dict(name="fm-fp8-wide-s", T=600, d=512, d_e=256, d_e_shared=96), True),
+    ("fusedmoe-8x2048", dict(name="fm-fp8-narrow-s", T=300, d=512, d_e=256, d_e_shared=96), False),
     ("fusedmoe-8x2048", dict(name="fm-fp8-narrow", T=400, d=512, d_e=256, d_e_shared=256), False),
     ("decode-256x2048", dict(name="decode-fp8-dq", d=512, d_e=256, d_e_shared=256), False),
 ])
