@@ -11,7 +11,7 @@
 //   permute   dx[t] = sum_j dx_perm[pos[t,j]]        (the combine kernel, unit weights)
 //   router    dlogits through the softmax (and renormalisation), selection fixed
 //             (k_router_bwd); dW_g = x^T dlogits, dbias = sum_t dlogits
-//             (k_router_wgrad); dx += dlogits W_g^T (k_router_dx)
+//             (k_router_wgrad); dx += dlogits W_g^T (k_router_dx_v8, k_router_dx)
 //
 // The GEMM kernels keep the 128-row kernel's structure (8 waves, 128 x 512 tiles,
 // four 40 KB ring slots of 32-deep slices filled by 16-byte global->LDS copies, fp32
@@ -711,64 +711,6 @@ k_router_bwd(const float* __restrict__ logits, const int32_t* __restrict__ idx,
   }
 }
 
-// dW_g[c, e] = sum_t x[t, c] dlogits[t, e]; dbias[e] = sum_t dlogits[t, e].  The tokens
-// are cut into contiguous chunks of tchunk (blockIdx.z); a block owns 32 columns c and 16
-// experts of one chunk, its 256 threads being 32 columns x 8 token phases: a thread sums
-// tokens t = begin + phase, + 8, ... in ascending order, and the 8 phase sums are added in
-// phase order through LDS.  Chunk z's sums go to ow + z * ow_stride ([d][E]) and
-// ob + z * ob_stride ([E]; ob NULL: not written); k_router_wgrad_reduce adds the chunks
-// in order when there are several.  The 32 lanes of a phase read one dlogits row (a
-// broadcast) and 64 contiguous bytes of x.
-static constexpr int kRwCols = 32, kRwExp = 16, kRwPhases = 8;
-
-__global__ void __launch_bounds__(kRwCols * kRwPhases)
-k_router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dl, int T, int d, int E,
-               int tchunk, float* __restrict__ ow, size_t ow_stride, float* __restrict__ ob,
-               size_t ob_stride) {
-  __shared__ float part[kRwPhases][kRwExp][kRwCols + 1];
-  __shared__ float bpart[kRwPhases][kRwExp];
-  const int cl = threadIdx.x % kRwCols, ph = threadIdx.x / kRwCols;
-  const int c = blockIdx.x * kRwCols + cl, e0 = blockIdx.y * kRwExp;
-  const int ne = min(kRwExp, E - e0);
-  const int tb = blockIdx.z * tchunk, te = min(T, tb + tchunk);
-  float acc[kRwExp], bacc[kRwExp];
-#pragma unroll
-  for (int i = 0; i < kRwExp; ++i) acc[i] = bacc[i] = 0.f;
-#pragma unroll 4
-  for (int t = tb + ph; t < te; t += kRwPhases) {
-    const float xv = c < d ? bf16_to_f32(x[(size_t)t * d + c]) : 0.f;
-    const float* dr = dl + (size_t)t * E + e0;
-#pragma unroll
-    for (int i = 0; i < kRwExp; ++i) {
-      const float gv = i < ne ? dr[i] : 0.f;
-      acc[i] = fmaf(xv, gv, acc[i]);
-      bacc[i] += gv;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kRwExp; ++i) part[ph][i][cl] = acc[i];
-  if (cl == 0) {
-#pragma unroll
-    for (int i = 0; i < kRwExp; ++i) bpart[ph][i] = bacc[i];
-  }
-  __syncthreads();
-  float* const w = ow + blockIdx.z * ow_stride;
-  for (int o = threadIdx.x; o < kRwCols * kRwExp; o += kRwCols * kRwPhases) {
-    const int oc = o % kRwCols, oi = o / kRwCols;
-    float v = 0.f;
-#pragma unroll
-    for (int p = 0; p < kRwPhases; ++p) v += part[p][oi][oc];
-    const int cc = blockIdx.x * kRwCols + oc;
-    if (ow && cc < d && oi < ne) w[(size_t)cc * E + e0 + oi] = v;
-  }
-  if (ob && blockIdx.x == 0 && threadIdx.x < ne) {
-    float v = 0.f;
-#pragma unroll
-    for (int p = 0; p < kRwPhases; ++p) v += bpart[p][threadIdx.x];
-    ob[blockIdx.z * ob_stride + e0 + threadIdx.x] = v;
-  }
-}
-
 // dW_g = sum over the chunks in order (and dbias likewise; either output may be NULL).
 __global__ void __launch_bounds__(256)
 k_router_wgrad_reduce(const float* __restrict__ pw, const float* __restrict__ pb, int nchunks,
@@ -776,6 +718,7 @@ k_router_wgrad_reduce(const float* __restrict__ pw, const float* __restrict__ pb
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (dwg && i < n) {
     float v = 0.f;
+#pragma unroll 8
     for (int z = 0; z < nchunks; ++z) v += pw[(size_t)z * n + i];
     dwg[i] = v;
   }
@@ -786,11 +729,95 @@ k_router_wgrad_reduce(const float* __restrict__ pw, const float* __restrict__ pb
   }
 }
 
-// Token chunks of the router's weight gradient: enough blocks to fill the chip (about
-// 2048), chunks of at least 256 tokens.
+// dW_g[c, e] = sum_t x[t, c] dlogits[t, e]; dbias[e] = sum_t dlogits[t, e], for rows whose
+// width is a multiple of 8 (16-byte aligned).  The tokens are cut into contiguous chunks of
+// tchunk (blockIdx.z); a block owns 256 columns and 8 experts of one chunk, its 256 threads
+// being 32 groups of 8 adjacent columns (one 16-byte load of x per token) x 8 token phases.
+// A thread sums tokens t = begin + phase, + 8, ... in ascending order and the 8 phase sums
+// are added in phase order through LDS.  Chunk z's sums go to ow + z * ow_stride ([d][E])
+// and ob + z * ob_stride ([E]; ob NULL: not written); k_router_wgrad_reduce adds the chunks
+// in order when there are several.  dl_vec: the dlogits rows are 16-byte aligned and E a
+// multiple of 4, so a full group of 8 experts is read as two float4 (same values otherwise).
+static constexpr int kRvExp = 8, kRvCols = 256;
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4_t v, float* f) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    f[2 * h] = __uint_as_float(v[h] << 16);
+    f[2 * h + 1] = __uint_as_float(v[h] & 0xffff0000u);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+k_router_wgrad(const bf16_t* __restrict__ x, const float* __restrict__ dl, int T, int d,
+                  int E, int tchunk, float* __restrict__ ow, size_t ow_stride,
+                  float* __restrict__ ob, size_t ob_stride, int dl_vec) {
+  __shared__ float s_w[kRvExp][kRvCols + 4];
+  __shared__ float s_b[kRvExp];
+  const int cg = threadIdx.x % 32, ph = threadIdx.x / 32;
+  const int c = blockIdx.x * kRvCols + cg * 8, e0 = blockIdx.y * kRvExp;
+  const int ne = min(kRvExp, E - e0);
+  const bool full4 = ne == kRvExp && dl_vec;
+  const bool cok = c < d;
+  const int tb = blockIdx.z * tchunk, te = min(T, tb + tchunk);
+  float acc[kRvExp][8], bacc[kRvExp];
+#pragma unroll
+  for (int i = 0; i < kRvExp; ++i) {
+    bacc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  }
+#pragma unroll 4
+  for (int t = tb + ph; t < te; t += 8) {
+    u32x4_t xv = {0u, 0u, 0u, 0u};
+    if (cok) xv = *reinterpret_cast<const u32x4_t*>(x + (size_t)t * d + c);
+    const float* dr = dl + (size_t)t * E + e0;
+    float g[kRvExp];
+    if (full4) {
+      const float4 g0 = reinterpret_cast<const float4*>(dr)[0];
+      const float4 g1 = reinterpret_cast<const float4*>(dr)[1];
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+      g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRvExp; ++i) g[i] = i < ne ? dr[i] : 0.f;
+    }
+    float xf[8];
+    unpack_bf16x8(xv, xf);
+#pragma unroll
+    for (int i = 0; i < kRvExp; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xf[j], g[i], acc[i][j]);
+      bacc[i] += g[i];
+    }
+  }
+  for (int p = 0; p < 8; ++p) {
+    if (ph == p) {
+#pragma unroll
+      for (int i = 0; i < kRvExp; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          s_w[i][cg * 8 + j] = p == 0 ? acc[i][j] : s_w[i][cg * 8 + j] + acc[i][j];
+        if (cg == 0) s_b[i] = p == 0 ? bacc[i] : s_b[i] + bacc[i];
+      }
+    }
+    __syncthreads();
+  }
+  float* const w = ow + blockIdx.z * ow_stride;
+  for (int o = threadIdx.x; o < kRvCols * kRvExp; o += 256) {
+    const int oc = o / kRvExp, oi = o % kRvExp;
+    const int cc = blockIdx.x * kRvCols + oc;
+    if (ow && cc < d && oi < ne) w[(size_t)cc * E + e0 + oi] = s_w[oi][oc];
+  }
+  if (ob && blockIdx.x == 0 && threadIdx.x < ne)
+    ob[blockIdx.z * ob_stride + e0 + threadIdx.x] = s_b[threadIdx.x];
+}
+
+// Token chunks of the router's weight gradient: blocks that all fit on the chip at once
+// (about 768: 3 per compute unit at the kernel's register use), chunks of at least 256 tokens.
 static int router_wgrad_chunks(const moe_shape& s) {
-  const int64_t blocks2d = ceil_div(s.d, kRwCols) * ceil_div(s.E, kRwExp);
-  const int64_t want = ceil_div(2048, blocks2d);
+  const int64_t blocks2d = ceil_div(s.d, kRvCols) * ceil_div(s.E, kRvExp);
+  const int64_t want = 768 / blocks2d;
   const int64_t most = ceil_div(s.T, 256);
   int64_t n = want < most ? want : most;
   return (int)(n < 1 ? 1 : n);
@@ -836,6 +863,79 @@ k_router_dx(const float* __restrict__ dl, const bf16_t* __restrict__ wg, const b
   }
 }
 
+// The same for rows whose width and E are multiples of 8 (16-byte aligned operands): a
+// thread owns 8 adjacent columns and 8 of the block's 16 tokens (one 16-byte store per
+// token), the block being 128 column groups (1024 columns) x 2 token groups.  W_g is read
+// 8 columns x 8 experts at a time (eight 16-byte loads) and every output sums e in
+// ascending order, so the result equals k_router_dx's bit for bit.
+static constexpr int kRdvCols = 1024;
+
+__global__ void __launch_bounds__(256)
+k_router_dx_v8(const float* __restrict__ dl, const bf16_t* __restrict__ wg,
+               const bf16_t* __restrict__ base, int T, int d, int E, bf16_t* __restrict__ out) {
+  extern __shared__ float s_dl[];   // [kRdTok][E]
+  const int t0 = blockIdx.x * kRdTok;
+  const int nt = min(kRdTok, T - t0);
+  const int cg = threadIdx.x % (kRdvCols / 8), tg = threadIdx.x / (kRdvCols / 8);
+  const int c = blockIdx.y * kRdvCols + cg * 8;
+  // the base rows are loaded first, to be in flight during the sums
+  u32x4_t bv[8];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    bv[tt] = u32x4_t{0u, 0u, 0u, 0u};
+    if (base && c < d && tg * 8 + tt < nt)
+      bv[tt] = *reinterpret_cast<const u32x4_t*>(base + (size_t)(t0 + tg * 8 + tt) * d + c);
+  }
+  for (int i = threadIdx.x; i < kRdTok * E; i += 256) {
+    const int tt = i / E;
+    s_dl[i] = tt < nt ? dl[(size_t)(t0 + tt) * E + i % E] : 0.f;
+  }
+  __syncthreads();
+  if (c >= d) return;
+  const float* sd = s_dl + tg * 8 * E;
+  float v[8][8];
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[tt][j] = 0.f;
+  for (int e = 0; e < E; e += 8) {
+    float w[8][8];   // [column][expert e + i]
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      unpack_bf16x8(*reinterpret_cast<const u32x4_t*>(wg + (size_t)(c + j) * E + e), w[j]);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const float4 g0 = *reinterpret_cast<const float4*>(sd + tt * E + e);
+      const float4 g1 = *reinterpret_cast<const float4*>(sd + tt * E + e + 4);
+      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[tt][j] = fmaf(g[i], w[j][i], v[tt][j]);
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    if (tg * 8 + tt >= nt) break;
+    const size_t o = (size_t)(t0 + tg * 8 + tt) * d + c;
+    float b[8];
+    if (base) {
+      unpack_bf16x8(bv[tt], b);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] += v[tt][j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = v[tt][j];
+    }
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) r[h] = pack_bf16x2(b[2 * h], b[2 * h + 1]);
+    *reinterpret_cast<u32x4_t*>(out + o) = r;
+  }
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_gate,
                              const float* logits, const int32_t* idx, const float* dw,
                              float* dlogits, float* dw_gate, float* dbias, const void* dx_base,
@@ -849,22 +949,25 @@ moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_ga
   // with T == 0 the weight gradients are zeros (the kernel reads no rows)
   if (dw_gate || dbias) {
     const int nch = router_wgrad_chunks(s);
-    const int tchunk = (int)(ceil_div(ceil_div(s.T, nch), kRwPhases) * kRwPhases);
-    const dim3 grid((unsigned)ceil_div(s.d, kRwCols), (unsigned)ceil_div(s.E, kRwExp),
-                    (unsigned)nch);
+    const int tchunk = (int)(ceil_div(ceil_div(s.T, nch), 8) * 8);
     const int64_t n = (int64_t)s.d * s.E;
+    if (s.d % 8 || !aligned16(x)) return MOE_EINVAL;
+    const int dl_vec = s.E % 4 == 0 && aligned16(dlogits);
+    const dim3 grid((unsigned)ceil_div(s.d, kRvCols), (unsigned)ceil_div(s.E, kRvExp),
+                    (unsigned)nch);
+    auto sums = [&](float* ow, size_t ows, float* ob, size_t obs) {
+      hipLaunchKernelGGL(k_router_wgrad, grid, dim3(256), 0, st,
+                         static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E, tchunk, ow, ows,
+                         ob, obs, dl_vec);
+    };
     if (nch == 1) {
       // one chunk: the sums go straight to the outputs (either may be NULL)
-      hipLaunchKernelGGL(k_router_wgrad, grid, dim3(kRwCols * kRwPhases), 0, st,
-                         static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E, tchunk,
-                         dw_gate, (size_t)0, dbias, (size_t)0);
+      sums(dw_gate, 0, dbias, 0);
     } else {
       if (!scratch) return MOE_EWORKSPACE;
       float* pw = static_cast<float*>(scratch);
       float* pb = pw + (size_t)nch * n;
-      hipLaunchKernelGGL(k_router_wgrad, grid, dim3(kRwCols * kRwPhases), 0, st,
-                         static_cast<const bf16_t*>(x), dlogits, s.T, s.d, s.E, tchunk, pw,
-                         (size_t)n, pb, (size_t)s.E);
+      sums(pw, (size_t)n, pb, (size_t)s.E);
       if (hipGetLastError() != hipSuccess) return MOE_EHIP;
       hipLaunchKernelGGL(k_router_wgrad_reduce, dim3((unsigned)ceil_div(n > s.E ? n : s.E, 256)),
                          dim3(256), 0, st, pw, pb, nch, n, s.E, dw_gate, dbias);
@@ -872,11 +975,19 @@ moe_status launch_router_bwd(const moe_shape& s, const void* x, const void* w_ga
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   }
   if (s.T > 0) {
-    hipLaunchKernelGGL(k_router_dx, dim3((unsigned)ceil_div(s.T, kRdTok), (unsigned)ceil_div(s.d, 256)),
-                       dim3(256), (size_t)kRdTok * s.E * sizeof(float), st,
-                       dlogits, static_cast<const bf16_t*>(w_gate),
-                       static_cast<const bf16_t*>(dx_base), s.T, s.d, s.E,
-                       static_cast<bf16_t*>(dx_out));
+    const bool vec = s.d % 8 == 0 && s.E % 8 == 0 && aligned16(w_gate) && aligned16(dx_out) &&
+                     (!dx_base || aligned16(dx_base));
+    const dim3 grid((unsigned)ceil_div(s.T, kRdTok),
+                    (unsigned)ceil_div(s.d, vec ? kRdvCols : 256));
+    const size_t lds = (size_t)kRdTok * s.E * sizeof(float);
+    if (vec)
+      hipLaunchKernelGGL(k_router_dx_v8, grid, dim3(256), lds, st, dlogits,
+                         static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(dx_base),
+                         s.T, s.d, s.E, static_cast<bf16_t*>(dx_out));
+    else
+      hipLaunchKernelGGL(k_router_dx, grid, dim3(256), lds, st, dlogits,
+                         static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(dx_base),
+                         s.T, s.d, s.E, static_cast<bf16_t*>(dx_out));
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   }
   return MOE_OK;

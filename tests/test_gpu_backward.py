@@ -339,3 +339,68 @@ def test_layer_bwd_is_deterministic(name, scale):
             continue
         v = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(a.view(v), g2[n].view(v)), n
+
+
+# Router backward off and on the 8-wide kernels: expert counts that are not multiples of
+# 8, a partial group of experts, column tails, one and several token chunks.  Operands 4
+# bytes past a 16-byte boundary (dlogits, W_g) send the work to the scalar loads.
+ROUTER_BWD_SHAPES = [
+    dict(T=700, d=192, E=6, k=2, renormalize=True),
+    dict(T=520, d=288, E=12, k=3, renormalize=False),
+    dict(T=1000, d=544, E=16, k=4, renormalize=True),
+    dict(T=5, d=256, E=8, k=2, renormalize=False),
+]
+
+
+def _shifted(t):
+    """A contiguous tensor equal to t that starts 4 bytes past a 16-byte boundary."""
+    off = 4 // t.element_size()
+    buf = torch.empty(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("sh", ROUTER_BWD_SHAPES, ids=lambda s: f"T{s['T']}-d{s['d']}-E{s['E']}")
+def test_router_bwd_shapes_and_alignment(sh):
+    T, d, E, k = sh["T"], sh["d"], sh["E"], sh["k"]
+    print(f"router bwd T={T} d={d} E={E} k={k}", flush=True)
+    g = torch.Generator().manual_seed(1000 * E + d)
+    x = torch.randn(T, d, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(d, E, generator=g) / d ** 0.5).to(torch.bfloat16)
+    logits = torch.randn(T, E, generator=g)
+    idx = torch.topk(logits, k, dim=1).indices.to(torch.int32)
+    dtw = torch.randn(T, k, generator=g)
+    base = torch.randn(T, d, generator=g).to(torch.bfloat16)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=128, block_m=128, renormalize=sh["renormalize"])
+    xd, wgd, ld, idd, dtd, bd = (t.to(DEV) for t in (x, wg, logits, idx, dtw, base))
+    f = lambda *shp: torch.full(shp, float("nan"), dtype=torch.float32, device=DEV)
+    outs = []
+    for shift in (False, True):
+        dl = _shifted(f(T, E)) if shift else f(T, E)
+        wgs = _shifted(wgd) if shift else wgd
+        dwg, db = f(d, E), f(E)
+        dxr = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+        dx0 = torch.empty(T, d, dtype=torch.bfloat16, device=DEV)
+        B.moe_router_bwd(s, xd, wgs, ld, idd, dtd, dl, dwg, db, bd, dxr)
+        B.moe_router_bwd(s, xd, wgs, ld, idd, dtd, dl, dwg, None, None, dx0)
+        torch.cuda.synchronize()
+        outs.append((dl.clone(), dwg.clone(), db.clone(), dxr.clone(), dx0.clone()))
+    dl_ref = BW.router_backward(logits.double().numpy(), idx.numpy(), dtw.double().numpy(),
+                                sh["renormalize"])
+    dl, dwg, db, dxr, dx0 = outs[0]
+    assert_close(f64(dl), dl_ref, TOL_DLOGITS, "dlogits")
+    dl_h = f64(dl)
+    xh, wh = x.double().numpy(), wg.double().numpy()
+    assert_close(f64(dwg), xh.T @ dl_h, TOL_WGRAD, "dW_g")
+    assert_close(f64(db), dl_h.sum(axis=0), TOL_WGRAD, "dbias")
+    assert_close(f64(dxr), base.double().numpy() + dl_h @ wh.T, TOL_STAGE["bf16"], "router dx")
+    assert_close(f64(dx0), dl_h @ wh.T, TOL_STAGE["bf16"], "router dx, no base")
+    # aligned and shifted operands take the same additions: equal bit for bit
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(_bits(a), _bits(b))
