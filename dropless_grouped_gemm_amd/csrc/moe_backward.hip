@@ -899,19 +899,21 @@ k_router_dx_v8(const float* __restrict__ dl, const bf16_t* __restrict__ wg,
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[tt][j] = 0.f;
   for (int e = 0; e < E; e += 8) {
-    float w[8][8];   // [column][expert e + i]
+    u32x4_t wp[8];   // column c + j: experts e .. e + 7, packed
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      unpack_bf16x8(*reinterpret_cast<const u32x4_t*>(wg + (size_t)(c + j) * E + e), w[j]);
+    for (int j = 0; j < 8; ++j) wp[j] = *reinterpret_cast<const u32x4_t*>(wg + (size_t)(c + j) * E + e);
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const float4 g0 = *reinterpret_cast<const float4*>(sd + tt * E + e);
-      const float4 g1 = *reinterpret_cast<const float4*>(sd + tt * E + e + 4);
-      const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    for (int i = 0; i < 8; ++i) {
+      float w[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int j = 0; j < 8; ++j)
+        w[j] = __uint_as_float(i & 1 ? wp[j][i >> 1] & 0xffff0000u : wp[j][i >> 1] << 16);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[tt][j] = fmaf(g[i], w[j][i], v[tt][j]);
+      for (int tt = 0; tt < 8; ++tt) {
+        const float g = sd[tt * E + e + i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[tt][j] = fmaf(g, w[j], v[tt][j]);
+      }
     }
   }
 #pragma unroll
