@@ -110,7 +110,8 @@ static void layout_of(const moe_shape& s, moe_ws_layout& L) {
   L.pos = take(cur, M * 4);
   L.row_src = take(cur, rows * 4);
   L.err_flag = take(cur, 4);
-  L.x_perm = take(cur, rows * s.d * b);
+  // where the permute is fused into the gate/up loads x_perm is never written
+  L.x_perm = take(cur, gather_supported(s) ? 0 : rows * s.d * b);
   L.act = take(cur, rows * s.d_e * b);
   L.y = take(cur, rows * s.d * b);
   L.shared_act = take(cur, s.d_e_shared ? T * s.d_e_shared * b : 0);

@@ -26,7 +26,9 @@
 //     operand, D as B).  Rows past the expert's count copy its first row and are zeroed
 //     in LDS by the wave that copied them once its copies have landed.  fp32 output;
 //     experts without rows get zeros.
-// No atomics anywhere: every output element has one writer and a fixed summation order.
+// No floating-point atomics: every output element has one writer and a fixed summation
+// order.  The one atomic is an integer work-queue counter in k_gg_wgrad, which only
+// decides which work group takes which item, so results do not depend on scheduling.
 #include "moe_gemm_common.h"
 
 namespace moe {
@@ -167,7 +169,7 @@ k_gg_nt(NTOperands ops, int K, int N, const int32_t* __restrict__ meta,
   // items: (block, 128-row sub-tile, 512-column tile); a dense set uses 128-row blocks
   const int bm = dense_rows > 0 ? 128 : block_m;
   const int nsub = bm / 128;
-  const int nblocks = dense_rows > 0 ? (dense_rows + 127) / 128 : min(num_blocks_ptr[0], max_blocks);
+  const int nblocks = dense_rows > 0 ? (dense_rows + 127) / 128 : max(0, min(num_blocks_ptr[0], max_blocks));
   const int total = nblocks * nsub * n_tiles;
   const int nk = K / kBBK;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {

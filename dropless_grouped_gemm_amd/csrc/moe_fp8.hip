@@ -176,7 +176,7 @@ k_gg_fp8w(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb_dense = (dense_rows + 127) / 128;
-  const int nblocks = nb_dense + (max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0);
+  const int nblocks = nb_dense + (max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0);
   const int total = nblocks * n_tiles;
   const int nk = K / kFBK;
   const int KB = (K + kQBlock - 1) / kQBlock, NBq = (N + kQBlock - 1) / kQBlock;

@@ -96,7 +96,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = max_blocks > 0 ? min(num_blocks_ptr[0], max_blocks) : 0;
+  const int nb = max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0;
 
   // ---- group list ----------------------------------------------------------------
   // Built in the ring while it is idle: the table is staged at s_meta, then wave 0 forms

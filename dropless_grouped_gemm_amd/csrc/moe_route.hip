@@ -78,7 +78,7 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int NTB>
 __global__ void __launch_bounds__(kRouteThreads)
 k_router_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, int T, int d, int E,
-              int k_per_split, float* __restrict__ partial) {
+              int k_per_split, int wg_vec, float* __restrict__ partial) {
   constexpr int EB = 16 * NTB;
   constexpr int EV = EB / 8;               // 16-byte pieces per staged k row
   constexpr int kPitch = RouteTile<NTB>::kPitch;
@@ -137,7 +137,7 @@ k_router_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, int T
         v[u] = u32x4_t{0u, 0u, 0u, 0u};
         if (i < total && kk < klen) {
           const bf16_t* src = wg + (size_t)(kc0 + kk) * E + e0 + ev * 8;
-          if ((E & 7) == 0) {
+          if (wg_vec) {                    // E % 8 == 0 and W_g 16-byte aligned
             if (e0 + ev * 8 < E) v[u] = *reinterpret_cast<const u32x4_t*>(src);
           } else {
 #pragma unroll
@@ -404,9 +404,10 @@ moe_status launch_route(const moe_shape& s, const void* x, const void* w_gate, c
               (unsigned)ceil_div(s.E, 16 * ntb));
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w_gate);
+    const int wg_vec = (s.E % 8 == 0) && (reinterpret_cast<uintptr_t>(w_gate) & 15u) == 0;
 #define MOE_ROUTER_LAUNCH(NTBV)                                                               \
   hipLaunchKernelGGL(k_router_bf16<NTBV>, grid, dim3(kRouteThreads), 0, st, xb, wb, s.T, s.d, \
-                     s.E, k_per_split, partial)
+                     s.E, k_per_split, wg_vec, partial)
     switch (ntb) {
       case 1: MOE_ROUTER_LAUNCH(1); break;
       case 2: MOE_ROUTER_LAUNCH(2); break;

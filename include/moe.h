@@ -110,7 +110,8 @@ size_t moe_workspace_bytes(const moe_shape* s);
  *   "largest remaining logit", ties to the lower expert id, so slot j holds the
  *   j-th largest.  topk_w[t, j] = softmax over all E logits at topk_idx[t, j],
  *   divided by the sum of the token's k weights when renormalize is set.
- * In:  x [T, d] (dtype), w_gate [d, E] (dtype), bias [E] fp32 or NULL.
+ * In:  x [T, d] (dtype, 16-byte aligned), w_gate [d, E] (dtype; needs only 4-byte
+ *      alignment), bias [E] fp32 or NULL.
  * Out: logits [T, E] fp32 (NULL: not stored), topk_idx [T, k] int32,
  *      topk_w [T, k] fp32.
  * ws:  device workspace of ws_bytes >= moe_workspace_bytes(s).
@@ -491,7 +492,10 @@ moe_status moe_layer_bwd(const moe_shape* s, const void* x, const void* w_gate,
 /*
  * Byte offsets of the intermediates inside the moe_layer_fwd workspace, so that a
  * caller (tests, profilers) can inspect them after a call.  Host-only and pure.
- * Each field is an offset from the workspace base; a field is 0-sized when unused.
+ * Each field is an offset from the workspace base; a field is 0-sized when unused:
+ * x_perm where the permute is fused into the gate/up loads (bf16, d % 32 == 0: x's
+ * rows are gathered instead, see moe_grouped_gemm_gather), shared_act and shared_out
+ * without a shared expert.
  */
 typedef struct moe_ws_layout {
   size_t logits, topk_idx, topk_w, counts, offsets, padded_offsets, block_meta,

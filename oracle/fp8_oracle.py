@@ -94,8 +94,9 @@ def quantize(w, block: int = BLOCK):
 
 def dequantize(codes, scales, block: int = BLOCK):
     """fp64 weights: code value * its block's scale."""
-    codes = np.asarray(codes)
+    codes = np.asarray(codes, dtype=np.uint8)
     E, K, N = codes.shape
     full = np.repeat(np.repeat(np.asarray(scales, np.float64), block, axis=1), block,
                      axis=2)[:, :K, :N]
-    return e4m3_decode(codes) * full
+    table = e4m3_decode(np.arange(256))            # the value of every code
+    return table[codes] * full

@@ -387,17 +387,6 @@ def direct_layer(x, w1, w3, w2, topk_idx, topk_w, ws1=None, ws3=None, ws2=None):
     return out
 
 
-def token_output(x_row, idx_row, w_row, w1, w3, w2, ws1=None, ws3=None, ws2=None):
-    """out for one token, from its routing: the sampled-output check at full size."""
-    xr = np.asarray(x_row, F64)[None, :]
-    acc = np.zeros(np.asarray(w2).shape[-1], dtype=F64)
-    for j, e in enumerate(idx_row):
-        acc += float(w_row[j]) * expert_ffn(xr, w1[int(e)], w3[int(e)], w2[int(e)])[0]
-    if ws1 is not None:
-        acc += expert_ffn(xr, ws1, ws3, ws2)[0]
-    return acc
-
-
 # ----------------------------------------------------------------------------
 # Padding-waste report of the skewed-routing simulation [TL §2.3 item 3]
 # ----------------------------------------------------------------------------

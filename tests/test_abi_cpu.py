@@ -227,7 +227,9 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert all(o % 256 == 0 for o in offs)
         assert len(set(offs)) == len(offs) or True   # zero-sized fields may share an offset
         rows = B.moe_max_rows(s)
-        assert L["act"] - L["x_perm"] >= rows * s.d * 2
+        # bf16 with d % 32 == 0: the permute is fused into the gate/up loads and x_perm
+        # takes no room
+        assert L["act"] - L["x_perm"] == 0
         assert L["y"] - L["act"] >= rows * s.d_e * 2
         assert L["total"] > L["scratch"]
 
@@ -473,6 +475,28 @@ def test_unpadded_max_blocks_bounds_every_table(M, E, bm):
     assert B.moe_max_rows(s) == M
     L = B.moe_workspace_layout(s)
     assert L["act"] - L["x_perm"] >= M * s.d * 4
+
+
+def test_workspace_has_no_x_perm_where_the_permute_is_fused():
+    """bf16 with d % 32 == 0 gathers x's rows in the gate/up loads: the workspace holds
+    no x_perm there (forward and fp8 forward), and shrinks by max_rows * d * 2 bytes
+    against a shape that needs it (d % 32 != 0); the fp32 path keeps it."""
+    kw = dict(T=600, E=8, k=4, d_e=256, block_m=128)
+    fused = good_shape(d=512, **kw)
+    assert B.gather_supported(fused)
+    L = B.moe_workspace_layout(fused)
+    assert L["act"] == L["x_perm"]
+    rows = B.moe_max_rows(fused)
+    need = L["act"] + rows * 256 * 2
+    assert L["y"] >= need
+    assert B.moe_fp8_workspace_bytes(fused) >= B.moe_workspace_bytes(fused)
+    unfused = good_shape(d=520, **kw)                  # d % 32 != 0: permute, then GEMM
+    assert not B.gather_supported(unfused)
+    Lu = B.moe_workspace_layout(unfused)
+    assert Lu["act"] - Lu["x_perm"] >= B.moe_max_rows(unfused) * 520 * 2
+    f32 = B.make_shape(T=600, d=512, E=8, k=4, d_e=256, block_m=128, dtype="fp32")
+    Lf = B.moe_workspace_layout(f32)
+    assert Lf["act"] - Lf["x_perm"] >= B.moe_max_rows(f32) * 512 * 4
 
 
 def test_unpadded_flag_is_validated():

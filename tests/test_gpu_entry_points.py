@@ -154,6 +154,40 @@ def test_route_standalone(T, d, E, k, ng, tg, renorm, dtype):
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
 
 
+def _shifted4(t):
+    """A contiguous tensor equal to t that starts 4 bytes past a 16-byte boundary."""
+    off = 4 // t.element_size()
+    buf = torch.empty(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 512, 8, 2), (4100, 264, 16, 4), (96, 7168, 64, 6),
+                                     (64, 1024, 256, 8)])
+def test_route_with_a_w_gate_off_16_byte_alignment(T, d, E, k):
+    """W_g need only be 4-byte aligned: one that starts 4 bytes past a 16-byte boundary
+    gives logits, ids and weights bitwise equal to the aligned run's."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T + E)
+    x = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
+    wg = (torch.randn((d, E), generator=g, device=DEV) / d ** 0.5).to(torch.bfloat16)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=8, block_m=128)
+    ws = B.alloc_workspace(s)
+    res = []
+    for w_in in (wg, _shifted4(wg)):
+        assert (w_in.data_ptr() % 16 == 0) == (w_in is wg)
+        logits = torch.empty((T, E), device=DEV)
+        idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        w = torch.empty((T, k), device=DEV)
+        B.moe_route(s, x, w_in, None, logits, idx, w, ws)
+        torch.cuda.synchronize()
+        res.append((logits, idx, w))
+    assert_close(f64(res[0][0]), O.router_logits(f64(x), f64(wg)), TOL_LOGITS["bf16"], "logits")
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_route_exact_ties_go_to_the_lower_id():
     """Duplicated router columns give bitwise-equal logits; the lower id must win."""
     T, d, E, k = 64, 256, 16, 4
@@ -457,3 +491,46 @@ def test_combine_skips_negative_positions():
             if p[t, j] >= 0:
                 ref[t] += wh[t, j] * yh[p[t, j]]
     assert_close(f64(out), ref, TOL_STAGE["bf16"], "out")
+
+
+@pytest.mark.parametrize("tile", ["128", "384"])
+@pytest.mark.parametrize("op", ["gateup", "down"])
+def test_negative_block_count_runs_no_routed_block(tile, op, monkeypatch):
+    """A block count below zero in device memory (a caller's corrupt table) is read as
+    zero: no routed row is written, and the shared expert's dense segment in the same
+    launch is still computed, bitwise as with the real table."""
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", tile)
+    T, d, E, k, d_e = 256, 256, 4, 2, 128
+    rng = np.random.default_rng(41)
+    idx = rng.integers(0, E, size=(T, k))
+    dt = torch.bfloat16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(41)
+    rnd = lambda *sh: (torch.randn(sh, generator=g, device=DEV) / sh[-2] ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16", d_e_shared=d_e)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err,
+                        B.alloc_workspace(s))
+    if op == "gateup":
+        opc, K, N = B.MOE_OP_GATEUP_SWIGLU, d, d_e
+        w0, w1 = rnd(E, d, d_e), rnd(E, d, d_e)
+        s0, s1 = rnd(d, d_e), rnd(d, d_e)
+    else:
+        opc, K, N = B.MOE_OP_DOWN, d_e, d
+        w0, w1, s0, s1 = rnd(E, d_e, d), None, rnd(d_e, d), None
+    A = torch.randn((rows, K), generator=g, device=DEV).to(dt)
+    A_sh = torch.randn((T, K), generator=g, device=DEV).to(dt)
+    sentinel = torch.full((rows, N), -7.0, dtype=dt, device=DEV)
+    C = sentinel.clone()
+    C_sh, C_sh_ref = (torch.empty((T, N), dtype=dt, device=DEV) for _ in range(2))
+    C_ref = torch.empty((rows, N), dtype=dt, device=DEV)
+    B.moe_grouped_gemm_shared(s, opc, A, w0, w1, meta, nblk, mb, C_ref, A_sh, s0, s1, C_sh_ref)
+    bad = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    B.moe_grouped_gemm_shared(s, opc, A, w0, w1, meta, bad, mb, C, A_sh, s0, s1, C_sh)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), sentinel.view(torch.int16))
+    assert torch.equal(C_sh.view(torch.int16), C_sh_ref.view(torch.int16))

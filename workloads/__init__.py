@@ -6,4 +6,4 @@ the HIP path and the CPU oracle can take their inputs from it without sharing
 any of the method's code.
 """
 from .configs import CONFIGS, MoEConfig, get_config  # noqa: F401
-from .gen import make_inputs, MoEInputs  # noqa: F401
+from .gen import make_inputs, make_fp8_weights, MoEInputs, Fp8Weights  # noqa: F401

@@ -59,7 +59,11 @@ def _normal(g, shape, std, dtype, device, chunk_elems=1 << 26):
     return out
 
 
-def make_inputs(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> MoEInputs:
+def make_inputs(cfg: MoEConfig, device="cpu", seed: Optional[int] = None,
+                expert_weights: bool = True) -> MoEInputs:
+    """Every input of the workload.  expert_weights=False leaves w1, w3, w2 (and the
+    shared expert's) as None and draws everything else exactly as with them (the
+    weights come last in the stream), for runs that take their weights elsewhere."""
     device = torch.device(device)
     g = torch.Generator(device=device)
     g.manual_seed(cfg.seed if seed is None else seed)
@@ -96,6 +100,10 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> MoE
         ex = -torch.log1p(-u)                      # Exp(1)
         topk_w = (ex / ex.sum(dim=1, keepdim=True)).to(torch.float32).contiguous()
 
+    if not expert_weights:
+        return MoEInputs(cfg, x, w_gate, bias, None, None, None, None, None, None, topk_idx,
+                         topk_w)
+
     w1 = torch.empty((E, d, de), dtype=dt, device=device)
     w3 = torch.empty((E, d, de), dtype=dt, device=device)
     w2 = torch.empty((E, de, d), dtype=dt, device=device)
@@ -112,3 +120,65 @@ def make_inputs(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> MoE
         ws2 = _normal(g, (ds, d), 1.0 / math.sqrt(ds), dt, device)
 
     return MoEInputs(cfg, x, w_gate, bias, w1, w3, w2, ws1, ws3, ws2, topk_idx, topk_w)
+
+
+@dataclass
+class Fp8Weights:
+    """fp8 (e4m3) expert weights as codes plus one fp32 scale per 128 x 128 block, the
+    inputs of the fp8-weight layer: q* uint8 in the bf16 weights' [E, K, N] layout,
+    s* fp32 [E, ceil(K/128), ceil(N/128)]; the shared expert's without the E axis."""
+    q1: torch.Tensor
+    s1: torch.Tensor
+    q3: torch.Tensor
+    s3: torch.Tensor
+    q2: torch.Tensor
+    s2: torch.Tensor
+    qs1: Optional[torch.Tensor] = None
+    ss1: Optional[torch.Tensor] = None
+    qs3: Optional[torch.Tensor] = None
+    ss3: Optional[torch.Tensor] = None
+    qs2: Optional[torch.Tensor] = None
+    ss2: Optional[torch.Tensor] = None
+
+
+FP8_CODE_STD = 64.0
+
+
+def _fp8_matrix(g, lead, K, N, device):
+    """Seeded codes and scales of lead matrices [K, N] (lead == 0: one matrix without
+    the leading axis).  Codes: the e4m3 value nearest to a N(0, 64^2) draw (torch's own
+    conversion; |draw| > 448 is clipped first), so codes span the format's range like
+    those of a quantised Gaussian matrix.  Scales: U(0.75, 1.25) / (64 sqrt(K)), so the
+    weights code * scale are ~N(0, 1/K) within a factor 1.25, as the bf16 recipe."""
+    n = max(lead, 1)
+    kb, nb = -(-K // 128), -(-N // 128)
+    q = torch.empty((n, K, N), dtype=torch.uint8, device=device)
+    for i in range(n):
+        v = torch.randn((K, N), generator=g, device=device, dtype=torch.float32)
+        v.mul_(FP8_CODE_STD).clamp_(-448.0, 448.0)
+        q[i].copy_(v.to(torch.float8_e4m3fn).view(torch.uint8))
+    u = torch.rand((n, kb, nb), generator=g, device=device, dtype=torch.float32)
+    sc = (0.75 + 0.5 * u) / (FP8_CODE_STD * math.sqrt(K))
+    if lead == 0:
+        return q[0], sc[0].contiguous()
+    return q, sc
+
+
+def make_fp8_weights(cfg: MoEConfig, device="cpu", seed: Optional[int] = None) -> Fp8Weights:
+    """fp8 expert weights for the workload's shapes, from their own seeded stream
+    (seed + 500 by default), so they do not depend on whether make_inputs drew the
+    bf16 weights."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed((cfg.seed if seed is None else seed) + 500)
+    d, E, de = cfg.d, cfg.E, cfg.d_e
+    q1, s1 = _fp8_matrix(g, E, d, de, device)
+    q3, s3 = _fp8_matrix(g, E, d, de, device)
+    q2, s2 = _fp8_matrix(g, E, de, d, device)
+    w = Fp8Weights(q1, s1, q3, s3, q2, s2)
+    if cfg.d_e_shared:
+        ds = cfg.d_e_shared
+        w.qs1, w.ss1 = _fp8_matrix(g, 0, d, ds, device)
+        w.qs3, w.ss3 = _fp8_matrix(g, 0, d, ds, device)
+        w.qs2, w.ss2 = _fp8_matrix(g, 0, ds, d, device)
+    return w
