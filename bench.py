@@ -62,30 +62,31 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain elementwise kernel reading and writing 1 GiB "
                          "(counter scale reference)")
+    ap.add_argument("--no-others", dest="others", action="store_false",
+                    help="measure only --config (by default the fusedmoe run also measures the "
+                         "ep-share, decode (bf16 and fp8 weights) and zipf-skew workloads, "
+                         "reported under 'workloads')")
+    ap.add_argument("--other-steps", type=int, default=10,
+                    help="timed steps of each of the other workloads")
     ap.add_argument("--traffic", default=None,
                     help="traffic summary written by dropless_grouped_gemm_amd.profsum "
                          "(default: the one under profiles/ for the dominant kernel)")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        sys.exit(2)
+def measure(args, cfg_name, weights="bf16", unpadded=False, steps=20, warmup=5, full=True):
+    """One workload's staged layer step, timed with events between the C-ABI calls.
+    Returns the inputs, the buffers and every figure; full=False skips the
+    moe_layer_fwd cross-check and its graph replay (the other workloads of the
+    default run)."""
     import torch
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
-        sys.exit(2)
-
     from dropless_grouped_gemm_amd import binding as B
     from dropless_grouped_gemm_amd import ledger as LG
     from dropless_grouped_gemm_amd import profsum as PS
     from workloads import get_config, make_inputs
 
-    cfg = get_config(args.config)
-    if args.unpadded:
+    cfg = get_config(cfg_name)
+    if unpadded:
         cfg = cfg.scaled(name=cfg.name, unpadded=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -119,7 +120,7 @@ def main():
         sh_act = torch.empty((T, ds), dtype=dt, device=dev)
         sh_out = torch.empty((T, d), dtype=dt, device=dev)
 
-    fp8 = args.weights == "fp8"
+    fp8 = weights == "fp8"
     if fp8 and not B.fp8_supported(s):
         print(f"fp8 weights are not supported for {cfg.name}", file=sys.stderr)
         sys.exit(2)
@@ -221,7 +222,7 @@ def main():
         if ev is not None:
             ev[i].record()
 
-    if args.copy_probe:
+    if args.copy_probe and full:
         # a plain elementwise kernel that reads exactly 1 GiB and writes exactly 1 GiB:
         # the reference that scales the FETCH_SIZE / WRITE_SIZE counters
         a = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
@@ -230,18 +231,18 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     nst = len(stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
     # a 1 GiB write before each timed step evicts L2 and the Infinity Cache, so no step
     # reads what the previous one left cached; it lies outside the step's events
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for kk in range(args.steps):
+    for kk in range(steps):
         if flush is not None:
             flush.fill_(kk & 0x7F)
         step(evs[kk])
@@ -250,14 +251,14 @@ def main():
     stage_ms = {st: 0.0 for st in stages}
     total_ms = 0.0
     per_step = []
-    for kk in range(args.steps):
+    for kk in range(steps):
         for j, st in enumerate(stages):
             stage_ms[st] += evs[kk][j].elapsed_time(evs[kk][j + 1])
         per_step.append(evs[kk][0].elapsed_time(evs[kk][nst]))
         total_ms += per_step[-1]
-    ms_per_step = total_ms / args.steps
+    ms_per_step = total_ms / steps
     for st in stages:
-        stage_ms[st] /= args.steps
+        stage_ms[st] /= steps
     if int(err.item()) != 0:
         raise RuntimeError("device reported out-of-range expert ids")
     if gather:
@@ -266,7 +267,7 @@ def main():
         for _ in range(2):
             B.moe_permute(s, inp.x, pos, x_perm)
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+               for _ in range(steps)]
         for p0, p1 in pev:
             if flush is not None:
                 flush.fill_(0x2A)
@@ -274,59 +275,61 @@ def main():
             B.moe_permute(s, inp.x, pos, x_perm)
             p1.record()
         torch.cuda.synchronize()
-        permute_ms = sum(p0.elapsed_time(p1) for p0, p1 in pev) / args.steps
+        permute_ms = sum(p0.elapsed_time(p1) for p0, p1 in pev) / steps
     else:
         permute_ms = stage_ms["permute"]
 
     # cross-check: the single moe_layer_fwd call runs the same kernels
-    out2 = torch.empty_like(out)
-    ws2 = B.alloc_workspace(s, dev, fp8=fp8)
-    def layer_call():
-        if fp8:
-            B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *q1, *q3, *q2, *qs1, *qs3, *qs2,
-                                inp.topk_idx, inp.topk_w, out2, ws2)
-        else:
-            B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1,
-                            inp.ws3, inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
-    layer_call()
-    torch.cuda.synchronize()
-    nrep = max(3, args.steps // 2)
-    lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nrep)]
-    for a0, a1 in lev:
-        if flush is not None:
-            flush.fill_(0x55)
-        a0.record()
+    layer_fwd_ms = layer_graph_ms = same = None
+    if full:
+        out2 = torch.empty_like(out)
+        ws2 = B.alloc_workspace(s, dev, fp8=fp8)
+        def layer_call():
+            if fp8:
+                B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *q1, *q3, *q2, *qs1, *qs3, *qs2,
+                                    inp.topk_idx, inp.topk_w, out2, ws2)
+            else:
+                B.moe_layer_fwd(s, inp.x, inp.w_gate, inp.bias, inp.w1, inp.w3, inp.w2, inp.ws1,
+                                inp.ws3, inp.ws2, inp.topk_idx, inp.topk_w, out2, ws2)
         layer_call()
-        a1.record()
-    torch.cuda.synchronize()
-    layer_fwd_ms = sum(a0.elapsed_time(a1) for a0, a1 in lev) / nrep
-    # the same call captured once in a HIP graph and replayed (the library only enqueues
-    # kernels: no allocation, memset or host synchronisation), which removes the
-    # per-launch host overhead
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        layer_call()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        layer_call()
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nrep)]
-    for a0, a1 in gev:
-        if flush is not None:
-            flush.fill_(0x3C)
-        a0.record()
-        graph.replay()
-        a1.record()
-    torch.cuda.synchronize()
-    layer_graph_ms = sum(a0.elapsed_time(a1) for a0, a1 in gev) / nrep
-    del graph
-    same = bool(torch.equal(out.view(torch.int16) if eb == 2 else out.view(torch.int32),
-                            out2.view(torch.int16) if eb == 2 else out2.view(torch.int32)))
-    del ws2, out2
+        torch.cuda.synchronize()
+        nrep = max(3, steps // 2)
+        lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nrep)]
+        for a0, a1 in lev:
+            if flush is not None:
+                flush.fill_(0x55)
+            a0.record()
+            layer_call()
+            a1.record()
+        torch.cuda.synchronize()
+        layer_fwd_ms = sum(a0.elapsed_time(a1) for a0, a1 in lev) / nrep
+        # the same call captured once in a HIP graph and replayed (the library only enqueues
+        # kernels: no allocation, memset or host synchronisation), which removes the
+        # per-launch host overhead
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer_call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            layer_call()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nrep)]
+        for a0, a1 in gev:
+            if flush is not None:
+                flush.fill_(0x3C)
+            a0.record()
+            graph.replay()
+            a1.record()
+        torch.cuda.synchronize()
+        layer_graph_ms = sum(a0.elapsed_time(a1) for a0, a1 in gev) / nrep
+        del graph
+        same = bool(torch.equal(out.view(torch.int16) if eb == 2 else out.view(torch.int32),
+                                out2.view(torch.int16) if eb == 2 else out2.view(torch.int32)))
+        del ws2, out2
 
     # ---- algorithmic work per launch --------------------------------------------
     cnt = counts.cpu().tolist()
@@ -402,16 +405,46 @@ def main():
                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": gemm[dom]["frac"],
                     "traffic": traffic}
 
+
+    # the whole layer's algorithmic bytes: the router (when it runs), both GEMM
+    # launches (weights of every expert with rows, activations in and out) and combine
+    layer_bytes = gu_bytes + dn_bytes + cb + (0 if routed else LG.router_bytes(T, d, E, eb))
+    return dict(cfg=cfg, inp=inp, s=s, fp8=fp8, deq=deq, fp8k=fp8k, flush=flush, stages=stages,
+                stage_ms=stage_ms, per_step=per_step, ms_per_step=ms_per_step, gemm=gemm,
+                moves=moves, roofline=roofline, layer_fwd_ms=layer_fwd_ms,
+                layer_graph_ms=layer_graph_ms, same=same, active=active,
+                blocks=int(nblk.item()), rows=int(pad[E].item()), wall=wall,
+                layer_bytes=layer_bytes,
+                fw=dict(topk_idx=topk_idx, topk_w=topk_w, counts=counts, pad=pad, meta=meta,
+                        nblk=nblk, pos=pos, row_src=row_src, act=act, y=y, logits=logits,
+                        sh_act=sh_act if shared else None))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(2)
+
+    from dropless_grouped_gemm_amd import binding as B
+    from dropless_grouped_gemm_amd import ledger as LG
+
+    r = measure(args, args.config, args.weights, args.unpadded, args.steps, args.warmup)
+    cfg, inp, s, fp8, deq = r["cfg"], r["inp"], r["s"], r["fp8"], r["deq"]
+    T, d, E, k, de = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_e
+    ms_per_step, flush = r["ms_per_step"], r["flush"]
     bwd = None
     if args.backward:
         if fp8 or not B.backward_supported(s):
             print(f"the backward pass is not supported for {cfg.name} ({args.weights} weights)",
                   file=sys.stderr)
             sys.exit(2)
-        bwd = bench_backward(args, cfg, inp, s, B, LG, dict(
-            topk_idx=topk_idx, topk_w=topk_w, counts=counts, pad=pad, meta=meta, nblk=nblk,
-            pos=pos, row_src=row_src, act=act, y=y, logits=logits,
-            sh_act=sh_act if shared else None), ms_per_step)
+        bwd = bench_backward(args, cfg, inp, s, B, LG, r["fw"], ms_per_step)
 
     # ---- CPU oracle on a bounded sample -----------------------------------------
     cpu = None
@@ -426,7 +459,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "ms_per_step_median": statistics.median(per_step),
+        "ms_per_step_median": statistics.median(r["per_step"]),
         "caches": "cold: 1 GiB written before each timed step" if flush is not None else "warm",
         "higher_is_better": True,
         "scaling": "weak",
@@ -439,22 +472,73 @@ def main():
                    "d_e": de, "d_e_shared": cfg.d_e_shared, "block_m": cfg.block_m,
                    "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups, "seed": cfg.seed,
                    "layout": "unpadded" if cfg.unpadded else "padded"},
-        "roofline": roofline,
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
-        "stages_us": {st: round(v * 1e3, 2) for st, v in stage_ms.items()},
-        "gemm": gemm,
-        "moves": moves,
-        "layer_fwd_ms_per_call": layer_fwd_ms,
-        "layer_fwd_graph_ms_per_call": layer_graph_ms,
-        "layer_fwd_matches_staged": same,
-        "active_experts": active,
-        "blocks": int(nblk.item()),
-        "rows": int(pad[E].item()),
-        "wall_s": wall,
+        "stages_us": {st: round(v * 1e3, 2) for st, v in r["stage_ms"].items()},
+        "gemm": r["gemm"],
+        "moves": r["moves"],
+        "layer_fwd_ms_per_call": r["layer_fwd_ms"],
+        "layer_fwd_graph_ms_per_call": r["layer_graph_ms"],
+        "layer_fwd_matches_staged": r["same"],
+        "active_experts": r["active"],
+        "blocks": r["blocks"],
+        "rows": r["rows"],
+        "wall_s": r["wall"],
     }
     if bwd is not None:
         res["backward"] = bwd
+    # the other workloads, measured in the same process after the headline one (fewer
+    # steps; the same staged step, events and cold caches): the 65,536-row expert
+    # share's GEMMs against the MFMA roofline, decode's layer against HBM (bf16 and fp8
+    # weights), the skewed routing's GEMMs
+    if args.others and args.config == "fusedmoe-8x2048" and not args.unpadded and \
+            args.weights == "bf16" and not args.backward:
+        del r, inp
+        torch.cuda.empty_cache()
+        res["workloads"] = {}
+        for name, wts in OTHER_WORKLOADS:
+            o = measure(args, name, wts, False, args.other_steps, 3, full=False)
+            res["workloads"][name + ("" if wts == "bf16" else "-" + wts)] = summarize(o)
+            del o
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
+
+
+# workloads measured after the headline one in the default run: (name, weights)
+OTHER_WORKLOADS = (("ep-share-4x2048", "bf16"), ("decode-256x2048", "bf16"),
+                   ("decode-256x2048", "fp8"), ("zipf-skew-64x1408", "bf16"))
+
+
+def summarize(o):
+    """The figures of one of the other workloads: step time, tokens/s, each GEMM launch
+    against its roofline (MFMA or HBM), the two GEMM launches together, the data
+    movers, and the whole layer's algorithmic bytes over its step time."""
+    cfg = o["cfg"]
+    g = o["gemm"]
+    gu, dn = g["gateup"], g["down"]
+    both_us = gu["us"] + dn["us"]
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    pair_tflops = (gu["flops"] + dn["flops"]) / (both_us * 1e6)
+    pair_gbps = (gu["bytes"] + dn["bytes"]) / (both_us * 1e3)
+    ms = o["ms_per_step"]
+    return {
+        "ms_per_step": ms,
+        "ms_per_step_median": statistics.median(o["per_step"]),
+        "tokens_per_s": cfg.T / (ms / 1e3),
+        "weights": "fp8-e4m3" if o["fp8"] else cfg.dtype,
+        "stages_us": {st: round(v * 1e3, 2) for st, v in o["stage_ms"].items()},
+        "gemm": {n: {kk: (round(v, 4) if isinstance(v, float) else v)
+                     for kk, v in gg.items() if kk in ("us", "tflops", "gbps", "bound", "frac")}
+                 for n, gg in g.items()},
+        "gemm_pair": {"us": round(both_us, 2), "tflops": pair_tflops, "gbps": pair_gbps,
+                      "frac_mfma": pair_tflops / peak, "frac_hbm": pair_gbps / PEAK_HBM_GBPS},
+        "moves": {n: {"us": round(v["us"], 2), "gbps": v["gbps"], "frac": v["frac"]}
+                  for n, v in o["moves"].items()},
+        "layer_hbm": {"bytes": o["layer_bytes"], "gbps": o["layer_bytes"] / (ms * 1e6),
+                      "frac": o["layer_bytes"] / (ms * 1e6) / PEAK_HBM_GBPS},
+        "active_experts": o["active"],
+        "blocks": o["blocks"],
+    }
 
 
 def bench_backward(args, cfg, inp, s, B, LG, fw, fwd_ms):

@@ -213,7 +213,7 @@ moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate, cons
   if (st != MOE_OK) return st;
   if ((st = check_routing(*s)) != MOE_OK) return st;
   if (!x || !w_gate || !topk_idx || !topk_w) return MOE_EINVAL;
-  if (!aligned16(x) || !aligned4(w_gate) || !aligned4(topk_idx) || !aligned4(topk_w) ||
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned4(topk_idx) || !aligned4(topk_w) ||
       (bias && !aligned4(bias)) || (logits && !aligned4(logits)))
     return MOE_EINVAL;
   if (s->T == 0) return MOE_OK;
@@ -507,7 +507,7 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
     if (shared && (!qs[i] || !ss[i] || !aligned16(qs[i]) || !aligned4(ss[i]))) return MOE_EINVAL;
     if (!shared && (qs[i] || ss[i])) return MOE_EINVAL;
   }
-  if ((w_gate && !aligned4(w_gate)) || (bias && !aligned4(bias)) ||
+  if ((w_gate && !aligned16(w_gate)) || (bias && !aligned4(bias)) ||
       (topk_idx_in && !aligned4(topk_idx_in)) || (topk_w_in && !aligned4(topk_w_in)))
     return MOE_EINVAL;
   moe_ws_layout L;
@@ -600,7 +600,7 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
   for (const void* p : p16)
     if (!aligned16(p)) return MOE_EINVAL;
   if (shared && (!aligned16(ws1) || !aligned16(ws3) || !aligned16(ws2))) return MOE_EINVAL;
-  if ((w_gate && !aligned4(w_gate)) || (bias && !aligned4(bias)) ||
+  if ((w_gate && !aligned16(w_gate)) || (bias && !aligned4(bias)) ||
       (topk_idx_in && !aligned4(topk_idx_in)) || (topk_w_in && !aligned4(topk_w_in)))
     return MOE_EINVAL;
   moe_ws_layout L;

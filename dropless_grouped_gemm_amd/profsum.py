@@ -90,6 +90,8 @@ def kernels_summary(d: str, command: str, bench_log: str | None) -> str:
             out += ["", "Event-timed stage averages printed by the benchmark in the same run (us):",
                     "", "```", json.dumps(b.get("stages_us")), "```",
                     f"roofline: {json.dumps(b.get('roofline'))}"]
+            for name, w in (b.get("workloads") or {}).items():
+                out += [f"{name}: stages (us) {json.dumps(w.get('stages_us'))}"]
             bw = b.get("backward")
             if bw:
                 out += ["", "Backward stages in the same run (us), and each backward GEMM launch's "
@@ -115,7 +117,9 @@ def _pick(vals, needle):
     return hits[0], sum(v) / len(v), len(v)
 
 
-def traffic_summary(fetch_dir, write_dir, kernel, label, workload, command, algo_bytes=None):
+def traffic_summary(fetch_dir, write_dir, kernel, label, workload, command, algo_bytes=None,
+                    source=None):
+    source = source or GEMM_SOURCE
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _per_kernel(os.path.join(d, "run_counter_collection.csv"), counter)
@@ -140,8 +144,8 @@ def traffic_summary(fetch_dir, write_dir, kernel, label, workload, command, algo
     if algo_bytes:
         out.append(f"Algorithmic bytes per launch: {algo_bytes:.4e} (traffic / algorithmic = "
                    f"{total / algo_bytes:.2f})")
-    blob = {"kernel": label, "config": workload, "source": GEMM_SOURCE,
-            "source_sha256": source_digest(GEMM_SOURCE), "bytes_per_launch": total,
+    blob = {"kernel": label, "config": workload, "source": source,
+            "source_sha256": source_digest(source), "bytes_per_launch": total,
             "fetch_bytes": res["FETCH_SIZE"]["bytes"], "write_bytes": res["WRITE_SIZE"]["bytes"]}
     out += ["", "```json", json.dumps(blob), "```"]
     return "\n".join(out) + "\n"
@@ -179,13 +183,16 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--algo-bytes", type=float, default=None)
+    t.add_argument("--source", action="append", default=None,
+                   help="source file (from the repository root) the kernel is built from, "
+                        "repeatable; default: the grouped-GEMM sources")
     t.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.cmd == "kernels":
         text = kernels_summary(a.dir, a.command, a.bench)
     else:
         text = traffic_summary(a.fetch_dir, a.write_dir, a.kernel, a.label, a.workload, a.command,
-                               a.algo_bytes)
+                               a.algo_bytes, a.source)
     with open(a.out, "w") as f:
         f.write(text)
 

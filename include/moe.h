@@ -110,8 +110,9 @@ size_t moe_workspace_bytes(const moe_shape* s);
  *   "largest remaining logit", ties to the lower expert id, so slot j holds the
  *   j-th largest.  topk_w[t, j] = softmax over all E logits at topk_idx[t, j],
  *   divided by the sum of the token's k weights when renormalize is set.
- * In:  x [T, d] (dtype, 16-byte aligned), w_gate [d, E] (dtype; needs only 4-byte
- *      alignment), bias [E] fp32 or NULL.
+ * In:  x [T, d] (dtype), w_gate [d, E] (dtype), bias [E] fp32 or NULL; x and w_gate
+ *      16-byte aligned (MOE_EINVAL otherwise, as for moe_layer_fwd and
+ *      moe_layer_fwd_fp8, which take the same w_gate).
  * Out: logits [T, E] fp32 (NULL: not stored), topk_idx [T, k] int32,
  *      topk_w [T, k] fp32.
  * ws:  device workspace of ws_bytes >= moe_workspace_bytes(s).

@@ -304,6 +304,27 @@ def test_fp8_entry_point_argument_rules():
               need - 1, None) == B.MOE_EWORKSPACE
 
 
+def test_forward_router_needs_a_16_byte_aligned_w_gate():
+    """The forward router stages W_g slices with 16-byte copies: moe_route, moe_layer_fwd and
+    moe_layer_fwd_fp8 reject a W_g that is only 4-byte aligned (EINVAL, nothing launched)
+    and accept an aligned one."""
+    L = B.lib()
+    s = good_shape(T=64, d=256, E=8, k=2)
+    ps = ctypes.byref(s)
+    w4 = ctypes.c_void_p(0x10004)
+    need = L.moe_workspace_bytes(ps)
+    assert L.moe_route(ps, FAKE, w4, None, None, FAKE, FAKE, FAKE, need, None) == B.MOE_EINVAL
+    assert L.moe_layer_fwd(ps, FAKE, w4, None, FAKE, FAKE, FAKE, None, None, None, None, None,
+                           FAKE, FAKE, need, None) == B.MOE_EINVAL
+    need8 = L.moe_fp8_workspace_bytes(ps)
+    assert L.moe_layer_fwd_fp8(ps, FAKE, w4, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE,
+                               FAKE, need8, None) == B.MOE_EINVAL
+    s0 = good_shape(T=0)                      # T == 0 enqueues nothing: validation only
+    p0 = ctypes.byref(s0)
+    assert L.moe_route(p0, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.MOE_OK
+    assert L.moe_route(p0, FAKE, w4, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.MOE_EINVAL
+
+
 def test_fp8_workspace_size_rule():
     """moe_fp8_workspace_bytes: moe_workspace_bytes's layout, plus room for the
     dequantised bf16 weights exactly where the layer takes the dequantised path (routed

@@ -154,40 +154,6 @@ def test_route_standalone(T, d, E, k, ng, tg, renorm, dtype):
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
 
 
-def _shifted4(t):
-    """A contiguous tensor equal to t that starts 4 bytes past a 16-byte boundary."""
-    off = 4 // t.element_size()
-    buf = torch.empty(t.numel() + 16, dtype=t.dtype, device=t.device)
-    v = buf[off:off + t.numel()].view(t.shape)
-    v.copy_(t)
-    return v
-
-
-@pytest.mark.parametrize("T,d,E,k", [(300, 512, 8, 2), (4100, 264, 16, 4), (96, 7168, 64, 6),
-                                     (64, 1024, 256, 8)])
-def test_route_with_a_w_gate_off_16_byte_alignment(T, d, E, k):
-    """W_g need only be 4-byte aligned: one that starts 4 bytes past a 16-byte boundary
-    gives logits, ids and weights bitwise equal to the aligned run's."""
-    g = torch.Generator(device=DEV)
-    g.manual_seed(T + E)
-    x = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
-    wg = (torch.randn((d, E), generator=g, device=DEV) / d ** 0.5).to(torch.bfloat16)
-    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=8, block_m=128)
-    ws = B.alloc_workspace(s)
-    res = []
-    for w_in in (wg, _shifted4(wg)):
-        assert (w_in.data_ptr() % 16 == 0) == (w_in is wg)
-        logits = torch.empty((T, E), device=DEV)
-        idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
-        w = torch.empty((T, k), device=DEV)
-        B.moe_route(s, x, w_in, None, logits, idx, w, ws)
-        torch.cuda.synchronize()
-        res.append((logits, idx, w))
-    assert_close(f64(res[0][0]), O.router_logits(f64(x), f64(wg)), TOL_LOGITS["bf16"], "logits")
-    for a, b in zip(*res):
-        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
-
-
 def test_route_exact_ties_go_to_the_lower_id():
     """Duplicated router columns give bitwise-equal logits; the lower id must win."""
     T, d, E, k = 64, 256, 16, 4
