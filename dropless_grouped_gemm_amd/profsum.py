@@ -123,7 +123,9 @@ def traffic_summary(fetch_dir, write_dir, kernel, label, workload, command, algo
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals = _per_kernel(os.path.join(d, "run_counter_collection.csv"), counter)
-        _, probe_kib, _ = _pick(vals, PROBE_KERNEL)
+        # the probe is the largest elementwise negation (a workload's input generator may
+        # negate small tensors of its own)
+        probe_kib = max(max(v) for k, v in vals.items() if PROBE_KERNEL in k)
         name, kib, n = _pick(vals, kernel)
         factor = PROBE_BYTES / (probe_kib * 1024.0)
         res[counter] = dict(kib=kib, dispatches=n, probe_kib=probe_kib, factor=factor,
