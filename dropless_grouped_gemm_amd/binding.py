@@ -23,6 +23,8 @@ MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
 
 ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
+                "moe_build_offsets_noalloc", "moe_build_offsets_noalloc_capacity",
+                "moe_build_offsets_scratch_bytes",
                 "moe_grouped_gemm", "moe_grouped_gemm_shared", "moe_grouped_gemm_gather",
                 "moe_combine", "moe_layer_fwd", "moe_quantize_fp8", "moe_dequantize_fp8",
                 "moe_grouped_gemm_fp8", "moe_fp8_workspace_bytes", "moe_layer_fwd_fp8",
@@ -91,6 +93,12 @@ def lib():
         L.moe_route.restype = ctypes.c_int32
         L.moe_build_offsets.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_build_offsets.restype = ctypes.c_int32
+        L.moe_build_offsets_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        L.moe_build_offsets_noalloc.restype = ctypes.c_int32
+        L.moe_build_offsets_noalloc_capacity.argtypes = []
+        L.moe_build_offsets_noalloc_capacity.restype = ctypes.c_size_t
+        L.moe_build_offsets_scratch_bytes.argtypes = [S]
+        L.moe_build_offsets_scratch_bytes.restype = ctypes.c_size_t
         L.moe_permute.argtypes = [S, P, P, P, P]
         L.moe_permute.restype = ctypes.c_int32
         L.moe_grouped_gemm.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
@@ -235,6 +243,21 @@ def moe_build_offsets(shape, topk_idx, counts, offsets, padded_offsets, block_me
         ctypes.byref(shape), _p(topk_idx), _p(counts), _p(offsets), _p(padded_offsets),
         _p(block_meta), _p(num_blocks), _p(pos), _p(row_src), _p(err_flag), _p(ws),
         ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_build_offsets_noalloc(shape, topk_idx, counts, offsets, padded_offsets, block_meta,
+                              num_blocks, pos, row_src, err_flag, stream=None):
+    _check("moe_build_offsets_noalloc", lib().moe_build_offsets_noalloc(
+        ctypes.byref(shape), _p(topk_idx), _p(counts), _p(offsets), _p(padded_offsets),
+        _p(block_meta), _p(num_blocks), _p(pos), _p(row_src), _p(err_flag), _stream(stream)))
+
+
+def moe_build_offsets_noalloc_capacity() -> int:
+    return lib().moe_build_offsets_noalloc_capacity()
+
+
+def moe_build_offsets_scratch_bytes(shape: moe_shape) -> int:
+    return lib().moe_build_offsets_scratch_bytes(ctypes.byref(shape))
 
 
 def moe_permute(shape, x, pos, x_perm, stream=None):

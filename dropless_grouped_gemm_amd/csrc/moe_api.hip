@@ -237,6 +237,30 @@ moe_status moe_build_offsets(const moe_shape* s, const int32_t* topk_idx, int32_
                               pos, row_src, err_flag, ws, static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_build_offsets_noalloc(const moe_shape* s, const int32_t* topk_idx,
+                                     int32_t* counts, int32_t* offsets, int32_t* padded_offsets,
+                                     int32_t* block_meta, int32_t* num_blocks, int32_t* pos,
+                                     int32_t* row_src, int32_t* err_flag, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const void* ptrs[] = {topk_idx, counts, offsets, padded_offsets, block_meta,
+                        num_blocks, pos, row_src, err_flag};
+  for (const void* p : ptrs)
+    if (!p || !aligned4(p)) return MOE_EINVAL;
+  if (offsets_scratch_bytes(*s) > static_scratch_capacity()) return MOE_ENOTSUP;
+  void* scratch = nullptr;
+  if ((st = static_scratch_address(&scratch)) != MOE_OK) return st;
+  return launch_build_offsets(*s, topk_idx, counts, offsets, padded_offsets, block_meta, num_blocks,
+                              pos, row_src, err_flag, scratch, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_build_offsets_noalloc_capacity(void) { return static_scratch_capacity(); }
+
+size_t moe_build_offsets_scratch_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return offsets_scratch_bytes(*s);
+}
+
 moe_status moe_permute(const moe_shape* s, const void* x, const int32_t* pos, void* x_perm,
                        void* stream) {
   moe_status st = check_shape(s);

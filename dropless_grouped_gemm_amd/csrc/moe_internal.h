@@ -69,6 +69,10 @@ moe_status launch_route(const moe_shape& s, const void* x, const void* w_gate,
 int offsets_chunk(const moe_shape& s);
 int64_t offsets_nchunks(const moe_shape& s);
 size_t offsets_scratch_bytes(const moe_shape& s);
+// The offsets kernels' scratch as a file-scope device array (moe_build_offsets_noalloc):
+// its size, and its address on the current device (looked up once per device).
+size_t static_scratch_capacity();
+moe_status static_scratch_address(void** out);
 moe_status launch_build_offsets(const moe_shape& s, const int32_t* topk_idx,
                                 int32_t* counts, int32_t* offsets, int32_t* padded,
                                 int32_t* block_meta, int32_t* num_blocks, int32_t* pos,

@@ -22,6 +22,8 @@
 // result equals a stable sort of the assignments by expert id.
 #include "moe_internal.h"
 
+#include <mutex>
+
 namespace moe {
 
 static constexpr int kCountThreads = 256;      // 4 waves
@@ -272,6 +274,40 @@ moe_status launch_build_offsets(const moe_shape& s, const int32_t* topk_idx, int
                      hist, lrank, padded, block_meta, num_blocks, s.block_m, s.unpadded, max_rows,
                      pos, row_src);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (moe_build_offsets_noalloc): the per-chunk
+// histograms and local ranks live in one file-scope device array instead of the caller's
+// workspace.  Each device holds its own copy of the array, at its own address, from the
+// library's first use on that device until the process ends.  In host code the array's
+// name is not a device address, so the address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is passed on.
+// Nothing in it must start at zero: k_count writes every histogram entry and every local
+// rank that k_scan_meta and k_scatter later read.  Calls on one device share the array,
+// so calls that overlap in time on one device race.
+// ---------------------------------------------------------------------------
+static constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char offsets_static_scratch[kStaticScratchBytes];
+
+static constexpr int kStaticMaxDevices = 64;
+static std::mutex g_static_mu;
+static void* g_static_ptr[kStaticMaxDevices];
+
+size_t static_scratch_capacity() { return kStaticScratchBytes; }
+
+moe_status static_scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kStaticMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(offsets_static_scratch)) != hipSuccess || !p)
+      return MOE_EHIP;
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace moe

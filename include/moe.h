@@ -157,6 +157,32 @@ moe_status moe_build_offsets(const moe_shape* s, const int32_t* topk_idx,
                              void* stream);
 
 /*
+ * moe_build_offsets without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same inputs, outputs, results (bit for bit) and errors as moe_build_offsets; its
+ * scratch (per-chunk histograms and per-assignment local ranks,
+ * moe_build_offsets_scratch_bytes(s) bytes) lives in a device array inside the library,
+ * moe_build_offsets_noalloc_capacity() = 8 MiB on each device, held from the first call
+ * on that device until the process ends.  The call allocates nothing.
+ *   - MOE_ENOTSUP when moe_build_offsets_scratch_bytes(s) exceeds the capacity (about
+ *     T*k <= 2,000,000 assignments for E <= 1024); nothing is launched then.
+ *   - MOE_EHIP if the array's device address cannot be obtained.
+ *   - Every call on one device uses that device's one array: calls that overlap in time
+ *     on the same device (another stream, another host thread) race and give undefined
+ *     results.  Calls in one stream, one after another, are safe: nothing in the array
+ *     needs to start at zero, every entry read is first written by the same call.
+ */
+moe_status moe_build_offsets_noalloc(const moe_shape* s, const int32_t* topk_idx,
+                                     int32_t* counts, int32_t* offsets,
+                                     int32_t* padded_offsets, int32_t* block_meta,
+                                     int32_t* num_blocks, int32_t* pos, int32_t* row_src,
+                                     int32_t* err_flag, void* stream);
+/* Host-only and pure: the static scratch's size in bytes, and the scratch bytes a shape
+ * needs (0 for an invalid shape). */
+size_t moe_build_offsets_noalloc_capacity(void);
+size_t moe_build_offsets_scratch_bytes(const moe_shape* s);
+
+/*
  * Permute (in-card dispatch; TileLang chapter section 2.3, dropless notes section 4
  * steps 5-6): x_perm[pos[t*k + j], :] = x[t, :] for every (t, j) with pos >= 0.
  * Pad rows of x_perm are neither written nor read.
