@@ -16,7 +16,7 @@
 // blockIdx.z so that small-T shapes (decode) still spread over the chip; each K
 // split writes fp32 partial logits and the selection kernel adds them in split
 // order, so the result is deterministic.
-#include "moe_internal.h"
+#include "moe_gemm_common.h"
 
 #include <float.h>
 
@@ -269,86 +269,18 @@ static inline int select_lanes(int E) {
   return g;
 }
 
+// The k selection rounds of one token held by its G lanes (lane lt holds experts
+// lt + G*r, r < PER, with logits l[r], exp(l - max) z[r], eligibility elig[r]): k rounds
+// of "largest remaining eligible logit" (one 64-bit key per candidate: the logit's
+// order bits above the complemented id, so ties go to the lower id), the weights
+// z / S, renormalised when asked.  Every lane of the group takes part; `live` lanes
+// write slot j from lane j % G.
 template <int G, int PER>
-__global__ void __launch_bounds__(kSelThreads)
-k_select(const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, int T, int E,
-         int k, int n_groups, int topk_groups, int renormalize, float* __restrict__ logits_out,
-         int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  __shared__ float gl[kSelLds];
-  constexpr int kTokPerBlock = kSelThreads / G;
-  const int lt = threadIdx.x % G;          // lane within the token's group
-  const int slot = threadIdx.x / G;        // token within the block
-  const int base_lane = (threadIdx.x & 63) - lt;
-  const int tok = blockIdx.x * kTokPerBlock + slot;
-  // Groups past T compute on the last token (so every lane of a wave takes part in
-  // the butterflies) and write nothing.
-  const bool live = tok < T;
-  const int t = live ? tok : T - 1;
-
-  bool has[PER];
-  float l[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int e = lt + G * r;
-    has[r] = e < E;
-    float pv[kRouteMaxSplit];
-#pragma unroll
-    for (int sidx = 0; sidx < kRouteMaxSplit; ++sidx)
-      pv[sidx] = (has[r] && sidx < nsplit) ? partial[((size_t)sidx * T + t) * E + e] : 0.f;
-    float acc = pv[0];
-#pragma unroll
-    for (int sidx = 1; sidx < kRouteMaxSplit; ++sidx)
-      if (sidx < nsplit) acc += pv[sidx];
-    if (bias && has[r]) acc += bias[e];
-    l[r] = has[r] ? acc : -FLT_MAX;
-    if (logits_out && live && has[r]) logits_out[(size_t)t * E + e] = acc;
-  }
-  // softmax over all E in fp32 (max-subtracted)
-  float m = -FLT_MAX;
-#pragma unroll
-  for (int r = 0; r < PER; ++r)
-    if (has[r]) m = fmaxf(m, l[r]);
-  m = group_max<G>(m);
-  float z[PER];
-  float zs = 0.f;
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    z[r] = has[r] ? expf(l[r] - m) : 0.f;
-    zs += z[r];
-  }
-  const float S = group_sum<G>(zs);
-
-  // eligibility (group-limited routing; n_groups <= min(E, 64) <= G)
-  bool elig[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) elig[r] = has[r];
-  if (n_groups > 0) {
-    const int gs = E / n_groups;
-    float* tl = gl + slot * E;
-#pragma unroll
-    for (int r = 0; r < PER; ++r)
-      if (has[r]) tl[lt + G * r] = l[r];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint64_t gkey = 0;
-    if (lt < n_groups) {
-      float gm = -FLT_MAX;
-      for (int e = lt * gs; e < (lt + 1) * gs; ++e) gm = fmaxf(gm, tl[e]);
-      gkey = sel_key(gm, lt);
-    }
-    uint64_t keep = 0;
-    for (int r = 0; r < topk_groups; ++r) {
-      const uint64_t b = group_max_key<G>(gkey);
-      const int gid = sel_id(b);
-      keep |= 1ull << gid;
-      if (lt == gid) gkey = 0;
-    }
-#pragma unroll
-    for (int r = 0; r < PER; ++r) elig[r] = has[r] && ((keep >> ((lt + G * r) / gs)) & 1ull);
-  }
-
-  // k rounds of "largest remaining eligible logit", ties to the lower id
+__device__ __forceinline__ void select_rounds(const float* l, const float* z, const bool* elig,
+                                              float S, int k, int renormalize, bool live, int t,
+                                              int lt, int base_lane,
+                                              int32_t* __restrict__ topk_idx,
+                                              float* __restrict__ topk_w) {
   uint64_t key[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) key[r] = elig[r] ? sel_key(l[r], lt + G * r) : 0ull;
@@ -392,9 +324,389 @@ k_select(const float* __restrict__ partial, int nsplit, const float* __restrict_
   }
 }
 
+// Logits of one token from a row its G lanes can read (LDS), their softmax over all E
+// in fp32 (max-subtracted; S = the group's sum).
+template <int G, int PER>
+__device__ __forceinline__ void load_softmax(const float* lrow, int E, int lt, bool* has, float* l,
+                                             float* z, float& S) {
+  float m = -FLT_MAX;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int e = lt + G * r;
+    has[r] = e < E;
+    l[r] = has[r] ? lrow[e] : -FLT_MAX;
+    if (has[r]) m = fmaxf(m, l[r]);
+  }
+  m = group_max<G>(m);
+  float zs = 0.f;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    z[r] = has[r] ? expf(l[r] - m) : 0.f;
+    zs += z[r];
+  }
+  S = group_sum<G>(zs);
+}
+
+// Selection of one token from its E logits (bias included) in a row `lrow` that the
+// token's G lanes can read (LDS): softmax, eligibility (group-limited routing: a group
+// scores its largest logit, the topk_groups best groups stay, ties to the lower group
+// id; n_groups <= G), then the k rounds.
+template <int G, int PER>
+__device__ __forceinline__ void select_token(const float* lrow, int E, int k, int n_groups,
+                                             int topk_groups, int renormalize, bool live, int t,
+                                             int lt, int base_lane, int32_t* __restrict__ topk_idx,
+                                             float* __restrict__ topk_w) {
+  bool has[PER], elig[PER];
+  float l[PER], z[PER], S;
+  load_softmax<G, PER>(lrow, E, lt, has, l, z, S);
+#pragma unroll
+  for (int r = 0; r < PER; ++r) elig[r] = has[r];
+  if (n_groups > 0) {
+    const int gs = E / n_groups;
+    uint64_t gkey = 0;
+    if (lt < n_groups) {
+      float gm = -FLT_MAX;
+      for (int e = lt * gs; e < (lt + 1) * gs; ++e) gm = fmaxf(gm, lrow[e]);
+      gkey = sel_key(gm, lt);
+    }
+    uint64_t keep = 0;
+    for (int r = 0; r < topk_groups; ++r) {
+      const uint64_t b = group_max_key<G>(gkey);
+      const int gid = sel_id(b);
+      keep |= 1ull << gid;
+      if (lt == gid) gkey = 0;
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) elig[r] = has[r] && ((keep >> ((lt + G * r) / gs)) & 1ull);
+  }
+  select_rounds<G, PER>(l, z, elig, S, k, renormalize, live, t, lt, base_lane, topk_idx, topk_w);
+}
+
+// The selection kernel after the split-K router: G lanes per token add the splits'
+// partial logits in split order and the bias, stage the row in LDS, then select.
+template <int G, int PER>
+__global__ void __launch_bounds__(kSelThreads)
+k_select(const float* __restrict__ partial, int nsplit, const float* __restrict__ bias, int T, int E,
+         int k, int n_groups, int topk_groups, int renormalize, float* __restrict__ logits_out,
+         int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  __shared__ float gl[kSelLds];
+  constexpr int kTokPerBlock = kSelThreads / G;
+  const int lt = threadIdx.x % G;          // lane within the token's group
+  const int slot = threadIdx.x / G;        // token within the block
+  const int base_lane = (threadIdx.x & 63) - lt;
+  const int tok = blockIdx.x * kTokPerBlock + slot;
+  // Groups past T compute on the last token (so every lane of a wave takes part in
+  // the butterflies) and write nothing.
+  const bool live = tok < T;
+  const int t = live ? tok : T - 1;
+  float* tl = gl + slot * E;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int e = lt + G * r;
+    if (e >= E) continue;
+    float pv[kRouteMaxSplit];
+#pragma unroll
+    for (int sidx = 0; sidx < kRouteMaxSplit; ++sidx)
+      pv[sidx] = sidx < nsplit ? partial[((size_t)sidx * T + t) * E + e] : 0.f;
+    float acc = pv[0];
+#pragma unroll
+    for (int sidx = 1; sidx < kRouteMaxSplit; ++sidx)
+      if (sidx < nsplit) acc += pv[sidx];
+    if (bias) acc += bias[e];
+    tl[e] = acc;
+    if (logits_out && live) logits_out[(size_t)t * E + e] = acc;
+  }
+  // a token's row is written and read by the lanes of one wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  select_token<G, PER>(tl, E, k, n_groups, topk_groups, renormalize, live, t, lt, base_lane,
+                       topk_idx, topk_w);
+}
+
+// ---------------------------------------------------------------------------
+// Fused router for large T (bf16, E a multiple of 8 up to 64, d a multiple of the
+// slice depth): one block of 4 waves owns TB tokens and the whole of K, so the logits
+// are complete inside the block and the selection runs there too (no partial logits,
+// no second launch).  x streams through an LDS ring of NS slices with 16-byte
+// global->LDS copies whose 64 lanes cover 1 KB: two (or four) rows of 512 (256)
+// contiguous bytes, instead of the 64 bytes per row a direct A-operand load covers.
+// A slice also holds W_g's rows [k0, k0 + SK) - one contiguous piece of W_g - read as
+// the B operand with ds_read_b64_tr_b16.  The 4 waves split each slice's 32-deep steps
+// (wave w takes steps w, w+4, ...) and accumulate TB x 16*NT partial logits each; at the
+// end the four partial sums are added in wave order through LDS (deterministic), the
+// bias added, and G lanes per token select as k_select does.
+// ---------------------------------------------------------------------------
+// Group-limited eligibility of one token by one lane (E <= 64): a group (n_groups
+// contiguous id ranges) scores its largest logit, the topk_groups best groups stay
+// (scanned upwards with a strict comparison: ties to the lower group id); returns the
+// mask of eligible experts.  lrow[e * stride] holds the token's logits.
+__device__ __forceinline__ uint64_t group_keep_mask(const float* lrow, int stride, int E,
+                                                    int n_groups, int topk_groups) {
+  const int gs = E / n_groups;
+  uint64_t taken = 0;
+  for (int r = 0; r < topk_groups; ++r) {
+    int best = -1;
+    float bv = -FLT_MAX;
+    for (int gi = 0; gi < n_groups; ++gi) {
+      if ((taken >> gi) & 1ull) continue;
+      float gm = -FLT_MAX;
+      for (int e = gi * gs; e < (gi + 1) * gs; ++e) gm = fmaxf(gm, lrow[e * stride]);
+      if (best < 0 || gm > bv) {
+        best = gi;
+        bv = gm;
+      }
+    }
+    taken |= 1ull << best;
+  }
+  uint64_t keep = 0;
+  for (int e = 0; e < E; ++e)
+    if ((taken >> (e / gs)) & 1ull) keep |= 1ull << e;
+  return keep;
+}
+
+static constexpr int kRfThreads = 256;
+static constexpr int kRfLds = 160 * 1024;
+
+// Slice depth: the largest power of two up to 256 whose slice (TB rows of x and SK
+// rows of W_g) stays within 20 KB, but at least one 1 KB copy per wave of x; W_g's
+// region is padded to whole copies per wave (the padding is never read).
+template <int TB, int E8>
+struct RouteFused {
+  static constexpr int EP = 8 * E8;                               // experts, padded to 8
+  static constexpr int NT = EP <= 16 ? 1 : EP / 16;               // 16-expert MFMA tiles
+  static constexpr int SK0 = 20480 / (2 * (TB + EP));
+  static constexpr int SKa = SK0 >= 256 ? 256 : SK0 >= 128 ? 128 : 64;
+  static constexpr int SK = TB * SKa * 2 >= 4096 ? SKa : 4096 / (2 * TB);
+  static constexpr int XB = TB * SK * 2;                          // x bytes per slice
+  static constexpr int CX = XB / 4096;                            // x copies per wave
+  static constexpr int CW = (SK * EP * 2 + 4095) / 4096;          // W_g copies per wave
+  static constexpr int WB = CW * 4096;                            // W_g region per slice
+  static constexpr int kSlot = XB + WB + 256;                     // + tr-read overrun slack
+  static constexpr int NS = (kRfLds / kSlot) < 12 ? (kRfLds / kSlot) : 12;
+  static constexpr int CPW = CX + CW;
+  static constexpr int KS = SK / 32;                              // 32-deep steps per slice
+  static constexpr int SWZ = (SK / 8 - 1) < 15 ? SK / 8 - 1 : 15;  // x chunk swizzle mask
+  static_assert(CX >= 1 && XB % 4096 == 0, "x copy split");
+  static_assert(NS >= 3 && (NS - 2) * CPW <= 63, "ring depth");
+  static_assert(KS == 2 || KS == 4 || KS == 8, "steps per slice");
+  static_assert(4 * TB * 16 * NT * 4 + TB * 16 * NT * 4 + TB * 8 <= NS * kSlot,
+                "reduction space");
+};
+
+template <int TB, int E8>
+__global__ void __launch_bounds__(kRfThreads, 1)
+k_route_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+              const float* __restrict__ bias, int T, int d, int E, int k, int n_groups,
+              int topk_groups, int renormalize, float* __restrict__ logits_out,
+              int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  using C = RouteFused<TB, E8>;
+  constexpr int SK = C::SK, NS = C::NS, CX = C::CX, CW = C::CW, KS = C::KS;
+  constexpr int NT = C::NT;
+  constexpr int kPitch = SK * 2;                  // bytes per staged x row
+  __shared__ __align__(1024) unsigned char lds[NS * C::kSlot];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = blockIdx.x * TB;
+  const int nsl = d / SK;
+  const int wrow = E * 2;                          // bytes per W_g row
+
+  // per-lane global offsets of this wave's copies (the same in every slice)
+  uint32_t xoff[CX], woff[CW];
+#pragma unroll
+  for (int c = 0; c < CX; ++c) {
+    const int p = (wave * CX + c) * 1024 + lane * 16;   // byte position in the x region
+    const int row = p / kPitch, pc = (p % kPitch) / 16;
+    const int lc = pc ^ (row & C::SWZ);                       // logical 16-byte chunk
+    const int rowc = min(t0 + row, T - 1) - t0;
+    xoff[c] = (uint32_t)(rowc * d * 2 + lc * 16);
+  }
+  const int wslice = SK * wrow;                    // real W_g bytes per slice
+#pragma unroll
+  for (int c = 0; c < CW; ++c)
+    woff[c] = (uint32_t)min(((wave * CW + c) * 64 + lane) * 16, wslice - 16);
+
+  // Blocks start at different slices (block b at slice b mod nsl, then wrapping round),
+  // so that blocks running at the same time read different pieces of W_g rather than
+  // all reading one piece from the same few L2 channels.  Each block's order is fixed.
+  const int rot = blockIdx.x % nsl;
+  auto issue = [&](int j) {                        // slice j of this block into slot j % NS
+    int js = min(j, nsl - 1) + rot;
+    if (js >= nsl) js -= nsl;
+    unsigned char* slot = lds + (j % NS) * C::kSlot;
+    const bf16_t* xb = uniform_ptr(x + (size_t)t0 * d + (size_t)js * SK);
+    const bf16_t* wb = uniform_ptr(wg + (size_t)js * SK * E);
+#pragma unroll
+    for (int c = 0; c < CX; ++c) copy16_to_lds(xb, xoff[c], slot + (wave * CX + c) * 1024);
+#pragma unroll
+    for (int c = 0; c < CW; ++c) copy16_to_lds(wb, woff[c], slot + C::XB + (wave * CW + c) * 1024);
+  };
+
+  // fragment addresses inside a slot
+  const int g = lane >> 4, r16 = lane & 15;
+  const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+  f32x4_t acc[TB / 16][NT];
+#pragma unroll
+  for (int ts = 0; ts < TB / 16; ++ts)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[ts][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j) issue(j);
+  for (int j = 0; j < nsl; ++j) {
+    MOE_WAIT_VMCNT((NS - 2) * (CX + CW));
+    __syncthreads();
+    issue(j + NS - 1);
+    const unsigned char* slot = lds + (j % NS) * C::kSlot;
+    const unsigned char* wl = slot + C::XB;
+#pragma unroll
+    for (int q = 0; q < (KS + 3) / 4; ++q) {
+      const int kk = wave + 4 * q;                 // this wave's 32-deep step
+      if (KS < 4 && kk >= KS) break;
+      bf16x8_t bop[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const unsigned char* bp = wl + (kk * 32 + g * 8 + tr_r) * wrow + nt * 32 + tr_c * 8;
+        const i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)bp);
+        const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(bp + 4 * wrow));
+        bop[nt] = __builtin_bit_cast(bf16x8_t,
+                                     __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int ts = 0; ts < TB / 16; ++ts) {
+        const int row = ts * 16 + r16;
+        const int pc = (kk * 4 + g) ^ (row & C::SWZ);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(slot + row * kPitch + pc * 16);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[ts][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[nt], acc[ts][nt], 0, 0, 0);
+      }
+    }
+  }
+  MOE_WAIT_VMCNT(0);                               // the copies past the last slice
+  __syncthreads();
+
+  // partial logits of each wave -> LDS [wave][TB][16 NT]; then the sum in wave order,
+  // plus the bias, into lg[e][TB] (token-minor, so that lane tt reads its token's
+  // logits from consecutive addresses)
+  constexpr int EP = 16 * NT;             // columns of the partial-logit tiles
+  float* red = reinterpret_cast<float*>(lds);
+  float* lg = red + 4 * TB * EP;
+#pragma unroll
+  for (int ts = 0; ts < TB / 16; ++ts)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        red[(wave * TB + ts * 16 + g * 4 + i) * EP + nt * 16 + r16] = acc[ts][nt][i];
+  __syncthreads();
+  for (int i = tid; i < TB * E; i += kRfThreads) {
+    const int tt = i / E, e = i % E;
+    float v = red[(0 * TB + tt) * EP + e];
+    v += red[(1 * TB + tt) * EP + e];
+    v += red[(2 * TB + tt) * EP + e];
+    v += red[(3 * TB + tt) * EP + e];
+    if (bias) v += bias[e];
+    lg[e * TB + tt] = v;
+    if (logits_out && t0 + tt < T) logits_out[(size_t)(t0 + tt) * E + e] = v;
+  }
+  __syncthreads();
+  // group-limited eligibility, one lane per token, as a mask in LDS (after lg)
+  uint64_t* keep_s = reinterpret_cast<uint64_t*>(lg + TB * EP);
+  if (n_groups > 0 && tid < TB)
+    keep_s[tid] = group_keep_mask(lg + tid, TB, E, n_groups, topk_groups);
+  __syncthreads();
+  // selection: G = 256 / TB lanes per token (all tokens in one pass), lane lt holding
+  // experts lt + G*r
+  constexpr int G = kRfThreads / TB;
+  constexpr int PER = (EP + G - 1) / G;
+  const int tt = tid / G, lt = tid % G;
+  const int t = t0 + tt;
+  const bool live = t < T;
+  bool has[PER], elig[PER];
+  float l[PER], z[PER], S;
+  {
+    // the token's logits, token-minor in lg: expert e at lg[e * TB + tt]
+    float m = -FLT_MAX;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int e = lt + G * r;
+      has[r] = e < E;
+      l[r] = has[r] ? lg[e * TB + tt] : -FLT_MAX;
+      if (has[r]) m = fmaxf(m, l[r]);
+    }
+    m = group_max<G>(m);
+    float zs = 0.f;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      z[r] = has[r] ? expf(l[r] - m) : 0.f;
+      zs += z[r];
+    }
+    S = group_sum<G>(zs);
+  }
+  const uint64_t keep = n_groups > 0 ? keep_s[tt] : ~0ull;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) elig[r] = has[r] && ((keep >> (lt + G * r)) & 1ull);
+  select_rounds<G, PER>(l, z, elig, S, k, renormalize, live, live ? t : T - 1, lt, lane - lt,
+                        topk_idx, topk_w);
+}
+
+// The fused router applies to bf16, E a multiple of 8 up to 64 and T >= 4096 (at least
+// 256 blocks of 16 tokens), with d a multiple of the slice depth; 16, 32 or 64 tokens
+// per block as T grows.
+static int e8_of(int E) { return E <= 8 ? 1 : E <= 16 ? 2 : E <= 32 ? 4 : 8; }
+
+static int route_fused_sk(int tb, int E) {
+  switch (tb * 16 + e8_of(E)) {
+#define MOE_RF_SK(TBV, E8V) case TBV * 16 + E8V: return RouteFused<TBV, E8V>::SK;
+    MOE_RF_SK(16, 1) MOE_RF_SK(16, 2) MOE_RF_SK(16, 4) MOE_RF_SK(16, 8)
+    MOE_RF_SK(32, 1) MOE_RF_SK(32, 2) MOE_RF_SK(32, 4) MOE_RF_SK(32, 8)
+    MOE_RF_SK(64, 1) MOE_RF_SK(64, 2) MOE_RF_SK(64, 4) MOE_RF_SK(64, 8)
+#undef MOE_RF_SK
+    default: return 1 << 30;
+  }
+}
+
+static int route_fused_tb(const moe_shape& s) {
+  if (s.dtype != MOE_DTYPE_BF16 || s.E % 8 || s.E > 64 || s.T < 4096) return 0;
+  const int tb = s.T >= 16384 ? 64 : (s.T >= 8192 ? 32 : 16);
+  // per-lane copy offsets reach tb rows of x: 32-bit byte offsets
+  if ((int64_t)tb * s.d * 2 >= ((int64_t)1 << 31)) return 0;
+  return s.d % route_fused_sk(tb, s.E) == 0 ? tb : 0;
+}
+
+bool route_is_fused(const moe_shape& s) { return route_fused_tb(s) > 0; }
+
+template <int TB, int E8>
+static void launch_route_fused_tb(const moe_shape& s, const bf16_t* x, const bf16_t* wg,
+                                  const float* bias, float* logits, int32_t* topk_idx,
+                                  float* topk_w, hipStream_t st) {
+  const dim3 grid((unsigned)ceil_div(s.T, TB));
+  hipLaunchKernelGGL((k_route_fused<TB, E8>), grid, dim3(kRfThreads), 0, st, x, wg, bias, s.T, s.d,
+                     s.E, s.k, s.n_groups, s.topk_groups, s.renormalize, logits, topk_idx, topk_w);
+}
+
 moe_status launch_route(const moe_shape& s, const void* x, const void* w_gate, const float* bias,
                         float* logits, int32_t* topk_idx, float* topk_w, float* partial,
                         hipStream_t st) {
+  if (const int tb = route_fused_tb(s)) {
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* wb = static_cast<const bf16_t*>(w_gate);
+    const int e8 = e8_of(s.E);
+#define MOE_RF_TB(TBV)                                                                      \
+  do {                                                                                      \
+    if (e8 == 1) launch_route_fused_tb<TBV, 1>(s, xb, wb, bias, logits, topk_idx, topk_w, st); \
+    else if (e8 == 2) launch_route_fused_tb<TBV, 2>(s, xb, wb, bias, logits, topk_idx, topk_w, st); \
+    else if (e8 == 4) launch_route_fused_tb<TBV, 4>(s, xb, wb, bias, logits, topk_idx, topk_w, st); \
+    else launch_route_fused_tb<TBV, 8>(s, xb, wb, bias, logits, topk_idx, topk_w, st);     \
+  } while (0)
+    if (tb == 16) MOE_RF_TB(16);
+    else if (tb == 32) MOE_RF_TB(32);
+    else MOE_RF_TB(64);
+#undef MOE_RF_TB
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  }
   const int nsplit = router_nsplit(s);
   if (s.dtype == MOE_DTYPE_BF16) {
     const int ntb = route_ntb(s);

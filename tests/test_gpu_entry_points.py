@@ -126,6 +126,17 @@ def test_offsets_out_of_range_ids_set_the_flag():
     (77, 640, 20, 5, 0, 0, False, "bf16"),       # 32 lanes per token
     (4500, 256, 96, 6, 0, 0, False, "bf16"),     # many token blocks: all experts per block
     (4100, 264, 8, 2, 0, 0, True, "bf16"),       # many token blocks, K tail in a window
+    # the fused router (one block per 16 / 32 / 64 tokens, whole K, selection in the
+    # block): every tile configuration, token tails, E not a multiple of 16, group limits
+    (4096, 512, 8, 2, 0, 0, False, "bf16"),
+    (5000, 768, 32, 4, 0, 0, False, "bf16"),
+    (4104, 1024, 64, 6, 0, 0, True, "bf16"),
+    (8192, 1024, 64, 6, 0, 0, True, "bf16"),
+    (9000, 384, 24, 3, 0, 0, False, "bf16"),
+    (8200, 512, 16, 4, 4, 2, True, "bf16"),
+    (16384, 256, 16, 4, 4, 2, True, "bf16"),
+    (16390, 256, 40, 8, 8, 4, False, "bf16"),
+    (16400, 384, 32, 5, 0, 0, True, "bf16"),
 ])
 def test_route_standalone(T, d, E, k, ng, tg, renorm, dtype):
     g = torch.Generator(device=DEV)
@@ -154,9 +165,11 @@ def test_route_standalone(T, d, E, k, ng, tg, renorm, dtype):
     assert torch.equal(idx, idx2) and torch.equal(w, w2)
 
 
-def test_route_exact_ties_go_to_the_lower_id():
-    """Duplicated router columns give bitwise-equal logits; the lower id must win."""
-    T, d, E, k = 64, 256, 16, 4
+@pytest.mark.parametrize("T", [64, 4096])
+def test_route_exact_ties_go_to_the_lower_id(T):
+    """Duplicated router columns give bitwise-equal logits; the lower id must win (the
+    split-K router with its selection kernel, and the fused router)."""
+    d, E, k = 256, 16, 4
     g = torch.Generator(device=DEV)
     g.manual_seed(5)
     x = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
