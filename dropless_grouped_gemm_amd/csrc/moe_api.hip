@@ -394,17 +394,21 @@ static moe_status run_fp8_op(const moe_shape& s, int op, const void* A, const ui
   GemmSegmentsF8 g{A, Q0, S0, Q1, S1, C, K, N, meta, nblk, mb,
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                    row_src, s.k, s.T};
+  // experts averaging at most 64 rows (decode): the launch streams weights, and the
+  // 64-row kernel reads them in wider rows
+  const int64_t M = (int64_t)s.T * s.k;
+  const bool few = mb > 0 ? M <= 64 * (M < s.E ? M : (int64_t)s.E) : s.T <= 64;
   if (shared && Ks == K && Ns == N) {
     g.Ad = As; g.Q0d = Q0s; g.S0d = S0s; g.Q1d = Q1s; g.S1d = S1s; g.Cd = Cs; g.dense_rows = s.T;
-    return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), st);
+    return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), few, st);
   }
   if (shared) {
     GemmSegmentsF8 d{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Ks, Ns, nullptr, nullptr,
                      0, As, Q0s, S0s, Q1s, S1s, Cs, s.T, nullptr, 1, 1};
-    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, s.T, st);
+    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, s.T, s.T <= 64, st);
     if (st2 != MOE_OK) return st2;
   }
-  return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), st);
+  return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), few, st);
 }
 
 moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, const uint8_t* Q0,

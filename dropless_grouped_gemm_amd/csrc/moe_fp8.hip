@@ -20,6 +20,9 @@
 #include "moe_gemm_common.h"
 
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
 
 namespace moe {
 
@@ -404,14 +407,301 @@ k_gg_fp8w(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped GEMM with fp8 B for few rows per expert (decode): the launch streams the
+// weights, so a work item is 64 rows (a half of a 128-row block; halves without valid
+// rows are skipped, 32-row subtiles without valid rows are not multiplied) and wide
+// columns: 512 act columns for gate/up (512 bytes of each of W1 and W3 per k row) and
+// 1024 columns for down (1 KB per k row), so that every 32-deep slice moves 32 KB of
+// weights as 1 KB copies of one or two rows - the memory shape of the bf16 128-row
+// kernel, which streams its weights near 6.1 TB/s.  8 waves; wave w owns 64 act columns
+// (gate/up: W1 and the matching W3 columns) or 128 down columns, two 32-row subtiles x
+// four 32-column tiles of v_mfma_f32_32x32x16_bf16.  Fragments are dequantised in
+// registers as in k_gg_fp8w.
+// ---------------------------------------------------------------------------
+static constexpr int kDRows = 64;                          // rows per work item
+static constexpr int kDABytes = kDRows * kFBK * 2;        // 4 KB of A per slice
+static constexpr int kDBBytes = 32 * 1024;                // 32 KB of B per slice
+static constexpr int kDStage = kDABytes + kDBBytes;       // 36 KB
+static constexpr int kDStages = 4;
+static constexpr int kDBCopies = kDBBytes / 1024 / 8;     // 4 B copies per wave per slice
+
+template <int OP>
+__global__ void __launch_bounds__(kFThreads, 1)
+k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
+          const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
+          int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles) {
+  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU;
+  constexpr int kOutCols = GU ? 512 : 1024;               // output columns per item
+  constexpr int kPitch = GU ? 512 : 1024;                 // bytes per staged B row (per matrix)
+  __shared__ __align__(1024) unsigned char lds[kDStages * kDStage];
+  // the item's block scales: [kb][8] (gate/up: W1 n-blocks 0..3 of the tile, then W3's;
+  // down: n-blocks 0..7)
+  __shared__ float s_scale[kFMaxKB * 8];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb_dense = (dense_rows + 127) / 128;
+  const int nblocks = nb_dense + (max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0);
+  // items (half, block, column tile), half outermost: decode blocks rarely have a second
+  // half, and with the half inner a persistent grid would give some work groups only
+  // empty items
+  const int per_half = nblocks * n_tiles;
+  const int total = 2 * per_half;
+  const int nk = K / kFBK;
+  const int KB = (K + kQBlock - 1) / kQBlock, NBq = (N + kQBlock - 1) / kQBlock;
+  const bool has_a = wave < kDABytes / 1024;               // waves 0..3 copy A
+
+  // B fragment reads (ds_read_b64_tr_b8, as k_gg_fp8w): 16-lane group g, lane gi; tile j
+  // of the wave: matrix region and first column within it.
+  const int g = lane >> 4, gi = lane & 15;
+  uint32_t b_lane[4];
+  int sidx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int region = GU ? (j >> 1) : 0;                 // gate/up: W1 for j < 2, W3 after
+    const int col0 = GU ? wave * 64 + (j & 1) * 32 : wave * 128 + j * 32;
+    const int k = 8 * (g >> 1) + (gi >> 1);               // row within a 16-deep step
+    const int chunk = col0 / 16 + (g & 1);
+    b_lane[j] = (uint32_t)(region * (kDBBytes / 2) + k * kPitch + (chunk ^ (k & 15)) * 16 +
+                           (gi & 1) * 8);
+    sidx[j] = GU ? region * 4 + (col0 >> 7) : (col0 >> 7);
+  }
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int half = w / per_half;
+    const int rem = w - half * per_half;
+    const int nt = rem % n_tiles;
+    const int blk = rem / n_tiles;
+    const bool in_dense = blk < nb_dense;
+    Tile tile;
+    if (in_dense) {
+      if (!decode_block(blk, half, kDRows, 128, nullptr, dense_rows, 1, dense_rows, tile)) continue;
+    } else {
+      if (!decode_block(blk - nb_dense, half, kDRows, 128, meta, 0, E, max_rows, tile)) continue;
+    }
+    const GGOperandsF8& ops = in_dense ? dense : routed;
+    bf16_t* const C = ops.base.C;
+    const int n0 = nt * kOutCols;
+    const int e = tile.e;
+
+    // block scales of this item's columns, every k-block
+    {
+      const float* s0 = ops.S0 + (size_t)e * KB * NBq;
+      const float* s1 = GU ? ops.S1 + (size_t)e * KB * NBq : s0;
+      for (int i = tid; i < KB * 8; i += kFThreads) {
+        const int kb = i >> 3, slot = i & 7;
+        const int nb = (n0 >> 7) + (GU ? (slot & 3) : slot);
+        const float* sp = (GU && slot >= 4) ? s1 : s0;
+        s_scale[i] = nb < NBq ? sp[(size_t)kb * NBq + nb] : 1.0f;
+      }
+    }
+
+    // A copy (waves 0..3, one per slice): 16 rows x 64 bytes; rows past valid_m copy
+    // row 0, gathered rows come from x.
+    const bf16_t* asrc = ops.base.A + (size_t)tile.m0 * K;
+    uint32_t a_voff = 0;
+    if (has_a) {
+      const int row = wave * 16 + (lane >> 2);
+      const int c = swz_a(row, lane & 3);
+      const int rr = row < tile.valid ? row : 0;
+      const int src = ops.base.gather ? gather_row(ops.base, tile.m0 + rr) : rr;
+      a_voff = (uint32_t)(src * K + c * 8) * 2u;
+    }
+    asrc = uniform_ptr(ops.base.gather ? ops.base.A : asrc);
+    // B copies: copy u = 4 wave + p of 32.  Gate/up: region u / 16 (W1, W3), rows
+    // 2 (u % 16) and 2 (u % 16) + 1 of the region, 32 lanes per 512-byte row; down:
+    // row u, 64 lanes per 1 KB row.  The logical chunk of lane l is its position
+    // XOR (k & 15); columns past N copy column 0.
+    const uint8_t* qb[2];
+    qb[0] = ops.Q0 + (size_t)e * K * N;
+    qb[1] = GU ? ops.Q1 + (size_t)e * K * N : qb[0];
+    uint32_t b_voff[kDBCopies];
+    int b_row[kDBCopies];
+#pragma unroll
+    for (int p = 0; p < kDBCopies; ++p) {
+      const int u = wave * kDBCopies + p;
+      int k, pos;
+      if (GU) {
+        k = 2 * (u & 15) + (lane >> 5);
+        pos = lane & 31;
+      } else {
+        k = u;
+        pos = lane;
+      }
+      int col = n0 + (pos ^ (k & 15)) * 16;
+      if (col >= N) col = 0;
+      b_row[p] = GU ? 2 * (u & 15) : u;
+      b_voff[p] = (uint32_t)((k - b_row[p]) * N + col);
+    }
+    const uint8_t* bsrc = uniform_ptr(qb[GU ? (wave * kDBCopies) >> 4 : 0]);
+    auto issue = [&](int ks, int slot) {
+      unsigned char* st = lds + slot * kDStage;
+      const int k0 = ks * kFBK;
+      if (has_a) copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
+#pragma unroll
+      for (int p = 0; p < kDBCopies; ++p) {
+        const int u = wave * kDBCopies + p;
+        copy16_to_lds(bsrc + (size_t)(k0 + b_row[p]) * N, b_voff[p], st + kDABytes + u * 1024);
+      }
+    };
+    // every copy a wave has issued lands in order: wait until at most n slices of its
+    // copies are outstanding (waves 0..3 issue one more copy per slice)
+    auto wait_slices = [&](auto n_c) {
+      constexpr int n = decltype(n_c)::value;
+      if (has_a) MOE_WAIT_VMCNT(n * (kDBCopies + 1));
+      else MOE_WAIT_VMCNT(n * kDBCopies);
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    const int nsub = __builtin_amdgcn_readfirstlane(min(2, (tile.valid + 31) >> 5));
+    bf16x8_t af[2], bf[4];
+    auto read_frags = [&](int ks, int kk) {
+      const unsigned char* sa = lds + (ks % kDStages) * kDStage;
+      const unsigned char* sb = sa + kDABytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i >= nsub) break;
+        const int row = i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
+      }
+      const int kb = (ks * kFBK) >> 7;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (MOE_LDS v2i*)(sb + b_lane[j] + kk * 16 * kPitch));
+        const float sc = s_scale[kb * 8 + sidx[j]];
+        bf16x8_t o;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], false);   // bytes 0, 1
+          const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], true);    // bytes 2, 3
+          o[4 * h + 0] = static_cast<__bf16>(f0[0] * sc);
+          o[4 * h + 1] = static_cast<__bf16>(f0[1] * sc);
+          o[4 * h + 2] = static_cast<__bf16>(f1[0] * sc);
+          o[4 * h + 3] = static_cast<__bf16>(f1[1] * sc);
+        }
+        bf[j] = o;
+      }
+    };
+    auto mfma_block = [&]() {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i >= nsub) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    // Prologue: every slot in flight (slices past the end re-copy the last slice into a
+    // slot that is never read), then wait for slice 0; the barrier also publishes the
+    // scale table.
+#pragma unroll
+    for (int p = 0; p < kDStages; ++p) issue(min(p, nk - 1), p);
+    wait_slices(std::integral_constant<int, kDStages - 1>{});
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks > 0) issue(min(ks - 1 + kDStages, nk - 1), (ks - 1) % kDStages);
+      read_frags(ks, 0);
+      mfma_block();
+      read_frags(ks, 1);
+      mfma_block();
+      if (ks + 1 < nk) {
+        wait_slices(std::integral_constant<int, kDStages - 2>{});   // slice ks+1 has landed
+        __syncthreads();
+      }
+    }
+    MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
+    __syncthreads();
+
+    // Epilogue through LDS: bf16 staging per wave (64 rows x 64 act / 128 down columns),
+    // 16-byte stores of valid rows and columns.
+    constexpr int kWCols = GU ? 64 : 128;
+    constexpr int kLd = kWCols + 8;
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kDRows * kLd;
+    const int col0 = n0 + wave * kWCols;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i >= nsub) break;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        if (GU) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            stg[r * kLd + j * 32 + (lane & 31)] =
+                f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            stg[r * kLd + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][q]);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int kChunks = kWCols / 8;
+    constexpr int kRowsPerPass = 64 / kChunks;
+    const int nrows = nsub * 32;
+    for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
+      const int r = r0 + lane / kChunks;
+      const int ch = lane % kChunks;
+      const int gcol = col0 + ch * 8;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + ch * 8);
+      if (r < tile.valid && gcol < N)
+        *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + r) * N + gcol) = v;
+    }
+    __syncthreads();  // staging and scale reads done before the next item refills
+  }
+}
+
 bool fp8_gemm_supported(int K, int N) {
   return K % kFBK == 0 && N % 16 == 0 && ceil_div(K, kQBlock) <= kFMaxKB;
 }
 
 moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64_t max_rows,
-                                   hipStream_t st) {
+                                   bool few_rows, hipStream_t st) {
   const bool routed = g.max_blocks > 0, dense = g.dense_rows > 0;
   if (!routed && !dense) return MOE_OK;
+  // MOE_FP8_ITEM_ROWS=64 or 128 forces one kernel (tests run both on the same shapes)
+  if (const char* f = getenv("MOE_FP8_ITEM_ROWS")) {
+    if (strcmp(f, "64") == 0) few_rows = true;
+    if (strcmp(f, "128") == 0) few_rows = false;
+  }
+  const GGOperandsF8 rd{{static_cast<const bf16_t*>(g.A), nullptr, nullptr, static_cast<bf16_t*>(g.C),
+                         g.gather, g.gather_div, g.gather_rows},
+                        g.Q0, g.Q1, g.S0, g.S1};
+  const GGOperandsF8 dd{{static_cast<const bf16_t*>(g.Ad), nullptr, nullptr, static_cast<bf16_t*>(g.Cd),
+                         nullptr, 1, 1},
+                        g.Q0d, g.Q1d, g.S0d, g.S1d};
+  if (few_rows) {
+    const int n_tiles = (int)ceil_div(g.N, op == MOE_OP_GATEUP_SWIGLU ? 512 : 1024);
+    const int64_t blocks_ub = (routed ? (int64_t)g.max_blocks : 0) +
+                              (dense ? ceil_div(g.dense_rows, 128) : 0);
+    const int64_t items = blocks_ub * 2 * n_tiles;
+    const int cus = device_cu_count();
+    int64_t grid = items < cus ? items : cus;
+    if (grid < 1) grid = 1;
+    if (op == MOE_OP_GATEUP_SWIGLU)
+      hipLaunchKernelGGL(k_gg_fp8d<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kFThreads), 0,
+                         st, rd, dd, g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E,
+                         max_rows, g.dense_rows, n_tiles);
+    else
+      hipLaunchKernelGGL(k_gg_fp8d<MOE_OP_DOWN>, dim3((unsigned)grid), dim3(kFThreads), 0, st, rd,
+                         dd, g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E, max_rows,
+                         g.dense_rows, n_tiles);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+  }
   const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;
   const int n_tiles = (int)ceil_div(g.N, out_cols);
   const int64_t blocks_ub = (routed ? (int64_t)g.max_blocks : 0) + (dense ? ceil_div(g.dense_rows, 128) : 0);

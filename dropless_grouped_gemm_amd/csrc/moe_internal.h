@@ -149,8 +149,10 @@ struct GemmSegmentsF8 {
   int gather_div;
   int gather_rows;
 };
+// few_rows: the 64-row kernel with wide weight rows (experts average at most 64 rows);
+// otherwise the 128-row kernel.
 moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64_t max_rows,
-                                   hipStream_t st);
+                                   bool few_rows, hipStream_t st);
 
 // Backward kernels (moe_backward.hip).
 // dy[pos[t,j]] = w[t,j] dout[t] (bf16), dw[t,j] = <dout[t], y[pos[t,j]]> (fp32); d <= 8192.

@@ -70,8 +70,14 @@ def _routes(T, E, k, seed):
     (64, 1024, 16, 4, 128, 0),       # decode-like: few rows per expert
     (150, 256, 4, 2, 384, 128),      # shared expert in launches of its own; ragged n-blocks
     (40, 1280, 3, 3, 160, 0),        # partial 128-blocks in both k and n
+    (300, 256, 2, 1, 1056, 96),      # blocks of 128 valid rows: both 64-row halves; N tails
+    (64, 2048, 64, 8, 768, 768),     # decode-like: 512 rows over 64 experts + shared
 ])
-def test_grouped_gemm_fp8_against_oracle(T, d, E, k, d_e, d_es):
+@pytest.mark.parametrize("item_rows", ["64", "128"])
+def test_grouped_gemm_fp8_against_oracle(T, d, E, k, d_e, d_es, item_rows, monkeypatch):
+    """Both fp8 kernels (64-row items with wide weight rows, 128-row items) on every
+    shape, forced with MOE_FP8_ITEM_ROWS."""
+    monkeypatch.setenv("MOE_FP8_ITEM_ROWS", item_rows)
     idx = _routes(T, E, k, T + d)
     g = torch.Generator(device=DEV)
     g.manual_seed(T + d_e)
