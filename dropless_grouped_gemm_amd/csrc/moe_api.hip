@@ -394,21 +394,28 @@ static moe_status run_fp8_op(const moe_shape& s, int op, const void* A, const ui
   GemmSegmentsF8 g{A, Q0, S0, Q1, S1, C, K, N, meta, nblk, mb,
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                    row_src, s.k, s.T};
-  // experts averaging at most 64 rows (decode): the launch streams weights, and the
-  // 64-row kernel reads them in wider rows
+  // Experts averaging at most 64 rows (decode): the launch streams weights, and the
+  // 64-row kernel reads them in wider rows.  At least 256 rows (and a block table the
+  // wide kernel takes): compute-bound, the wide kernel with in-register dequantisation.
+  // In between: 128-row items.
   const int64_t M = (int64_t)s.T * s.k;
-  const bool few = mb > 0 ? M <= 64 * (M < s.E ? M : (int64_t)s.E) : s.T <= 64;
+  const int64_t act = M < s.E ? M : (int64_t)s.E;
+  const Fp8Kernel kind = mb > 0 ? (M <= 64 * act ? kFp8Rows64
+                                   : (M >= 256 * act && mb <= wide_max_blocks()) ? kFp8Wide
+                                   : kFp8Rows128)
+                                : (s.T <= 64 ? kFp8Rows64 : s.T >= 384 ? kFp8Wide : kFp8Rows128);
   if (shared && Ks == K && Ns == N) {
     g.Ad = As; g.Q0d = Q0s; g.S0d = S0s; g.Q1d = Q1s; g.S1d = S1s; g.Cd = Cs; g.dense_rows = s.T;
-    return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), few, st);
+    return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), kind, st);
   }
   if (shared) {
     GemmSegmentsF8 d{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Ks, Ns, nullptr, nullptr,
                      0, As, Q0s, S0s, Q1s, S1s, Cs, s.T, nullptr, 1, 1};
-    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, s.T, s.T <= 64, st);
+    const Fp8Kernel dk = s.T <= 64 ? kFp8Rows64 : s.T >= 384 ? kFp8Wide : kFp8Rows128;
+    moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, s.T, dk, st);
     if (st2 != MOE_OK) return st2;
   }
-  return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), few, st);
+  return launch_grouped_gemm_fp8(op, g, s.E, max_rows_of(s), kind, st);
 }
 
 moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, const uint8_t* Q0,
@@ -464,10 +471,13 @@ static moe_status run_bf16_experts(const moe_shape& s, const void* x, char* base
 }
 
 // With fp8 weights, where experts average at least 256 rows (the wide bf16 kernel's
-// regime, compute-bound), the layer dequantises the weights once into its workspace and
-// runs the bf16 kernels: the same bf16 weights as the fp8 kernels' own in-register
-// dequantisation; below that (decode-like routing, weight streaming) the fp8 kernels
-// read half the bytes.
+// regime, compute-bound) and the workspace has room for them, the layer dequantises the
+// weights once into its workspace and runs the bf16 kernels: the same bf16 weights as the
+// fp8 kernels' own in-register dequantisation, and faster than the wide kernel doing that
+// dequantisation itself (its 192 accumulator registers leave the extra conversions no
+// room to hide).  With a workspace of moe_workspace_bytes only, the wide kernel
+// dequantises in registers; below 256 rows (decode-like routing, weight streaming) the
+// fp8 kernels read half the bytes.
 static bool fp8_dequantised_path(const moe_shape& s) {
   const int64_t M = (int64_t)s.T * s.k;
   return M > 0 && M >= 256 * (M < s.E ? M : (int64_t)s.E);
@@ -542,7 +552,8 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
   layout_of(*s, L);
   Fp8Layout F8;
   fp8_layout_of(*s, L, F8);
-  if (!ws || !aligned16(ws) || ws_bytes < F8.total) return MOE_EWORKSPACE;
+  // at least the intermediates; the dequantised weights only where there is room
+  if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -569,7 +580,7 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
     st = launch_permute(*s, x, pos, at(L.x_perm), hs);
     if (st != MOE_OK) return st;
   }
-  if (fp8_dequantised_path(*s)) {
+  if (fp8_dequantised_path(*s) && ws_bytes >= F8.total) {
     const int E = s->E, d = s->d, de = s->d_e, des = s->d_e_shared;
     st = launch_dequantize_fp8(E, d, de, q1, s1, at(F8.w1), hs);
     if (st == MOE_OK) st = launch_dequantize_fp8(E, d, de, q3, s3, at(F8.w3), hs);
@@ -633,6 +644,9 @@ moe_status moe_layer_fwd(const moe_shape* s, const void* x, const void* w_gate, 
     return MOE_EINVAL;
   moe_ws_layout L;
   layout_of(*s, L);
+  Fp8Layout F8;
+  fp8_layout_of(*s, L, F8);
+  // at least the intermediates; the dequantised weights only where there is room
   if (!ws || !aligned16(ws) || ws_bytes < L.total) return MOE_EWORKSPACE;
   if (s->T == 0) return MOE_OK;
 

@@ -670,13 +670,30 @@ bool fp8_gemm_supported(int K, int N) {
 }
 
 moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64_t max_rows,
-                                   bool few_rows, hipStream_t st) {
+                                   Fp8Kernel kind, hipStream_t st) {
   const bool routed = g.max_blocks > 0, dense = g.dense_rows > 0;
   if (!routed && !dense) return MOE_OK;
-  // MOE_FP8_ITEM_ROWS=64 or 128 forces one kernel (tests run both on the same shapes)
+  // MOE_FP8_ITEM_ROWS=64, 128 or 384 forces one kernel (tests run each on the same
+  // shapes; 384 needs a block table of at most wide_max_blocks() entries)
   if (const char* f = getenv("MOE_FP8_ITEM_ROWS")) {
-    if (strcmp(f, "64") == 0) few_rows = true;
-    if (strcmp(f, "128") == 0) few_rows = false;
+    if (strcmp(f, "64") == 0) kind = kFp8Rows64;
+    if (strcmp(f, "128") == 0) kind = kFp8Rows128;
+    if (strcmp(f, "384") == 0 && g.max_blocks <= wide_max_blocks()) kind = kFp8Wide;
+  }
+  const bool few_rows = kind == kFp8Rows64;
+  if (kind == kFp8Wide) {
+    GGOperands ro{static_cast<const bf16_t*>(g.A), reinterpret_cast<const bf16_t*>(g.Q0),
+                  reinterpret_cast<const bf16_t*>(g.Q1), static_cast<bf16_t*>(g.C), g.gather,
+                  g.gather_div, g.gather_rows, nullptr};
+    ro.S0 = g.S0;
+    ro.S1 = g.S1;
+    GGOperands dn{static_cast<const bf16_t*>(g.Ad), reinterpret_cast<const bf16_t*>(g.Q0d),
+                  reinterpret_cast<const bf16_t*>(g.Q1d), static_cast<bf16_t*>(g.Cd), nullptr, 1, 1,
+                  nullptr};
+    dn.S0 = g.S0d;
+    dn.S1 = g.S1d;
+    return launch_gg_wide(op, ro, dn, g.K, g.N, g.block_meta, g.num_blocks,
+                          routed ? g.max_blocks : 0, max_rows, E, g.dense_rows, st, true);
   }
   const GGOperandsF8 rd{{static_cast<const bf16_t*>(g.A), nullptr, nullptr, static_cast<bf16_t*>(g.C),
                          g.gather, g.gather_div, g.gather_rows},

@@ -73,6 +73,10 @@ struct GGOperands {
   int gather_rows;
   // kOpGateUpBwd only: dact [rows, N]; C is then dg | du, [rows, 2 N]
   const bf16_t* D;
+  // fp8 weights (the wide kernel's fp8 variant): B0 / B1 then point at e4m3 codes
+  // [E][K][N] and these at their fp32 scales [E][ceil(K/128)][ceil(N/128)]
+  const float* S0 = nullptr;
+  const float* S1 = nullptr;
 };
 
 // SwiGLU backward of one element from the recomputed gate g, up u and the incoming
@@ -128,8 +132,10 @@ __device__ __forceinline__ bool decode_block(int b, int sub, int sub_rows, int b
 // Wide-tile kernel (moe_gemm_wide.hip): 384-row groups of one expert's blocks x 256
 // B-columns, for block_m == 128, K % 32 == 0 and max_blocks <= wide_max_blocks().
 int wide_max_blocks();
+// fp8: B0 / B1 of both operand sets are e4m3 codes with scales S0 / S1 (forward ops).
 moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, int K, int N,
                           const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
-                          int64_t max_rows, int E, int32_t dense_rows, hipStream_t st);
+                          int64_t max_rows, int E, int32_t dense_rows, hipStream_t st,
+                          bool fp8 = false);
 
 }  // namespace moe

@@ -74,22 +74,30 @@ __device__ __forceinline__ void wide_item(int slot, int ngt, int n_tiles, int& g
   t = sc * Ts + within % tc;
 }
 
-template <int OP, int NW>
+template <int OP, int NW, bool FP8>
 __global__ void __launch_bounds__(NW * 64, 1)
 k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
           const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
           int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles) {
   constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU || OP == kOpGateUpBwd;
   constexpr bool BWD = OP == kOpGateUpBwd;
+  static_assert(!(FP8 && BWD), "fp8 weights: forward ops only");
   constexpr int NT = NW * 64;
   constexpr int WR = kWRows * 2 / NW;     // rows per wave
   constexpr int MI = WR / 32;             // 32-row subtiles per wave
+  // fp8 weights: a slice's B is half the bytes (8 KB), so a slot is 32 KB and five fit
+  constexpr int kBBytes = FP8 ? kWBBytes / 2 : kWBBytes;
+  constexpr int kStage = kWABytes + kBBytes;
+  constexpr int kStages = FP8 ? 5 : kWStages;
   constexpr int CPA = kWACopies / NW;     // copies per wave per slice
-  constexpr int CPB = kWBCopies / NW;
+  constexpr int CPB = kBBytes / 1024 / NW;
   constexpr int CPW = CPA + CPB;
   constexpr int kOutCols = GU ? 128 : 256;
-  constexpr int kBPitch = GU ? 256 : 512; // bytes per staged B row
-  static_assert(kWACopies % NW == 0 && kWBCopies % NW == 0 && WR % 32 == 0, "tile split");
+  // bytes per staged B row (per matrix region for gate/up)
+  constexpr int kBPitch = (GU ? 128 : 256) * (FP8 ? 1 : 2);
+  constexpr int kEB = FP8 ? 1 : 2;        // bytes per weight
+  static_assert(kWACopies % NW == 0 && (kBBytes / 1024) % NW == 0 && WR % 32 == 0, "tile split");
+  static_assert(kStages * kStage <= kWStages * kWStage, "ring fits the LDS array");
 
   __shared__ __align__(1024) unsigned char lds[kWStages * kWStage];
 
@@ -190,9 +198,24 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   }
 #pragma unroll
   for (int jb = 0; jb < NBL; ++jb) {
-    const int cj = (GU ? ch * 64 + jb * 32 : ch * 128 + jb * 32) >> 3;
-    const int chunk = (cj ^ (4 * tr_r)) | (2 * (g & 1) + (tr_c4 >> 1));
-    b_lane[jb] = (uint32_t)(((g >> 1) * 8 + tr_r) * kBPitch + chunk * 16 + (tr_c4 & 1) * 8);
+    if constexpr (FP8) {
+      // ds_read_b64_tr_b8: in 16-lane group g, lane gi points at row gi / 2 of an 8-row
+      // block, bytes 8 (gi % 2) .. +7 of a 16-byte (16-column) chunk, and receives that
+      // chunk's column gi for the 8 rows: rows 8 (g >> 1) + .. (the k group of the
+      // 32x32x16 operand) and the chunk of columns 16 (g & 1) of the 32-column subtile.
+      // The fp8 chunk swizzle is c ^ (k & 7) (gate/up, 8 chunks per row) or c ^ (k & 15)
+      // (down, 16 chunks per row).
+      const int gi = lane & 15;
+      const int k = 8 * (g >> 1) + (gi >> 1);
+      const int col0 = GU ? ch * 64 + jb * 32 : ch * 128 + jb * 32;
+      const int chunk = col0 / 16 + (g & 1);
+      const int pc = chunk ^ (k & (GU ? 7 : 15));
+      b_lane[jb] = (uint32_t)(k * kBPitch + pc * 16 + (gi & 1) * 8);
+    } else {
+      const int cj = (GU ? ch * 64 + jb * 32 : ch * 128 + jb * 32) >> 3;
+      const int chunk = (cj ^ (4 * tr_r)) | (2 * (g & 1) + (tr_c4 >> 1));
+      b_lane[jb] = (uint32_t)(((g >> 1) * 8 + tr_r) * kBPitch + chunk * 16 + (tr_c4 & 1) * 8);
+    }
   }
 
   const int ngt = ng_dense + ngroups;
@@ -233,8 +256,9 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     bf16_t* const C = ops.C;
     const int n0 = nt * kOutCols;
     const bf16_t* asrc = ops.A + (size_t)m0 * K;
-    const bf16_t* b0e = ops.B0 + (size_t)e * K * N;
-    const bf16_t* b1e = GU ? ops.B1 + (size_t)e * K * N : b0e;
+    const unsigned char* b0e = reinterpret_cast<const unsigned char*>(ops.B0) + (size_t)e * K * N * kEB;
+    const unsigned char* b1e =
+        GU ? reinterpret_cast<const unsigned char*>(ops.B1) + (size_t)e * K * N * kEB : b0e;
 
     // Copies go out in two groups per slice, each behind one M0 load: the wave's A
     // windows, then its B rows.  Copy i of a group carries the immediate offset 1 KB * i,
@@ -267,40 +291,71 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     // is p's parity (CPB is even).
     const int u0 = wave * CPB;
     uint32_t b_voff[CPB];
-#pragma unroll
-    for (int p = 0; p < CPB; ++p) {
-      const int kl = GU ? (lane >> 4) : (lane >> 5);
-      const int k = GU ? kl : 2 * (p & 1) + kl;           // row within the slice, mod 4
-      const int cpos = GU ? (lane & 15) : (lane & 31);
-      int col = n0 + swz_b(k, cpos) * 8;                  // past N -> column 0
-      if (col >= N) col = 0;
-      const int rows_before = (GU ? 4 : 2) * p;           // slice rows of earlier copies
-      b_voff[p] = (uint32_t)((rows_before + kl) * N + col) * 2u + (uint32_t)(CPB - 1 - p) * 1024u;
-    }
     const unsigned char* b_gbase;
     int b_ldst;
-    if (GU) {
-      b_gbase = reinterpret_cast<const unsigned char*>((u0 < 8 ? b0e : b1e) + (size_t)4 * (u0 & 7) * N);
-      b_ldst = kWABytes + (u0 >> 3) * (kWBBytes / 2) + (u0 & 7) * 1024;
+    if constexpr (FP8) {
+      // fp8 B: one copy per wave and slice.  GATEUP: copy u < 4 moves W1 rows 8u..8u+7
+      // (u >= 4: the same rows of W3), 8 lanes per 128-byte row; DOWN: copy u moves rows
+      // 4u..4u+3, 16 lanes per 256-byte row.  Lane l's logical chunk is its position
+      // XOR the row's swizzle (k & 7, or k & 15).
+      const int rows_per = GU ? 8 : 4;
+      const int uu = GU ? (u0 & 3) : u0;
+      const int kl = GU ? (lane >> 3) : (lane >> 4);
+      const int k = rows_per * uu + kl;
+      const int cpos = GU ? (lane & 7) : (lane & 15);
+      int col = n0 + (cpos ^ (k & (GU ? 7 : 15))) * 16;   // past N -> column 0
+      if (col >= N) col = 0;
+      b_voff[0] = (uint32_t)(kl * N + col);
+      b_gbase = (GU ? (u0 < 4 ? b0e : b1e) : b0e) + (size_t)rows_per * uu * N;
+      b_ldst = kWABytes + (GU ? (u0 >> 2) * (kBBytes / 2) + uu * 1024 : u0 * 1024);
     } else {
-      b_gbase = reinterpret_cast<const unsigned char*>(b0e + (size_t)2 * u0 * N);
-      b_ldst = kWABytes + u0 * 1024;
+#pragma unroll
+      for (int p = 0; p < CPB; ++p) {
+        const int kl = GU ? (lane >> 4) : (lane >> 5);
+        const int k = GU ? kl : 2 * (p & 1) + kl;           // row within the slice, mod 4
+        const int cpos = GU ? (lane & 15) : (lane & 31);
+        int col = n0 + swz_b(k, cpos) * 8;                  // past N -> column 0
+        if (col >= N) col = 0;
+        const int rows_before = (GU ? 4 : 2) * p;           // slice rows of earlier copies
+        b_voff[p] = (uint32_t)((rows_before + kl) * N + col) * 2u + (uint32_t)(CPB - 1 - p) * 1024u;
+      }
+      if (GU) {
+        b_gbase = (u0 < 8 ? b0e : b1e) + (size_t)4 * (u0 & 7) * N * 2;
+        b_ldst = kWABytes + (u0 >> 3) * (kWBBytes / 2) + (u0 & 7) * 1024;
+      } else {
+        b_gbase = b0e + (size_t)2 * u0 * N * 2;
+        b_ldst = kWABytes + u0 * 1024;
+      }
+      b_gbase -= (CPB - 1) * 1024;
     }
-    b_gbase -= (CPB - 1) * 1024;
+    // fp8: the scales of this item's columns, one per 128-deep k-block (wave-uniform:
+    // gate/up's 64 act columns of a wave lie in one 128-column block of W1 and of W3,
+    // down's 128 columns in one block)
+    const int KBq = (K + 127) / 128, NBq = (N + 127) / 128;
+    // (read through the constant address space: wave-uniform scalar loads into SGPRs,
+    // which the copies' vmcnt waits do not count)
+    typedef const __attribute__((address_space(4))) float* cfloat_p;
+    cfloat_p sc0 = nullptr;
+    cfloat_p sc1 = nullptr;
+    if constexpr (FP8) {
+      const int nb = GU ? (n0 >> 7) : ((n0 + ch * 128) >> 7);
+      sc0 = (cfloat_p)uniform_ptr(ops.S0 + (size_t)e * KBq * NBq + nb);
+      sc1 = GU ? (cfloat_p)uniform_ptr(ops.S1 + (size_t)e * KBq * NBq + nb) : sc0;
+    }
     // copy i of slice ks's A group (i == 0 loads M0 first) into ring slot `slot`
     auto issue_a = [&](int ks, int slot, int i) {
-      if (i == 0) set_lds_dma_base(lds + slot * kWStage + a_ldst);
+      if (i == 0) set_lds_dma_base(lds + slot * kStage + a_ldst);
       copy16_to_lds_nth(i, a_gbase + (size_t)ks * (kWBK * 2), a_voff[i]);
     };
     auto issue_b = [&](int ks, int slot, int p) {
-      if (p == 0) set_lds_dma_base(lds + slot * kWStage + b_ldst);
-      copy16_to_lds_nth(p, b_gbase + (size_t)ks * kWBK * N * 2, b_voff[p]);
+      if (p == 0) set_lds_dma_base(lds + slot * kStage + b_ldst);
+      copy16_to_lds_nth(p, b_gbase + (size_t)ks * kWBK * N * kEB, b_voff[p]);
     };
     auto issue = [&](int ks) {
 #pragma unroll
-      for (int i = 0; i < CPA; ++i) issue_a(ks, ks % kWStages, i);
+      for (int i = 0; i < CPA; ++i) issue_a(ks, ks % kStages, i);
 #pragma unroll
-      for (int p = 0; p < CPB; ++p) issue_b(ks, ks % kWStages, p);
+      for (int p = 0; p < CPB; ++p) issue_b(ks, ks % kStages, p);
     };
 
     f32x16_t acc[MI][4];
@@ -314,37 +369,82 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     // One set of fragment registers (192 accumulators leave no room for two): the
     // other wave on the SIMD covers each wave's LDS read latency.
     bf16x8_t af[MI], bf[4];
-    auto read_frags = [&](int stage, int kk) {
-      const unsigned char* sa = lds + stage * kWStage;
+    // fp8: the memory phase only reads the codes (8 per lane and fragment) and the
+    // block scales; the MFMA phase dequantises fragment j (code * scale, rounded to
+    // nearest even: the values moe_dequantize_fp8 writes) while the MFMAs of fragment
+    // j-1 run, so the conversion overlaps the matrix pipe and no more registers are live
+    // than with bf16 fragments.
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    v2i braw[FP8 ? 4 : 1];
+    float s_g = 0.f, s_u = 0.f;
+    auto dequant = [&](int j) {
+      const float sc = (GU && j >= 2) ? s_u : s_g;
+      bf16x8_t o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(braw[j][h], false);   // bytes 0, 1
+        const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(braw[j][h], true);    // bytes 2, 3
+        o[4 * h + 0] = static_cast<__bf16>(f0[0] * sc);
+        o[4 * h + 1] = static_cast<__bf16>(f0[1] * sc);
+        o[4 * h + 2] = static_cast<__bf16>(f1[0] * sc);
+        o[4 * h + 3] = static_cast<__bf16>(f1[1] * sc);
+      }
+      return o;
+    };
+    auto read_frags = [&](int ks, int kk) {
+      const unsigned char* sa = lds + (ks % kStages) * kStage;
       const unsigned char* sb = sa + kWABytes;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         af[i] = *reinterpret_cast<const bf16x8_t*>(sa + a_lane[kk] + i * 2048);
+      if constexpr (FP8) {
+        const int kb = (ks * kWBK) >> 7;
+        s_g = sc0[(size_t)kb * NBq];
+        s_u = GU ? sc1[(size_t)kb * NBq] : s_g;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned char* hb = sb + (GU ? (j >> 1) * (kWBBytes / 2) + b_lane[j & 1] : b_lane[j]) +
-                                  kk * 16 * kBPitch;
-        i16x4_t hv[2];
+        for (int j = 0; j < 4; ++j) {
+          const unsigned char* hb = sb + (GU ? (j >> 1) * (kBBytes / 2) + b_lane[j & 1] : b_lane[j]) +
+                                    kk * 16 * kBPitch;
+          braw[j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MOE_LDS v2i*)hb);
+        }
+        bf[0] = dequant(0);   // ready when this wave's MFMA phase starts
+      } else {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(hb + hh * 4 * kBPitch));
-        bf[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int j = 0; j < 4; ++j) {
+          const unsigned char* hb = sb + (GU ? (j >> 1) * (kWBBytes / 2) + b_lane[j & 1] : b_lane[j]) +
+                                    kk * 16 * kBPitch;
+          i16x4_t hv[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(hb + hh * 4 * kBPitch));
+          bf[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
     };
     auto mfma_block = [&]() {
+      if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t b = j == 0 ? bf[0] : dequant(j);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < MI; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], b, acc[i][j], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      }
     };
 
     // Prologue: every slot in flight (slices past the end re-copy the last slice into a
     // slot that is never read again, so every slice issues the same number of copies
     // and the waits are constants), then wait for slice 0.
 #pragma unroll
-    for (int p = 0; p < kWStages; ++p) issue(min(p, nk - 1));
-    MOE_WAIT_VMCNT((kWStages - 1) * CPW);
+    for (int p = 0; p < kStages; ++p) issue(min(p, nk - 1));
+    MOE_WAIT_VMCNT((kStages - 1) * CPW);
     __syncthreads();
 
     if constexpr (!BWD) {
@@ -368,13 +468,13 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       // copies there and its B copies in the second half's (measured: each op's faster
       // split)
       constexpr bool kSplitCopies = !GU;
-      const int ksrc = min(ks - 1 + kWStages, nk - 1);
-      const int slot = (ks + kWStages - 1) % kWStages;
+      const int ksrc = min(ks - 1 + kStages, nk - 1);
+      const int slot = (ks + kStages - 1) % kStages;
       if (kk == 0) {
         if (ks == 0) {
-          MOE_WAIT_VMCNT((kWStages - 2) * CPW);   // slice 1 has landed
+          MOE_WAIT_VMCNT((kStages - 2) * CPW);   // slice 1 has landed
         } else {
-          MOE_WAIT_VMCNT((kWStages - 3) * CPW);   // slice ks+1 has landed
+          MOE_WAIT_VMCNT((kStages - 3) * CPW);   // slice ks+1 has landed
 #pragma unroll
           for (int i = 0; i < CPA; ++i) issue_a(ksrc, slot, i);
           if (!kSplitCopies) {
@@ -386,7 +486,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
         for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
       }
-      read_frags(ks % kWStages, kk);
+      read_frags(ks, kk);
       // scheduling barriers keep each phase's instructions on its side of the barriers
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
@@ -405,10 +505,9 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     // barrier ending slice ks-1 freed its slot; slice ks-1+S refills it, the A copies
     // spread between the first half's MFMAs and the B copies between the second's.
     for (int ks = 0; ks < nk; ++ks) {
-      const int stage = ks % kWStages;
-      const int ksrc = min(ks - 1 + kWStages, nk - 1);
-      const int slot = (ks + kWStages - 1) % kWStages;
-      read_frags(stage, 0);
+      const int ksrc = min(ks - 1 + kStages, nk - 1);
+      const int slot = (ks + kStages - 1) % kStages;
+      read_frags(ks, 0);
       if (ks > 0) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -424,7 +523,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       } else {
         mfma_block();
       }
-      read_frags(stage, 1);
+      read_frags(ks, 1);
       if (ks > 0) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -440,7 +539,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         mfma_block();
       }
       if (ks + 1 < nk) {
-        MOE_WAIT_VMCNT((kWStages - 2) * CPW);   // slice ks+1 has landed
+        MOE_WAIT_VMCNT((kStages - 2) * CPW);   // slice ks+1 has landed
         __syncthreads();
       }
     }
@@ -555,7 +654,7 @@ static constexpr int kWideWaves = 8;
 
 moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, int K, int N,
                           const int32_t* block_meta, const int32_t* num_blocks, int32_t max_blocks,
-                          int64_t max_rows, int E, int32_t dense_rows, hipStream_t st) {
+                          int64_t max_rows, int E, int32_t dense_rows, hipStream_t st, bool fp8) {
   const int out_cols = op == MOE_OP_DOWN ? 256 : 128;
   const int n_tiles = (int)ceil_div(N, out_cols);
   // groups: at most one per block, and at most a third of the blocks plus one per expert
@@ -573,18 +672,21 @@ moe_status launch_gg_wide(int op, const GGOperands& ro, const GGOperands& dn, in
   }
   if (grid < 1) grid = 1;
   constexpr int NT = kWideWaves * 64;
-  if (op == MOE_OP_GATEUP_SWIGLU)
-    hipLaunchKernelGGL((k_gg_wide<MOE_OP_GATEUP_SWIGLU, kWideWaves>), dim3((unsigned)grid), dim3(NT),
-                       0, st, ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows,
-                       dense_rows, n_tiles);
-  else if (op == kOpGateUpBwd)
-    hipLaunchKernelGGL((k_gg_wide<kOpGateUpBwd, kWideWaves>), dim3((unsigned)grid), dim3(NT),
-                       0, st, ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows,
-                       dense_rows, n_tiles);
-  else
-    hipLaunchKernelGGL((k_gg_wide<MOE_OP_DOWN, kWideWaves>), dim3((unsigned)grid), dim3(NT), 0, st,
-                       ro, dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows, dense_rows,
-                       n_tiles);
+#define MOE_WIDE_LAUNCH(OPV, F8)                                                               \
+  hipLaunchKernelGGL((k_gg_wide<OPV, kWideWaves, F8>), dim3((unsigned)grid), dim3(NT), 0, st, ro, \
+                     dn, K, N, block_meta, num_blocks, max_blocks, E, max_rows, dense_rows, n_tiles)
+  if (fp8) {
+    if (op == MOE_OP_GATEUP_SWIGLU) MOE_WIDE_LAUNCH(MOE_OP_GATEUP_SWIGLU, true);
+    else if (op == MOE_OP_DOWN) MOE_WIDE_LAUNCH(MOE_OP_DOWN, true);
+    else return MOE_ENOTSUP;
+  } else if (op == MOE_OP_GATEUP_SWIGLU) {
+    MOE_WIDE_LAUNCH(MOE_OP_GATEUP_SWIGLU, false);
+  } else if (op == kOpGateUpBwd) {
+    MOE_WIDE_LAUNCH(kOpGateUpBwd, false);
+  } else {
+    MOE_WIDE_LAUNCH(MOE_OP_DOWN, false);
+  }
+#undef MOE_WIDE_LAUNCH
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 

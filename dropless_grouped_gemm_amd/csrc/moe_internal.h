@@ -149,10 +149,14 @@ struct GemmSegmentsF8 {
   int gather_div;
   int gather_rows;
 };
-// few_rows: the 64-row kernel with wide weight rows (experts average at most 64 rows);
-// otherwise the 128-row kernel.
+// Which fp8 grouped-GEMM kernel runs: 64-row items with wide weight rows (experts
+// average at most 64 rows: weight streaming), 128-row items, or the wide bf16 kernel's
+// 384-row groups with in-register dequantisation (experts average at least 256 rows).
+enum Fp8Kernel { kFp8Rows64 = 0, kFp8Rows128 = 1, kFp8Wide = 2 };
+// Block-table limit of the wide kernel (moe_gemm_wide.hip).
+int wide_max_blocks();
 moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64_t max_rows,
-                                   bool few_rows, hipStream_t st);
+                                   Fp8Kernel kind, hipStream_t st);
 
 // Backward kernels (moe_backward.hip).
 // dy[pos[t,j]] = w[t,j] dout[t] (bf16), dw[t,j] = <dout[t], y[pos[t,j]]> (fp32); d <= 8192.

@@ -337,7 +337,11 @@ moe_status moe_dequantize_fp8(int32_t E, int32_t K, int32_t N, const uint8_t* q,
  * B0 / B1 are (Q0, S0) / (Q1, S1) code and scale arrays of W1 / W3 (gate/up) or W2
  * (down: Q1 = S1 = NULL).  Each 16-deep weight fragment is dequantised to bf16
  * (code * scale, rounded to nearest even) just before the bf16 MFMA; accumulation and
- * the epilogue are fp32, outputs bf16.
+ * the epilogue are fp32, outputs bf16.  The tiling follows the rows per expert
+ * (M = T * k over min(E, M) experts): at most 64 on average, 64-row items with wide
+ * weight rows (weight streaming); at least 256, the 384-row groups of moe_grouped_gemm's
+ * wide kernel (bitwise the same as that kernel on moe_dequantize_fp8's weights); in
+ * between, 128-row items.
  * row_src: NULL (A is x_perm) or, for op == MOE_OP_GATEUP_SWIGLU only, the
  * permutation, so that A is x [T, d] and row r reads x[row_src[r] / k] (the permute
  * fused into the loads, as moe_grouped_gemm_gather).
@@ -360,12 +364,16 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A,
  * (qs1, ss1), (qs3, ss3), (qs2, ss2) the shared expert's (NULLs when d_e_shared == 0).
  * Same pipeline and requirements as moe_grouped_gemm_fp8.  Where the routed rows
  * M = T * k reach 256 * min(E, M) (experts average at least 256 rows: compute-bound
- * GEMMs), the layer first dequantises every weight into its workspace
- * (moe_dequantize_fp8) and runs moe_layer_fwd's bf16 kernels on them; below that it
- * runs moe_grouped_gemm_fp8, which reads half the weight bytes.  Both use the same
- * bf16 weight values, so the outputs agree to the order of the fp32 sums.
- * Workspace: moe_fp8_workspace_bytes(s) bytes (moe_workspace_bytes's layout, then the
- * dequantised weights where they are used), 16-byte aligned.
+ * GEMMs) and the workspace has room for them, the layer first dequantises every weight
+ * into its workspace (moe_dequantize_fp8) and runs moe_layer_fwd's bf16 kernels on them
+ * (the faster way there); otherwise it runs moe_grouped_gemm_fp8's kernels, which
+ * dequantise in registers (below 256 rows they also read half the weight bytes).  All
+ * paths use the same bf16 weight values; in the 256-row regime both give bitwise the
+ * same output.
+ * Workspace, 16-byte aligned: moe_fp8_workspace_bytes(s) bytes (moe_workspace_bytes's
+ * layout, then the dequantised weights where that path applies), or as little as
+ * moe_workspace_bytes(s) bytes (no dequantised copy: the in-register path);
+ * MOE_EWORKSPACE below that.
  */
 size_t moe_fp8_workspace_bytes(const moe_shape* s);
 

@@ -325,6 +325,21 @@ def test_forward_router_needs_a_16_byte_aligned_w_gate():
     assert L.moe_route(p0, FAKE, w4, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == B.MOE_EINVAL
 
 
+def test_fp8_layer_accepts_the_minimal_workspace():
+    """moe_layer_fwd_fp8 takes any workspace of at least moe_workspace_bytes (then the wide
+    kernel dequantises in registers); moe_fp8_workspace_bytes adds the room for the
+    dequantised weights (then they are dequantised once).  One byte short of the minimum
+    is MOE_EWORKSPACE.  T = 0: validation only, nothing is launched."""
+    L = B.lib()
+    s = good_shape(T=0, d_e_shared=0)
+    ps = ctypes.byref(s)
+    lo = L.moe_workspace_bytes(ps)
+    args = lambda n: (ps, FAKE, FAKE, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE, n,
+                      None)
+    assert L.moe_layer_fwd_fp8(*args(lo)) == B.MOE_OK
+    assert L.moe_layer_fwd_fp8(*args(lo - 1)) == B.MOE_EWORKSPACE
+
+
 def test_fp8_workspace_size_rule():
     """moe_fp8_workspace_bytes: moe_workspace_bytes's layout, plus room for the
     dequantised bf16 weights exactly where the layer takes the dequantised path (routed

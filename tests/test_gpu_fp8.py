@@ -73,10 +73,10 @@ def _routes(T, E, k, seed):
     (300, 256, 2, 1, 1056, 96),      # blocks of 128 valid rows: both 64-row halves; N tails
     (64, 2048, 64, 8, 768, 768),     # decode-like: 512 rows over 64 experts + shared
 ])
-@pytest.mark.parametrize("item_rows", ["64", "128"])
+@pytest.mark.parametrize("item_rows", ["64", "128", "384"])
 def test_grouped_gemm_fp8_against_oracle(T, d, E, k, d_e, d_es, item_rows, monkeypatch):
-    """Both fp8 kernels (64-row items with wide weight rows, 128-row items) on every
-    shape, forced with MOE_FP8_ITEM_ROWS."""
+    """Every fp8 kernel (64-row items with wide weight rows, 128-row items, the wide
+    kernel's 384-row groups) on every shape, forced with MOE_FP8_ITEM_ROWS."""
     monkeypatch.setenv("MOE_FP8_ITEM_ROWS", item_rows)
     idx = _routes(T, E, k, T + d)
     g = torch.Generator(device=DEV)
@@ -142,6 +142,17 @@ def test_grouped_gemm_fp8_against_oracle(T, d, E, k, d_e, d_es, item_rows, monke
         lo, hi = P[ex], P[ex] + c[ex]
         y_ref[lo:hi] = act_dev[lo:hi] @ W2[ex]
     assert_close(f64(y)[valid], y_ref[valid], TOL_STAGE_FP8, "y")
+    if item_rows == "384":
+        # the same bf16 weights, the same tiles and the same order of the fp32 sums as the
+        # wide bf16 kernel on moe_dequantize_fp8's weights: bit for bit
+        monkeypatch.setenv("MOE_GG_TILE_ROWS", "384")
+        dw1, dw3, dw2 = (B.dequantize_fp8(qq, ss) for qq, ss in ((q1, s1), (q3, s3), (q2, s2)))
+        act16, y16 = e(rows, d_e), e(rows, d)
+        B.moe_grouped_gemm(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, dw1, dw3, meta, nblk, mb, act16)
+        B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, dw2, None, meta, nblk, mb, y16)
+        torch.cuda.synchronize()
+        assert torch.equal(act[dv].view(torch.int16), act16[dv].view(torch.int16))
+        assert torch.equal(y[dv].view(torch.int16), y16[dv].view(torch.int16))
     if d_es:
         assert torch.equal(sact.view(torch.int16), sact_g.view(torch.int16))
         Ws1, Ws3, Ws2 = (dq(qa, sa)[0], dq(qb, sb)[0], dq(qc, sc)[0])
@@ -203,10 +214,13 @@ def test_layer_fwd_fp8(name, scale):
     ("decode-256x2048", dict(name="decode-fp8-dq", d=512, d_e=256, d_e_shared=256), False),
 ])
 def test_layer_fwd_fp8_against_bf16_layer_on_dequantised_weights(name, scale, wide):
-    """Where experts average >= 256 rows the fp8 layer dequantises its weights and runs
-    the bf16 layer's kernels: bitwise equal to moe_layer_fwd on moe_dequantize_fp8's
-    weights.  Below that it runs the fp8 kernels, which build the same bf16 weights in
-    registers: equal up to the order of the fp32 sums (5e-3 * max|out|)."""
+    """Where experts average >= 256 rows the fp8 layer either dequantises its weights into
+    the workspace and runs the bf16 layer's kernels (a workspace of
+    moe_fp8_workspace_bytes) or runs the wide kernel with the fragments dequantised in
+    registers (a workspace of moe_workspace_bytes only): both bitwise equal to
+    moe_layer_fwd on moe_dequantize_fp8's weights (the same bf16 values, tiles and order
+    of the sums).  Below that the fp8 kernels with other tiles build the same bf16
+    weights: equal up to the order of the fp32 sums (5e-3 * max|out|)."""
     cfg = get_config(name).scaled(**scale)
     inp = make_inputs(cfg, device=DEV)
     s = B.shape_of_config(cfg)
@@ -232,6 +246,12 @@ def test_layer_fwd_fp8_against_bf16_layer_on_dequantised_weights(name, scale, wi
     assert torch.isfinite(out8.float()).all()
     if wide:
         assert torch.equal(out8.view(torch.int16), out16.view(torch.int16))
+        out8m = torch.empty_like(out8)
+        wsm = torch.full((B.moe_workspace_bytes(s),), 0xFF, dtype=torch.uint8, device=DEV)
+        B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, *qz[0], *qz[1], *qz[2], *qs[0],
+                            *qs[1], *qs[2], ri, rw, out8m, wsm)
+        torch.cuda.synchronize()
+        assert torch.equal(out8m.view(torch.int16), out16.view(torch.int16))
     else:
         assert_close(f64(out8), f64(out16), 5e-3, "fp8 kernels vs bf16 kernels")
 

@@ -192,6 +192,19 @@ def test_fp8_full_size_sampled_tokens(fp8_full):
                            TOL_STAGE_FP8, f"{cfg.name} fp8")
 
 
+def test_fp8_full_size_minimal_workspace_gives_the_same_output(fp8_full):
+    """With a workspace of moe_workspace_bytes only, the fp8 layer dequantises in registers
+    (the wide kernel where experts average >= 256 rows) instead of into the workspace: the
+    same bf16 weights, tiles and order of the sums, so the output is bitwise the same."""
+    cfg, inp, w, s, ws, out = fp8_full
+    wsm = torch.empty(B.moe_workspace_bytes(s), dtype=torch.uint8, device=DEV)
+    out2 = torch.empty_like(out)
+    B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, w.q1, w.s1, w.q3, w.s3, w.q2, w.s2,
+                        w.qs1, w.ss1, w.qs3, w.ss3, w.qs2, w.ss2, None, None, out2, wsm)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------
 # Unpadded segments at full size
 # ----------------------------------------------------------------------------
