@@ -435,9 +435,9 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
   constexpr int kOutCols = GU ? 512 : 1024;               // output columns per item
   constexpr int kPitch = GU ? 512 : 1024;                 // bytes per staged B row (per matrix)
   __shared__ __align__(1024) unsigned char lds[kDStages * kDStage];
-  // the item's block scales: [kb][8] (gate/up: W1 n-blocks 0..3 of the tile, then W3's;
-  // down: n-blocks 0..7)
-  __shared__ float s_scale[kFMaxKB * 8];
+  // block scales of two items (the current one and the next, double-buffered): [kb][8]
+  // (gate/up: W1 n-blocks 0..3 of the tile, then W3's; down: n-blocks 0..7)
+  __shared__ float s_scale[2][kFMaxKB * 8];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -451,6 +451,9 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
   const int nk = K / kFBK;
   const int KB = (K + kQBlock - 1) / kQBlock, NBq = (N + kQBlock - 1) / kQBlock;
   const bool has_a = wave < kDABytes / 1024;               // waves 0..3 copy A
+  // consecutive items of a work group run as one stream of slices: the last refills of
+  // an item fetch the next item's first slices (the launcher guarantees nk >= the ring
+  // depth)
 
   // B fragment reads (ds_read_b64_tr_b8, as k_gg_fp8w): 16-lane group g, lane gi; tile j
   // of the wave: matrix region and first column within it.
@@ -468,56 +471,58 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
     sidx[j] = GU ? region * 4 + (col0 >> 7) : (col0 >> 7);
   }
 
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int half = w / per_half;
-    const int rem = w - half * per_half;
-    const int nt = rem % n_tiles;
-    const int blk = rem / n_tiles;
-    const bool in_dense = blk < nb_dense;
+  // One work item's operands.
+  struct Item {
+    int w;                        // item number, -1: none
     Tile tile;
-    if (in_dense) {
-      if (!decode_block(blk, half, kDRows, 128, nullptr, dense_rows, 1, dense_rows, tile)) continue;
-    } else {
-      if (!decode_block(blk - nb_dense, half, kDRows, 128, meta, 0, E, max_rows, tile)) continue;
+    int n0;
+    bool dense;
+    const bf16_t* asrc;           // A base (wave-uniform)
+    uint32_t a_voff;              // this lane's A offset (waves 0..3)
+    const uint8_t* bsrc;          // the wave's B matrix base (wave-uniform)
+    uint32_t b_voff[kDBCopies];
+    int b_row[kDBCopies];
+  };
+  // the first valid item at or after number w of this work group's sequence
+  auto find_item = [&](int w, Item& it) {
+    it.w = -1;
+    for (; w < total; w += gridDim.x) {
+      const int half = w / per_half;
+      const int rem = w - half * per_half;
+      const int nt = rem % n_tiles;
+      const int blk = rem / n_tiles;
+      const bool in_dense = blk < nb_dense;
+      bool ok;
+      if (in_dense)
+        ok = decode_block(blk, half, kDRows, 128, nullptr, dense_rows, 1, dense_rows, it.tile);
+      else
+        ok = decode_block(blk - nb_dense, half, kDRows, 128, meta, 0, E, max_rows, it.tile);
+      if (!ok) continue;
+      it.w = w;
+      it.dense = in_dense;
+      it.n0 = nt * kOutCols;
+      break;
     }
-    const GGOperandsF8& ops = in_dense ? dense : routed;
-    bf16_t* const C = ops.base.C;
-    const int n0 = nt * kOutCols;
-    const int e = tile.e;
-
-    // block scales of this item's columns, every k-block
-    {
-      const float* s0 = ops.S0 + (size_t)e * KB * NBq;
-      const float* s1 = GU ? ops.S1 + (size_t)e * KB * NBq : s0;
-      for (int i = tid; i < KB * 8; i += kFThreads) {
-        const int kb = i >> 3, slot = i & 7;
-        const int nb = (n0 >> 7) + (GU ? (slot & 3) : slot);
-        const float* sp = (GU && slot >= 4) ? s1 : s0;
-        s_scale[i] = nb < NBq ? sp[(size_t)kb * NBq + nb] : 1.0f;
-      }
-    }
-
+    if (it.w < 0) return;
+    const GGOperandsF8& ops = it.dense ? dense : routed;
+    const int e = it.tile.e;
     // A copy (waves 0..3, one per slice): 16 rows x 64 bytes; rows past valid_m copy
     // row 0, gathered rows come from x.
-    const bf16_t* asrc = ops.base.A + (size_t)tile.m0 * K;
-    uint32_t a_voff = 0;
+    it.a_voff = 0;
     if (has_a) {
       const int row = wave * 16 + (lane >> 2);
       const int c = swz_a(row, lane & 3);
-      const int rr = row < tile.valid ? row : 0;
-      const int src = ops.base.gather ? gather_row(ops.base, tile.m0 + rr) : rr;
-      a_voff = (uint32_t)(src * K + c * 8) * 2u;
+      const int rr = row < it.tile.valid ? row : 0;
+      const int src = ops.base.gather ? gather_row(ops.base, it.tile.m0 + rr) : rr;
+      it.a_voff = (uint32_t)(src * K + c * 8) * 2u;
     }
-    asrc = uniform_ptr(ops.base.gather ? ops.base.A : asrc);
+    it.asrc = uniform_ptr(ops.base.gather ? ops.base.A : ops.base.A + (size_t)it.tile.m0 * K);
     // B copies: copy u = 4 wave + p of 32.  Gate/up: region u / 16 (W1, W3), rows
     // 2 (u % 16) and 2 (u % 16) + 1 of the region, 32 lanes per 512-byte row; down:
     // row u, 64 lanes per 1 KB row.  The logical chunk of lane l is its position
     // XOR (k & 15); columns past N copy column 0.
-    const uint8_t* qb[2];
-    qb[0] = ops.Q0 + (size_t)e * K * N;
-    qb[1] = GU ? ops.Q1 + (size_t)e * K * N : qb[0];
-    uint32_t b_voff[kDBCopies];
-    int b_row[kDBCopies];
+    const uint8_t* qb0 = ops.Q0 + (size_t)e * K * N;
+    const uint8_t* qb1 = GU ? ops.Q1 + (size_t)e * K * N : qb0;
 #pragma unroll
     for (int p = 0; p < kDBCopies; ++p) {
       const int u = wave * kDBCopies + p;
@@ -529,30 +534,65 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
         k = u;
         pos = lane;
       }
-      int col = n0 + (pos ^ (k & 15)) * 16;
+      int col = it.n0 + (pos ^ (k & 15)) * 16;
       if (col >= N) col = 0;
-      b_row[p] = GU ? 2 * (u & 15) : u;
-      b_voff[p] = (uint32_t)((k - b_row[p]) * N + col);
+      it.b_row[p] = GU ? 2 * (u & 15) : u;
+      it.b_voff[p] = (uint32_t)((k - it.b_row[p]) * N + col);
     }
-    const uint8_t* bsrc = uniform_ptr(qb[GU ? (wave * kDBCopies) >> 4 : 0]);
-    auto issue = [&](int ks, int slot) {
-      unsigned char* st = lds + slot * kDStage;
-      const int k0 = ks * kFBK;
-      if (has_a) copy16_to_lds(asrc + k0, a_voff, st + wave * 1024);
+    it.bsrc = uniform_ptr((GU && ((wave * kDBCopies) >> 4)) ? qb1 : qb0);
+  };
+  // slice ks of an item into ring slot `slot`
+  auto issue = [&](const Item& it, int ks, int slot) {
+    unsigned char* st = lds + slot * kDStage;
+    const int k0 = ks * kFBK;
+    if (has_a) copy16_to_lds(it.asrc + k0, it.a_voff, st + wave * 1024);
 #pragma unroll
-      for (int p = 0; p < kDBCopies; ++p) {
-        const int u = wave * kDBCopies + p;
-        copy16_to_lds(bsrc + (size_t)(k0 + b_row[p]) * N, b_voff[p], st + kDABytes + u * 1024);
-      }
-    };
-    // every copy a wave has issued lands in order: wait until at most n slices of its
-    // copies are outstanding (waves 0..3 issue one more copy per slice)
-    auto wait_slices = [&](auto n_c) {
-      constexpr int n = decltype(n_c)::value;
-      if (has_a) MOE_WAIT_VMCNT(n * (kDBCopies + 1));
-      else MOE_WAIT_VMCNT(n * kDBCopies);
-    };
+    for (int p = 0; p < kDBCopies; ++p) {
+      const int u = wave * kDBCopies + p;
+      copy16_to_lds(it.bsrc + (size_t)(k0 + it.b_row[p]) * N, it.b_voff[p], st + kDABytes + u * 1024);
+    }
+  };
+  // an item's block scales into buffer `buf` (plain LDS stores: a barrier publishes them)
+  auto load_scales = [&](const Item& it, int buf) {
+    const GGOperandsF8& ops = it.dense ? dense : routed;
+    const int e = it.tile.e;
+    const float* s0 = ops.S0 + (size_t)e * KB * NBq;
+    const float* s1 = GU ? ops.S1 + (size_t)e * KB * NBq : s0;
+    for (int i = tid; i < KB * 8; i += kFThreads) {
+      const int kb = i >> 3, slot = i & 7;
+      const int nb = (it.n0 >> 7) + (GU ? (slot & 3) : slot);
+      const float* sp = (GU && slot >= 4) ? s1 : s0;
+      s_scale[buf][i] = nb < NBq ? sp[(size_t)kb * NBq + nb] : 1.0f;
+    }
+  };
+  // every copy a wave has issued lands in order: wait until at most n slices of its
+  // copies are outstanding (waves 0..3 issue one more copy per slice)
+  auto wait_slices = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    if (has_a) MOE_WAIT_VMCNT(n * (kDBCopies + 1));
+    else MOE_WAIT_VMCNT(n * kDBCopies);
+  };
 
+  Item cur, nxt;
+  find_item(blockIdx.x, cur);
+  if (cur.w < 0) return;
+  find_item(cur.w + gridDim.x, nxt);
+  load_scales(cur, 0);
+  // Prologue: every slot in flight (slices past the end re-copy the last slice into a
+  // slot that is never read), then wait for slice 0; the barrier also publishes the
+  // scale table.
+#pragma unroll
+  for (int p = 0; p < kDStages; ++p) issue(cur, min(p, nk - 1), p);
+  wait_slices(std::integral_constant<int, kDStages - 1>{});
+  __syncthreads();
+
+  int gbase = 0;      // stream position of the current item's slice 0
+  int buf = 0;        // its scale buffer
+  while (true) {
+    // the next item's scales, read only once its slices are computed (the barriers in
+    // between publish them)
+    if (nxt.w >= 0) load_scales(nxt, buf ^ 1);
+    const int nsub = __builtin_amdgcn_readfirstlane(min(2, (cur.tile.valid + 31) >> 5));
     f32x16_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -561,10 +601,9 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    const int nsub = __builtin_amdgcn_readfirstlane(min(2, (tile.valid + 31) >> 5));
     bf16x8_t af[2], bf[4];
-    auto read_frags = [&](int ks, int kk) {
-      const unsigned char* sa = lds + (ks % kDStages) * kDStage;
+    auto read_frags = [&](int slot, int ks, int kk) {
+      const unsigned char* sa = lds + slot * kDStage;
       const unsigned char* sb = sa + kDABytes;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -578,7 +617,7 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
         typedef int v2i __attribute__((ext_vector_type(2)));
         const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (MOE_LDS v2i*)(sb + b_lane[j] + kk * 16 * kPitch));
-        const float sc = s_scale[kb * 8 + sidx[j]];
+        const float sc = s_scale[buf][kb * 8 + sidx[j]];
         bf16x8_t o;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -602,67 +641,67 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
       }
     };
 
-    // Prologue: every slot in flight (slices past the end re-copy the last slice into a
-    // slot that is never read), then wait for slice 0; the barrier also publishes the
-    // scale table.
-#pragma unroll
-    for (int p = 0; p < kDStages; ++p) issue(min(p, nk - 1), p);
-    wait_slices(std::integral_constant<int, kDStages - 1>{});
-    __syncthreads();
     for (int ks = 0; ks < nk; ++ks) {
-      if (ks > 0) issue(min(ks - 1 + kDStages, nk - 1), (ks - 1) % kDStages);
-      read_frags(ks, 0);
+      const int gs = gbase + ks;
+      if (gs > 0) {
+        // refill the slot of stream slice gs-1 (every wave has read it) with stream slice
+        // gs-1+S: this item's, the next item's, or a re-copy of this item's last slice
+        const int t = gs - 1 + kDStages - gbase;
+        const int slot = (gs - 1) % kDStages;
+        if (t < nk) issue(cur, t, slot);
+        else if (nxt.w >= 0) issue(nxt, t - nk, slot);
+        else issue(cur, nk - 1, slot);
+      }
+      const int slot = gs % kDStages;
+      read_frags(slot, ks, 0);
       mfma_block();
-      read_frags(ks, 1);
+      read_frags(slot, ks, 1);
       mfma_block();
-      if (ks + 1 < nk) {
-        wait_slices(std::integral_constant<int, kDStages - 2>{});   // slice ks+1 has landed
+      if (ks + 1 < nk || nxt.w >= 0) {
+        wait_slices(std::integral_constant<int, kDStages - 2>{});   // stream slice gs+1 landed
         __syncthreads();
       }
     }
-    MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
-    __syncthreads();
 
-    // Epilogue through LDS: bf16 staging per wave (64 rows x 64 act / 128 down columns),
-    // 16-byte stores of valid rows and columns.
-    constexpr int kWCols = GU ? 64 : 128;
-    constexpr int kLd = kWCols + 8;
-    bf16_t* stg = reinterpret_cast<bf16_t*>(lds) + wave * kDRows * kLd;
-    const int col0 = n0 + wave * kWCols;
+    // Epilogue: 16-bit stores straight from the accumulators (32 lanes store 64
+    // contiguous bytes of a row), valid rows and columns only; the ring is not touched,
+    // so the next item's slices keep landing.
+    {
+      const GGOperandsF8& ops = cur.dense ? dense : routed;
+      bf16_t* const C = ops.base.C;
+      constexpr int kWCols = GU ? 64 : 128;
+      const int col0 = cur.n0 + wave * kWCols;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (i >= nsub) break;
+      for (int i = 0; i < 2; ++i) {
+        if (i >= nsub) break;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        if (GU) {
+        for (int q = 0; q < 16; ++q) {
+          const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          if (r >= cur.tile.valid) continue;
+          bf16_t* crow = C + (size_t)(cur.tile.m0 + r) * N;
+          if (GU) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            stg[r * kLd + j * 32 + (lane & 31)] =
-                f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
-        } else {
+            for (int j = 0; j < 2; ++j) {
+              const int col = col0 + j * 32 + (lane & 31);
+              if (col < N) crow[col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+            }
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            stg[r * kLd + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][q]);
+            for (int j = 0; j < 4; ++j) {
+              const int col = col0 + j * 32 + (lane & 31);
+              if (col < N) crow[col] = f32_to_bf16(acc[i][j][q]);
+            }
+          }
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    constexpr int kChunks = kWCols / 8;
-    constexpr int kRowsPerPass = 64 / kChunks;
-    const int nrows = nsub * 32;
-    for (int r0 = 0; r0 < nrows; r0 += kRowsPerPass) {
-      const int r = r0 + lane / kChunks;
-      const int ch = lane % kChunks;
-      const int gcol = col0 + ch * 8;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + ch * 8);
-      if (r < tile.valid && gcol < N)
-        *reinterpret_cast<u32x4_t*>(C + (size_t)(tile.m0 + r) * N + gcol) = v;
-    }
-    __syncthreads();  // staging and scale reads done before the next item refills
+    if (nxt.w < 0) break;
+    cur = nxt;
+    find_item(cur.w + gridDim.x, nxt);
+    gbase += nk;
+    buf ^= 1;
   }
+  MOE_WAIT_VMCNT(0);  // the re-copies past the last slice land before the work group ends
 }
 
 bool fp8_gemm_supported(int K, int N) {
@@ -680,6 +719,8 @@ moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64
     if (strcmp(f, "128") == 0) kind = kFp8Rows128;
     if (strcmp(f, "384") == 0 && g.max_blocks <= wide_max_blocks()) kind = kFp8Wide;
   }
+  // the 64-row kernel streams consecutive items' slices through its ring: K >= 4 slices
+  if (kind == kFp8Rows64 && g.K / kFBK < kDStages) kind = kFp8Rows128;
   const bool few_rows = kind == kFp8Rows64;
   if (kind == kFp8Wide) {
     GGOperands ro{static_cast<const bf16_t*>(g.A), reinterpret_cast<const bf16_t*>(g.Q0),
