@@ -234,6 +234,53 @@ __device__ __forceinline__ int sel_id(uint64_t key) {
   return (int)(0xffffffffu - (uint32_t)key);
 }
 
+// The logit a key was made from (the inverse of the order mapping; -0 came in as +0).
+__device__ __forceinline__ float sel_value(uint64_t key) {
+  const uint32_t h = (uint32_t)(key >> 32);
+  return __uint_as_float((h & 0x80000000u) ? (h & 0x7fffffffu) : ~h);
+}
+
+// All-reduce over each 16-lane row of a wave with DPP moves (no LDS round trip): swaps
+// inside quads (lane xor 1, xor 2), then the 8-lane and the 16-lane mirror, so that
+// every lane of the row ends with the row's maximum (sum); the combining order is
+// symmetric, so all 16 lanes hold bitwise the same result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f32<kDppMirror>(v));
+}
+
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  return v + dpp_f32<kDppMirror>(v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_key_step(uint64_t k) {
+  const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(k >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)k);
+  return o > k ? o : k;
+}
+
+__device__ __forceinline__ uint64_t row16_max_key(uint64_t k) {
+  k = max_key_step<kDppXor1>(k);
+  k = max_key_step<kDppXor2>(k);
+  k = max_key_step<kDppHalfMirror>(k);
+  return max_key_step<kDppMirror>(k);
+}
+
 template <int G>
 __device__ __forceinline__ uint64_t group_max_key(uint64_t k) {
 #pragma unroll
@@ -432,10 +479,10 @@ k_select(const float* __restrict__ partial, int nsplit, const float* __restrict_
 // global->LDS copies whose 64 lanes cover 1 KB: two (or four) rows of 512 (256)
 // contiguous bytes, instead of the 64 bytes per row a direct A-operand load covers.
 // A slice also holds W_g's rows [k0, k0 + SK) - one contiguous piece of W_g - read as
-// the B operand with ds_read_b64_tr_b16.  The 4 waves split each slice's 32-deep steps
-// (wave w takes steps w, w+4, ...) and accumulate TB x 16*NT partial logits each; at the
-// end the four partial sums are added in wave order through LDS (deterministic), the
-// bias added, and G lanes per token select as k_select does.
+// the B operand with ds_read_b64_tr_b16.  Each wave owns a 16-token MFMA tile (with
+// TB < 64, TB / 16 tiles: the waves of a tile split its 32-deep steps and their partial
+// logits are added in a fixed order through LDS), so a tile's logits end up in one
+// wave's registers, where 16 lanes per token select with DPP reductions.
 // ---------------------------------------------------------------------------
 // Group-limited eligibility of one token by one lane (E <= 64): a group (n_groups
 // contiguous id ranges) scores its largest logit, the topk_groups best groups stay
@@ -465,6 +512,11 @@ __device__ __forceinline__ uint64_t group_keep_mask(const float* lrow, int strid
   return keep;
 }
 
+// W_g chunk permutation of the fused router at a 128-byte row pitch: the 8 rows that one
+// transposed B read touches at one bank half (row bits 1 and 3-4 vary) get 8 different
+// chunks.
+__device__ __forceinline__ int wg_swz(int row) { return 2 * ((row >> 3) & 3) + ((row >> 1) & 1); }
+
 static constexpr int kRfThreads = 256;
 static constexpr int kRfLds = 160 * 1024;
 
@@ -490,8 +542,10 @@ struct RouteFused {
   static_assert(CX >= 1 && XB % 4096 == 0, "x copy split");
   static_assert(NS >= 3 && (NS - 2) * CPW <= 63, "ring depth");
   static_assert(KS == 2 || KS == 4 || KS == 8, "steps per slice");
-  static_assert(4 * TB * 16 * NT * 4 + TB * 16 * NT * 4 + TB * 8 <= NS * kSlot,
-                "reduction space");
+  static_assert(TB == 16 || TB == 32 || TB == 64, "16-token tiles over 4 waves");
+  static_assert(4 * 64 * NT * 16 + 4 * 16 * 16 * NT * 4 <= NS * kSlot,
+                "partial-logit and selection space");
+  static_assert(E8 != 8 || SK * 128 <= CW * 4096, "swizzled W_g rows fit the region");
 };
 
 template <int TB, int E8>
@@ -524,8 +578,19 @@ k_route_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
   }
   const int wslice = SK * wrow;                    // real W_g bytes per slice
 #pragma unroll
-  for (int c = 0; c < CW; ++c)
-    woff[c] = (uint32_t)min(((wave * CW + c) * 64 + lane) * 16, wslice - 16);
+  for (int c = 0; c < CW; ++c) {
+    if constexpr (E8 == 8) {
+      // 33..64 experts: W_g rows staged at a 128-byte pitch with their 16-byte chunks
+      // permuted (physical chunk = logical ^ wg_swz(row)), so that the transposed B
+      // reads spread over all banks; chunks past E's read chunk 0 (never used)
+      const int P = ((wave * CW + c) * 64 + lane) * 16;
+      const int row = P >> 7;
+      const int lc = ((P >> 4) & 7) ^ wg_swz(row);
+      woff[c] = (uint32_t)(min(row, SK - 1) * wrow + (lc * 8 < E ? lc : 0) * 16);
+    } else {
+      woff[c] = (uint32_t)min(((wave * CW + c) * 64 + lane) * 16, wslice - 16);
+    }
+  }
 
   // Blocks start at different slices (block b at slice b mod nsl, then wrapping round),
   // so that blocks running at the same time read different pieces of W_g rather than
@@ -543,15 +608,26 @@ k_route_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
     for (int c = 0; c < CW; ++c) copy16_to_lds(wb, woff[c], slot + C::XB + (wave * CW + c) * 1024);
   };
 
-  // fragment addresses inside a slot
+  // Work split: 16-token MFMA tiles, NTT = TB / 16 of them; wave w owns tile w % NTT
+  // and, when there are fewer tiles than waves, the k-phase w / NTT of KW = 4 / NTT:
+  // the 32-deep steps kk = phase, phase + KW, ... of every slice.
+  constexpr int NTT = TB / 16, KW = 4 / NTT;
+  const int tw = wave % NTT, kw = wave / NTT;
   const int g = lane >> 4, r16 = lane & 15;
   const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
-  f32x4_t acc[TB / 16][NT];
+  f32x4_t acc[NT];
 #pragma unroll
-  for (int ts = 0; ts < TB / 16; ++ts)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[ts][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // the bias of the lane's experts (16 nt + l % 16 in the MFMA output), loaded before
+  // the ring fills so that its latency hides behind the loop (an extra older load only
+  // makes the copy waits below wait longer, never shorter)
+  float bv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = (lane & 15) + 16 * nt;
+    bv[nt] = (bias && e < E) ? bias[e] : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j) issue(j);
   for (int j = 0; j < nsl; ++j) {
@@ -561,95 +637,158 @@ k_route_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
     const unsigned char* slot = lds + (j % NS) * C::kSlot;
     const unsigned char* wl = slot + C::XB;
 #pragma unroll
-    for (int q = 0; q < (KS + 3) / 4; ++q) {
-      const int kk = wave + 4 * q;                 // this wave's 32-deep step
-      if (KS < 4 && kk >= KS) break;
+    for (int q = 0; q < (KS + KW - 1) / KW; ++q) {
+      const int kk = kw + KW * q;                  // this wave's 32-deep step
+      if (KS % KW != 0 && kk >= KS) break;
       bf16x8_t bop[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const unsigned char* bp = wl + (kk * 32 + g * 8 + tr_r) * wrow + nt * 32 + tr_c * 8;
+        const unsigned char* bp;
+        int bpitch;
+        if constexpr (E8 == 8) {
+          // row kk*32 + g*8 + tr_r: its swizzle is 2g + tr_r / 2 (rows +4 the same)
+          bp = wl + (kk * 32 + g * 8 + tr_r) * 128 +
+               (((2 * nt + (tr_c >> 1)) ^ (2 * g + (tr_r >> 1))) * 16) + (tr_c & 1) * 8;
+          bpitch = 128;
+        } else {
+          bp = wl + (kk * 32 + g * 8 + tr_r) * wrow + nt * 32 + tr_c * 8;
+          bpitch = wrow;
+        }
         const i16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)bp);
-        const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(bp + 4 * wrow));
+        const i16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(bp + 4 * bpitch));
         bop[nt] = __builtin_bit_cast(bf16x8_t,
                                      __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+      const int row = tw * 16 + r16;
+      const int pc = (kk * 4 + g) ^ (row & C::SWZ);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(slot + row * kPitch + pc * 16);
 #pragma unroll
-      for (int ts = 0; ts < TB / 16; ++ts) {
-        const int row = ts * 16 + r16;
-        const int pc = (kk * 4 + g) ^ (row & C::SWZ);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(slot + row * kPitch + pc * 16);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[ts][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[nt], acc[ts][nt], 0, 0, 0);
-      }
+      for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop[nt], acc[nt], 0, 0, 0);
     }
   }
   MOE_WAIT_VMCNT(0);                               // the copies past the last slice
   __syncthreads();
 
-  // partial logits of each wave -> LDS [wave][TB][16 NT]; then the sum in wave order,
-  // plus the bias, into lg[e][TB] (token-minor, so that lane tt reads its token's
-  // logits from consecutive addresses)
-  constexpr int EP = 16 * NT;             // columns of the partial-logit tiles
+  // k-phases of one tile: phases 1.. leave their partial logits in LDS (each lane its
+  // own 4 NT values), phase 0 adds them in phase order (deterministic)
   float* red = reinterpret_cast<float*>(lds);
-  float* lg = red + 4 * TB * EP;
+  if constexpr (KW > 1) {
+    if (kw > 0) {
 #pragma unroll
-  for (int ts = 0; ts < TB / 16; ++ts)
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4_t*>(red + ((wave * 64 + lane) * NT + nt) * 4) = acc[nt];
+    }
+    __syncthreads();
+    if (kw == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int ph = 1; ph < KW; ++ph)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        red[(wave * TB + ts * 16 + g * 4 + i) * EP + nt * 16 + r16] = acc[ts][nt][i];
-  __syncthreads();
-  for (int i = tid; i < TB * E; i += kRfThreads) {
-    const int tt = i / E, e = i % E;
-    float v = red[(0 * TB + tt) * EP + e];
-    v += red[(1 * TB + tt) * EP + e];
-    v += red[(2 * TB + tt) * EP + e];
-    v += red[(3 * TB + tt) * EP + e];
-    if (bias) v += bias[e];
-    lg[e * TB + tt] = v;
-    if (logits_out && t0 + tt < T) logits_out[(size_t)(t0 + tt) * E + e] = v;
+        for (int nt = 0; nt < NT; ++nt) {
+          const f32x4_t o =
+              *reinterpret_cast<const f32x4_t*>(red + (((ph * NTT + tw) * 64 + lane) * NT + nt) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nt][i] += o[i];
+        }
+    }
   }
-  __syncthreads();
-  // group-limited eligibility, one lane per token, as a mask in LDS (after lg)
-  uint64_t* keep_s = reinterpret_cast<uint64_t*>(lg + TB * EP);
-  if (n_groups > 0 && tid < TB)
-    keep_s[tid] = group_keep_mask(lg + tid, TB, E, n_groups, topk_groups);
-  __syncthreads();
-  // selection: G = 256 / TB lanes per token (all tokens in one pass), lane lt holding
-  // experts lt + G*r
-  constexpr int G = kRfThreads / TB;
-  constexpr int PER = (EP + G - 1) / G;
-  const int tt = tid / G, lt = tid % G;
-  const int t = t0 + tt;
-  const bool live = t < T;
-  bool has[PER], elig[PER];
-  float l[PER], z[PER], S;
+
+  if (kw != 0) return;   // (no block-wide barrier follows)
+
+  // The tile's logits are in registers (16x16 MFMA output: element i of lane l is
+  // token (l / 16) * 4 + i of the tile, expert 16 nt + l % 16).  Bias, the optional
+  // logits store, then the logits move through a wave-private LDS patch [16 NT][16]
+  // (token-minor) to the selection layout: 4 lanes per token, lane lq holding experts
+  // lq + 4 r (r < 4 NT), one token per lane quad, 16 tokens per wave at once.
+  constexpr int EPT = 16 * NT;                     // expert columns of the tile
+  constexpr int PER = EPT / 4;
+  float* lgw = red + (KW > 1 ? 4 * 64 * NT * 4 : 0) + wave * 16 * EPT;
   {
-    // the token's logits, token-minor in lg: expert e at lg[e * TB + tt]
-    float m = -FLT_MAX;
+    const int lt = lane & 15;
+    const int tt0 = tw * 16 + g * 4;               // the lane's first token in the block
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int e = lt + G * r;
-      has[r] = e < E;
-      l[r] = has[r] ? lg[e * TB + tt] : -FLT_MAX;
-      if (has[r]) m = fmaxf(m, l[r]);
-    }
-    m = group_max<G>(m);
-    float zs = 0.f;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int e = lt + 16 * nt;
+      const bool he = e < E;
+      const float b = bv[nt];
+      f32x4_t v;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      z[r] = has[r] ? expf(l[r] - m) : 0.f;
-      zs += z[r];
+      for (int i = 0; i < 4; ++i) {
+        v[i] = acc[nt][i] + b;
+        if (logits_out && he && t0 + tt0 + i < T) logits_out[(size_t)(t0 + tt0 + i) * E + e] = v[i];
+      }
+      *reinterpret_cast<f32x4_t*>(lgw + e * 16 + g * 4) = v;
     }
-    S = group_sum<G>(zs);
   }
-  const uint64_t keep = n_groups > 0 ? keep_s[tt] : ~0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int tk = lane >> 2, lq = lane & 3;
+  const int t = t0 + tw * 16 + tk;
+  float l[PER], z[PER];
+  bool has[PER];
+  float m = -FLT_MAX;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) elig[r] = has[r] && ((keep >> (lt + G * r)) & 1ull);
-  select_rounds<G, PER>(l, z, elig, S, k, renormalize, live, live ? t : T - 1, lt, lane - lt,
-                        topk_idx, topk_w);
+  for (int r = 0; r < PER; ++r) {
+    const int e = lq + 4 * r;
+    has[r] = e < E;
+    l[r] = has[r] ? lgw[e * 16 + tk] : -FLT_MAX;
+    m = fmaxf(m, l[r]);
+  }
+  m = fmaxf(m, dpp_f32<kDppXor1>(m));
+  m = fmaxf(m, dpp_f32<kDppXor2>(m));
+  float zs = 0.f;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    z[r] = has[r] ? expf(l[r] - m) : 0.f;
+    zs += z[r];
+  }
+  zs += dpp_f32<kDppXor1>(zs);
+  const float S = zs + dpp_f32<kDppXor2>(zs);
+  // group-limited eligibility: each of the token's lanes forms the same mask
+  const uint64_t keep = n_groups > 0 ? group_keep_mask(lgw + tk, 16, E, n_groups, topk_groups) : ~0ull;
+  // k rounds of "largest remaining eligible logit, ties to the lower id": the quad's
+  // largest value (a local tree, then two DPP steps), the lowest id holding it (the
+  // same), and that entry taken out (-inf).  -0 and +0 compare equal, as in the keys
+  // of the other selection paths.
+  float lv[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) lv[r] = (has[r] && ((keep >> (lq + 4 * r)) & 1ull)) ? l[r] : -INFINITY;
+  // the round's weights wait in the wave's patch (its logits are all read by now)
+  // until the renormalisation scale is known: slot j of the token at lgw[tk * EPT + j]
+  float* pw = lgw + tk * EPT;
+  float wsum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float c[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) c[r] = lv[r];
+#pragma unroll
+    for (int w = PER / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int r = 0; r < w; ++r) c[r] = fmaxf(c[r], c[r + w]);
+    float mq = fmaxf(c[0], dpp_f32<kDppXor1>(c[0]));
+    mq = fmaxf(mq, dpp_f32<kDppXor2>(mq));
+    int id = 1 << 30;
+#pragma unroll
+    for (int r = PER - 1; r >= 0; --r)
+      if (lv[r] == mq) id = lq + 4 * r;
+    id = min(id, (int)dpp_u32<kDppXor1>((uint32_t)id));
+    id = min(id, (int)dpp_u32<kDppXor2>((uint32_t)id));
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+      if (lq + 4 * r == id) lv[r] = -INFINITY;
+    // the winner's weight: exactly the owner's exp(l - m), computed by every lane
+    const float p = expf(mq - m) / S;
+    wsum += p;
+    if (lq == (j & 3)) {
+      if (t < T) topk_idx[(size_t)t * k + j] = id;
+      pw[j] = p;
+    }
+  }
+  if (t < T) {
+    const float scale = 1.0f / wsum;
+    for (int j = lq; j < k; j += 4) topk_w[(size_t)t * k + j] = renormalize ? pw[j] * scale : pw[j];
+  }
 }
 
 // The fused router applies to bf16, E a multiple of 8 up to 64 and T >= 4096 (at least
