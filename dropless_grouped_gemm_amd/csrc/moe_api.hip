@@ -59,10 +59,15 @@ static moe_status check_shape(const moe_shape* sp) {
   // one expert matrix is indexed with 32-bit element offsets
   const int64_t de_max = s.d_e > s.d_e_shared ? s.d_e : s.d_e_shared;
   if ((int64_t)s.d * de_max >= (int64_t)1 << 31) return MOE_ENOTSUP;
-  // the padded row space must stay addressable with int32 row indices
+  // the tiles of the block table must stay addressable with int32 row indices: those of
+  // the padded layout and, unpadded, those of its own table (ceil(T*k / block_m) tiles
+  // plus up to E - 1 entries for tiles shared by two experts)
   const int64_t M = (int64_t)s.T * s.k;
-  const int64_t mb = (M + (int64_t)(M < s.E ? M : s.E) * (s.block_m - 1)) / s.block_m;
+  const int64_t ne = M < s.E ? M : s.E;
+  const int64_t mb = (M + ne * (s.block_m - 1)) / s.block_m;
   if (mb * s.block_m >= (int64_t)1 << 31) return MOE_EINVAL;
+  if (s.unpadded && M > 0 && (ceil_div(M, s.block_m) + ne - 1) * s.block_m >= (int64_t)1 << 31)
+    return MOE_EINVAL;
   return MOE_OK;
 }
 

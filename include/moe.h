@@ -52,7 +52,9 @@ typedef int32_t moe_status;
 /*
  * The layer's shape.
  *   T >= 0 tokens (T == 0 is a no-op); d, d_e >= 1 with d % 8 == 0 and d_e % 8 == 0
- *   (bf16) or % 4 == 0 (fp32); 1 <= E <= 1024; 1 <= k <= 1024; T * k < 2^31.  The
+ *   (bf16) or % 4 == 0 (fp32); 1 <= E <= 1024; 1 <= k <= 1024; T * k < 2^31, and
+ *   the block-table bound times block_m < 2^31, for the padded bound of moe_max_blocks
+ *   and, unpadded, for the unpadded one too (MOE_EINVAL otherwise).  The
  *   router picks k distinct experts, so routing (moe_route, moe_layer_fwd without
  *   given routes) needs k <= E; rows routed elsewhere may repeat an expert within a
  *   token (k > E is then allowed).

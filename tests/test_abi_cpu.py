@@ -63,6 +63,9 @@ BAD_SHAPES = [
     (dict(block_m=32), B.MOE_ENOTSUP),         # bf16 grouped GEMM works in 128-row tiles
     (dict(d_e_shared=12), B.MOE_EINVAL),
     (dict(T=1 << 29, k=4), B.MOE_EINVAL),      # T*k >= 2^31
+    # the padded bound fits 2^31 rows (2^31 - 128), the unpadded table's
+    # (ceil(T*k / 128) + E - 1) * 128 does not
+    (dict(T=16776199 * 128, k=1, E=1024, unpadded=1), B.MOE_EINVAL),
 ]
 
 
