@@ -8,6 +8,7 @@ if the library is missing, ``lib()`` raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -16,10 +17,14 @@ import torch  # loads the HIP runtime libmoe.so links against (same soname)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
+# the same library built with MOE_DEBUG (kernels report the indices they skip or clamp)
+DEBUG_LIB_PATH = os.path.join(HERE, "libmoe_debug.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 MOE_OP_GATEUP_SWIGLU, MOE_OP_DOWN = 0, 1
+(MOE_DBG_BLOCK_TABLE, MOE_DBG_BLOCK_COUNT, MOE_DBG_POSITION, MOE_DBG_GATHER_ROW,
+ MOE_DBG_EXPERT_ID) = 0x1, 0x2, 0x4, 0x8, 0x10
 
 ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspace_bytes",
                 "moe_workspace_layout", "moe_route", "moe_build_offsets", "moe_permute",
@@ -33,7 +38,7 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
                 "moe_router_bwd", "moe_router_bwd_workspace_bytes",
                 "moe_grouped_gemm_dgrad_workspace_bytes",
                 "moe_bwd_workspace_bytes",
-                "moe_bwd_workspace_layout", "moe_layer_bwd")
+                "moe_bwd_workspace_layout", "moe_layer_bwd", "moe_debug_flags")
 
 
 class moe_shape(ctypes.Structure):
@@ -67,89 +72,120 @@ class MoEError(RuntimeError):
 
 
 _lib = None
+_debug_lib = None
+_active = None   # the library the wrappers call inside debug_library()
 
 
 def lib():
-    """Load libmoe.so once; raise if it has not been built."""
+    """Load libmoe.so once; raise if it has not been built.  Inside debug_library() the
+    debug variant instead."""
     global _lib
+    if _active is not None:
+        return _active
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m dropless_grouped_gemm_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        S = ctypes.POINTER(moe_shape)
-        L.moe_status_str.argtypes = [ctypes.c_int32]
-        L.moe_status_str.restype = ctypes.c_char_p
-        L.moe_max_blocks.argtypes = [S]
-        L.moe_max_blocks.restype = ctypes.c_int32
-        L.moe_max_rows.argtypes = [S]
-        L.moe_max_rows.restype = ctypes.c_int64
-        L.moe_workspace_bytes.argtypes = [S]
-        L.moe_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_workspace_layout.argtypes = [S, ctypes.POINTER(moe_ws_layout)]
-        L.moe_workspace_layout.restype = ctypes.c_int32
-        L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        L.moe_route.restype = ctypes.c_int32
-        L.moe_build_offsets.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        L.moe_build_offsets.restype = ctypes.c_int32
-        L.moe_build_offsets_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
-        L.moe_build_offsets_noalloc.restype = ctypes.c_int32
-        L.moe_build_offsets_noalloc_capacity.argtypes = []
-        L.moe_build_offsets_noalloc_capacity.restype = ctypes.c_size_t
-        L.moe_build_offsets_scratch_bytes.argtypes = [S]
-        L.moe_build_offsets_scratch_bytes.restype = ctypes.c_size_t
-        L.moe_permute.argtypes = [S, P, P, P, P]
-        L.moe_permute.restype = ctypes.c_int32
-        L.moe_grouped_gemm.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
-        L.moe_grouped_gemm.restype = ctypes.c_int32
-        L.moe_grouped_gemm_shared.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P,
-                                              P, P, P, P, P]
-        L.moe_grouped_gemm_shared.restype = ctypes.c_int32
-        L.moe_grouped_gemm_gather.argtypes = [S, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
-        L.moe_grouped_gemm_gather.restype = ctypes.c_int32
-        L.moe_quantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
-        L.moe_quantize_fp8.restype = ctypes.c_int32
-        L.moe_dequantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
-        L.moe_dequantize_fp8.restype = ctypes.c_int32
-        L.moe_fp8_workspace_bytes.argtypes = [S]
-        L.moe_fp8_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_grouped_gemm_fp8.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32,
-                                           P, P, P, P, P, P, P, P, P]
-        L.moe_grouped_gemm_fp8.restype = ctypes.c_int32
-        L.moe_layer_fwd_fp8.argtypes = [S] + [P] * 19 + [ctypes.c_size_t, P]
-        L.moe_layer_fwd_fp8.restype = ctypes.c_int32
-        L.moe_combine.argtypes = [S, P, P, P, P, P, P]
-        L.moe_combine.restype = ctypes.c_int32
-        L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        L.moe_layer_fwd.restype = ctypes.c_int32
-        L.moe_combine_bwd.argtypes = [S, P, P, P, P, P, P, P]
-        L.moe_combine_bwd.restype = ctypes.c_int32
-        L.moe_swiglu_bwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P]
-        L.moe_swiglu_bwd.restype = ctypes.c_int32
-        L.moe_grouped_gemm_dgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P,
-                                             ctypes.c_size_t, P]
-        L.moe_grouped_gemm_dgrad_workspace_bytes.argtypes = [S, ctypes.c_int32]
-        L.moe_grouped_gemm_dgrad_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_grouped_gemm_dgrad.restype = ctypes.c_int32
-        L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P,
-                                             ctypes.c_size_t, P]
-        L.moe_grouped_gemm_wgrad_workspace_bytes.argtypes = [S]
-        L.moe_grouped_gemm_wgrad_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_grouped_gemm_wgrad.restype = ctypes.c_int32
-        L.moe_router_bwd.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
-        L.moe_router_bwd_workspace_bytes.argtypes = [S]
-        L.moe_router_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_router_bwd.restype = ctypes.c_int32
-        L.moe_bwd_workspace_bytes.argtypes = [S]
-        L.moe_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.moe_bwd_workspace_layout.argtypes = [S, ctypes.POINTER(moe_bwd_ws_layout)]
-        L.moe_bwd_workspace_layout.restype = ctypes.c_int32
-        L.moe_layer_bwd.argtypes = ([S] + [P] * 12 + [ctypes.c_size_t] + [P] * 11 +
-                                    [ctypes.c_size_t, P])
-        L.moe_layer_bwd.restype = ctypes.c_int32
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def debug_lib():
+    """Load libmoe_debug.so once; raise if it has not been built."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+@contextlib.contextmanager
+def debug_library():
+    """Every wrapper called inside the block runs libmoe_debug.so."""
+    global _active
+    prev = _active
+    _active = debug_lib()
+    try:
+        yield _active
+    finally:
+        _active = prev
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m dropless_grouped_gemm_amd.build`")
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    S = ctypes.POINTER(moe_shape)
+    L.moe_status_str.argtypes = [ctypes.c_int32]
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_max_blocks.argtypes = [S]
+    L.moe_max_blocks.restype = ctypes.c_int32
+    L.moe_max_rows.argtypes = [S]
+    L.moe_max_rows.restype = ctypes.c_int64
+    L.moe_workspace_bytes.argtypes = [S]
+    L.moe_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_workspace_layout.argtypes = [S, ctypes.POINTER(moe_ws_layout)]
+    L.moe_workspace_layout.restype = ctypes.c_int32
+    L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_route.restype = ctypes.c_int32
+    L.moe_build_offsets.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_build_offsets.restype = ctypes.c_int32
+    L.moe_build_offsets_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+    L.moe_build_offsets_noalloc.restype = ctypes.c_int32
+    L.moe_build_offsets_noalloc_capacity.argtypes = []
+    L.moe_build_offsets_noalloc_capacity.restype = ctypes.c_size_t
+    L.moe_build_offsets_scratch_bytes.argtypes = [S]
+    L.moe_build_offsets_scratch_bytes.restype = ctypes.c_size_t
+    L.moe_permute.argtypes = [S, P, P, P, P]
+    L.moe_permute.restype = ctypes.c_int32
+    L.moe_grouped_gemm.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P]
+    L.moe_grouped_gemm.restype = ctypes.c_int32
+    L.moe_grouped_gemm_shared.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P,
+                                          P, P, P, P, P]
+    L.moe_grouped_gemm_shared.restype = ctypes.c_int32
+    L.moe_grouped_gemm_gather.argtypes = [S, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P]
+    L.moe_grouped_gemm_gather.restype = ctypes.c_int32
+    L.moe_quantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+    L.moe_quantize_fp8.restype = ctypes.c_int32
+    L.moe_dequantize_fp8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]
+    L.moe_dequantize_fp8.restype = ctypes.c_int32
+    L.moe_fp8_workspace_bytes.argtypes = [S]
+    L.moe_fp8_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_grouped_gemm_fp8.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32,
+                                       P, P, P, P, P, P, P, P, P]
+    L.moe_grouped_gemm_fp8.restype = ctypes.c_int32
+    L.moe_layer_fwd_fp8.argtypes = [S] + [P] * 19 + [ctypes.c_size_t, P]
+    L.moe_layer_fwd_fp8.restype = ctypes.c_int32
+    L.moe_combine.argtypes = [S, P, P, P, P, P, P]
+    L.moe_combine.restype = ctypes.c_int32
+    L.moe_layer_fwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_layer_fwd.restype = ctypes.c_int32
+    L.moe_combine_bwd.argtypes = [S, P, P, P, P, P, P, P]
+    L.moe_combine_bwd.restype = ctypes.c_int32
+    L.moe_swiglu_bwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P]
+    L.moe_swiglu_bwd.restype = ctypes.c_int32
+    L.moe_grouped_gemm_dgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, ctypes.c_int32, P, P,
+                                         ctypes.c_size_t, P]
+    L.moe_grouped_gemm_dgrad_workspace_bytes.argtypes = [S, ctypes.c_int32]
+    L.moe_grouped_gemm_dgrad_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_grouped_gemm_dgrad.restype = ctypes.c_int32
+    L.moe_grouped_gemm_wgrad.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P,
+                                         ctypes.c_size_t, P]
+    L.moe_grouped_gemm_wgrad_workspace_bytes.argtypes = [S]
+    L.moe_grouped_gemm_wgrad_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_grouped_gemm_wgrad.restype = ctypes.c_int32
+    L.moe_router_bwd.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
+    L.moe_router_bwd_workspace_bytes.argtypes = [S]
+    L.moe_router_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_router_bwd.restype = ctypes.c_int32
+    L.moe_bwd_workspace_bytes.argtypes = [S]
+    L.moe_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_bwd_workspace_layout.argtypes = [S, ctypes.POINTER(moe_bwd_ws_layout)]
+    L.moe_bwd_workspace_layout.restype = ctypes.c_int32
+    L.moe_layer_bwd.argtypes = ([S] + [P] * 12 + [ctypes.c_size_t] + [P] * 11 +
+                                [ctypes.c_size_t, P])
+    L.moe_layer_bwd.restype = ctypes.c_int32
+    L.moe_debug_flags.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]
+    L.moe_debug_flags.restype = ctypes.c_int32
+    return L
 
 
 def status_str(status: int) -> str:
@@ -198,6 +234,14 @@ def moe_max_blocks(shape: moe_shape) -> int:
 
 def moe_max_rows(shape: moe_shape) -> int:
     return lib().moe_max_rows(ctypes.byref(shape))
+
+
+def moe_debug_flags(clear: bool = True) -> int:
+    """MOE_DBG_* bits the debug library's kernels set on the current device since the last
+    clear (synchronises the device); raises MoEError(MOE_ENOTSUP) on the release library."""
+    v = ctypes.c_uint32(0)
+    _check("moe_debug_flags", lib().moe_debug_flags(ctypes.byref(v), int(bool(clear))))
+    return v.value
 
 
 def moe_workspace_bytes(shape: moe_shape) -> int:

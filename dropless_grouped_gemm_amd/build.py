@@ -1,6 +1,9 @@
-"""Build libmoe.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+"""Build libmoe.so (the HIP kernels and the C ABI) for gfx950, in-tree, and its debug
+variant libmoe_debug.so (MOE_DEBUG: the kernels' bounds checks also report what they
+skip or clamp, read back with moe_debug_flags).
 
-    python -m dropless_grouped_gemm_amd.build
+    python -m dropless_grouped_gemm_amd.build           # both
+    python -m dropless_grouped_gemm_amd.build release   # libmoe.so only
 
 Packed-fp32 instructions are disabled for all device code: the compiler would
 otherwise form v_pk_* fp32 operations from ordinary float code.
@@ -16,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe.so")
+DEBUG_LIB = os.path.join(HERE, "libmoe_debug.so")
 SOURCES = ["moe_api.hip", "moe_route.hip", "moe_offsets.hip", "moe_permute.hip", "moe_gemm.hip", "moe_gemm_wide.hip", "moe_fp8.hip", "moe_backward.hip"]
 
 
@@ -26,12 +30,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, arch: str = "gfx950", jobs: int = 8) -> str:
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, arch: str = "gfx950", debug: bool = False) -> str:
+    objdir = os.path.join(HERE, "_build_debug" if debug else "_build")
     os.makedirs(objdir, exist_ok=True)
     common = [hipcc(), f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-I", os.path.join(ROOT, "include"), "-Wno-pass-failed"]
+    if debug:
+        common.append("-DMOE_DEBUG")
+    lib_path = DEBUG_LIB if debug else LIB
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
@@ -53,12 +60,22 @@ def build(verbose: bool = False, arch: str = "gfx950", jobs: int = 8) -> str:
             print("\n".join(lines))
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={arch}", "-shared", "-fPIC", "-o", tmp] + objs
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build_all(verbose: bool = False) -> None:
+    """The release library and the debug variant."""
+    build(verbose=verbose)
+    build(verbose=verbose, debug=True)
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "release" in sys.argv:
+        print(build(verbose="-v" in sys.argv))
+    else:
+        build_all(verbose="-v" in sys.argv)
+        print(LIB, DEBUG_LIB)

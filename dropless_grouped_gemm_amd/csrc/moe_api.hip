@@ -169,11 +169,38 @@ static void bwd_layout_of(const moe_shape& s, moe_bwd_ws_layout& L) {
   L.total = cur;
 }
 
+#ifdef MOE_DEBUG
+// The debug word readers of the library's source files, registered while the library
+// loads (zero-initialised storage, so the order of the units' initialisers is free).
+static moe_status (*g_debug_readers[16])(uint32_t*, bool);
+static int g_debug_nreaders;
+int debug_register(moe_status (*read)(uint32_t*, bool)) {
+  if (g_debug_nreaders < 16) g_debug_readers[g_debug_nreaders++] = read;
+  return g_debug_nreaders;
+}
+#endif
+
 }  // namespace moe
 
 using namespace moe;
 
 extern "C" {
+
+moe_status moe_debug_flags(uint32_t* flags, int32_t clear) {
+  if (!flags) return MOE_EINVAL;
+  *flags = 0;
+#ifdef MOE_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
+  for (int i = 0; i < g_debug_nreaders; ++i) {
+    const moe_status st = g_debug_readers[i](flags, clear != 0);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+#else
+  (void)clear;
+  return MOE_ENOTSUP;
+#endif
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {

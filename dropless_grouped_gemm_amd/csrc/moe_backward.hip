@@ -77,6 +77,7 @@ k_combine_bwd(const u32x4_t* __restrict__ dout, const u32x4_t* __restrict__ y,
       auto use_row = [&](int j, const u32x4_t* yv) {
         const int p = pos[(size_t)t * k + j];
         const bool ok = p >= 0 && p < max_rows;
+        if (p < -1 || p >= max_rows) MOE_DEBUG_REPORT(MOE_DBG_POSITION);
         const float wj = w[(size_t)t * k + j];
         float dot = 0.f;
         if (ok) {
@@ -169,7 +170,7 @@ k_gg_nt(NTOperands ops, int K, int N, const int32_t* __restrict__ meta,
   // items: (block, 128-row sub-tile, 512-column tile); a dense set uses 128-row blocks
   const int bm = dense_rows > 0 ? 128 : block_m;
   const int nsub = bm / 128;
-  const int nblocks = dense_rows > 0 ? (dense_rows + 127) / 128 : max(0, min(num_blocks_ptr[0], max_blocks));
+  const int nblocks = dense_rows > 0 ? (dense_rows + 127) / 128 : clamp_block_count(num_blocks_ptr, max_blocks);
   const int total = nblocks * nsub * n_tiles;
   const int nk = K / kBBK;
   for (int w = blockIdx.x; w < total; w += gridDim.x) {

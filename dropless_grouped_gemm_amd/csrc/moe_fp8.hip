@@ -179,7 +179,7 @@ k_gg_fp8w(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb_dense = (dense_rows + 127) / 128;
-  const int nblocks = nb_dense + (max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0);
+  const int nblocks = nb_dense + (max_blocks > 0 ? clamp_block_count(num_blocks_ptr, max_blocks) : 0);
   const int total = nblocks * n_tiles;
   const int nk = K / kFBK;
   const int KB = (K + kQBlock - 1) / kQBlock, NBq = (N + kQBlock - 1) / kQBlock;
@@ -442,7 +442,7 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb_dense = (dense_rows + 127) / 128;
-  const int nblocks = nb_dense + (max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0);
+  const int nblocks = nb_dense + (max_blocks > 0 ? clamp_block_count(num_blocks_ptr, max_blocks) : 0);
   // items (half, block, column tile), half outermost: decode blocks rarely have a second
   // half, and with the half inner a persistent grid would give some work groups only
   // empty items

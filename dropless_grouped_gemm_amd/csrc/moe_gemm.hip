@@ -59,7 +59,7 @@ k_gg_bf16(const bf16_t* __restrict__ A, const bf16_t* __restrict__ B0,
   constexpr int kOutCols = OP == MOE_OP_GATEUP_SWIGLU ? 128 : 256;
   const int tpb = block_m / kBM;  // 128-row sub-tiles per metadata block
   const int nblocks =
-      dense_rows > 0 ? (dense_rows + block_m - 1) / block_m : max(0, min(num_blocks_ptr[0], max_blocks));
+      dense_rows > 0 ? (dense_rows + block_m - 1) / block_m : clamp_block_count(num_blocks_ptr, max_blocks);
   const int total = nblocks * tpb * n_tiles;
   const int nk = (K + kBK - 1) / kBK;
 
@@ -263,7 +263,7 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
   constexpr int kOutCols = GU ? 256 : 512;
   const int tpb = block_m / kBM;
   const int nb_dense = (dense_rows + block_m - 1) / block_m;
-  const int nblocks = nb_dense + (max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0);
+  const int nblocks = nb_dense + (max_blocks > 0 ? clamp_block_count(num_blocks_ptr, max_blocks) : 0);
   const int total = nblocks * tpb * n_tiles;
   const int nk = K / kV2BK;
 
@@ -574,7 +574,7 @@ k_gg_f32(const float* __restrict__ A, const float* __restrict__ B0, const float*
   const int tid = threadIdx.x;
   const int tpb = (block_m + kFM - 1) / kFM;
   const int nblocks =
-      dense_rows > 0 ? (dense_rows + block_m - 1) / block_m : max(0, min(num_blocks_ptr[0], max_blocks));
+      dense_rows > 0 ? (dense_rows + block_m - 1) / block_m : clamp_block_count(num_blocks_ptr, max_blocks);
   const int total = nblocks * tpb * n_tiles;
   const int ty = tid / 16, tx = tid % 16;  // rows ty*2 + {0,1}, cols tx*4 + {0..3}
   for (int w = blockIdx.x; w < total; w += gridDim.x) {

@@ -99,6 +99,7 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 
 __device__ __forceinline__ int gather_row(const GGOperands& ops, int r) {
   const int src = ops.gather[r] / ops.gather_div;
+  if (src < 0 || src >= ops.gather_rows) MOE_DEBUG_REPORT(MOE_DBG_GATHER_ROW);
   return min(max(src, 0), ops.gather_rows - 1);
 }
 
@@ -123,9 +124,11 @@ __device__ __forceinline__ bool decode_block(int b, int sub, int sub_rows, int b
   t.e = e;
   t.m0 = m_start + sub * sub_rows;
   t.valid = min(sub_rows, vm - sub * sub_rows);
-  // a table entry that does not fit the expert range or the row buffers is skipped
-  if (e < 0 || e >= E || m_start < 0 || vm > block_m || (int64_t)m_start + vm > max_rows)
-    return false;
+  // a table entry that does not fit the expert range or the row buffers is skipped (an
+  // entry without rows runs nothing either way)
+  const bool bad = e < 0 || e >= E || m_start < 0 || vm > block_m || (int64_t)m_start + vm > max_rows;
+  if (bad || vm < 1) MOE_DEBUG_REPORT(MOE_DBG_BLOCK_TABLE);
+  if (bad) return false;
   return t.valid > 0;
 }
 

@@ -104,7 +104,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = max_blocks > 0 ? max(0, min(num_blocks_ptr[0], max_blocks)) : 0;
+  const int nb = max_blocks > 0 ? clamp_block_count(num_blocks_ptr, max_blocks) : 0;
 
   // ---- group list ----------------------------------------------------------------
   // Built in the ring while it is idle: the table is staged at s_meta, then wave 0 forms
@@ -133,8 +133,10 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       const int per = (nb + 63) / 64;
       const int lo = min(lane * per, nb), hi = min(lo + per, nb);
       int last_rs = -1;
-      for (int b = lo; b < hi; ++b)
+      for (int b = lo; b < hi; ++b) {
+        if (!ok(b)) MOE_DEBUG_REPORT(MOE_DBG_BLOCK_TABLE);
         if (ok(b) && !joins(b)) last_rs = b;
+      }
       int incl = last_rs;
       for (int off = 1; off < 64; off <<= 1) {
         const int o = __shfl_up(incl, off, 64);

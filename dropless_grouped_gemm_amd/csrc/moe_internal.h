@@ -45,6 +45,39 @@ template <> struct Elem<bf16_t> {
 // SiLU in fp32: z * sigmoid(z) = z / (1 + exp(-z)).
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// ---- debug builds (-DMOE_DEBUG) ---------------------------------------------------
+// Where a kernel skips or clamps an index it cannot use, MOE_DEBUG_REPORT(bits) ORs
+// MOE_DBG_* bits into this translation unit's word on the device (each source file of
+// the library has its own; moe_debug_flags reads all of them).  Release builds compile
+// the reports away, leaving the checks themselves as they are.
+#ifdef MOE_DEBUG
+static __device__ uint32_t g_debug_word;
+__device__ __forceinline__ void debug_report(uint32_t bits) { atomicOr(&g_debug_word, bits); }
+#define MOE_DEBUG_REPORT(bits) ::moe::debug_report(bits)
+// Registers a reader of one unit's word; moe_debug_flags calls every registered reader.
+int debug_register(moe_status (*read)(uint32_t* acc, bool clear));
+static moe_status debug_read_unit(uint32_t* acc, bool clear) {
+  uint32_t w = 0;
+  if (hipMemcpyFromSymbol(&w, HIP_SYMBOL(g_debug_word), sizeof w) != hipSuccess) return MOE_EHIP;
+  *acc |= w;
+  const uint32_t zero = 0;
+  if (clear && hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &zero, sizeof zero) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+[[maybe_unused]] static const int g_debug_registered = debug_register(&debug_read_unit);
+#else
+#define MOE_DEBUG_REPORT(bits) ((void)0)
+#endif
+
+// The block count a kernel runs: *num_blocks, clamped into [0, max_blocks] (the host's
+// bound sizes the launch and the buffers).
+__device__ __forceinline__ int clamp_block_count(const int32_t* num_blocks, int max_blocks) {
+  const int n = num_blocks[0];
+  if (n < 0 || n > max_blocks) MOE_DEBUG_REPORT(MOE_DBG_BLOCK_COUNT);
+  return max(0, min(n, max_blocks));
+}
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

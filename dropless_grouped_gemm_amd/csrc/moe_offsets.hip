@@ -129,7 +129,7 @@ __device__ int block_inclusive_scan(int v, int* sh_wave /*[16]*/) {
 
 __global__ void __launch_bounds__(kScanThreads)
 k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m, int unpadded,
-            int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+            int max_blocks, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
             int32_t* __restrict__ padded, int32_t* __restrict__ meta,
             int32_t* __restrict__ num_blocks, int32_t* __restrict__ err_flag) {
   __shared__ int sh_wave[16];
@@ -187,7 +187,9 @@ k_scan_meta(int32_t* __restrict__ hist, int64_t nchunks, int E, int block_m, int
   }
   __syncthreads();
   if (tid == 0) err_flag[0] = s_bad > 0 ? 1 : 0;
-  const int total_blocks = s_boff[E];
+  // at most moe_max_blocks entries by construction (the bound the buffers are sized at)
+  if (tid == 0 && s_boff[E] > max_blocks) MOE_DEBUG_REPORT(MOE_DBG_BLOCK_COUNT);
+  const int total_blocks = min(s_boff[E], max_blocks);
   for (int b = tid; b < total_blocks; b += kScanThreads) {
     // the last expert whose first block index is <= b (empty experts never match last)
     int lo = 0, hi = E - 1;
@@ -224,6 +226,12 @@ __global__ void k_scatter(const int32_t* __restrict__ idx, int64_t M, int E, int
     if (e >= 0 && e < E) {
       const int64_t ch = a / chunk;
       const int p = padded[e] + hist[ch * (E + 1) + e] + lrank[a];
+      // in range by construction (the scan's segment bases and the chunk ranks)
+      if (p < 0 || p >= max_rows) {
+        MOE_DEBUG_REPORT(MOE_DBG_POSITION);
+        pos[a] = -1;
+        continue;
+      }
       pos[a] = p;
       row_src[p] = (int32_t)a;
     } else {
@@ -262,7 +270,7 @@ moe_status launch_build_offsets(const moe_shape& s, const int32_t* topk_idx, int
     if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   }
   hipLaunchKernelGGL(k_scan_meta, dim3(1), dim3(kScanThreads), 0, st, hist, nchunks, s.E, s.block_m,
-                     s.unpadded, counts, offsets, padded, block_meta, num_blocks, err_flag);
+                     s.unpadded, (int)moe_max_blocks(&s), counts, offsets, padded, block_meta, num_blocks, err_flag);
   if (hipGetLastError() != hipSuccess) return MOE_EHIP;
   const int64_t max_rows = (int64_t)moe_max_rows(&s);
   const int64_t work = M > max_rows ? M : max_rows;

@@ -46,6 +46,7 @@ k_permute(const u32x4_t* __restrict__ x, const int32_t* __restrict__ pos, int T,
       const int pl = lane < nj ? pos[(size_t)t * k + j0 + lane] : -1;
       for (int jj = 0; jj < nj; ++jj) {
         const int p = __shfl(pl, jj, 64);
+        if (p < -1 || p >= max_rows) MOE_DEBUG_REPORT(MOE_DBG_POSITION);
         if (p < 0 || p >= max_rows) continue;
         u32x4_t* dst = x_perm + (size_t)p * nvec;
 #pragma unroll
@@ -132,6 +133,7 @@ k_combine(const u32x4_t* __restrict__ y, const int32_t* __restrict__ pos,
         for (int u = 0; u < kCombSlots; ++u) {
           const int p = __shfl(pl, min(jj + u, 63), 64);
           ok[u] = jj + u < nj && p >= 0 && p < max_rows;
+          if (jj + u < nj && (p < -1 || p >= max_rows)) MOE_DEBUG_REPORT(MOE_DBG_POSITION);
           const u32x4_t* src = y + (size_t)(ok[u] ? p : 0) * nvec;
 #pragma unroll
           for (int i = 0; i < kCombVec; ++i) {

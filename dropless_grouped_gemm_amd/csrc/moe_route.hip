@@ -324,8 +324,8 @@ static inline int select_lanes(int E) {
 // write slot j from lane j % G.
 template <int G, int PER>
 __device__ __forceinline__ void select_rounds(const float* l, const float* z, const bool* elig,
-                                              float S, int k, int renormalize, bool live, int t,
-                                              int lt, int base_lane,
+                                              float S, int E, int k, int renormalize, bool live,
+                                              int t, int lt, int base_lane,
                                               int32_t* __restrict__ topk_idx,
                                               float* __restrict__ topk_w) {
   uint64_t key[PER];
@@ -365,6 +365,7 @@ __device__ __forceinline__ void select_rounds(const float* l, const float* z, co
   for (int q = 0; q < PER; ++q) {
     const int j = lt + G * q;
     if (j < k) {
+      if (my_idx[q] < 0 || my_idx[q] >= E) MOE_DEBUG_REPORT(MOE_DBG_EXPERT_ID);
       topk_idx[(size_t)t * k + j] = my_idx[q];
       topk_w[(size_t)t * k + j] = renormalize ? my_w[q] * scale : my_w[q];
     }
@@ -426,7 +427,7 @@ __device__ __forceinline__ void select_token(const float* lrow, int E, int k, in
 #pragma unroll
     for (int r = 0; r < PER; ++r) elig[r] = has[r] && ((keep >> ((lt + G * r) / gs)) & 1ull);
   }
-  select_rounds<G, PER>(l, z, elig, S, k, renormalize, live, t, lt, base_lane, topk_idx, topk_w);
+  select_rounds<G, PER>(l, z, elig, S, E, k, renormalize, live, t, lt, base_lane, topk_idx, topk_w);
 }
 
 // The selection kernel after the split-K router: G lanes per token add the splits'
@@ -781,6 +782,7 @@ k_route_fused(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
     const float p = expf(mq - m) / S;
     wsum += p;
     if (lq == (j & 3)) {
+      if (t < T && (id < 0 || id >= E)) MOE_DEBUG_REPORT(MOE_DBG_EXPERT_ID);
       if (t < T) topk_idx[(size_t)t * k + j] = id;
       pw[j] = p;
     }

@@ -24,7 +24,8 @@
  *     *err_flag to 1 on the device; the outputs are then unspecified.
  *   - Results are bitwise reproducible run to run: no floating-point atomics, and
  *     every reduction has a fixed order.
- *   - Entry points are reentrant; the library keeps no mutable global state.
+ *   - Entry points are reentrant; the library keeps no mutable global state (a
+ *     debug build keeps one word per device, see moe_debug_flags).
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -540,6 +541,30 @@ typedef struct moe_ws_layout {
          scratch, total;
 } moe_ws_layout;
 moe_status moe_workspace_layout(const moe_shape* s, moe_ws_layout* layout);
+
+/*
+ * Debug builds (the library compiled with MOE_DEBUG defined: libmoe_debug.so next to
+ * libmoe.so).  The kernels check what they index with before they use it, and skip or
+ * clamp what does not fit; a release build does so silently, a debug build also sets
+ * a bit of a word kept on each device, so that bad tables and positions handed to an
+ * entry point, or produced by an earlier stage, become visible:
+ */
+#define MOE_DBG_BLOCK_TABLE 0x1u  /* a block-table entry with an expert outside [0, E), a row
+                                     count outside [1, block_m] or rows beyond the row
+                                     buffers (the entry is skipped) */
+#define MOE_DBG_BLOCK_COUNT 0x2u  /* *num_blocks outside [0, max_blocks] (clamped), or a block
+                                     table longer than moe_max_blocks while it is built */
+#define MOE_DBG_POSITION    0x4u  /* a row position outside [-1, rows) (skipped) */
+#define MOE_DBG_GATHER_ROW  0x8u  /* a gathered A row outside the unpermuted rows (clamped) */
+#define MOE_DBG_EXPERT_ID   0x10u /* the router wrote an expert id outside [0, E) (NaN
+                                     logits; moe_build_offsets then flags it too) */
+/*
+ * OR of the bits set on the current device since the last clear, into *flags; with
+ * clear != 0 the word is reset.  Synchronises the device first, so it reports every
+ * kernel enqueued before the call.  Release builds: *flags = 0 and MOE_ENOTSUP.
+ * Errors: MOE_EINVAL for flags == NULL, MOE_EHIP if the device cannot be read.
+ */
+moe_status moe_debug_flags(uint32_t* flags, int32_t clear);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,32 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, fn), fn
 
 
+def test_debug_library_exports_every_declared_symbol():
+    L = B.debug_lib()
+    for fn in header_functions():
+        assert hasattr(L, fn), fn
+
+
+def test_debug_flags_on_release_and_debug_builds():
+    """The release library has no debug word: moe_debug_flags reports MOE_ENOTSUP (and 0)
+    without touching a device; both builds reject a NULL output."""
+    v = ctypes.c_uint32(7)
+    assert B.lib().moe_debug_flags(ctypes.byref(v), 1) == B.MOE_ENOTSUP
+    assert v.value == 0
+    assert B.lib().moe_debug_flags(None, 0) == B.MOE_EINVAL
+    assert B.debug_lib().moe_debug_flags(None, 0) == B.MOE_EINVAL
+    with B.debug_library():
+        assert B.lib() is B.debug_lib()
+    assert B.lib() is not B.debug_lib()
+
+
+def test_debug_bits_match_the_header():
+    text = open(HEADER).read()
+    bits = dict((n, int(v, 16)) for n, v in re.findall(r"#define (MOE_DBG_[A-Z_]+)\s+(0x[0-9a-f]+)u", text))
+    assert bits == {n: getattr(B, n) for n in bits} and len(bits) == 5
+    assert len(set(bits.values())) == 5 and all(v & (v - 1) == 0 for v in bits.values())
+
+
 def test_status_strings():
     assert B.status_str(B.MOE_OK) == "ok"
     assert "workspace" in B.status_str(B.MOE_EWORKSPACE)
