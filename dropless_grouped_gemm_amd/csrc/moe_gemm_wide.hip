@@ -18,9 +18,14 @@
 //     item: runs of such blocks, cut into threes from the start of each run.  The
 //     dense segment's groups are 384-row spans of its rows.
 //   * NW waves (4: one per SIMD, 384 accumulator registers each; 8: two per SIMD, 192
-//     each).  Wave w owns rows [(w / 2) * 768 / NW, ...) of the tile and column half
-//     w % 2.  GATEUP: 64 act columns, i.e. the matching 64 gate (W1) and 64 up (W3)
-//     columns, so SiLU*mul stays in registers; DOWN: 128 columns.
+//     each).  Wave w owns column half w % 2 of 32-row subtiles interleaved across the
+//     NW / 2 wave pairs: subtile i of pair p = w / 2 is tile rows (i NW/2 + p) 32 ..
+//     +31.  So a group of b blocks (rows below 128 b) leaves every wave about b live
+//     subtiles, and a wave multiplies only its live ones (the forward loop is
+//     specialised on their number, decided once per item), which balances the SIMDs
+//     on groups of one or two blocks.  GATEUP: 64 act columns, i.e. the matching 64
+//     gate (W1) and 64 up (W3) columns, so SiLU*mul stays in registers; DOWN: 128
+//     columns.
 //   * Operands move HBM -> LDS with 16-byte global_load_lds copies into a 4-slot ring of
 //     32-deep K slices (40 KB each, the whole LDS).  A is [384 rows][64 B] with the chunk swizzle
 //     c ^ ((row >> 2) & 3); B keeps its [k][n] layout (GATEUP: W1 and W3 regions of
@@ -72,6 +77,21 @@ __device__ __forceinline__ void wide_item(int slot, int ngt, int n_tiles, int& g
   const int tc = min(Ts, n_tiles - sc * Ts);
   g = sr * Gs + within / tc;
   t = sc * Ts + within % tc;
+}
+
+// f(std::integral_constant<int, clamp(n, 1, N)>): one instance per count, so that code
+// specialised on the count runs without branches inside it.  The full count is the
+// expected one and comes first (measured: without the hint the full-tile items of
+// ep-share's gate/up ran 1 % slower; without the zero-count instance a wave with no live
+// subtile multiplies one, whose rows are never stored).
+template <int N, class F>
+__device__ __forceinline__ void dispatch_live(int n, F&& f) {
+  if constexpr (N == 1) {
+    f(std::integral_constant<int, 1>{});
+  } else {
+    if (__builtin_expect(n >= N, 1)) f(std::integral_constant<int, N>{});
+    else dispatch_live<N - 1>(n, f);
+  }
 }
 
 template <int OP, int NW, bool FP8>
@@ -179,9 +199,9 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
 
   // Fixed per-lane parts of the fragment addresses, so that inside the loop an address
   // is slot base + one of these + an immediate.
-  //   A (ds_read_b128): row rbase + 32i + (l & 31), logical chunk 2kk + (l >> 5); the
+  //   A (ds_read_b128): row rsub(i) + (l & 31), logical chunk 2kk + (l >> 5); the
   //   swizzle c ^ ((row >> 2) & 3) sees the row only through (l >> 2) & 7, so subtile i
-  //   is the immediate 2048 * i and kk selects one of two lane offsets.
+  //   is the immediate 2048 NP i and kk selects one of two lane offsets.
   //   B (ds_read_b64_tr_b16): 16-lane group g, row r = (l & 15) >> 2, column quad
   //   c4 = l & 3; slice row k = 16kk + 8(g >> 1) + 4hh + r and column
   //   n = 32j' + 16(g & 1) + 4c4 of the wave's columns, at chunk (n >> 3) ^ 4r (k & 3 is r).
@@ -190,12 +210,15 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   //   lane offset depends on j (GATEUP: on j & 1, the W1/W3 region being an immediate).
   const int g = lane >> 4, tr_r = (lane & 15) >> 2, tr_c4 = lane & 3;
   const int ch = wave & 1;                 // column half
-  const int rbase = (wave >> 1) * WR;      // first tile row of the wave
+  constexpr int NP = NW / 2;               // wave pairs
+  const int rpair = wave >> 1;
+  // first tile row of the wave's subtile i
+  auto rsub = [&](int i) { return (i * NP + rpair) * 32; };
   constexpr int NBL = GU ? 2 : 4;          // distinct B lane offsets
   uint32_t a_lane[2], b_lane[NBL];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    const int row = rbase + (lane & 31);
+    const int row = rpair * 32 + (lane & 31);
     a_lane[kk] = (uint32_t)(row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
   }
 #pragma unroll
@@ -393,12 +416,15 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       }
       return o;
     };
-    auto read_frags = [&](int ks, int kk) {
+    // the fragments and MFMAs of the wave's first NL subtiles (its live ones)
+    auto read_frags = [&](int ks, int kk, auto nl_c) {
+      constexpr int NL = decltype(nl_c)::value;
+      if constexpr (NL == 0) return;
       const unsigned char* sa = lds + (ks % kStages) * kStage;
       const unsigned char* sb = sa + kWABytes;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + a_lane[kk] + i * 2048);
+      for (int i = 0; i < NL; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + a_lane[kk] + i * NP * 2048);
       if constexpr (FP8) {
         const int kb = (ks * kWBK) >> 7;
         s_g = sc0[(size_t)kb * NBq];
@@ -423,23 +449,26 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         }
       }
     };
-    auto mfma_block = [&]() {
+    auto mfma_block = [&](auto nl_c) {
+      constexpr int NL = decltype(nl_c)::value;
+      if constexpr (NL == 0) return;
       if constexpr (FP8) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x8_t b = j == 0 ? bf[0] : dequant(j);
 #pragma unroll
-          for (int i = 0; i < MI; ++i)
+          for (int i = 0; i < NL; ++i)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], b, acc[i][j], 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < NL; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
       }
     };
+    using AllSub = std::integral_constant<int, MI>;
 
     // Prologue: every slot in flight (slices past the end re-copy the last slice into a
     // slot that is never read again, so every slice issues the same number of copies
@@ -461,8 +490,13 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     //   reads completed before the barriers since), so its slot takes slice ks-1+S
     //   (down: its B copies in MEM(2 ks + 1)).  The wait counts whole slices: at
     //   MEM(2 ks) every slice up to ks-2+S has been issued in full.
+    // The loop is instantiated per number of live subtiles (1 .. MI); every instance
+    // issues the same copies and barriers.
+    const int live = __builtin_amdgcn_readfirstlane(
+        [&] { int n = 0; for (int i = 0; i < MI; ++i) n += rsub(i) < valid; return n; }());
     const bool lag = wave >= kWideLagFrom;
     if (lag) __syncthreads();
+    auto ping_pong = [&](auto nl_c) {
     for (int t = 0; t < 2 * nk; ++t) {
       const int ks = t >> 1, kk = t & 1;
       // the refill of slice ks-1's slot (after every wave's last read of slice ks-1):
@@ -488,16 +522,18 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
         for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
       }
-      read_frags(ks, kk);
+      read_frags(ks, kk, nl_c);
       // scheduling barriers keep each phase's instructions on its side of the barriers
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      mfma_block();
+      mfma_block(nl_c);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
+    };
+    dispatch_live<MI>(live, ping_pong);
     if (!lag) __syncthreads();
     } else {
     // The SwiGLU-backward op keeps the one-barrier slice loop: its epilogue's register
@@ -509,7 +545,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     for (int ks = 0; ks < nk; ++ks) {
       const int ksrc = min(ks - 1 + kStages, nk - 1);
       const int slot = (ks + kStages - 1) % kStages;
-      read_frags(ks, 0);
+      read_frags(ks, 0, AllSub{});
       if (ks > 0) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -523,9 +559,9 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
           }
         }
       } else {
-        mfma_block();
+        mfma_block(AllSub{});
       }
-      read_frags(ks, 1);
+      read_frags(ks, 1, AllSub{});
       if (ks > 0) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
@@ -538,7 +574,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
           }
         }
       } else {
-        mfma_block();
+        mfma_block(AllSub{});
       }
       if (ks + 1 < nk) {
         MOE_WAIT_VMCNT((kStages - 2) * CPW);   // slice ks+1 has landed
@@ -567,10 +603,10 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       const int dcc = dcol < N ? dcol : 0;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const int rsub = rbase + i * 32;
+        const int r0s = rsub(i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int r = rsub + 8 * j + (lane >> 3);
+          const int r = r0s + 8 * j + (lane >> 3);
           const int rr = r < valid ? r : 0;
           copy16_to_lds(dbase, (uint32_t)(rr * N + dcc) * 2u, sda + j * 1024);
         }
@@ -596,7 +632,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
 #pragma unroll
           for (int r0 = 0; r0 < 32; r0 += 8) {
             const int r = r0 + (lane >> 3);
-            const int grow = rsub + r;
+            const int grow = r0s + r;
             const u32x4_t v = *reinterpret_cast<const u32x4_t*>(so + (ps * 32 + r) * kLd + (lane & 7) * 8);
             if (grow < valid && dcol < N)
               *reinterpret_cast<u32x4_t*>(C + (size_t)(m0 + grow) * 2 * N + ps * N + dcol) = v;
@@ -637,7 +673,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       for (int r0 = 0; r0 < WR; r0 += 8) {
         const int r = r0 + (lane >> 3);
         const int c8 = lane & 7;
-        const int grow = rbase + r;
+        const int grow = rsub(r0 >> 5) + (r & 31);   // staging row r: subtile r / 32
         const int gcol = col0 + c8 * 8;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stg + r * kLd + c8 * 8);
         if (grow < valid && gcol < N)

@@ -253,6 +253,41 @@ def check_wide_item_order(ngt, n_tiles):
     assert seen == {(g, t) for g in range(ngt) for t in range(n_tiles)}
 
 
+def wide_subtile_row(wave, i, NW=8):
+    """First tile row of 32-row subtile i of a wave of the wide kernel: wave pair p = wave // 2
+    owns subtiles p, p + NW/2, p + NW, ... (interleaved), each with both column halves split
+    between the pair's two waves."""
+    return (i * (NW // 2) + (wave >> 1)) * 32
+
+
+def wide_live_subtiles(wave, valid, NW=8):
+    """Subtiles of the wave that hold a row below valid (the kernel multiplies only these)."""
+    MI = W_ROWS * 2 // NW // 32
+    return sum(1 for i in range(MI) if wide_subtile_row(wave, i, NW) < valid)
+
+
+def check_wide_row_split(NW=8):
+    """The waves' subtiles cover the tile's rows once per column half, and for every valid
+    count the live subtiles of each wave are its first ones and hold every valid row."""
+    MI = W_ROWS * 2 // NW // 32
+    for ch in (0, 1):
+        owned = np.zeros(W_ROWS, int)
+        for wave in range(ch, NW, 2):
+            for i in range(MI):
+                r0 = wide_subtile_row(wave, i, NW)
+                owned[r0:r0 + 32] += 1
+        assert np.all(owned == 1)
+    for valid in range(1, W_ROWS + 1):
+        for wave in range(NW):
+            n = wide_live_subtiles(wave, valid, NW)
+            rows = [wide_subtile_row(wave, i, NW) for i in range(MI)]
+            assert all(r < valid for r in rows[:n]) and all(r >= valid for r in rows[n:])
+        # a group of b blocks (valid in (128 (b-1), 128 b]) gives every wave at most b live
+        # subtiles, and b to the waves of every SIMD but the last rows'
+        b = -(-valid // 128)
+        assert max(wide_live_subtiles(w, valid, NW) for w in range(NW)) == b
+
+
 def check_wide_item(op, fp8, K, N, e, m0, valid, a_rows, n_e, gather=None, n_tiles_check=None):
     """Every copy, fragment read and store of one row group (all column tiles, or the
     listed ones) of k_gg_wide<op, 8, fp8>; slices 0 and the last.  gather: per-row source
@@ -330,9 +365,9 @@ def check_wide_item(op, fp8, K, N, e, m0, valid, a_rows, n_e, gather=None, n_til
             g, gi = lane >> 4, lane & 15
             tr_r, tr_c4 = gi >> 2, gi & 3
             for wave in range(NW):
-                ch, rbase = wave & 1, (wave >> 1) * WR
+                ch = wave & 1
                 for i in range(MI):
-                    row = rbase + i * 32 + (lane & 31)
+                    row = wide_subtile_row(wave, i, NW) + (lane & 31)
                     for kk in (0, 1):
                         addr = row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16
                         assert (addr + 16).max() <= W_ABYTES
@@ -371,11 +406,12 @@ def check_wide_item(op, fp8, K, N, e, m0, valid, a_rows, n_e, gather=None, n_til
                             assert np.all(got[live] == want[live]), ("B", op, fp8, wave, j, kk)
         # epilogue: a row r < valid of the group and an 8-column chunk c < N
         for wave in range(NW):
-            rbase = (wave >> 1) * WR
+            r = np.arange(WR)[:, None]
             for ps in range(1 if GU else 2):
                 col0 = n0 + ((wave & 1) * 64 if GU else (wave & 1) * 128 + ps * 64)
                 gcol = col0 + (lane & 7) * 8
-                grow = rbase + np.arange(WR)[:, None]
+                # staging row r of the wave holds tile row subtile_row(r // 32) + r % 32
+                grow = np.array([[wide_subtile_row(wave, int(x) // 32, NW) + int(x) % 32] for x in r[:, 0]])
                 ok = (grow < valid) & (gcol[None, :] < N)
                 rows = (m0 + grow) * np.ones_like(gcol)[None, :]
                 assert np.all(rows[ok] < a_rows) and np.all((gcol[None, :] * np.ones_like(grow) + 8)[ok] <= N)

@@ -112,6 +112,10 @@ def test_wide_gathered_a_rows():
                            gather=gather, n_tiles_check=[0])
 
 
+def test_wide_row_split():
+    KM.check_wide_row_split()
+
+
 @pytest.mark.parametrize("op,K,N", [(0, 7168, 2048), (1, 2048, 7168), (0, 512, 256),
                                     (1, 1280, 160), (0, 256, 384), (1, 160, 1280)])
 def test_fp8d_stage(op, K, N):
