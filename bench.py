@@ -155,6 +155,9 @@ def measure(args, cfg_name, weights="bf16", unpadded=False, steps=20, warmup=5, 
     # runs the bf16 kernels on them; the staged step does the same
     deq = fp8 and B.fp8_dequantises(s)
     fp8k = fp8 and not deq
+    # the fp8 GEMM's optional scratch (its weight-streaming kernel splits the last round of
+    # its persistent grid along K with it), as moe_layer_fwd_fp8's workspace holds it
+    gemm_ws = B.alloc_fp8_gemm_workspace(s, dev) if fp8k else None
     w1_, w3_, w2_ = inp.w1, inp.w3, inp.w2
     ws1_, ws3_, ws2_ = inp.ws1, inp.ws3, inp.ws2
     if deq:
@@ -205,7 +208,7 @@ def measure(args, cfg_name, weights="bf16", unpadded=False, steps=20, warmup=5, 
             B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, inp.x if gather else x_perm, *q1,
                                    *q3, meta, nblk, mb, row_src if gather else None, act,
                                    inp.x if shared else None, *qs1, *qs3,
-                                   sh_act if shared else None)
+                                   sh_act if shared else None, ws=gemm_ws)
         elif gather:
             B.moe_grouped_gemm_gather(s, inp.x, row_src, w1_, w3_, meta, nblk, mb, act,
                                       ws1_, ws3_, sh_act if shared else None)
@@ -227,7 +230,7 @@ def measure(args, cfg_name, weights="bf16", unpadded=False, steps=20, warmup=5, 
         if fp8k:
             B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, *q2, None, None, meta, nblk, mb, None, y,
                                    sh_act if shared else None, *qs2, None, None,
-                                   sh_out if shared else None)
+                                   sh_out if shared else None, ws=gemm_ws)
         elif shared:
             B.moe_grouped_gemm_shared(s, B.MOE_OP_DOWN, act, w2_, None, meta, nblk, mb, y,
                                       sh_act, ws2_, None, sh_out)

@@ -38,7 +38,8 @@ ENTRY_POINTS = ("moe_status_str", "moe_max_blocks", "moe_max_rows", "moe_workspa
                 "moe_router_bwd", "moe_router_bwd_workspace_bytes",
                 "moe_grouped_gemm_dgrad_workspace_bytes",
                 "moe_bwd_workspace_bytes",
-                "moe_bwd_workspace_layout", "moe_layer_bwd", "moe_debug_flags")
+                "moe_bwd_workspace_layout", "moe_layer_bwd", "moe_debug_flags",
+                "moe_grouped_gemm_fp8_workspace_bytes")
 
 
 class moe_shape(ctypes.Structure):
@@ -150,7 +151,9 @@ def _load(path):
     L.moe_fp8_workspace_bytes.argtypes = [S]
     L.moe_fp8_workspace_bytes.restype = ctypes.c_size_t
     L.moe_grouped_gemm_fp8.argtypes = [S, ctypes.c_int32, P, P, P, P, P, P, P, ctypes.c_int32,
-                                       P, P, P, P, P, P, P, P, P]
+                                       P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_grouped_gemm_fp8_workspace_bytes.argtypes = [S]
+    L.moe_grouped_gemm_fp8_workspace_bytes.restype = ctypes.c_size_t
     L.moe_grouped_gemm_fp8.restype = ctypes.c_int32
     L.moe_layer_fwd_fp8.argtypes = [S] + [P] * 19 + [ctypes.c_size_t, P]
     L.moe_layer_fwd_fp8.restype = ctypes.c_int32
@@ -366,8 +369,9 @@ def moe_fp8_workspace_bytes(shape: moe_shape) -> int:
 
 def fp8_dequantises(shape: moe_shape) -> bool:
     """moe_layer_fwd_fp8 dequantises the weights into its workspace and runs the bf16
-    kernels (its workspace then holds room for them)."""
-    return moe_fp8_workspace_bytes(shape) > moe_workspace_bytes(shape)
+    kernels: where the routed rows M = T * k reach 256 * min(E, M) (the header's rule)."""
+    M = shape.T * shape.k
+    return M > 0 and M >= 256 * min(shape.E, M)
 
 
 def fp8_scale_shape(w_shape):
@@ -386,11 +390,24 @@ def quantize_fp8(w, stream=None):
 
 def moe_grouped_gemm_fp8(shape, op, A, Q0, S0, Q1, S1, block_meta, num_blocks, max_blocks,
                          row_src, C, A_shared=None, Q0_shared=None, S0_shared=None,
-                         Q1_shared=None, S1_shared=None, C_shared=None, stream=None):
+                         Q1_shared=None, S1_shared=None, C_shared=None, ws=None, stream=None):
+    """ws: None, or a uint8 tensor of moe_grouped_gemm_fp8_workspace_bytes(shape) bytes."""
     _check("moe_grouped_gemm_fp8", lib().moe_grouped_gemm_fp8(
         ctypes.byref(shape), op, _p(A), _p(Q0), _p(S0), _p(Q1), _p(S1), _p(block_meta),
         _p(num_blocks), int(max_blocks), _p(row_src), _p(C), _p(A_shared), _p(Q0_shared),
-        _p(S0_shared), _p(Q1_shared), _p(S1_shared), _p(C_shared), _stream(stream)))
+        _p(S0_shared), _p(Q1_shared), _p(S1_shared), _p(C_shared), _p(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def moe_grouped_gemm_fp8_workspace_bytes(shape) -> int:
+    return lib().moe_grouped_gemm_fp8_workspace_bytes(ctypes.byref(shape))
+
+
+def alloc_fp8_gemm_workspace(shape, device="cuda") -> torch.Tensor:
+    """The optional scratch of moe_grouped_gemm_fp8 (uninitialised: every byte read is
+    first written by the same call)."""
+    return torch.empty(moe_grouped_gemm_fp8_workspace_bytes(shape), dtype=torch.uint8,
+                       device=device)
 
 
 def moe_layer_fwd_fp8(shape, x, w_gate, bias, q1, s1, q3, s3, q2, s2, qs1, ss1, qs3, ss3,

@@ -418,14 +418,14 @@ static moe_status run_fp8_op(const moe_shape& s, int op, const void* A, const ui
                              const int32_t* meta, const int32_t* nblk, int32_t mb,
                              const int32_t* row_src, void* C, const void* As,
                              const uint8_t* Q0s, const float* S0s, const uint8_t* Q1s,
-                             const float* S1s, void* Cs, hipStream_t st) {
+                             const float* S1s, void* Cs, float* tail, hipStream_t st) {
   const bool gu = op == MOE_OP_GATEUP_SWIGLU;
   const int K = gu ? s.d : s.d_e, N = gu ? s.d_e : s.d;
   const bool shared = As != nullptr;
   const int Ks = gu ? s.d : s.d_e_shared, Ns = gu ? s.d_e_shared : s.d;
   GemmSegmentsF8 g{A, Q0, S0, Q1, S1, C, K, N, meta, nblk, mb,
                    nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
-                   row_src, s.k, s.T};
+                   row_src, s.k, s.T, tail};
   // Experts averaging at most 64 rows (decode): the launch streams weights, and the
   // 64-row kernel reads them in wider rows.  At least 256 rows (and a block table the
   // wide kernel takes): compute-bound, the wide kernel with in-register dequantisation.
@@ -442,7 +442,7 @@ static moe_status run_fp8_op(const moe_shape& s, int op, const void* A, const ui
   }
   if (shared) {
     GemmSegmentsF8 d{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, Ks, Ns, nullptr, nullptr,
-                     0, As, Q0s, S0s, Q1s, S1s, Cs, s.T, nullptr, 1, 1};
+                     0, As, Q0s, S0s, Q1s, S1s, Cs, s.T, nullptr, 1, 1, tail};
     const Fp8Kernel dk = s.T <= 64 ? kFp8Rows64 : s.T >= 384 ? kFp8Wide : kFp8Rows128;
     moe_status st2 = launch_grouped_gemm_fp8(op, d, 1, s.T, dk, st);
     if (st2 != MOE_OK) return st2;
@@ -456,11 +456,13 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, c
                                 int32_t max_blocks, const int32_t* row_src, void* C,
                                 const void* A_shared, const uint8_t* Q0_shared,
                                 const float* S0_shared, const uint8_t* Q1_shared,
-                                const float* S1_shared, void* C_shared, void* stream) {
+                                const float* S1_shared, void* C_shared, void* ws,
+                                size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (op != MOE_OP_GATEUP_SWIGLU && op != MOE_OP_DOWN) return MOE_EINVAL;
   if ((st = check_fp8(*s)) != MOE_OK) return st;
+  if (ws && (!aligned16(ws) || ws_bytes < fp8_tail_scratch_bytes())) return MOE_EWORKSPACE;
   if (!fp8_operands_ok(op, A, Q0, S0, Q1, S1, C)) return MOE_EINVAL;
   if (!block_table_ok(*s, block_meta, num_blocks, max_blocks)) return MOE_EINVAL;
   if (row_src) {
@@ -476,7 +478,12 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A, c
   if (s->T == 0) return MOE_OK;
   return run_fp8_op(*s, op, A, Q0, S0, Q1, S1, block_meta, num_blocks, max_blocks, row_src, C,
                     shared ? A_shared : nullptr, Q0_shared, S0_shared, Q1_shared, S1_shared,
-                    C_shared, static_cast<hipStream_t>(stream));
+                    C_shared, static_cast<float*>(ws), static_cast<hipStream_t>(stream));
+}
+
+size_t moe_grouped_gemm_fp8_workspace_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return fp8_tail_scratch_bytes();
 }
 
 // The bf16 gate/up (rows gathered from x where the kernels can) and down launches of
@@ -515,8 +522,15 @@ static bool fp8_dequantised_path(const moe_shape& s) {
   return M > 0 && M >= 256 * (M < s.E ? M : (int64_t)s.E);
 }
 
+// Experts averaging at most 64 rows: the 64-row fp8 kernel streams the weights, and
+// scratch lets it split its last round along K.
+static bool fp8_streaming_path(const moe_shape& s) {
+  const int64_t M = (int64_t)s.T * s.k;
+  return M > 0 && M <= 64 * (M < s.E ? M : (int64_t)s.E);
+}
+
 struct Fp8Layout {
-  size_t w1, w3, w2, ws1, ws3, ws2, total;
+  size_t w1, w3, w2, ws1, ws3, ws2, tail, total;
 };
 static void fp8_layout_of(const moe_shape& s, const moe_ws_layout& L, Fp8Layout& F) {
   size_t cur = L.total;
@@ -528,6 +542,7 @@ static void fp8_layout_of(const moe_shape& s, const moe_ws_layout& L, Fp8Layout&
   F.ws1 = take(cur, deq ? d * ds * 2 : 0);
   F.ws3 = take(cur, deq ? d * ds * 2 : 0);
   F.ws2 = take(cur, deq ? ds * d * 2 : 0);
+  F.tail = take(cur, fp8_streaming_path(s) ? fp8_tail_scratch_bytes() : 0);
   F.total = cur;
 }
 
@@ -628,13 +643,16 @@ moe_status moe_layer_fwd_fp8(const moe_shape* s, const void* x, const void* w_ga
     return launch_combine(*s, at(L.y), pos, wts, shared ? at(L.shared_out) : nullptr, out, hs);
   }
   const int32_t mb = (int32_t)max_blocks_of(*s);
+  // the streaming kernel's last-round scratch, where the workspace has room for it
+  float* tail = (F8.total > F8.tail && ws_bytes >= F8.total) ? static_cast<float*>(at(F8.tail))
+                                                              : nullptr;
   st = run_fp8_op(*s, MOE_OP_GATEUP_SWIGLU, gather ? x : at(L.x_perm), q1, s1, q3, s3, meta, nblk,
                   mb, gather ? rsrc : nullptr, at(L.act), shared ? x : nullptr, qs1, ss1, qs3, ss3,
-                  shared ? at(L.shared_act) : nullptr, hs);
+                  shared ? at(L.shared_act) : nullptr, tail, hs);
   if (st != MOE_OK) return st;
   st = run_fp8_op(*s, MOE_OP_DOWN, at(L.act), q2, s2, nullptr, nullptr, meta, nblk, mb, nullptr,
                   at(L.y), shared ? at(L.shared_act) : nullptr, qs2, ss2, nullptr, nullptr,
-                  shared ? at(L.shared_out) : nullptr, hs);
+                  shared ? at(L.shared_out) : nullptr, tail, hs);
   if (st != MOE_OK) return st;
   const void* sh = shared ? at(L.shared_out) : nullptr;
   return launch_combine(*s, at(L.y), pos, wts, sh, out, hs);

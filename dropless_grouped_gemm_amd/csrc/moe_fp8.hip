@@ -418,6 +418,15 @@ k_gg_fp8w(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
 // (gate/up: W1 and the matching W3 columns) or 128 down columns, two 32-row subtiles x
 // four 32-column tiles of v_mfma_f32_32x32x16_bf16.  Fragments are dequantised in
 // registers as in k_gg_fp8w.
+//
+// Last round.  A persistent grid of G work groups runs the V items in ceil(V / G)
+// rounds, the last with only R = V mod G of them.  Given scratch (and a table whose
+// blocks all hold at most 64 rows, as decode's do), the kernel runs the first V - R
+// items as above and then spreads the R items' R * nk slices evenly over all G work
+// groups: work group q takes slices [q R nk / G, (q+1) R nk / G) of them, a contiguous
+// range that touches at most two items, and writes each piece's fp32 sums (valid rows)
+// to scratch slot 2q or 2q+1.  k_fp8d_tail then adds an item's pieces in slice order
+// (fixed, so the result does not depend on timing) and applies the epilogue.
 // ---------------------------------------------------------------------------
 static constexpr int kDRows = 64;                          // rows per work item
 static constexpr int kDABytes = kDRows * kFBK * 2;        // 4 KB of A per slice
@@ -425,12 +434,59 @@ static constexpr int kDBBytes = 32 * 1024;                // 32 KB of B per slic
 static constexpr int kDStage = kDABytes + kDBBytes;       // 36 KB
 static constexpr int kDStages = 4;
 static constexpr int kDBCopies = kDBBytes / 1024 / 8;     // 4 B copies per wave per slice
+// last-round scratch: a 256-byte header (the plan: on, F, R, written by work group 0),
+// then two slots per work group of at most kDTailGrid, each 64 rows x 1024 fp32
+// (gate/up: 512 gate sums then 512 up sums; down: 1024 sums)
+static constexpr int kDTailGrid = 256;
+static constexpr int kDTailCols = 1024;
+static constexpr int kDTailHeader = 64;                    // floats
+static constexpr size_t kDTailSlot = (size_t)kDRows * kDTailCols * 4;
+static constexpr int kDTailRowGroups = 8;                  // tail kernel: row strides
+
+size_t fp8_tail_scratch_bytes() { return kDTailHeader * 4 + 2 * (size_t)kDTailGrid * kDTailSlot; }
+
+// Whether the last round of a 64-row launch over G work groups splits along K, and its
+// shape: V items (all of them valid, the blocks' first halves), F full rounds, R items
+// left.  Every work group of both kernels derives the same answer from the table.
+struct FP8Tail {
+  int V, F, R;
+  bool on;
+};
+__device__ __forceinline__ bool fp8d_table_fits(const int32_t* __restrict__ meta, int nroutes,
+                                                int E, int64_t max_rows, int dense_rows,
+                                                int wave, int lane, int* s_flag) {
+  // one wave checks every entry (in range, 1..64 rows); the answer goes through LDS
+  if (wave == 0) {
+    bool bad = dense_rows > kDRows;
+    for (int b = lane; b < nroutes; b += 64) {
+      const int e = meta[3 * b], m = meta[3 * b + 1], v = meta[3 * b + 2];
+      bad |= e < 0 || e >= E || m < 0 || v < 1 || v > kDRows || (int64_t)m + v > max_rows;
+    }
+    const bool any = __ballot(bad) != 0ull;
+    if (lane == 0) *s_flag = any ? 0 : 1;
+  }
+  __syncthreads();
+  const bool fits = *s_flag != 0;
+  __syncthreads();
+  return fits;
+}
+__device__ __forceinline__ FP8Tail fp8d_tail_plan(bool fits, int per_half, int G) {
+  FP8Tail t;
+  t.V = per_half;
+  t.F = per_half / G;
+  t.R = per_half - t.F * G;
+  // worth it while the last round is at most 90 % full; with at least G / 16 items left
+  // every work group takes at least nk / 16 - 1 slices, so an item has at most 34 pieces
+  t.on = fits && G <= kDTailGrid && t.R > 0 && 10 * t.R <= 9 * G && 16 * t.R >= G;
+  return t;
+}
 
 template <int OP>
 __global__ void __launch_bounds__(kFThreads, 1)
 k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
           const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
-          int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles) {
+          int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles,
+          float* __restrict__ tail) {
   constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU;
   constexpr int kOutCols = GU ? 512 : 1024;               // output columns per item
   constexpr int kPitch = GU ? 512 : 1024;                 // bytes per staged B row (per matrix)
@@ -471,9 +527,11 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
     sidx[j] = GU ? region * 4 + (col0 >> 7) : (col0 >> 7);
   }
 
-  // One work item's operands.
+  // One work item's operands: slices [k0, k0 + n) of item w, written to C (slot < 0) or
+  // as fp32 sums to scratch slot `slot`.
   struct Item {
     int w;                        // item number, -1: none
+    int k0, n, slot;
     Tile tile;
     int n0;
     bool dense;
@@ -483,27 +541,24 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
     uint32_t b_voff[kDBCopies];
     int b_row[kDBCopies];
   };
-  // the first valid item at or after number w of this work group's sequence
-  auto find_item = [&](int w, Item& it) {
-    it.w = -1;
-    for (; w < total; w += gridDim.x) {
-      const int half = w / per_half;
-      const int rem = w - half * per_half;
-      const int nt = rem % n_tiles;
-      const int blk = rem / n_tiles;
-      const bool in_dense = blk < nb_dense;
-      bool ok;
-      if (in_dense)
-        ok = decode_block(blk, half, kDRows, 128, nullptr, dense_rows, 1, dense_rows, it.tile);
-      else
-        ok = decode_block(blk - nb_dense, half, kDRows, 128, meta, 0, E, max_rows, it.tile);
-      if (!ok) continue;
-      it.w = w;
-      it.dense = in_dense;
-      it.n0 = nt * kOutCols;
-      break;
-    }
-    if (it.w < 0) return;
+  // item w's tile, if it has valid rows
+  auto decode_item = [&](int w, Item& it) {
+    const int half = w / per_half;
+    const int rem = w - half * per_half;
+    const int nt = rem % n_tiles;
+    const int blk = rem / n_tiles;
+    const bool in_dense = blk < nb_dense;
+    bool ok;
+    if (in_dense)
+      ok = decode_block(blk, half, kDRows, 128, nullptr, dense_rows, 1, dense_rows, it.tile);
+    else
+      ok = decode_block(blk - nb_dense, half, kDRows, 128, meta, 0, E, max_rows, it.tile);
+    it.dense = in_dense;
+    it.n0 = nt * kOutCols;
+    return ok;
+  };
+  // the copy offsets of a decoded item
+  auto setup_item = [&](Item& it) {
     const GGOperandsF8& ops = it.dense ? dense : routed;
     const int e = it.tile.e;
     // A copy (waves 0..3, one per slice): 16 rows x 64 bytes; rows past valid_m copy
@@ -541,6 +596,21 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
     }
     it.bsrc = uniform_ptr((GU && ((wave * kDBCopies) >> 4)) ? qb1 : qb0);
   };
+  // the first valid item at or after number w of this work group's sequence, below
+  // `limit`: all its slices, to C
+  auto find_item = [&](int w, int limit, Item& it) {
+    it.w = -1;
+    for (; w < limit; w += gridDim.x) {
+      if (!decode_item(w, it)) continue;
+      it.w = w;
+      break;
+    }
+    if (it.w < 0) return;
+    it.k0 = 0;
+    it.n = nk;
+    it.slot = -1;
+    setup_item(it);
+  };
   // slice ks of an item into ring slot `slot`
   auto issue = [&](const Item& it, int ks, int slot) {
     unsigned char* st = lds + slot * kDStage;
@@ -573,135 +643,279 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
     else MOE_WAIT_VMCNT(n * kDBCopies);
   };
 
-  Item cur, nxt;
-  find_item(blockIdx.x, cur);
-  if (cur.w < 0) return;
-  find_item(cur.w + gridDim.x, nxt);
-  load_scales(cur, 0);
-  // Prologue: every slot in flight (slices past the end re-copy the last slice into a
-  // slot that is never read), then wait for slice 0; the barrier also publishes the
-  // scale table.
+  // Item `cur` and, for whole items, the ones after it in this work group's sequence
+  // below `limit`, as one stream of slices through the ring; returns with every copy
+  // landed.
+  auto run = [&](Item cur, int limit) {
+    Item nxt;
+    nxt.w = -1;
+    if (cur.slot < 0) find_item(cur.w + gridDim.x, limit, nxt);
+    load_scales(cur, 0);
+    // Prologue: every slot in flight (slices past the end re-copy the last slice into a
+    // slot that is never read), then wait for slice 0; the barrier also publishes the
+    // scale table.
 #pragma unroll
-  for (int p = 0; p < kDStages; ++p) issue(cur, min(p, nk - 1), p);
-  wait_slices(std::integral_constant<int, kDStages - 1>{});
-  __syncthreads();
+    for (int p = 0; p < kDStages; ++p) issue(cur, cur.k0 + min(p, cur.n - 1), p);
+    wait_slices(std::integral_constant<int, kDStages - 1>{});
+    __syncthreads();
 
-  int gbase = 0;      // stream position of the current item's slice 0
-  int buf = 0;        // its scale buffer
-  while (true) {
-    // the next item's scales, read only once its slices are computed (the barriers in
-    // between publish them)
-    if (nxt.w >= 0) load_scales(nxt, buf ^ 1);
-    const int nsub = __builtin_amdgcn_readfirstlane(min(2, (cur.tile.valid + 31) >> 5));
-    f32x16_t acc[2][4];
+    int gbase = 0;      // stream position of the current item's first slice
+    int buf = 0;        // its scale buffer
+    while (true) {
+      // the next item's scales, read only once its slices are computed (the barriers in
+      // between publish them)
+      if (nxt.w >= 0) load_scales(nxt, buf ^ 1);
+      const int nsub = __builtin_amdgcn_readfirstlane(min(2, (cur.tile.valid + 31) >> 5));
+      f32x16_t acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-    bf16x8_t af[2], bf[4];
-    auto read_frags = [&](int slot, int ks, int kk) {
-      const unsigned char* sa = lds + slot * kDStage;
-      const unsigned char* sb = sa + kDABytes;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (i >= nsub) break;
-        const int row = i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
-      }
-      const int kb = (ks * kFBK) >> 7;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (MOE_LDS v2i*)(sb + b_lane[j] + kk * 16 * kPitch));
-        const float sc = s_scale[buf][kb * 8 + sidx[j]];
-        bf16x8_t o;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], false);   // bytes 0, 1
-          const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], true);    // bytes 2, 3
-          o[4 * h + 0] = static_cast<__bf16>(f0[0] * sc);
-          o[4 * h + 1] = static_cast<__bf16>(f0[1] * sc);
-          o[4 * h + 2] = static_cast<__bf16>(f1[0] * sc);
-          o[4 * h + 3] = static_cast<__bf16>(f1[1] * sc);
-        }
-        bf[j] = o;
-      }
-    };
-    auto mfma_block = [&]() {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (i >= nsub) break;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
-    };
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    for (int ks = 0; ks < nk; ++ks) {
-      const int gs = gbase + ks;
-      if (gs > 0) {
-        // refill the slot of stream slice gs-1 (every wave has read it) with stream slice
-        // gs-1+S: this item's, the next item's, or a re-copy of this item's last slice
-        const int t = gs - 1 + kDStages - gbase;
-        const int slot = (gs - 1) % kDStages;
-        if (t < nk) issue(cur, t, slot);
-        else if (nxt.w >= 0) issue(nxt, t - nk, slot);
-        else issue(cur, nk - 1, slot);
-      }
-      const int slot = gs % kDStages;
-      read_frags(slot, ks, 0);
-      mfma_block();
-      read_frags(slot, ks, 1);
-      mfma_block();
-      if (ks + 1 < nk || nxt.w >= 0) {
-        wait_slices(std::integral_constant<int, kDStages - 2>{});   // stream slice gs+1 landed
-        __syncthreads();
-      }
-    }
+      bf16x8_t af[2], bf[4];
+      auto read_frags = [&](int slot, int ks, int kk) {
+        const unsigned char* sa = lds + slot * kDStage;
+        const unsigned char* sb = sa + kDABytes;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (i >= nsub) break;
+          const int row = i * 32 + (lane & 31);
+          af[i] = *reinterpret_cast<const bf16x8_t*>(sa + row * 64 + swz_a(row, kk * 2 + (lane >> 5)) * 16);
+        }
+        const int kb = (ks * kFBK) >> 7;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          typedef int v2i __attribute__((ext_vector_type(2)));
+          const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (MOE_LDS v2i*)(sb + b_lane[j] + kk * 16 * kPitch));
+          const float sc = s_scale[buf][kb * 8 + sidx[j]];
+          bf16x8_t o;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], false);   // bytes 0, 1
+            const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(raw[h], true);    // bytes 2, 3
+            o[4 * h + 0] = static_cast<__bf16>(f0[0] * sc);
+            o[4 * h + 1] = static_cast<__bf16>(f0[1] * sc);
+            o[4 * h + 2] = static_cast<__bf16>(f1[0] * sc);
+            o[4 * h + 3] = static_cast<__bf16>(f1[1] * sc);
+          }
+          bf[j] = o;
+        }
+      };
+      auto mfma_block = [&]() {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (i >= nsub) break;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+      };
 
-    // Epilogue: 16-bit stores straight from the accumulators (32 lanes store 64
-    // contiguous bytes of a row), valid rows and columns only; the ring is not touched,
-    // so the next item's slices keep landing.
-    {
-      const GGOperandsF8& ops = cur.dense ? dense : routed;
-      bf16_t* const C = ops.base.C;
-      constexpr int kWCols = GU ? 64 : 128;
-      const int col0 = cur.n0 + wave * kWCols;
+      for (int ks = 0; ks < cur.n; ++ks) {
+        const int gs = gbase + ks;
+        if (gs > 0) {
+          // refill the slot of stream slice gs-1 (every wave has read it) with stream
+          // slice gs-1+S: this item's, the next item's, or a re-copy of this item's last
+          // slice (whole items have n = nk >= S slices; the launcher checks)
+          const int t = gs - 1 + kDStages - gbase;
+          const int slot = (gs - 1) % kDStages;
+          if (t < cur.n) issue(cur, cur.k0 + t, slot);
+          else if (nxt.w >= 0) issue(nxt, nxt.k0 + t - cur.n, slot);
+          else issue(cur, cur.k0 + cur.n - 1, slot);
+        }
+        const int slot = gs % kDStages;
+        read_frags(slot, cur.k0 + ks, 0);
+        mfma_block();
+        read_frags(slot, cur.k0 + ks, 1);
+        mfma_block();
+        if (ks + 1 < cur.n || nxt.w >= 0) {
+          wait_slices(std::integral_constant<int, kDStages - 2>{});   // stream slice gs+1 landed
+          __syncthreads();
+        }
+      }
+
+      // Epilogue: 16-bit stores straight from the accumulators (32 lanes store 64
+      // contiguous bytes of a row), valid rows and columns only; a piece of a split item
+      // stores its fp32 sums to its scratch slot instead.  The ring is not touched, so
+      // the next item's slices keep landing.
+      {
+        const GGOperandsF8& ops = cur.dense ? dense : routed;
+        bf16_t* const C = ops.base.C;
+        constexpr int kWCols = GU ? 64 : 128;
+        const int col0 = cur.n0 + wave * kWCols;
+        float* const P =
+            cur.slot >= 0 ? tail + kDTailHeader + (size_t)cur.slot * (kDTailSlot / 4) : nullptr;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (i >= nsub) break;
+        for (int i = 0; i < 2; ++i) {
+          if (i >= nsub) break;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-          if (r >= cur.tile.valid) continue;
-          bf16_t* crow = C + (size_t)(cur.tile.m0 + r) * N;
-          if (GU) {
+          for (int q = 0; q < 16; ++q) {
+            const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+            if (r >= cur.tile.valid) continue;
+            if (P) {
+              float* prow = P + (size_t)r * kDTailCols;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const int col = col0 + j * 32 + (lane & 31);
-              if (col < N) crow[col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+              for (int j = 0; j < 4; ++j) {
+                const int c = GU ? (j >> 1) * 512 + wave * 64 + (j & 1) * 32 + (lane & 31)
+                                 : wave * 128 + j * 32 + (lane & 31);
+                prow[c] = acc[i][j][q];
+              }
+              continue;
             }
-          } else {
+            bf16_t* crow = C + (size_t)(cur.tile.m0 + r) * N;
+            if (GU) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int col = col0 + j * 32 + (lane & 31);
-              if (col < N) crow[col] = f32_to_bf16(acc[i][j][q]);
+              for (int j = 0; j < 2; ++j) {
+                const int col = col0 + j * 32 + (lane & 31);
+                if (col < N) crow[col] = f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i][j + 2][q]);
+              }
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int col = col0 + j * 32 + (lane & 31);
+                if (col < N) crow[col] = f32_to_bf16(acc[i][j][q]);
+              }
             }
           }
         }
       }
+      if (nxt.w < 0) break;
+      gbase += cur.n;
+      cur = nxt;
+      find_item(cur.w + gridDim.x, limit, nxt);
+      buf ^= 1;
     }
-    if (nxt.w < 0) break;
-    cur = nxt;
-    find_item(cur.w + gridDim.x, nxt);
-    gbase += nk;
-    buf ^= 1;
+    MOE_WAIT_VMCNT(0);  // the re-copies past the last slice land before the ring is reused
+  };
+
+  // the last round split along K where it applies (tail: scratch, or NULL)
+  const bool fits = tail != nullptr &&
+                    fp8d_table_fits(meta, nblocks - nb_dense, E, max_rows, dense_rows, wave, lane,
+                                    reinterpret_cast<int*>(lds));
+  const FP8Tail plan = fp8d_tail_plan(fits, per_half, (int)gridDim.x);
+  const int limit = plan.on ? plan.F * (int)gridDim.x : total;
+  if (tail && blockIdx.x == 0 && tid == 0) {   // the plan, for k_fp8d_tail
+    int* hdr = reinterpret_cast<int*>(tail);
+    hdr[0] = plan.on ? 1 : 0;
+    hdr[1] = plan.F;
+    hdr[2] = plan.R;
   }
-  MOE_WAIT_VMCNT(0);  // the re-copies past the last slice land before the work group ends
+  {
+    Item first;
+    find_item(blockIdx.x, limit, first);
+    if (first.w >= 0) run(first, limit);
+  }
+  if (!plan.on) return;
+  // this work group's slices of the last R items: [lo, hi) of R * nk
+  const int64_t S = (int64_t)plan.R * nk, G = gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * S / G, hi = ((int64_t)blockIdx.x + 1) * S / G;
+  for (int64_t sl = lo; sl < hi;) {
+    const int r = (int)(sl / nk);
+    Item pc;
+    pc.w = plan.F * (int)gridDim.x + r;
+    decode_item(pc.w, pc);             // valid: every item below V is (the table fits)
+    pc.k0 = (int)(sl - (int64_t)r * nk);
+    const int64_t end = (int64_t)(r + 1) * nk;
+    pc.n = (int)((hi < end ? hi : end) - sl);
+    pc.slot = 2 * (int)blockIdx.x + (sl == lo ? 0 : 1);
+    setup_item(pc);
+    __syncthreads();                   // every wave is done with the ring and the scales
+    run(pc, 0);
+    sl = (int64_t)(r + 1) * nk;
+  }
+}
+
+typedef float tail_f32x4 __attribute__((ext_vector_type(4)));
+
+// The last round's items of a split 64-row launch (k_gg_fp8d): item r's pieces, from the
+// work groups whose slice ranges overlap it, added in slice order, then the epilogue.
+// Work group (r, y) takes rows y, y + 8, ... of item r (the ones past the plan's R or the
+// item's valid rows exit); each thread sums 4 adjacent columns (gate/up: of the gate and
+// the up sums), issuing the loads of four pieces before adding them in order.
+template <int OP>
+__global__ void __launch_bounds__(256)
+k_fp8d_tail(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
+            const int32_t* __restrict__ meta, const int32_t* __restrict__ num_blocks_ptr,
+            int max_blocks, int E, int64_t max_rows, int dense_rows, int n_tiles, int G,
+            const float* __restrict__ tail) {
+  constexpr bool GU = OP == MOE_OP_GATEUP_SWIGLU;
+  constexpr int kOutCols = GU ? 512 : 1024;
+  constexpr int kMaxPieces = 64;
+  __shared__ int s_slot[kMaxPieces];
+  __shared__ int s_npieces;
+  const int tid = threadIdx.x;
+  const int* hdr = reinterpret_cast<const int*>(tail);
+  if (hdr[0] == 0) return;
+  const int F = hdr[1], R = hdr[2];
+  const int r = blockIdx.x;
+  if (r >= R) return;
+  const int nb_dense = (dense_rows + 127) / 128;
+  const int nk = K / kFBK;
+  const int w = F * G + r;
+  const int nt = w % n_tiles, blk = w / n_tiles;
+  Tile tile;
+  const bool in_dense = blk < nb_dense;
+  if (in_dense) decode_block(blk, 0, kDRows, 128, nullptr, dense_rows, 1, dense_rows, tile);
+  else decode_block(blk - nb_dense, 0, kDRows, 128, meta, 0, E, max_rows, tile);
+  if ((int)blockIdx.y >= tile.valid) return;
+  const GGOperandsF8& ops = in_dense ? dense : routed;
+  bf16_t* const C = ops.base.C;
+  const int n0 = nt * kOutCols;
+  // The item's pieces, in slice order: the slots of the work groups whose ranges
+  // [q S / G, (q+1) S / G) overlap its slices [a, b) (S = R nk <= 256 * 1024, so the
+  // products stay within 32 bits), listed once by thread 0.
+  if (tid == 0) {
+    const int S = R * nk;
+    const int a = r * nk, b = a + nk;
+    int q = a / (S / G + 1);              // a start; the loops find the first overlap
+    while (q > 0 && q * S / G > a) --q;
+    while ((q + 1) * S / G <= a) ++q;
+    int n = 0;
+    for (; q < G && n < kMaxPieces; ++q) {
+      const int lo = q * S / G, hi = (q + 1) * S / G;
+      if (lo >= b) break;
+      if (hi <= lo) continue;
+      s_slot[n++] = 2 * q + (lo >= a ? 0 : 1);   // its first piece, or its second
+    }
+    s_npieces = n;
+  }
+  __syncthreads();
+  const int np = s_npieces;
+  const int c = tid * 4;                  // this thread's first column of the item
+  if (c >= kOutCols) return;
+  const float* base = tail + kDTailHeader;
+  for (int row = blockIdx.y; row < tile.valid; row += gridDim.y) {
+    const size_t roff = (size_t)row * kDTailCols + c;
+    tail_f32x4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < np; p0 += 4) {
+      tail_f32x4 vg[4], vu[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (p0 + t < np) {
+          const float* prow = base + (size_t)s_slot[p0 + t] * (kDTailSlot / 4) + roff;
+          vg[t] = *reinterpret_cast<const tail_f32x4*>(prow);
+          if (GU) vu[t] = *reinterpret_cast<const tail_f32x4*>(prow + 512);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (p0 + t < np) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            g[i] += vg[t][i];
+            if (GU) u[i] += vu[t][i];
+          }
+        }
+      }
+    }
+    bf16_t* crow = C + (size_t)(tile.m0 + row) * N + n0 + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (n0 + c + i < N) crow[i] = f32_to_bf16(GU ? silu_f32(g[i]) * u[i] : g[i]);
+  }
 }
 
 bool fp8_gemm_supported(int K, int N) {
@@ -750,14 +964,33 @@ moe_status launch_grouped_gemm_fp8(int op, const GemmSegmentsF8& g, int E, int64
     const int cus = device_cu_count();
     int64_t grid = items < cus ? items : cus;
     if (grid < 1) grid = 1;
+    // the last round splits along K only with scratch, a grid of at most kDTailGrid work
+    // groups and (decided on the device) a table whose blocks hold at most 64 rows;
+    // MOE_FP8D_TAIL=0 turns it off
+    float* tail = grid <= kDTailGrid ? g.tail : nullptr;
+    if (const char* f = getenv("MOE_FP8D_TAIL"))
+      if (strcmp(f, "0") == 0) tail = nullptr;
     if (op == MOE_OP_GATEUP_SWIGLU)
       hipLaunchKernelGGL(k_gg_fp8d<MOE_OP_GATEUP_SWIGLU>, dim3((unsigned)grid), dim3(kFThreads), 0,
                          st, rd, dd, g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E,
-                         max_rows, g.dense_rows, n_tiles);
+                         max_rows, g.dense_rows, n_tiles, tail);
     else
       hipLaunchKernelGGL(k_gg_fp8d<MOE_OP_DOWN>, dim3((unsigned)grid), dim3(kFThreads), 0, st, rd,
                          dd, g.K, g.N, g.block_meta, g.num_blocks, g.max_blocks, E, max_rows,
-                         g.dense_rows, n_tiles);
+                         g.dense_rows, n_tiles, tail);
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+    if (tail) {
+      const int G = (int)grid;
+      const dim3 tgrid((unsigned)G, kDTailRowGroups);
+      if (op == MOE_OP_GATEUP_SWIGLU)
+        hipLaunchKernelGGL(k_fp8d_tail<MOE_OP_GATEUP_SWIGLU>, tgrid, dim3(256), 0, st, rd, dd, g.K,
+                           g.N, g.block_meta, g.num_blocks, g.max_blocks, E, max_rows, g.dense_rows,
+                           n_tiles, G, tail);
+      else
+        hipLaunchKernelGGL(k_fp8d_tail<MOE_OP_DOWN>, tgrid, dim3(256), 0, st, rd, dd, g.K, g.N,
+                           g.block_meta, g.num_blocks, g.max_blocks, E, max_rows, g.dense_rows,
+                           n_tiles, G, tail);
+    }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
   }
   const int out_cols = op == MOE_OP_GATEUP_SWIGLU ? 256 : 512;

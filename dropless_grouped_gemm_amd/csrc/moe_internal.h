@@ -181,7 +181,11 @@ struct GemmSegmentsF8 {
   const int32_t* gather;
   int gather_div;
   int gather_rows;
+  // scratch of fp8_tail_scratch_bytes() for the 64-row kernel's split last round, or NULL
+  float* tail;
 };
+// Scratch that lets the 64-row fp8 kernel split its last round along K.
+size_t fp8_tail_scratch_bytes();
 // Which fp8 grouped-GEMM kernel runs: 64-row items with wide weight rows (experts
 // average at most 64 rows: weight streaming), 128-row items, or the wide bf16 kernel's
 // 384-row groups with in-register dequantisation (experts average at least 256 rows).

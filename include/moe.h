@@ -350,6 +350,13 @@ moe_status moe_dequantize_fp8(int32_t E, int32_t K, int32_t N, const uint8_t* q,
  * fused into the loads, as moe_grouped_gemm_gather).
  * A_shared, Q0_shared, S0_shared, Q1_shared, S1_shared, C_shared: all NULL, or the
  * shared expert (needs d_e_shared > 0) as moe_grouped_gemm_shared's second half.
+ * ws, ws_bytes: NULL, or device scratch of moe_grouped_gemm_fp8_workspace_bytes(s) bytes
+ * (16-byte aligned; MOE_EWORKSPACE if smaller).  With it, the 64-row (weight-streaming)
+ * kernel splits the items of its persistent grid's last, partly filled round along the
+ * contraction across every work group, then adds each item's pieces in a fixed order
+ * in a second small launch, where every block of the table holds at most 64 rows
+ * (decode); the results do not depend on timing, only on the device's compute-unit
+ * count (which sets the split).  Without it every item runs whole.
  * Requires dtype bf16, block_m == 128, d and d_e (and d_e_shared) multiples of 32,
  * at most 32768 (else MOE_ENOTSUP); the block table as for moe_grouped_gemm.
  */
@@ -360,7 +367,11 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A,
                                 const int32_t* row_src, void* C, const void* A_shared,
                                 const uint8_t* Q0_shared, const float* S0_shared,
                                 const uint8_t* Q1_shared, const float* S1_shared,
-                                void* C_shared, void* stream);
+                                void* C_shared, void* ws, size_t ws_bytes, void* stream);
+/* Host-only and pure: the optional scratch of moe_grouped_gemm_fp8 (two 64-row x 1024
+ * fp32 slots for each of up to 256 work groups, behind a 256-byte header: 128 MiB + 256
+ * bytes), 0 for an invalid shape. */
+size_t moe_grouped_gemm_fp8_workspace_bytes(const moe_shape* s);
 
 /*
  * moe_layer_fwd with fp8 weights: (q1, s1), (q3, s3), (q2, s2) replace w1, w3, w2 and
@@ -374,9 +385,10 @@ moe_status moe_grouped_gemm_fp8(const moe_shape* s, int32_t op, const void* A,
  * paths use the same bf16 weight values; in the 256-row regime both give bitwise the
  * same output.
  * Workspace, 16-byte aligned: moe_fp8_workspace_bytes(s) bytes (moe_workspace_bytes's
- * layout, then the dequantised weights where that path applies), or as little as
- * moe_workspace_bytes(s) bytes (no dequantised copy: the in-register path);
- * MOE_EWORKSPACE below that.
+ * layout, then the dequantised weights where that path applies, or, where experts
+ * average at most 64 rows, moe_grouped_gemm_fp8's optional scratch), or as little as
+ * moe_workspace_bytes(s) bytes (no dequantised copy: the in-register path; no scratch:
+ * whole items only); MOE_EWORKSPACE below that.
  */
 size_t moe_fp8_workspace_bytes(const moe_shape* s);
 

@@ -159,6 +159,7 @@ static void check_sizing(const moe_shape& s) {
   (void)moe_grouped_gemm_dgrad_workspace_bytes(&s, 7);
   (void)moe_grouped_gemm_wgrad_workspace_bytes(&s);
   (void)moe_router_bwd_workspace_bytes(&s);
+  CHECK(moe_grouped_gemm_fp8_workspace_bytes(&s) > 0, "fp8 gemm scratch size");
 }
 
 int main() {
@@ -206,7 +207,10 @@ int main() {
   CHECK(moe_quantize_fp8(-1, 256, 256, F, Fq, Ff, nullptr) == MOE_EINVAL, "quantize bad E");
   CHECK(moe_dequantize_fp8(1, 256, 255, Fq, Ff, F, nullptr) == MOE_EINVAL, "dequantize bad N");
   CHECK(moe_grouped_gemm_fp8(&s, 0, nullptr, Fq, Ff, Fq, Ff, Fi, Fi, 4, nullptr, F, nullptr, nullptr, nullptr,
-                             nullptr, nullptr, nullptr, nullptr) == MOE_EINVAL, "fp8 gemm null A");
+                             nullptr, nullptr, nullptr, nullptr, 0, nullptr) == MOE_EINVAL, "fp8 gemm null A");
+  CHECK(moe_grouped_gemm_fp8(&s, 0, F, Fq, Ff, Fq, Ff, Fi, Fi, 4, nullptr, F, nullptr, nullptr, nullptr,
+                             nullptr, nullptr, nullptr, F, short_ws, nullptr) == MOE_EWORKSPACE,
+        "fp8 gemm short scratch");
   CHECK(moe_layer_fwd_fp8(&s, F, F, nullptr, Fq, Ff, Fq, Ff, Fq, Ff, nullptr, nullptr, nullptr, nullptr, nullptr,
                           nullptr, nullptr, nullptr, F, F, short_ws, nullptr) == MOE_EWORKSPACE, "fp8 layer ws");
   CHECK(moe_combine_bwd(&s, nullptr, F, Fi, Ff, F, Ff, nullptr) == MOE_EINVAL, "combine bwd null");

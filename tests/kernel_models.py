@@ -726,3 +726,75 @@ def check_v2_copies(op, K, N, tiles, n_e, a_rows, block_m=128):
                             krow = ks * 32 + 2 * pr + (lane >> 5)
                             idx = e * K * N + krow * N + col
                             assert krow.max() < K and idx.min() >= 0 and (idx + 8).max() <= n_e * K * N
+
+
+# ---------------------------------------------------------------------------
+# The 64-row fp8 kernel's split last round (moe_fp8.hip: k_gg_fp8d, k_fp8d_tail): the
+# pieces the work groups compute and the slots the tail kernel adds, integer arithmetic
+# written as in the kernels.
+# ---------------------------------------------------------------------------
+def fp8d_tail_plan(V, G, fits=True, max_grid=256):
+    F, R = V // G, V % G
+    return F, R, fits and G <= max_grid and R > 0 and 10 * R <= 9 * G and 16 * R >= G
+
+
+def fp8d_tail_pieces(R, nk, G):
+    """{item r: [(q, slot, k0, n), ...]} in the order the work groups compute them."""
+    S = R * nk
+    out = {}
+    for q in range(G):
+        lo, hi = q * S // G, (q + 1) * S // G
+        sl = lo
+        while sl < hi:
+            r = sl // nk
+            k0 = sl - r * nk
+            end = (r + 1) * nk
+            n = min(hi, end) - sl
+            out.setdefault(r, []).append((q, 2 * q + (0 if sl == lo else 1), k0, n))
+            sl = end
+    return out
+
+
+def fp8d_tail_slots(R, nk, G, r):
+    """The slots k_fp8d_tail adds for item r, in its order."""
+    S = R * nk
+    a, b = r * nk, r * nk + nk
+    q0 = a // (S // G + 1)
+    while q0 > 0 and q0 * S // G > a:
+        q0 -= 1
+    while (q0 + 1) * S // G <= a:
+        q0 += 1
+    slots = []
+    for q in range(q0, G):
+        lo, hi = q * S // G, (q + 1) * S // G
+        if lo >= b:
+            break
+        if hi <= lo:
+            continue
+        slots.append(2 * q + (0 if lo >= a else 1))
+    return slots
+
+
+def check_fp8d_tail(R, nk, G):
+    pieces = fp8d_tail_pieces(R, nk, G)
+    assert sorted(pieces) == list(range(R))
+    used = set()
+    for r in range(R):
+        ps = pieces[r]
+        # the item's slices, each once, in slice order
+        assert [p[2] for p in ps] == sorted(p[2] for p in ps)
+        cov = 0
+        for (q, slot, k0, n) in ps:
+            assert k0 == cov and n >= 1
+            cov += n
+            assert slot in (2 * q, 2 * q + 1) and slot not in used and 0 <= slot < 2 * G
+            used.add(slot)
+        assert cov == nk
+        assert fp8d_tail_slots(R, nk, G, r) == [p[1] for p in ps]
+        assert len(ps) <= 34               # the tail kernel lists at most 64
+    # every work group computes at most two pieces
+    per_q = {}
+    for ps in pieces.values():
+        for p in ps:
+            per_q[p[0]] = per_q.get(p[0], 0) + 1
+    assert max(per_q.values()) <= 2

@@ -311,9 +311,9 @@ def test_fp8_entry_point_argument_rules():
     # fp32 activations, or 256-row blocks: not supported
     for bad in (good_shape(dtype="fp32", block_m=128), good_shape(block_m=256), good_shape(d=272)):
         assert g(ctypes.byref(bad), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE,
-                 *n6, None) == B.MOE_ENOTSUP
+                 *n6, None, 0, None) == B.MOE_ENOTSUP
     assert B.fp8_supported(s) and not B.fp8_supported(good_shape(d=272))
-    ok = lambda op, *a: g(ps, op, *a, None)
+    ok = lambda op, *a: g(ps, op, *a, None, 0, None)
     assert ok(0, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1, None, FAKE, *n6) == B.MOE_EINVAL
     assert ok(1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, *n6) == B.MOE_EINVAL
     assert ok(0, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, *n6) == B.MOE_EINVAL
@@ -329,8 +329,32 @@ def test_fp8_entry_point_argument_rules():
               None) == B.MOE_EINVAL
     assert lf(ps, FAKE, FAKE, None, *([FAKE] * 6), FAKE, *([None] * 5), None, None, FAKE, FAKE,
               need, None) == B.MOE_EINVAL
+    least = L.moe_workspace_bytes(ps)
     assert lf(ps, FAKE, FAKE, None, *([FAKE] * 6), *([None] * 6), None, None, FAKE, FAKE,
-              need - 1, None) == B.MOE_EWORKSPACE
+              least - 1, None) == B.MOE_EWORKSPACE
+    # the optional scratch of the GEMM: too small or misaligned is an error, NULL is none
+    args = (0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, *n6)
+    sk = L.moe_grouped_gemm_fp8_workspace_bytes(ps)
+    assert sk == 256 + 2 * 256 * 64 * 1024 * 4
+    assert g(ps, *args, FAKE, sk - 1, None) == B.MOE_EWORKSPACE
+    assert g(ps, *args, ctypes.c_void_p(0x10004), sk, None) == B.MOE_EWORKSPACE
+
+
+def test_fp8_layer_workspace_holds_the_streaming_scratch():
+    """Where experts average at most 64 rows the fp8 layer's full workspace ends with the
+    GEMM's last-round scratch; elsewhere it does not."""
+    L = B.lib()
+    dec = good_shape(T=64, d=256, E=64, k=4, d_e=256)          # 4 rows per expert
+    pre = good_shape(T=4096, d=256, E=8, k=2, d_e=256)         # 1024 rows per expert
+    mid = good_shape(T=1024, d=256, E=8, k=1, d_e=256)         # 128 rows per expert
+    sk = L.moe_grouped_gemm_fp8_workspace_bytes(ctypes.byref(dec))
+    for shp, extra in ((dec, True), (pre, False), (mid, False)):
+        p = ctypes.byref(shp)
+        base, full = L.moe_workspace_bytes(p), L.moe_fp8_workspace_bytes(p)
+        if extra:
+            assert full == base + sk
+        else:
+            assert full < base + sk
 
 
 def test_forward_router_needs_a_16_byte_aligned_w_gate():
@@ -372,7 +396,8 @@ def test_fp8_layer_accepts_the_minimal_workspace():
 def test_fp8_workspace_size_rule():
     """moe_fp8_workspace_bytes: moe_workspace_bytes's layout, plus room for the
     dequantised bf16 weights exactly where the layer takes the dequantised path (routed
-    rows M = T * k at least 256 * min(E, M))."""
+    rows M = T * k at least 256 * min(E, M)), or for the streaming GEMM's last-round
+    scratch exactly where experts average at most 64 rows."""
     L = B.lib()
     for kw in (dict(T=64), dict(T=1023), dict(T=1024), dict(T=4096, d_e_shared=512),
                dict(T=0), dict(T=70, E=1, k=4), dict(T=512, E=300, k=8)):
@@ -380,9 +405,13 @@ def test_fp8_workspace_size_rule():
         base, f8 = L.moe_workspace_bytes(ctypes.byref(s)), L.moe_fp8_workspace_bytes(ctypes.byref(s))
         M = s.T * s.k
         wide = M > 0 and M >= 256 * min(s.E, M)
+        streaming = M > 0 and M <= 64 * min(s.E, M)
+        assert B.fp8_dequantises(s) == wide, kw
         w = 2 * (3 * s.E * s.d * s.d_e + 3 * s.d * s.d_e_shared)
         if wide:
             assert w <= f8 - base <= w + 6 * 256, kw
+        elif streaming:
+            assert f8 - base == L.moe_grouped_gemm_fp8_workspace_bytes(ctypes.byref(s)), kw
         else:
             assert f8 == base, kw
     assert L.moe_fp8_workspace_bytes(ctypes.byref(good_shape(k=0))) == 0

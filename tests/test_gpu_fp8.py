@@ -228,7 +228,10 @@ def test_layer_fwd_fp8_against_bf16_layer_on_dequantised_weights(name, scale, wi
     assert (M >= 256 * min(cfg.E, M)) == wide
     extra = B.moe_fp8_workspace_bytes(s) - B.moe_workspace_bytes(s)
     wbytes = 2 * 3 * cfg.E * cfg.d * cfg.d_e + 2 * 3 * cfg.d * cfg.d_e_shared
-    assert extra >= wbytes if wide else extra == 0
+    # where experts average at most 64 rows the extra room is the streaming GEMM's scratch
+    streaming = M <= 64 * min(cfg.E, M)
+    sk = B.moe_grouped_gemm_fp8_workspace_bytes(s) if streaming else 0
+    assert extra >= wbytes if wide else extra == sk
     qz = [B.quantize_fp8(w) for w in (inp.w1, inp.w3, inp.w2)]
     qs = [B.quantize_fp8(w) for w in (inp.ws1, inp.ws3, inp.ws2)] if cfg.d_e_shared else [(None, None)] * 3
     dqz = [B.dequantize_fp8(*p) for p in qz]
@@ -276,3 +279,125 @@ def test_layer_fwd_fp8_is_deterministic(name, scale):
         torch.cuda.synchronize()
         outs.append(out)
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def _split_plan(nblocks, n_tiles, G):
+    """Whether the 64-row kernel splits its last round (the rule of moe_fp8.hip)."""
+    V = nblocks * n_tiles
+    R = V % G
+    return G <= 256 and R > 0 and 10 * R <= 9 * G
+
+
+@pytest.mark.parametrize("T,d,E,k,d_e,d_es,skew", [
+    (64, 1024, 64, 8, 512, 0, False),      # every item of both launches split (no full round)
+    (64, 512, 40, 3, 256, 256, False),     # the shared expert's block in the same launch
+    (96, 512, 40, 3, 256, 256, False),     # ... with 96 dense rows: whole items only
+    (40, 1280, 24, 3, 160, 0, False),      # down with K = 160: five slices per item
+    (64, 1024, 64, 8, 512, 0, True),       # a block of 100 rows: whole items only
+])
+def test_fp8_split_last_round(T, d, E, k, d_e, d_es, skew, monkeypatch):
+    """The 64-row kernel given scratch: the items of its grid's last round split along K
+    over every work group, then added in slice order by the tail kernel.  Against the
+    oracle at the stage bound, within bf16 rounding of the whole-item run, and bitwise the
+    same when repeated; a table with a block of more than 64 rows runs whole items,
+    bitwise as without scratch."""
+    monkeypatch.setenv("MOE_FP8_ITEM_ROWS", "64")
+    rng = np.random.default_rng(T * 7 + E)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    if skew:
+        # expert 0 in slot 0 of every token and slot 1 of 40 (a repeat within a token is
+        # a valid route): more than 100 rows in its block
+        idx[:, 0] = 0
+        idx[:40, 1] = 0
+    g = torch.Generator(device=DEV)
+    g.manual_seed(T + d_e)
+    dt = torch.bfloat16
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    (q1, s1), (q3, s3), (q2, s2) = B.quantize_fp8(w1), B.quantize_fp8(w3), B.quantize_fp8(w2)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16", d_e_shared=d_es)
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err,
+                        B.alloc_workspace(s))
+    x_perm = torch.zeros((rows, d), dtype=dt, device=DEV)
+    B.moe_permute(s, x, pos, x_perm)
+    sh = {}
+    if d_es:
+        ws1 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+        ws3 = (torch.randn((d, d_es), generator=g, device=DEV) / d ** 0.5).to(dt)
+        ws2 = (torch.randn((d_es, d), generator=g, device=DEV) / d_es ** 0.5).to(dt)
+        sh = dict(q=[B.quantize_fp8(w) for w in (ws1, ws3, ws2)])
+    scratch = B.alloc_fp8_gemm_workspace(s)
+    e = lambda *shp: torch.full(shp, 7.0, dtype=dt, device=DEV)
+
+    def run(ws):
+        act, y = e(rows, d_e), e(rows, d)
+        sact, sout = (e(T, d_es), e(T, d)) if d_es else (None, None)
+        if d_es:
+            (qa, sa), (qb, sb), (qc, sc) = sh["q"]
+            B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, q1, s1, q3, s3, meta, nblk,
+                                   mb, None, act, x, qa, sa, qb, sb, sact, ws=ws)
+            B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, q2, s2, None, None, meta, nblk, mb,
+                                   None, y, sact, qc, sc, None, None, sout, ws=ws)
+        else:
+            B.moe_grouped_gemm_fp8(s, B.MOE_OP_GATEUP_SWIGLU, x_perm, q1, s1, q3, s3, meta, nblk,
+                                   mb, None, act, ws=ws)
+            B.moe_grouped_gemm_fp8(s, B.MOE_OP_DOWN, act, q2, s2, None, None, meta, nblk, mb,
+                                   None, y, ws=ws)
+        torch.cuda.synchronize()
+        return act, y, sact, sout
+
+    print(f"[fp8 split] T={T} d={d} E={E} k={k} d_e={d_e} skew={skew}", flush=True)
+    whole = run(None)
+    split = run(scratch)
+    again = run(scratch)
+    assert int(err.item()) == 0
+    ref_pos, ref_src = O.permutation(idx, E, 128)
+    valid = np.nonzero(ref_src >= 0)[0]
+    dv = torch.from_numpy(valid).to(DEV)
+    for a, b in zip(split, again):
+        if a is not None:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the plan the kernels follow: blocks of the table, column tiles, grid
+    nb = int(nblk.item()) + (1 if d_es else 0)
+    vm = i64(meta)[:3 * int(nblk.item())].reshape(-1, 3)[:, 2]
+    fits = bool(np.all(vm <= 64)) and (not d_es or T <= 64)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for op, out_s, out_w, n_cols, N in ((0, split[0], whole[0], 512, d_e), (1, split[1], whole[1], 1024, d)):
+        n_tiles = -(-N // n_cols)
+        G = min((mb + (1 if d_es else 0)) * 2 * n_tiles, cus)
+        on = fits and _split_plan(nb, n_tiles, G)
+        if not fits:
+            assert not on
+            assert torch.equal(out_s[dv].view(torch.int16), out_w[dv].view(torch.int16))
+        elif skew is False:
+            assert on, (op, nb, n_tiles, G)
+        # the split changes only the order of fp32 partial sums: bf16 rounding apart
+        a, b = f64(out_s[dv]), f64(out_w[dv])
+        assert np.abs(a - b).max() <= 2 ** -6 * np.abs(b).max()
+    # against the oracle on the exactly dequantised weights
+    c = O.expert_counts(idx, E)
+    def dq(qq, ss):
+        qn, sn = qq.cpu().numpy(), ss.cpu().numpy()
+        return F.dequantize(qn.reshape((-1,) + qn.shape[-2:]), sn.reshape((-1,) + sn.shape[-2:]))
+    W1, W3, W2 = dq(q1, s1), dq(q3, s3), dq(q2, s2)
+    xp_ref = O.permute(f64(x), ref_pos, k, len(ref_src))
+    act_ref, _ = O.grouped_ffn(xp_ref, c, 128, W1, W3, W2)
+    assert_close(f64(split[0])[valid], act_ref[valid], TOL_STAGE_FP8, "act")
+    act_dev = f64(split[0])
+    P = O.padded_offsets(c, 128)
+    y_ref = np.zeros((len(ref_src), d))
+    for ex in range(E):
+        lo, hi = P[ex], P[ex] + c[ex]
+        y_ref[lo:hi] = act_dev[lo:hi] @ W2[ex]
+    assert_close(f64(split[1])[valid], y_ref[valid], TOL_STAGE_FP8, "y")
+    if d_es:
+        Ws = [dq(qq, ss)[0] for qq, ss in sh["q"]]
+        assert_close(f64(split[2]), O.swiglu_act(f64(x), Ws[0], Ws[1]), TOL_STAGE_FP8, "shared act")
+        assert_close(f64(split[3]), f64(split[2]) @ Ws[2], TOL_STAGE_FP8, "shared out")

@@ -195,14 +195,24 @@ def test_fp8_full_size_sampled_tokens(fp8_full):
 def test_fp8_full_size_minimal_workspace_gives_the_same_output(fp8_full):
     """With a workspace of moe_workspace_bytes only, the fp8 layer dequantises in registers
     (the wide kernel where experts average >= 256 rows) instead of into the workspace: the
-    same bf16 weights, tiles and order of the sums, so the output is bitwise the same."""
+    same bf16 weights, tiles and order of the sums, so the output is bitwise the same.
+    Where experts average at most 64 rows (decode) the full workspace also holds the
+    streaming kernel's scratch, with which the last round of its grid is split along K:
+    only the order of fp32 partial sums of those items differs, so the outputs agree to
+    bf16 rounding."""
     cfg, inp, w, s, ws, out = fp8_full
     wsm = torch.empty(B.moe_workspace_bytes(s), dtype=torch.uint8, device=DEV)
     out2 = torch.empty_like(out)
     B.moe_layer_fwd_fp8(s, inp.x, inp.w_gate, inp.bias, w.q1, w.s1, w.q3, w.s3, w.q2, w.s2,
                         w.qs1, w.ss1, w.qs3, w.ss3, w.qs2, w.ss2, None, None, out2, wsm)
     torch.cuda.synchronize()
-    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    M = cfg.T * cfg.k
+    if M <= 64 * min(cfg.E, M):
+        a, b = out2.double(), out.double()
+        assert torch.isfinite(a).all()
+        assert (a - b).abs().max().item() <= 2 ** -6 * b.abs().max().item()
+    else:
+        assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
 
 
 # ----------------------------------------------------------------------------

@@ -170,3 +170,21 @@ def test_nt_model_computes_the_data_gradient():
     for (e, m0, valid) in tiles:
         ref = A[m0:m0 + valid] @ np.concatenate([Bt0[e], Bt1[e]], axis=1).T
         np.testing.assert_allclose(C[m0:m0 + valid], ref, atol=1e-9)
+
+
+@pytest.mark.parametrize("G", [256, 255, 200, 37, 8])
+def test_fp8d_split_last_round(G):
+    """Every split item's slices are computed once, in order, into distinct slots, and the
+    tail kernel adds exactly those slots in slice order; the plan splits only a last
+    round that is at most 90 % full."""
+    for V in (1, 7, G - 1, G, G + 1, 920, 1610, 3 * G + G // 3, 5 * G + 9 * G // 10,
+              2 * G + (G + 15) // 16, 2 * G + max(1, G // 16 - 1)):
+        F, R, on = KM.fp8d_tail_plan(V, G)
+        assert F * G + R == V and 0 <= R < G
+        assert on == (R > 0 and 10 * R <= 9 * G and 16 * R >= G)
+        if not on:
+            continue
+        for nk in (1, 2, 4, 7, 15, 16, 17, 31, 33, 64, 224, 1000, 1024):
+            KM.check_fp8d_tail(R, nk, G)
+    assert not KM.fp8d_tail_plan(1610, 257)[2]          # grids past the scratch's slots
+    assert not KM.fp8d_tail_plan(1610, 256, fits=False)[2]
