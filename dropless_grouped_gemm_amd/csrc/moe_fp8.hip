@@ -539,7 +539,12 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
     uint32_t a_voff;              // this lane's A offset (waves 0..3)
     const uint8_t* bsrc;          // the wave's B matrix base (wave-uniform)
     uint32_t b_voff[kDBCopies];
-    int b_row[kDBCopies];
+  };
+  // the first slice row of B copy p of this wave (the same for every item): gate/up copies
+  // two rows, 2 (u % 16) and the next, down one, u (u = kDBCopies wave + p)
+  auto b_row = [&](int p) {
+    const int u = wave * kDBCopies + p;
+    return GU ? 2 * (u & 15) : u;
   };
   // item w's tile, if it has valid rows
   auto decode_item = [&](int w, Item& it) {
@@ -591,8 +596,7 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
       }
       int col = it.n0 + (pos ^ (k & 15)) * 16;
       if (col >= N) col = 0;
-      it.b_row[p] = GU ? 2 * (u & 15) : u;
-      it.b_voff[p] = (uint32_t)((k - it.b_row[p]) * N + col);
+      it.b_voff[p] = (uint32_t)((k - b_row(p)) * N + col);
     }
     it.bsrc = uniform_ptr((GU && ((wave * kDBCopies) >> 4)) ? qb1 : qb0);
   };
@@ -619,7 +623,7 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
 #pragma unroll
     for (int p = 0; p < kDBCopies; ++p) {
       const int u = wave * kDBCopies + p;
-      copy16_to_lds(it.bsrc + (size_t)(k0 + it.b_row[p]) * N, it.b_voff[p], st + kDABytes + u * 1024);
+      copy16_to_lds(it.bsrc + (size_t)(k0 + b_row(p)) * N, it.b_voff[p], st + kDABytes + u * 1024);
     }
   };
   // an item's block scales into buffer `buf` (plain LDS stores: a barrier publishes them)
@@ -746,8 +750,30 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
         bf16_t* const C = ops.base.C;
         constexpr int kWCols = GU ? 64 : 128;
         const int col0 = cur.n0 + wave * kWCols;
-        float* const P =
-            cur.slot >= 0 ? tail + kDTailHeader + (size_t)cur.slot * (kDTailSlot / 4) : nullptr;
+        if (cur.slot >= 0) {
+          // a piece: its fp32 sums to its scratch slot (one loop nest of its own, so that
+          // its addresses do not share registers with the bf16 stores below)
+          // lane base: row (l >> 5) * 4, this wave's first column; every store then adds
+          // a constant
+          float* const pl = tail + kDTailHeader + (size_t)cur.slot * (kDTailSlot / 4) +
+                            (size_t)((lane >> 5) * 4) * kDTailCols +
+                            (GU ? wave * 64 : wave * 128) + (lane & 31);
+          const int vrow = cur.tile.valid - (lane >> 5) * 4;   // rows r_off < vrow are valid
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            if (i >= nsub) break;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r_off = i * 32 + (q >> 2) * 8 + (q & 3);
+              if (r_off >= vrow) continue;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int c = GU ? (j >> 1) * 512 + (j & 1) * 32 : j * 32;
+                pl[r_off * kDTailCols + c] = acc[i][j][q];
+              }
+            }
+          }
+        } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           if (i >= nsub) break;
@@ -755,16 +781,6 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
           for (int q = 0; q < 16; ++q) {
             const int r = i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
             if (r >= cur.tile.valid) continue;
-            if (P) {
-              float* prow = P + (size_t)r * kDTailCols;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int c = GU ? (j >> 1) * 512 + wave * 64 + (j & 1) * 32 + (lane & 31)
-                                 : wave * 128 + j * 32 + (lane & 31);
-                prow[c] = acc[i][j][q];
-              }
-              continue;
-            }
             bf16_t* crow = C + (size_t)(cur.tile.m0 + r) * N;
             if (GU) {
 #pragma unroll
@@ -780,6 +796,7 @@ k_gg_fp8d(GGOperandsF8 routed, GGOperandsF8 dense, int K, int N,
               }
             }
           }
+        }
         }
       }
       if (nxt.w < 0) break;
