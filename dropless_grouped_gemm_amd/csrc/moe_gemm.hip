@@ -487,7 +487,7 @@ k_gg_bf16_v2(GGOperands routed, GGOperands dense, int K, int N,
           const int c = lane & 31;
           const float da = bf16_to_f32(*reinterpret_cast<const bf16_t*>(sda + (r * 32 + c) * 2));
           const float gv = acc[i][0][q], uv = acc[i][1][q];
-          const float sg = 1.0f / (1.0f + expf(-gv));
+          const float sg = sigmoid_f32(gv);
           so[r * kLd + c] = f32_to_bf16(da * uv * (sg * (1.0f + gv * (1.0f - sg))));
           so[(32 + r) * kLd + c] = f32_to_bf16(da * gv * sg);
         }

@@ -83,7 +83,7 @@ struct GGOperands {
 // gradient da of act = silu(g) u:  dg = da u silu'(g),  du = da silu(g),
 // silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
 __device__ __forceinline__ float swiglu_dgate(float g, float u, float da) {
-  const float s = 1.0f / (1.0f + expf(-g));
+  const float s = sigmoid_f32(g);
   return da * u * (s * (1.0f + g * (1.0f - s)));
 }
 __device__ __forceinline__ float swiglu_dup(float g, float da) { return da * silu_f32(g); }

@@ -619,7 +619,7 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
             const int c = jj * 32 + (lane & 31);
             const float da = bf16_to_f32(*reinterpret_cast<const bf16_t*>(sda + (r * 64 + c) * 2));
             const float gv = acc[i][jj][q], uv = acc[i][jj + 2][q];
-            const float sg = 1.0f / (1.0f + expf(-gv));
+            const float sg = sigmoid_f32(gv);
             so[r * kLd + c] = f32_to_bf16(da * uv * (sg * (1.0f + gv * (1.0f - sg))));
             so[(32 + r) * kLd + c] = f32_to_bf16(da * gv * sg);
           }
