@@ -500,10 +500,10 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     for (int t = 0; t < 2 * nk; ++t) {
       const int ks = t >> 1, kk = t & 1;
       // the refill of slice ks-1's slot (after every wave's last read of slice ks-1):
-      // gate/up issues all its copies in the first half's memory phase, down its A
-      // copies there and its B copies in the second half's (measured: each op's faster
-      // split)
-      constexpr bool kSplitCopies = !GU;
+      // the A copies in the first half's memory phase, the B copies in the second
+      // half's (measured faster for both ops than all copies in the first half, for
+      // gate/up once its barriers stopped waiting for the fragment reads)
+      constexpr bool kSplitCopies = true;
       const int ksrc = min(ks - 1 + kStages, nk - 1);
       const int slot = (ks + kStages - 1) % kStages;
       if (kk == 0) {
@@ -525,20 +525,15 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       read_frags(ks, kk, nl_c);
       // scheduling barriers keep each phase's instructions on its side of the barriers
       __builtin_amdgcn_sched_barrier(0);
-      // Gate/up: the barrier after a memory phase does not wait for the phase's fragment
-      // reads (the MFMAs wait for their operands), so the other wave on the SIMD starts
-      // its memory phase under them, except where a refill follows: the lagging waves'
+      // The barrier after a memory phase does not wait for the phase's fragment reads
+      // (the MFMAs wait for their operands), so the other wave on the SIMD starts its
+      // memory phase under them, except where a refill follows: the lagging waves'
       // second-half reads are the last reads of slice ks, whose slot the other waves
       // refill right after this barrier (MEM(2 ks + 2)).  The other waves' reads of a
       // slice complete before their own MFMA phase, before the barrier ahead of any
-      // refill of that slot.  (Measured: gate/up 0.7-0.9 % faster; down, whose B refill
-      // shares the second half's memory phase, 0.3 % slower, so it keeps the full wait.)
-      if constexpr (GU) {
-        if (lag && kk == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        asm volatile("s_barrier" ::: "memory");
-      } else {
-        __syncthreads();
-      }
+      // refill of that slot.
+      if (lag && kk == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       mfma_block(nl_c);
       __builtin_amdgcn_sched_barrier(0);
