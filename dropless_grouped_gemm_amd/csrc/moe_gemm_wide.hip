@@ -503,7 +503,6 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       // the A copies in the first half's memory phase, the B copies in the second
       // half's (measured faster for both ops than all copies in the first half, for
       // gate/up once its barriers stopped waiting for the fragment reads)
-      constexpr bool kSplitCopies = true;
       const int ksrc = min(ks - 1 + kStages, nk - 1);
       const int slot = (ks + kStages - 1) % kStages;
       if (kk == 0) {
@@ -513,12 +512,8 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
           MOE_WAIT_VMCNT((kStages - 3) * CPW);   // slice ks+1 has landed
 #pragma unroll
           for (int i = 0; i < CPA; ++i) issue_a(ksrc, slot, i);
-          if (!kSplitCopies) {
-#pragma unroll
-            for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
-          }
         }
-      } else if (kSplitCopies && ks > 0) {
+      } else if (ks > 0) {
 #pragma unroll
         for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
       }
