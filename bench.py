@@ -445,7 +445,7 @@ def measure(args, cfg_name, weights="bf16", unpadded=False, steps=20, warmup=5, 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch

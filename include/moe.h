@@ -40,7 +40,7 @@ extern "C" {
 typedef int32_t moe_status;
 #define MOE_OK          0
 #define MOE_EINVAL      1   /* a shape, pointer, alignment or argument is invalid   */
-#define MOE_ENOTSUP     2   /* valid, but not supported by this build (see below)   */
+#define MOE_ENOTSUP     2   /* valid, but not supported by this library (see below) */
 #define MOE_EWORKSPACE  3   /* workspace missing or smaller than moe_workspace_bytes */
 #define MOE_EHIP        4   /* a HIP launch or runtime call failed                   */
 
