@@ -453,6 +453,55 @@ def test_wide_tiles_with_a_capped_grid(cap, monkeypatch):
     assert torch.equal(y[valid].view(torch.int16), y2[valid].view(torch.int16))
 
 
+@pytest.mark.parametrize("d,d_e,cap", [(32, 32, "8"), (64, 96, "8"), (96, 64, "24"),
+                                       (160, 128, "8"), (224, 160, "0")])
+def test_wide_tiles_short_k(d, d_e, cap, monkeypatch):
+    """K of 1 to 7 slices (32 deep): the four-slot ring wraps within an item and
+    between consecutive items of a work group, and the refill copies of the last slices
+    re-copy the final slice.  The capped grids give each work group many items.  Gate/up
+    (gathered) and down match the 128-row kernel bit for bit."""
+    T, E, k = 4800, 3, 2          # ~25 blocks per expert: 9 groups each, one of 1 block
+    rng = np.random.default_rng(d + d_e)
+    idx = rng.integers(0, E, size=(T, k))
+    dt = torch.bfloat16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(d * 7 + d_e)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16")
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    ws = B.alloc_workspace(s)
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err, ws)
+    e = lambda *sh: torch.full(sh, 3.0, dtype=dt, device=DEV)
+    act, y, act2, y2 = e(rows, d_e), e(rows, d), e(rows, d_e), e(rows, d)
+    print(f"[wide short K] d={d} d_e={d_e} cap={cap}", flush=True)
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", "384")
+    if cap != "0":
+        monkeypatch.setenv("MOE_GG_GRID_CAP", cap)
+    B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, w2, None, meta, nblk, mb, y)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", "128")
+    monkeypatch.delenv("MOE_GG_GRID_CAP", raising=False)
+    B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act2)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act2, w2, None, meta, nblk, mb, y2)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy(np.nonzero(O.permutation(idx, E, 128)[1] >= 0)[0]).to(DEV)
+    assert torch.equal(act[valid].view(torch.int16), act2[valid].view(torch.int16))
+    assert torch.equal(y[valid].view(torch.int16), y2[valid].view(torch.int16))
+    c = O.expert_counts(idx, E)
+    xp_ref = O.permute(f64(x), O.permutation(idx, E, 128)[0], k, rows)
+    act_ref, _ = O.grouped_ffn(xp_ref, c, 128, f64(w1), f64(w3), np.zeros((E, d_e, d)))
+    vn = valid.cpu().numpy()
+    assert_close(f64(act)[vn], act_ref[vn], TOL_STAGE["bf16"], "act")
+
+
 def test_combine_skips_negative_positions():
     T, d, k = 8, 64, 2
     s = B.make_shape(T=T, d=d, E=4, k=k, d_e=64, block_m=128)
