@@ -478,7 +478,6 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     MOE_WAIT_VMCNT((kStages - 1) * CPW);
     __syncthreads();
 
-    if constexpr (!BWD) {
     // Ping-pong over half-slices t = 2 ks + kk: every wave runs MEM(t), barrier,
     // MFMA(t), barrier.  Waves 4-7 (the second wave on each SIMD) start one barrier
     // late and waves 0-3 end one barrier late, so on every SIMD one wave issues its
@@ -488,8 +487,8 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     //   MEM(2 ks), ks >= 1: slice ks+1 has landed for this wave (then, before any wave
     //   reads it, at least two barriers pass); every wave has read slice ks-1 (its
     //   reads completed before the barriers since), so its slot takes slice ks-1+S
-    //   (down: its B copies in MEM(2 ks + 1)).  The wait counts whole slices: at
-    //   MEM(2 ks) every slice up to ks-2+S has been issued in full.
+    //   (the A copies; the B copies in MEM(2 ks + 1)).  The wait counts whole slices:
+    //   at MEM(2 ks) every slice up to ks-2+S has been issued in full.
     // The loop is instantiated per number of live subtiles (1 .. MI); every instance
     // issues the same copies and barriers.
     const int live = __builtin_amdgcn_readfirstlane(
@@ -536,55 +535,12 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       __builtin_amdgcn_sched_barrier(0);
     }
     };
-    dispatch_live<MI>(live, ping_pong);
+    // The SwiGLU-backward op runs one instance over every subtile: with one instance
+    // per live count its register-heavy epilogue pushes spill reloads (and the waits
+    // for them, which also drain the copies in flight) into the K loop.
+    if constexpr (BWD) ping_pong(AllSub{});
+    else dispatch_live<MI>(live, ping_pong);
     if (!lag) __syncthreads();
-    } else {
-    // The SwiGLU-backward op keeps the one-barrier slice loop: its epilogue's register
-    // pressure spills a value that the ping-pong loop reloads every half-slice, and
-    // the wait for that reload also drains the copies in flight.
-    // Slice ks: two 16-deep halves, then a barrier once slice ks+1 has landed.  The
-    // barrier ending slice ks-1 freed its slot; slice ks-1+S refills it, the A copies
-    // spread between the first half's MFMAs and the B copies between the second's.
-    for (int ks = 0; ks < nk; ++ks) {
-      const int ksrc = min(ks - 1 + kStages, nk - 1);
-      const int slot = (ks + kStages - 1) % kStages;
-      read_frags(ks, 0, AllSub{});
-      if (ks > 0) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-            // A copy c goes after MFMA floor(c * MI * 4 / CPA)
-#pragma unroll
-            for (int c = 0; c < CPA; ++c)
-              if (c * MI * 4 / CPA == i * 4 + j) issue_a(ksrc, slot, c);
-          }
-        }
-      } else {
-        mfma_block(AllSub{});
-      }
-      read_frags(ks, 1, AllSub{});
-      if (ks > 0) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-            for (int c = 0; c < CPB; ++c)
-              if (c * MI * 4 / CPB == i * 4 + j) issue_b(ksrc, slot, c);
-          }
-        }
-      } else {
-        mfma_block(AllSub{});
-      }
-      if (ks + 1 < nk) {
-        MOE_WAIT_VMCNT((kStages - 2) * CPW);   // slice ks+1 has landed
-        __syncthreads();
-      }
-    }
-    }
     MOE_WAIT_VMCNT(0);  // no copy may land in the ring once it is reused below
     __syncthreads();
 
