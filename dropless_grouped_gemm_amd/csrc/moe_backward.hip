@@ -485,12 +485,23 @@ k_gg_wgrad(WgOperands ops, int Km, int Nn, const int32_t* __restrict__ counts,
       const int xb = rbase < cnt ? rbase : 0;
       const int lr = rbase + (lane >> 4) < cnt ? (lane >> 4) : 0;
       copy16_to_lds(xe + (size_t)xb * Km, (uint32_t)(lr * Km + mcol) * 2u, st + wave * 1024);
+      if (rbase + 4 <= cnt) {
+        // the four D rows as one group behind one M0 load: copy p lands at +1 KB p (the
+        // instruction's immediate moves both addresses), its global row is corrected
+        // through the lane offset against a base 3 KB below row rbase
+        set_lds_dma_base(st + kWgXBytes + 4 * wave * 1024);
+        const unsigned char* db = reinterpret_cast<const unsigned char*>(de + (size_t)rbase * Nn) - 3 * 1024;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int r = rbase + p;
-        const int rr = r < cnt ? r : 0;
-        copy16_to_lds(de + (size_t)rr * Nn, (uint32_t)ncol[p] * 2u,
-                      st + kWgXBytes + (4 * wave + p) * 1024);
+        for (int p = 0; p < 4; ++p)
+          copy16_to_lds_nth(p, db, (uint32_t)(p * Nn + ncol[p]) * 2u + (uint32_t)(3 - p) * 1024u);
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int r = rbase + p;
+          const int rr = r < cnt ? r : 0;
+          copy16_to_lds(de + (size_t)rr * Nn, (uint32_t)ncol[p] * 2u,
+                        st + kWgXBytes + (4 * wave + p) * 1024);
+        }
       }
     };
     // zero this wave's rows of slice s that lie past the count (after its copies landed)
