@@ -67,7 +67,7 @@ int wide_max_blocks() {
 // groups are dealt to the 8 XCDs in turn, so each XCD runs 32 consecutive items - one
 // supertile: a few A panels and B panels shared through that XCD's L2, instead of up to
 // 32 of each.
-__device__ __forceinline__ void wide_item(int slot, int ngt, int n_tiles, int& g, int& t) {
+__device__ __forceinline__ void wide_item_st(int slot, int ngt, int n_tiles, int& g, int& t) {
   const int Ts = min(n_tiles, 8);
   const int Gs = 32 / Ts;
   const int row_items = Gs * n_tiles;
@@ -77,6 +77,21 @@ __device__ __forceinline__ void wide_item(int slot, int ngt, int n_tiles, int& g
   const int tc = min(Ts, n_tiles - sc * Ts);
   g = sr * Gs + within / tc;
   t = sc * Ts + within % tc;
+}
+// The item order with a split last round: the first ngt - nsingle groups in supertiles,
+// then the nsingle single-block groups split off the list's end, group by group (their
+// items take the last round; consecutive items stay on one XCD, so a split group's three
+// singles share its weight panel there).
+__device__ __forceinline__ void wide_item(int slot, int ngt, int nsingle, int n_tiles, int& g,
+                                          int& t) {
+  const int main_items = (ngt - nsingle) * n_tiles;
+  if (slot < main_items) {
+    wide_item_st(slot, ngt - nsingle, n_tiles, g, t);
+  } else {
+    const int r = slot - main_items;
+    g = ngt - nsingle + r / n_tiles;
+    t = r - (r / n_tiles) * n_tiles;
+  }
 }
 
 // f(std::integral_constant<int, clamp(n, 1, N)>): one instance per count, so that code
@@ -130,8 +145,10 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
   // Built in the ring while it is idle: the table is staged at s_meta, then wave 0 forms
   // the groups into s_groups (lane l walks blocks [l*per, (l+1)*per); the run start that
   // governs its first block and its first output slot come from two wave-wide scans)
-  // and their number into *s_ngroups.  Every wave then keeps the entries of its next 64
+  // and their number into s_ngroups[0] (s_ngroups[1]: how many single-block groups the
+  // last-round split appended).  Every wave then keeps the entries of its next 64
   // work items in one register (lane j: item j), so the whole LDS holds the ring.
+  const int ng_dense = (dense_rows + kWRows - 1) / kWRows;
   int32_t* s_meta = reinterpret_cast<int32_t*>(lds);
   int32_t* s_groups = s_meta + 3 * nb;
   int32_t* s_ngroups = s_groups + nb;
@@ -186,14 +203,43 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
           s_groups[idx++] = (b << 2) | n;
         }
       }
-      if (lane == 63) *s_ngroups = inc;
+      if (lane == 63) {
+        // The last round of the persistent grid.  Items (group, column tile) cost about
+        // the same, so total items on G work groups take ceil(total / G) rounds and a
+        // short last round leaves most work groups idle.  Trailing three-block groups
+        // are split into single blocks (2 n_tiles more items each) when that adds no
+        // round and the last round then holds only single-block items (wide_item numbers
+        // the singles' items last), which multiply a third of the rows.  Each output
+        // row's sum is unchanged.
+        int ng = inc, nsingle = 0;
+        const int G = (int)gridDim.x;
+        const int total = (ng_dense + ng) * n_tiles;
+        const int F = total / G;
+        // (not in the SwiGLU-backward op: there the extra registers put a spill reload
+        // and a full wait into each item's first half-slice)
+        if (!BWD && total - F * G > 0) {
+          const int smax = ((F + 1) * G - total) / (2 * n_tiles);
+          int sp = 0;
+          while (sp < smax && sp < ng && (s_groups[ng - 1 - sp] & 3) == 3) ++sp;
+          if (sp > 0 && 3 * sp * n_tiles >= total + 2 * sp * n_tiles - F * G) {
+            for (int i = sp - 1; i >= 0; --i) {   // backwards: no entry overwritten unread
+              const int b = s_groups[ng - sp + i] >> 2;
+              for (int j2 = 2; j2 >= 0; --j2) s_groups[ng - sp + 3 * i + j2] = ((b + j2) << 2) | 1;
+            }
+            ng += 2 * sp;
+            nsingle = 3 * sp;
+          }
+        }
+        s_ngroups[0] = ng;
+        s_ngroups[1] = nsingle;
+      }
     }
     __syncthreads();
   };
   build_groups();
-  const int ngroups = __builtin_amdgcn_readfirstlane(*s_ngroups);
+  const int ngroups = __builtin_amdgcn_readfirstlane(s_ngroups[0]);
+  const int nsingle = __builtin_amdgcn_readfirstlane(s_ngroups[1]);
 
-  const int ng_dense = (dense_rows + kWRows - 1) / kWRows;
   const int total = (ng_dense + ngroups) * n_tiles;
   const int nk = K / kWBK;
 
@@ -254,13 +300,13 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       if (j > 0) build_groups();   // the ring is idle between items
       const int wl = q + (j + lane) * gridDim.x;
       int gl_g = 0, gl_t = 0;
-      if (wl < total) wide_item(wl, ngt, n_tiles, gl_g, gl_t);
+      if (wl < total) wide_item(wl, ngt, nsingle, n_tiles, gl_g, gl_t);
       const int gl = gl_g - ng_dense;
       my_groups = (wl < total && gl >= 0) ? s_groups[gl] : 0;
       __syncthreads();             // every wave has its entries before the ring refills
     }
     int gidx, nt;
-    wide_item(w, ngt, n_tiles, gidx, nt);
+    wide_item(w, ngt, nsingle, n_tiles, gidx, nt);
     const bool in_dense = gidx < ng_dense;
     int e, m0, valid;
     if (in_dense) {

@@ -237,6 +237,56 @@ def wide_groups_serial(meta, nb, E, max_rows, GB=3):
     return [tuple(x) for x in out]
 
 
+def wide_split_tail(groups, ng_dense, n_tiles, G):
+    """The group list after wide_build_groups' last-round split: trailing three-block
+    groups become single blocks when that adds no round of the persistent grid (G work
+    groups) and the last round then holds only single-block items."""
+    groups = list(groups)
+    ng = len(groups)
+    total = (ng_dense + ng) * n_tiles
+    F = total // G
+    if total - F * G == 0:
+        return groups, 0
+    smax = ((F + 1) * G - total) // (2 * n_tiles)
+    sp = 0
+    while sp < smax and sp < ng and groups[ng - 1 - sp][1] == 3:
+        sp += 1
+    if sp == 0 or 3 * sp * n_tiles < total + 2 * sp * n_tiles - F * G:
+        return groups, 0
+    tail = [(b + j, 1) for b, _ in groups[ng - sp:] for j in range(3)]
+    return groups[:ng - sp] + tail, sp
+
+
+def check_wide_split_tail(groups, ng_dense, n_tiles, G):
+    """The split keeps every block once, in order, adds no round, and (when it splits)
+    leaves only split single-block items in the last round."""
+    new, sp = wide_split_tail(groups, ng_dense, n_tiles, G)
+    blocks = lambda gl: [b + j for b, n in gl for j in range(n)]
+    assert blocks(new) == blocks(groups)
+    total, total2 = (ng_dense + len(groups)) * n_tiles, (ng_dense + len(new)) * n_tiles
+    assert -(-total2 // G) == -(-total // G)
+    ngt = ng_dense + len(new)
+    seen = set()
+    for w in range(total2):                               # every (group, tile) once
+        seen.add(wide_item_split(w, ngt, 3 * sp, n_tiles))
+    assert len(seen) == total2
+    if sp:
+        first_split = ngt - 3 * sp                        # group index of the first single
+        for w in range((total2 - 1) // G * G, total2):    # the last round
+            g, _ = wide_item_split(w, ngt, 3 * sp, n_tiles)
+            assert g >= first_split and new[g - ng_dense][1] == 1, (w, g, first_split)
+    return new, sp
+
+
+def wide_item_split(slot, ngt, nsingle, n_tiles):
+    """wide_item with nsingle trailing single-block groups numbered last, group-major."""
+    main = (ngt - nsingle) * n_tiles
+    if slot < main:
+        return wide_item(slot, ngt - nsingle, n_tiles)
+    r = slot - main
+    return ngt - nsingle + r // n_tiles, r % n_tiles
+
+
 def wide_item(slot, ngt, n_tiles):
     Ts = min(n_tiles, 8)
     Gs = 32 // Ts

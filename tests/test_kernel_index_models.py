@@ -188,3 +188,27 @@ def test_fp8d_split_last_round(G):
             KM.check_fp8d_tail(R, nk, G)
     assert not KM.fp8d_tail_plan(1610, 257)[2]          # grids past the scratch's slots
     assert not KM.fp8d_tail_plan(1610, 256, fits=False)[2]
+
+
+def test_wide_split_last_round():
+    """The 384-row kernel's last-round split on random group lists, grids and column
+    tile counts, and on the down launch of the fusedmoe workload's routing (3,136 items,
+    12.25 rounds of 256: three trailing groups become nine single blocks)."""
+    rng = np.random.default_rng(11)
+    for _ in range(3000):
+        ng = int(rng.integers(1, 200))
+        groups, b = [], 0
+        for _ in range(ng):
+            n = int(rng.choice([1, 2, 3], p=[0.1, 0.1, 0.8]))
+            groups.append((b, n))
+            b += n + int(rng.integers(0, 2))
+        KM.check_wide_split_tail(groups, int(rng.integers(0, 4)), int(rng.integers(1, 40)),
+                                 int(rng.choice([1, 3, 8, 24, 64, 256])))
+    # fusedmoe down: 22 dense groups + 90 routed, 28 column tiles, 256 work groups
+    routed = [(3 * i, 3) for i in range(90)]
+    new, sp = KM.check_wide_split_tail(routed, 22, 28, 256)
+    assert sp == 3 and len(new) == 96
+    # no split where the items fill whole rounds, or where a single round would not hold
+    # only singles
+    assert KM.wide_split_tail([(3 * i, 3) for i in range(64)], 0, 16, 256)[1] == 0
+    assert KM.wide_split_tail([(3 * i, 3) for i in range(173)], 0, 16, 256)[1] == 0
