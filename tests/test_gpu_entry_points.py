@@ -502,6 +502,69 @@ def test_wide_tiles_short_k(d, d_e, cap, monkeypatch):
     assert_close(f64(act)[vn], act_ref[vn], TOL_STAGE["bf16"], "act")
 
 
+def _random_wide_cases(n=24, seed=2024):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([32, 64, 96, 256, 544, 1024]))
+        d_e = int(rng.choice([32, 96, 128, 200, 384]))
+        E = int(rng.integers(1, 9))
+        k = int(rng.integers(1, min(E, 4) + 1))
+        T = int(rng.integers(200, 3000))
+        cap = str(rng.choice(["0", "0", "1", "5", "8", "37"]))
+        cases.append((i, T, d, E, k, d_e, cap))
+    return cases
+
+
+@pytest.mark.parametrize("i,T,d,E,k,d_e,cap", _random_wide_cases())
+def test_wide_tiles_random_shapes(i, T, d, E, k, d_e, cap, monkeypatch):
+    """Seeded random shapes, routings and persistent-grid caps: the 384-row kernel
+    (gathered gate/up, then down) matches the 128-row kernel bit for bit, whatever the
+    group sizes, K, column tails, last-round split and item order."""
+    rng = np.random.default_rng(1000 + i)
+    # skewed routing, so that groups of one, two and three blocks all occur
+    p = rng.dirichlet(np.full(E, 0.7))
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
+    dt = torch.bfloat16
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77 + i)
+    x = torch.randn((T, d), generator=g, device=DEV).to(dt)
+    w1 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w3 = (torch.randn((E, d, d_e), generator=g, device=DEV) / d ** 0.5).to(dt)
+    w2 = (torch.randn((E, d_e, d), generator=g, device=DEV) / d_e ** 0.5).to(dt)
+    s = B.make_shape(T=T, d=d, E=E, k=k, d_e=d_e, block_m=128, dtype="bf16")
+    mb, rows = B.moe_max_blocks(s), B.moe_max_rows(s)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=DEV)
+    d_idx = torch.from_numpy(idx.astype(np.int32).reshape(-1)).to(DEV)
+    counts, offs, pad, meta, nblk, pos, row_src, err = (i32(E), i32(E + 1), i32(E + 1), i32(3 * mb),
+                                                         i32(1), i32(T * k), i32(rows), i32(1))
+    B.moe_build_offsets(s, d_idx, counts, offs, pad, meta, nblk, pos, row_src, err,
+                        B.alloc_workspace(s))
+    e = lambda *sh: torch.full(sh, -5.0, dtype=dt, device=DEV)
+    act, y, act2, y2 = e(rows, d_e), e(rows, d), e(rows, d_e), e(rows, d)
+    print(f"[wide random {i}] T={T} d={d} E={E} k={k} d_e={d_e} cap={cap}", flush=True)
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", "384")
+    if cap != "0":
+        monkeypatch.setenv("MOE_GG_GRID_CAP", cap)
+    B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act, w2, None, meta, nblk, mb, y)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MOE_GG_TILE_ROWS", "128")
+    monkeypatch.delenv("MOE_GG_GRID_CAP", raising=False)
+    B.moe_grouped_gemm_gather(s, x, row_src, w1, w3, meta, nblk, mb, act2)
+    B.moe_grouped_gemm(s, B.MOE_OP_DOWN, act2, w2, None, meta, nblk, mb, y2)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    src = O.permutation(idx, E, 128)[1]
+    valid = torch.from_numpy(np.nonzero(src >= 0)[0]).to(DEV)
+    assert torch.equal(act[valid].view(torch.int16), act2[valid].view(torch.int16))
+    assert torch.equal(y[valid].view(torch.int16), y2[valid].view(torch.int16))
+    # pad rows are never written
+    padr = torch.from_numpy(np.nonzero(src < 0)[0]).to(DEV)
+    if len(padr):
+        assert torch.all(act[padr] == -5.0) and torch.all(y[padr] == -5.0)
+
+
 def test_combine_skips_negative_positions():
     T, d, k = 8, 64, 2
     s = B.make_shape(T=T, d=d, E=4, k=k, d_e=64, block_m=128)
