@@ -301,6 +301,28 @@ def test_fp8_split_last_round(T, d, E, k, d_e, d_es, skew, monkeypatch):
     oracle at the stage bound, within bf16 rounding of the whole-item run, and bitwise the
     same when repeated; a table with a block of more than 64 rows runs whole items,
     bitwise as without scratch."""
+    _check_fp8_split(T, d, E, k, d_e, d_es, skew, monkeypatch, expect_split=not skew)
+
+
+def _random_fp8_split_cases(n=12, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.integers(8, 97))
+        k = int(rng.integers(1, min(8, E) + 1))
+        out.append((int(rng.integers(1, 65)), int(rng.choice([256, 512, 768, 1024])), E, k,
+                    int(rng.choice([128, 256, 384])), int(rng.choice([0, 0, 128]))))
+    return out
+
+
+@pytest.mark.parametrize("T,d,E,k,d_e,d_es", _random_fp8_split_cases())
+def test_fp8_split_last_round_random(T, d, E, k, d_e, d_es, monkeypatch):
+    """Seeded random decode shapes through the 64-row kernel with and without scratch:
+    whichever of whole and split items the plan picks, the same checks as above."""
+    _check_fp8_split(T, d, E, k, d_e, d_es, False, monkeypatch, expect_split=None)
+
+
+def _check_fp8_split(T, d, E, k, d_e, d_es, skew, monkeypatch, expect_split):
     monkeypatch.setenv("MOE_FP8_ITEM_ROWS", "64")
     rng = np.random.default_rng(T * 7 + E)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
@@ -376,7 +398,7 @@ def test_fp8_split_last_round(T, d, E, k, d_e, d_es, skew, monkeypatch):
         if not fits:
             assert not on
             assert torch.equal(out_s[dv].view(torch.int16), out_w[dv].view(torch.int16))
-        elif skew is False:
+        elif expect_split:
             assert on, (op, nb, n_tiles, G)
         # the split changes only the order of fp32 partial sums: bf16 rounding apart
         a, b = f64(out_s[dv]), f64(out_w[dv])
