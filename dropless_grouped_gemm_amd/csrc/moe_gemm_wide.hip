@@ -541,7 +541,55 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         [&] { int n = 0; for (int i = 0; i < MI; ++i) n += rsub(i) < valid; return n; }());
     const bool lag = wave >= kWideLagFrom;
     if (lag) __syncthreads();
-    auto ping_pong = [&](auto nl_c) {
+    // One half-slice: MEM(2 ks + KK), barrier, MFMA(2 ks + KK), barrier.  KK and the
+    // first slice are compile-time, so the steady state branches only on the lag and at
+    // the end of each slice.
+    auto half = [&](int ks, auto kk_c, auto first_c, auto nl_c) {
+      constexpr int KK = decltype(kk_c)::value;
+      constexpr bool FIRST = decltype(first_c)::value;
+      // the refill of slice ks-1's slot (after every wave's last read of slice ks-1):
+      // the A copies in the first half's memory phase, the B copies in the second
+      // half's (measured faster for both ops than all copies in the first half, for
+      // gate/up once its barriers stopped waiting for the fragment reads)
+      const int ksrc = min(ks - 1 + kStages, nk - 1);
+      const int slot = (ks + kStages - 1) % kStages;
+      if constexpr (KK == 0) {
+        if constexpr (FIRST) {
+          MOE_WAIT_VMCNT((kStages - 2) * CPW);   // slice 1 has landed
+        } else {
+          MOE_WAIT_VMCNT((kStages - 3) * CPW);   // slice ks+1 has landed
+#pragma unroll
+          for (int i = 0; i < CPA; ++i) issue_a(ksrc, slot, i);
+        }
+      } else if constexpr (!FIRST) {
+#pragma unroll
+        for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
+      }
+      read_frags(ks, KK, nl_c);
+      // scheduling barriers keep each phase's instructions on its side of the barriers
+      __builtin_amdgcn_sched_barrier(0);
+      // The barrier after a memory phase does not wait for the phase's fragment reads
+      // (the MFMAs wait for their operands), so the other wave on the SIMD starts its
+      // memory phase under them, except where a refill follows: the lagging waves'
+      // second-half reads are the last reads of slice ks, whose slot the other waves
+      // refill right after this barrier (MEM(2 ks + 2)).  The other waves' reads of a
+      // slice complete before their own MFMA phase, before the barrier ahead of any
+      // refill of that slot.
+      if constexpr (KK == 1) {
+        if (lag) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(nl_c);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    // The same schedule with the half and the first slice decided at run time (one
+    // loop body).
+    auto ping_pong_rt = [&](auto nl_c) {
     for (int t = 0; t < 2 * nk; ++t) {
       const int ks = t >> 1, kk = t & 1;
       // the refill of slice ks-1's slot (after every wave's last read of slice ks-1):
@@ -580,6 +628,22 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
+    };
+    // The bf16 forward ops run the first slice on its own and then both halves of each
+    // slice with no branch between them.  The fp8 and SwiGLU-backward ops keep one loop
+    // over half-slices: with the duplicated first slice their register allocation puts
+    // spill reloads into the loop.
+    auto ping_pong = [&](auto nl_c) {
+      if constexpr (!FP8 && !BWD) {
+        half(0, K0{}, std::true_type{}, nl_c);
+        half(0, K1{}, std::true_type{}, nl_c);
+        for (int ks = 1; ks < nk; ++ks) {
+          half(ks, K0{}, std::false_type{}, nl_c);
+          half(ks, K1{}, std::false_type{}, nl_c);
+        }
+      } else {
+        ping_pong_rt(nl_c);
+      }
     };
     // The SwiGLU-backward op runs one instance over every subtile: with one instance
     // per live count its register-heavy epilogue pushes spill reloads (and the waits
