@@ -546,7 +546,10 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     // the end of each slice.
     auto half = [&](int ks, auto kk_c, auto first_c, auto nl_c) {
       constexpr int KK = decltype(kk_c)::value;
-      constexpr bool FIRST = decltype(first_c)::value;
+      // first_c: std::true_type / std::false_type, or a bool decided at run time
+      bool first;
+      if constexpr (std::is_same_v<decltype(first_c), bool>) first = first_c;
+      else first = decltype(first_c)::value;
       // the refill of slice ks-1's slot (after every wave's last read of slice ks-1):
       // the A copies in the first half's memory phase, the B copies in the second
       // half's (measured faster for both ops than all copies in the first half, for
@@ -554,14 +557,14 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
       const int ksrc = min(ks - 1 + kStages, nk - 1);
       const int slot = (ks + kStages - 1) % kStages;
       if constexpr (KK == 0) {
-        if constexpr (FIRST) {
+        if (first) {
           MOE_WAIT_VMCNT((kStages - 2) * CPW);   // slice 1 has landed
         } else {
           MOE_WAIT_VMCNT((kStages - 3) * CPW);   // slice ks+1 has landed
 #pragma unroll
           for (int i = 0; i < CPA; ++i) issue_a(ksrc, slot, i);
         }
-      } else if constexpr (!FIRST) {
+      } else if (!first) {
 #pragma unroll
         for (int c = 0; c < CPB; ++c) issue_b(ksrc, slot, c);
       }
@@ -630,9 +633,10 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
     }
     };
     // The bf16 forward ops run the first slice on its own and then both halves of each
-    // slice with no branch between them.  The fp8 and SwiGLU-backward ops keep one loop
-    // over half-slices: with the duplicated first slice their register allocation puts
-    // spill reloads into the loop.
+    // slice with no branch between them.  The SwiGLU-backward op unrolls the two halves
+    // but tests for the first slice at run time, and the fp8 ops keep one loop over
+    // half-slices: with the duplicated first slice their register allocation puts spill
+    // reloads into the loop.
     auto ping_pong = [&](auto nl_c) {
       if constexpr (!FP8 && !BWD) {
         half(0, K0{}, std::true_type{}, nl_c);
@@ -640,6 +644,11 @@ k_gg_wide(GGOperands routed, GGOperands dense, int K, int N,
         for (int ks = 1; ks < nk; ++ks) {
           half(ks, K0{}, std::false_type{}, nl_c);
           half(ks, K1{}, std::false_type{}, nl_c);
+        }
+      } else if constexpr (BWD) {
+        for (int ks = 0; ks < nk; ++ks) {
+          half(ks, K0{}, ks == 0, nl_c);
+          half(ks, K1{}, ks == 0, nl_c);
         }
       } else {
         ping_pong_rt(nl_c);
